@@ -1,0 +1,191 @@
+"""Pins of the oracle's per-head max logit and QK-Clip (no GPU)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _int_inputs(rng, B, H, S, dc, dr):
+    Q = rng.integers(-6, 7, (B, H, S, dc + dr)).astype(np.float64)
+    Kc = rng.integers(-6, 7, (B, H, S, dc)).astype(np.float64)
+    Kr = rng.integers(-6, 7, (B, S, dr)).astype(np.float64) if dr else None
+    return Q, Kc, Kr
+
+
+@pytest.mark.parametrize("dr", [0, 2])
+def test_max_logit_equals_bruteforce_bitwise(rng, dr):
+    # Integer inputs make every fp64 dot product exact, so the blocked oracle
+    # and the pure-Python triple loop must agree bit for bit.
+    Q, Kc, Kr = _int_inputs(rng, 2, 3, 8, 4, dr)
+    got = oracle.max_logit(Q, Kc, Kr, block=3)
+    ref = oracle.max_logit_bruteforce(Q, Kc, Kr)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_max_logit_uses_shared_rotary_key(rng):
+    # Changing only Kr must change the result (it is part of every head's key);
+    # dropping it (MHA form) must give the nope-only logits.
+    Q, Kc, Kr = _int_inputs(rng, 1, 2, 6, 4, 2)
+    full = oracle.max_logit(Q, Kc, Kr)
+    Kr2 = Kr.copy()
+    Kr2[0, 0] += 50.0
+    assert np.all(oracle.max_logit(Q, Kc, Kr2) != full)
+    nope = oracle.max_logit(Q[..., :4], Kc, None) * math.sqrt(4) / math.sqrt(6)
+    manual = max(float((Q[0, h, :, :4] @ Kc[0, h].T).max()) for h in range(1)) / math.sqrt(6)
+    assert nope[0] == pytest.approx(manual, rel=1e-15)
+
+
+def test_max_logit_closed_form():
+    # Q_i = c e_{i}, K_j = c e_{j+1}: the only non-zero logits are c^2 (i = j+1),
+    # so S = c^2 / sqrt(d).  With all keys negated every logit is <= 0 and the
+    # signed max is 0, not c^2 (no absolute value in the definition).
+    d, S, c = 16, 8, 3.0
+    Q = np.zeros((1, 1, S, d))
+    K = np.zeros((1, 1, S, d))
+    for i in range(S):
+        Q[0, 0, i, i] = c
+        K[0, 0, i, i + 1] = c
+    assert oracle.max_logit(Q, K)[0] == c * c / math.sqrt(d)
+    assert oracle.max_logit(Q, -K)[0] == 0.0
+    Kneg = -np.ones((1, 1, S, d))
+    Qpos = np.ones((1, 1, S, d))
+    assert oracle.max_logit(Qpos, Kneg)[0] == -d / math.sqrt(d)
+
+
+def test_max_logit_over_batch_is_max_of_parts(rng):
+    Q, Kc, Kr = _int_inputs(rng, 3, 2, 5, 4, 2)
+    whole = oracle.max_logit(Q, Kc, Kr)
+    parts = np.max([oracle.max_logit(Q[b:b + 1], Kc[b:b + 1], Kr[b:b + 1]) for b in range(3)], axis=0)
+    np.testing.assert_array_equal(whole, parts)
+
+
+def test_max_logit_nan_handling(rng):
+    Q, Kc, Kr = _int_inputs(rng, 1, 2, 4, 4, 0)
+    clean = oracle.max_logit(Q, Kc, None)
+    Qn = Q.copy()
+    Qn[0, 0, 1, 2] = np.nan  # one NaN row of logits in head 0 is ignored
+    got = oracle.max_logit(Qn, Kc, None)
+    assert got[1] == clean[1]
+    assert got[0] == oracle.max_logit_bruteforce(Qn, Kc, None)[0]
+    Qn[0, 1] = np.nan  # every logit of head 1 is NaN -> -inf
+    assert oracle.max_logit(Qn, Kc, None)[1] == -np.inf
+
+
+# ------------------------------------------------------------------ clip ----
+def _mla_weights(rng, H, dc, dr, d_in):
+    Wq = rng.standard_normal((H * (dc + dr), d_in))
+    Wkc = rng.standard_normal((H * dc, d_in))
+    Wkr = rng.standard_normal((dr, d_in))
+    return Wq, Wkc, Wkr
+
+
+def _mla_qk(X, Wq, Wkc, Wkr, H):
+    Q = oracle.project_heads(X, Wq, H)
+    Kc = oracle.project_heads(X, Wkc, H)
+    Kr = oracle.project_heads(X, Wkr, 1)[:, 0]
+    return Q, Kc, Kr
+
+
+def test_clip_brings_clipped_heads_to_tau_mla(rng):
+    # S recomputed on the clipped weights (same X, same weights S was measured
+    # on) equals tau for clipped heads: every logit of a clipped head is scaled
+    # by exactly gamma (sqrt(gamma) sqrt(gamma) on the nope part, gamma x 1 on
+    # the rotary part).  Unclipped heads and the shared rotary key are unchanged.
+    H, dc, dr, d_in = 4, 8, 4, 16
+    X = rng.standard_normal((2, 10, d_in))
+    Wq, Wkc, Wkr = _mla_weights(rng, H, dc, dr, d_in)
+    Wq[: dc + dr] *= 20.0  # head 0 far over tau
+    Wkc[:dc] *= 20.0
+    Q, Kc, Kr = _mla_qk(X, Wq, Wkc, Wkr, H)
+    S = oracle.max_logit(Q, Kc, Kr)
+    tau = float(np.sort(S)[-2]) * 1.5  # only head 0 above tau
+    Wq2, Wkc2, gamma, clipped = oracle.qk_clip(S, Wq, Wkc, dc + dr, dc, dc, tau=tau, w_dtype="f64")
+    assert list(clipped) == [1, 0, 0, 0]
+    Q2, Kc2, Kr2 = _mla_qk(X, Wq2, Wkc2, Wkr, H)
+    S2 = oracle.max_logit(Q2, Kc2, Kr2)
+    assert S2[0] == pytest.approx(tau, rel=1e-12)
+    np.testing.assert_array_equal(S2[1:], S[1:])
+    np.testing.assert_array_equal(Wq2[dc + dr:], Wq[dc + dr:])
+    np.testing.assert_array_equal(Wkc2[dc:], Wkc[dc:])
+    # every logit of head 0 scales by gamma
+    full = Q[0, 0] @ np.concatenate([Kc[0, 0], Kr[0]], 1).T
+    full2 = Q2[0, 0] @ np.concatenate([Kc2[0, 0], Kr2[0]], 1).T
+    np.testing.assert_allclose(full2, gamma[0] * full, rtol=1e-12, atol=1e-12)
+
+
+def test_clip_exact_when_gamma_is_power_of_four(rng):
+    # gamma = 1/4: sqrt(gamma) = 1/2 and gamma are exact, so the clipped weights
+    # and the recomputed max are exact in fp64.
+    H, dc, dr, d_in = 2, 4, 4, 8
+    Wq = rng.integers(-8, 9, (H * (dc + dr), d_in)).astype(np.float64)
+    Wkc = rng.integers(-8, 9, (H * dc, d_in)).astype(np.float64)
+    smax = np.array([400.0, 50.0])
+    Wq2, Wkc2, gamma, clipped = oracle.qk_clip(smax, Wq, Wkc, dc + dr, dc, dc, tau=100.0, w_dtype="f64")
+    assert gamma[0] == 0.25 and list(clipped) == [1, 0]
+    np.testing.assert_array_equal(Wq2[:dc], Wq[:dc] * 0.5)
+    np.testing.assert_array_equal(Wq2[dc:dc + dr], Wq[dc:dc + dr] * 0.25)
+    np.testing.assert_array_equal(Wkc2[:dc], Wkc[:dc] * 0.5)
+    np.testing.assert_array_equal(Wq2[dc + dr:], Wq[dc + dr:])
+
+
+def test_clip_mha_general_alpha(rng):
+    # MHA: W_q^h x gamma^alpha, W_k^h x gamma^(1-alpha); the logits of head h
+    # scale by gamma for any alpha.
+    H, dh, d_in = 3, 4, 12
+    X = rng.standard_normal((1, 6, d_in))
+    Wq = rng.standard_normal((H * dh, d_in))
+    Wk = rng.standard_normal((H * dh, d_in))
+    smax = np.array([250.0, 80.0, 1000.0])
+    for alpha in (0.5, 0.3, 1.0):
+        Wq2, Wk2, gamma, clipped = oracle.qk_clip(smax, Wq, Wk, dh, dh, dh, tau=100.0, alpha=alpha,
+                                                  w_dtype="f64")
+        assert list(clipped) == [1, 0, 1]
+        for h in range(H):
+            L = oracle.project_heads(X, Wq, H)[0, h] @ oracle.project_heads(X, Wk, H)[0, h].T
+            L2 = oracle.project_heads(X, Wq2, H)[0, h] @ oracle.project_heads(X, Wk2, H)[0, h].T
+            np.testing.assert_allclose(L2, gamma[h] * L, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(Wq2[dh:2 * dh], Wq[dh:2 * dh])
+
+
+def test_clip_tie_nan_and_unclipped_bitwise(rng):
+    Wq = oracle.round_to_bf16(rng.standard_normal((4 * 6, 8)) * 0.02)
+    Wk = oracle.round_to_bf16(rng.standard_normal((4 * 4, 8)) * 0.02)
+    smax = np.array([100.0, np.nan, -5.0, 100.0000001])
+    Wq2, Wk2, gamma, clipped = oracle.qk_clip(smax, Wq, Wk, 6, 4, 4, tau=100.0)
+    assert list(clipped) == [0, -1, 0, 1]  # tie at tau is not clipped; NaN flagged
+    np.testing.assert_array_equal(Wq2[:18], Wq[:18])
+    np.testing.assert_array_equal(Wk2[:12], Wk[:12])
+    assert gamma[3] == 100.0 / 100.0000001
+
+
+def test_clip_rounds_once_to_bf16(rng):
+    Wq = oracle.round_to_bf16(rng.standard_normal((6, 32)) * 0.02)
+    Wk = oracle.round_to_bf16(rng.standard_normal((4, 32)) * 0.02)
+    smax = np.array([523.25])
+    Wq2, Wk2, gamma, _ = oracle.qk_clip(smax, Wq, Wk, 6, 4, 4, tau=100.0)
+    g = 100.0 / 523.25
+    np.testing.assert_array_equal(Wq2[:4], oracle.round_to_bf16(Wq[:4] * math.sqrt(g)))
+    np.testing.assert_array_equal(Wq2[4:], oracle.round_to_bf16(Wq[4:] * g))
+    np.testing.assert_array_equal(Wk2, oracle.round_to_bf16(Wk * math.sqrt(g)))
+
+
+def test_full_step_composition(rng):
+    # One step = momentum, NS x scale, decoupled-decay update for every matrix,
+    # then QK-Clip on the updated attention weights (Algorithm 1 order).
+    H, dh, d_in = 2, 4, 8
+    W = {n: oracle.round_to_bf16(rng.standard_normal((H * dh, d_in)) * 0.1) for n in ("q", "k", "v")}
+    G = {n: (rng.standard_normal((H * dh, d_in)) * 1e-3).astype(np.float32) for n in W}
+    att = dict(q="q", k="k", q_rows_per_head=dh, q_c_rows=dh, k_rows_per_head=dh)
+    smax = np.array([300.0, 10.0])
+    new_w, new_m, gamma, clipped = oracle.muonclip_step(W, G, {}, smax, att, lr=0.02)
+    for n in W:
+        np.testing.assert_array_equal(new_m[n], G[n])  # M_0 = 0 -> M_1 = G
+    Wv = oracle.apply_update(W["v"], oracle.muon_orthogonalised_update(G["v"].astype(np.float64)), 0.02)
+    np.testing.assert_array_equal(new_w["v"], Wv)
+    Wq1 = oracle.apply_update(W["q"], oracle.muon_orthogonalised_update(G["q"].astype(np.float64)), 0.02)
+    np.testing.assert_array_equal(new_w["q"][:dh], oracle.round_to_bf16(Wq1[:dh] * math.sqrt(1 / 3)))
+    np.testing.assert_array_equal(new_w["q"][dh:], Wq1[dh:])
+    assert list(clipped) == [1, 0]
