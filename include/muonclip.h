@@ -1,0 +1,209 @@
+/*
+ * muonclip.h - C ABI of libmuonclip.so, the MuonClip optimizer step on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The step (Algorithm 1 of "Kimi K2 内部机制", the Kimi K2 internals deep
+ * dive, MuonClip section; the muonclip_step pseudocode of "Kimi K2: Open
+ * Agentic Intelligence", paper notes section 3.2) is split into the calls
+ * below.  A training loop calls, per step:
+ *
+ *   muonclip_momentum              M <- mu M + G              (every matrix)
+ *   muon_ns_orthogonalize_batched  O <- NewtonSchulz(M) * s   (per shape group)
+ *   muon_apply_update              W <- W - eta (O + lambda W)
+ *   qk_maxlogit                    S_max^h from the forward's Q, K
+ *   qk_clip_apply                  rescale W_q / W_k rows of heads over tau
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller, except
+ *    `coeffs` of muon_ns_orthogonalize_batched, which is host memory.  The
+ *    library never allocates device memory; scratch space is a caller
+ *    workspace whose size a query function returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls enqueue work on it and return without synchronising.
+ *  - Argument errors are reported before anything is enqueued, and then no
+ *    output is touched.  A failed launch returns MC_EHIP; the stream's work
+ *    is then undefined.  No C++ exception crosses the ABI.
+ *  - The library holds no mutable global state: calls on different streams
+ *    may run concurrently as long as their buffers do not overlap.
+ *  - Element counts and strides are in elements, not bytes.  Pointers must be
+ *    aligned to their element size; wider alignment enables vector paths.
+ *  - Dtypes: MC_F32 = IEEE binary32, MC_BF16 = bfloat16 (top half of binary32).
+ *    Rounding to bf16 is round-to-nearest-even.
+ */
+#ifndef MUONCLIP_H
+#define MUONCLIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MC_ABI_VERSION 1
+
+/* Entry points are the only symbols the library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MC_API __attribute__((visibility("default")))
+#else
+#define MC_API
+#endif
+
+typedef enum mc_status {
+  MC_OK = 0,
+  MC_EINVAL = 1,     /* null pointer, negative size, bad scalar (NaN lr, steps <= 0 ...) */
+  MC_ESHAPE = 2,     /* shape outside what the call supports */
+  MC_EDTYPE = 3,     /* dtype code not supported by the call */
+  MC_EALIGN = 4,     /* pointer not aligned to its element size */
+  MC_EWORKSPACE = 5, /* workspace missing or smaller than the query function's size */
+  MC_EHIP = 6        /* a HIP runtime call or kernel launch failed */
+} mc_status_t;
+
+typedef enum mc_dtype { MC_F32 = 0, MC_BF16 = 1 } mc_dtype_t;
+
+/* MC_ABI_VERSION of the loaded library. */
+MC_API int mc_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+MC_API const char* mc_status_string(int status);
+
+/*
+ * Momentum accumulation: M <- fl32(fl32(mu * M) + G), element-wise, in place.
+ *
+ * Defined by Algorithm 1 of the internals deep dive (M_t = mu M_{t-1} + G_t,
+ * M_0 = 0) and the paper-notes pseudocode, which performs it as a scale of M
+ * followed by an add of G: two float32 roundings, never a fused multiply-add,
+ * so the result is bit-identical to float32 multiply-then-add.
+ *
+ *   M      device float32[numel], read and written
+ *   G      device float32[numel], read
+ *   numel  >= 0 (0 enqueues nothing); several matrices may be passed as one
+ *          flat concatenated buffer, since the op is element-wise
+ *   mu     momentum (0.95 on the pages), used as given in float32
+ * Errors: MC_EINVAL (null pointer with numel > 0, numel < 0), MC_EALIGN.
+ */
+MC_API mc_status_t muonclip_momentum(float* M, const float* G, int64_t numel, float mu, void* stream);
+
+/*
+ * Workspace bytes that muon_ns_orthogonalize_batched needs for `batch`
+ * matrices of rows x cols.  Returns 0 for invalid sizes.
+ */
+MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+/*
+ * Batched Newton-Schulz orthogonalisation with the Muon output scale:
+ *   O_b = out_scale * NS(M_b)      for b in [0, batch)
+ * where, for one matrix M (rows x cols):
+ *   X_0 = M / (||M||_F + eps), taken as its transpose when rows > cols
+ *         (n = min(rows, cols) rows, m = max(rows, cols) columns);
+ *   for s in [0, steps): A = X X^T; B = b_s A + c_s A A; X <- a_s X + B X;
+ *   NS(M) = X (transposed back when rows > cols).
+ * The pages define O_t = NewtonSchulz(M_t) * sqrt(max(n, m)) * 0.2 (Algorithm 1
+ * of the internals deep dive; msign in the Zhihu thread's MuonClip formula) and
+ * describe Newton-Schulz only as a few iterations of an odd polynomial driving
+ * the singular values toward 1 ("Kimi K2, explained.", Muon update bullets).
+ * The polynomial coefficients, the step count and the Frobenius pre-scale are
+ * not on the pages and are arguments here.  Pass out_scale =
+ * sqrt(max(rows, cols)) * 0.2 for the pages' step.
+ *
+ * Arithmetic: the norm is accumulated in float32 (combined in double); X, A
+ * and B are held in bfloat16 between the GEMMs, which run on bf16 MFMA with
+ * float32 accumulation; each polynomial epilogue is float32, rounded once.
+ *
+ *   M              device, m_dtype (MC_F32 or MC_BF16); matrix b starts at
+ *                  element b * m_batch_stride and is row-major rows x cols
+ *   O              device, o_dtype, same layout with o_batch_stride; O may be
+ *                  the same buffer as M when dtypes and strides match
+ *   steps          1..64; coeffs: host float[steps][3] = (a_s, b_s, c_s)
+ *   eps            >= 0; out_scale: any finite value
+ *   workspace      device, >= muon_ns_workspace_bytes(batch, rows, cols)
+ *                  bytes, 256-byte aligned; contents on entry are ignored
+ *   gemm_events    NULL, or host array of 6 * steps hipEvent_t (as void*):
+ *                  events[2*(3s+g)] and events[2*(3s+g)+1] are recorded on
+ *                  `stream` right before and after GEMM g of step s
+ *                  (g = 0: X X^T, 1: b A + c A A, 2: a X + B X), for timing
+ * Sizes: batch >= 0 (0 enqueues nothing); 1 <= rows, cols; min(rows, cols)
+ * <= 16384 and max(rows, cols) <= 65536.
+ * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EWORKSPACE, MC_EHIP.
+ */
+MC_API mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t batch, int64_t rows,
+                                          int64_t cols, int64_t m_batch_stride, void* O, int o_dtype,
+                                          int64_t o_batch_stride, int32_t steps, const float* coeffs,
+                                          float eps, float out_scale, void* workspace,
+                                          size_t workspace_bytes, void* stream,
+                                          void* const* gemm_events);
+
+/*
+ * Decoupled weight-decay update: W <- W - lr * (O + weight_decay * W),
+ * element-wise, in place (Algorithm 1 of the internals deep dive; the
+ * paper-notes pseudocode W.add_(O + weight_decay * W, alpha=-lr)).
+ * Computed in float32 as t = weight_decay * W; u = O + t; v = lr * u;
+ * W' = W - v (no fused multiply-add), rounded once to W's dtype.
+ *
+ *   W      device, w_dtype (MC_F32 or MC_BF16), numel elements
+ *   O      device, o_dtype (MC_F32 or MC_BF16), numel elements, same layout
+ *   numel  >= 0; lr, weight_decay finite
+ * Errors: MC_EINVAL, MC_EDTYPE, MC_EALIGN, MC_EHIP.
+ */
+MC_API mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, int64_t numel,
+                              float lr, float weight_decay, void* stream);
+
+/*
+ * Per-head max logit over a batch, the logits never stored:
+ *   S_max^h = (1/sqrt(d)) * max_{b, i, j} Q[b,h,i,:] . K[b,h,j,:]
+ * with K[b,h,j,:] = [Kc[b,h,j,0:d_c] || Kr[b,j,0:d_r]] (MLA: the rotary key
+ * part is shared by all heads) or Kc alone when d_r = 0 (MHA), d = d_c + d_r.
+ * Defined in "Kimi K2 内部机制", MuonClip section, core maths (max over the
+ * batch and over all token pairs of the scaled dot product); the paper notes
+ * print 1/d, read as 1/sqrt(d).  No causal mask: every (i, j) pair counts.
+ * Logits that are NaN are skipped; a head with no numeric logit gets -inf.
+ *
+ *   Q      device [B, H, Sq, d] row-major, dtype
+ *   Kc     device [B, H, Sk, d_c] row-major, dtype
+ *   Kr     device [B, Sk, d_r] row-major, dtype; NULL iff d_r == 0
+ *   dtype  MC_BF16 (bf16 MFMA, float32 accumulation) or MC_F32 (float32 FMA)
+ *   smax   device float32[H]: overwritten when accumulate == 0; when
+ *          accumulate != 0 the result is max(smax, S_max) (batches split over
+ *          several calls)
+ * Sizes: B, H, Sq, Sk >= 1 (any zero enqueues nothing but the overwrite of
+ * smax with -inf); 1 <= d_c; 0 <= d_r; d <= 512.
+ * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EHIP.
+ */
+MC_API mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype, int64_t B, int64_t H,
+                        int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
+                        int32_t accumulate, void* stream);
+
+/*
+ * QK-Clip: for each head h with smax[h] > tau, gamma = tau / smax[h] and
+ *   W_q rows [h*qph, h*qph + q_c_rows)      *= gamma^alpha
+ *   W_q rows [h*qph + q_c_rows, (h+1)*qph)  *= gamma
+ *   W_k rows [h*kph, (h+1)*kph)             *= gamma^(1 - alpha)
+ * (qph = q_rows_per_head, kph = k_rows_per_head), in place, computed in
+ * float32 and rounded once to w_dtype.  Heads with smax[h] <= tau or NaN are
+ * not touched (bit-for-bit).  MLA: q_c_rows = nope rows, the rest of the head
+ * is the head-specific rotary query q^R, W_k is W_kc, and the shared rotary
+ * key is simply not passed; MHA: q_c_rows = q_rows_per_head.
+ * Defined in "Kimi K2 内部机制", MuonClip section: gamma_h = min(1, tau/S_max^h),
+ * only heads over tau touched, W_q^h by gamma^alpha and W_k^h by
+ * gamma^(1-alpha), and the MLA table (q^C, k^C by sqrt(gamma); q^R by gamma;
+ * shared k^R untouched); the paper-notes pseudocode skips heads at or below
+ * tau.  gamma^0.5 uses a correctly rounded sqrt, other exponents powf.
+ *
+ *   smax         device float32[H]
+ *   Wq, Wk       device, w_dtype, row-major [H*qph, d_in] and [H*kph, d_in]
+ *   gamma_out    device float32[H] or NULL: gamma (1 for untouched heads)
+ *   clipped_out  device int32[H] or NULL: 1 clipped, 0 not, -1 smax was NaN
+ * Sizes: H >= 0; d_in >= 1; 0 <= q_c_rows <= qph; kph >= 0.
+ * Errors: MC_EINVAL (also tau not finite and > 0, alpha outside [0, 1]),
+ * MC_EDTYPE, MC_EALIGN, MC_EHIP.
+ */
+MC_API mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+                          int w_dtype, int64_t d_in, int64_t q_rows_per_head, int64_t q_c_rows,
+                          int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUONCLIP_H */

@@ -1,0 +1,271 @@
+"""Python binding of libmuonclip.so (the MuonClip step on MI355X).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  The library must be
+built first (``python -m muonclip_muon_amd.build``); importing this package
+without it raises, and no function here has a CPU fallback.
+
+Functions take torch tensors on a ROCm device and call the C ABI of
+``include/muonclip.h`` of the same name.  ``muonclip_step`` rebuilds the
+page-level step (Algorithm 1 of the Kimi K2 internals deep dive, "Kimi K2
+内部机制"; the muonclip_step pseudocode of the paper notes "Kimi K2: Open
+Agentic Intelligence", section 3.2) on top of them.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH",
+    "MuonClipError",
+    "NS_COEFFS",
+    "NS_STEPS",
+    "NS_EPS",
+    "lib",
+    "abi_version",
+    "muonclip_momentum",
+    "muon_ns_workspace_bytes",
+    "muon_ns_orthogonalize_batched",
+    "muon_apply_update",
+    "qk_maxlogit",
+    "qk_clip_apply",
+    "muon_out_scale",
+    "muonclip_step",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuonclip.so")
+
+# Newton-Schulz polynomial used by default: the quintic
+# p(x) = a x + b x^3 + c x^5 with the same (a, b, c) for 5 steps, applied after
+# a Frobenius-norm pre-scale with eps 1e-7.  The pages leave these open (they
+# only call the orthogonaliser Newton-Schulz / msign); these are the public
+# Muon optimiser's constants.
+NS_STEPS = 5
+NS_COEFFS = ((3.4445, -4.7750, 2.0315),) * NS_STEPS
+NS_EPS = 1e-7
+
+MC_F32, MC_BF16 = 0, 1
+_DTYPES = {torch.float32: MC_F32, torch.bfloat16: MC_BF16}
+
+
+class MuonClipError(RuntimeError):
+    """A libmuonclip call returned a status other than MC_OK."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {lib.mc_status_string(status).decode()} (status {status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m muonclip_muon_amd.build` (hipcc, gfx950). "
+            "There is no fallback implementation.")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    L.mc_abi_version.restype = ctypes.c_int
+    L.mc_abi_version.argtypes = []
+    L.mc_status_string.restype = ctypes.c_char_p
+    L.mc_status_string.argtypes = [ctypes.c_int]
+    L.muonclip_momentum.restype = ctypes.c_int
+    L.muonclip_momentum.argtypes = [vp, vp, i64, f32, vp]
+    L.muon_ns_workspace_bytes.restype = ctypes.c_size_t
+    L.muon_ns_workspace_bytes.argtypes = [i64, i64, i64]
+    L.muon_ns_orthogonalize_batched.restype = ctypes.c_int
+    L.muon_ns_orthogonalize_batched.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, ctypes.c_int, i64,
+                                                i32, ctypes.POINTER(f32), f32, f32, vp, ctypes.c_size_t,
+                                                vp, ctypes.POINTER(vp)]
+    L.muon_apply_update.restype = ctypes.c_int
+    L.muon_apply_update.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, f32, f32, vp]
+    L.qk_maxlogit.restype = ctypes.c_int
+    L.qk_maxlogit.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp, i32, vp]
+    L.qk_clip_apply.restype = ctypes.c_int
+    L.qk_clip_apply.argtypes = [vp, i64, f32, f32, vp, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp]
+    return L
+
+
+lib = _load()
+
+
+def abi_version():
+    return lib.mc_abi_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MuonClipError(fn, status)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on a ROCm device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype(t, name):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"{name}: dtype {t.dtype} not supported (float32 or bfloat16)") from None
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def muonclip_momentum(M, G, mu=0.95, stream=None):
+    """M <- fl32(fl32(mu * M) + G) in place (float32, any shape)."""
+    _dev(M, "M"), _dev(G, "G")
+    if M.dtype != torch.float32 or G.dtype != torch.float32 or M.numel() != G.numel():
+        raise ValueError("M and G must be float32 tensors with the same number of elements")
+    _check("muonclip_momentum", lib.muonclip_momentum(M.data_ptr(), G.data_ptr(), M.numel(), mu,
+                                                      _stream(M, stream)))
+    return M
+
+
+def muon_ns_workspace_bytes(batch, rows, cols):
+    return lib.muon_ns_workspace_bytes(batch, rows, cols)
+
+
+def muon_out_scale(rows, cols):
+    """sqrt(max(n, m)) * 0.2, the Adam-RMS matching factor of Algorithm 1."""
+    return math.sqrt(max(rows, cols)) * 0.2
+
+
+def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS_EPS, out_scale=1.0,
+                                  workspace=None, out_dtype=None, gemm_events=None, stream=None):
+    """O[b] = out_scale * NS(M[b]) for M of shape [rows, cols] or [batch, rows, cols].
+
+    ``coeffs``: sequence of ``steps`` (a, b, c) triples (default NS_COEFFS).
+    ``workspace``: a uint8 device tensor of at least muon_ns_workspace_bytes bytes
+    (allocated here when None).  ``gemm_events``: optional list of 6 * steps
+    torch.cuda.Event objects recorded around each GEMM launch.
+    """
+    _dev(M, "M")
+    squeeze = M.dim() == 2
+    M3 = M.unsqueeze(0) if squeeze else M
+    if M3.dim() != 3:
+        raise ValueError("M must be [rows, cols] or [batch, rows, cols]")
+    batch, rows, cols = M3.shape
+    if O is None:
+        O = torch.empty(M.shape, dtype=out_dtype or M.dtype, device=M.device)
+    _dev(O, "O")
+    if O.shape != M.shape:
+        raise ValueError("O must have M's shape")
+    if coeffs is None:
+        coeffs = NS_COEFFS[:steps] if steps <= len(NS_COEFFS) else (NS_COEFFS[0],) * steps
+    flat = [float(x) for abc in coeffs for x in abc]
+    if len(flat) != 3 * steps:
+        raise ValueError("coeffs must hold `steps` (a, b, c) triples")
+    c_coeffs = (ctypes.c_float * len(flat))(*flat)
+    need = lib.muon_ns_workspace_bytes(batch, rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=M.device)
+    _dev(workspace, "workspace")
+    ev = None
+    if gemm_events is not None:
+        if len(gemm_events) != 6 * steps:
+            raise ValueError("gemm_events needs 6 * steps events")
+        st = stream or torch.cuda.current_stream(M.device)
+        for e in gemm_events:  # torch creates events lazily; make sure each exists
+            e.record(st)
+        ev = (ctypes.c_void_p * len(gemm_events))(*[e.cuda_event for e in gemm_events])
+    status = lib.muon_ns_orthogonalize_batched(
+        M.data_ptr(), _dtype(M, "M"), batch, rows, cols, rows * cols, O.data_ptr(), _dtype(O, "O"),
+        rows * cols, steps, c_coeffs, eps, out_scale, workspace.data_ptr(), workspace.numel(),
+        _stream(M, stream), ev)
+    _check("muon_ns_orthogonalize_batched", status)
+    return O
+
+
+def muon_apply_update(W, O, lr, weight_decay=0.1, stream=None):
+    """W <- W - lr * (O + weight_decay * W) in place."""
+    _dev(W, "W"), _dev(O, "O")
+    if W.numel() != O.numel():
+        raise ValueError("W and O must have the same number of elements")
+    _check("muon_apply_update", lib.muon_apply_update(W.data_ptr(), _dtype(W, "W"), O.data_ptr(),
+                                                      _dtype(O, "O"), W.numel(), lr, weight_decay,
+                                                      _stream(W, stream)))
+    return W
+
+
+def qk_maxlogit(Q, Kc, Kr=None, smax=None, accumulate=False, stream=None):
+    """Per-head max logit S_max^h (float32 [H]) of Q [B,H,Sq,d], Kc [B,H,Sk,d_c], Kr [B,Sk,d_r]."""
+    _dev(Q, "Q"), _dev(Kc, "Kc")
+    if Q.dim() != 4 or Kc.dim() != 4:
+        raise ValueError("Q and Kc must be 4-D [B, H, S, d]")
+    B, H, Sq, d = Q.shape
+    if Kc.shape[0] != B or Kc.shape[1] != H:
+        raise ValueError("Kc must be [B, H, Sk, d_c]")
+    Sk, d_c = Kc.shape[2], Kc.shape[3]
+    d_r = 0
+    if Kr is not None:
+        _dev(Kr, "Kr")
+        if Kr.dim() != 3 or Kr.shape[0] != B or Kr.shape[1] != Sk:
+            raise ValueError("Kr must be [B, Sk, d_r]")
+        d_r = Kr.shape[2]
+        if Kr.dtype != Q.dtype:
+            raise ValueError("Q, Kc and Kr must share a dtype")
+    if d != d_c + d_r or Kc.dtype != Q.dtype:
+        raise ValueError("Q's head dim must be d_c + d_r and Q, Kc must share a dtype")
+    if smax is None:
+        smax = torch.empty(H, dtype=torch.float32, device=Q.device)
+    _dev(smax, "smax")
+    status = lib.qk_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
+                             _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, smax.data_ptr(), int(bool(accumulate)),
+                             _stream(Q, stream))
+    _check("qk_maxlogit", status)
+    return smax
+
+
+def qk_clip_apply(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=100.0, alpha=0.5,
+                  gamma=None, clipped=None, stream=None):
+    """Rescale the W_q / W_k rows of every head with smax > tau, in place.
+
+    Returns (gamma [H] float32, clipped [H] int32)."""
+    _dev(smax, "smax"), _dev(Wq, "Wq"), _dev(Wk, "Wk")
+    H = smax.numel()
+    if Wq.dtype != Wk.dtype:
+        raise ValueError("Wq and Wk must share a dtype")
+    d_in = Wq.shape[-1]
+    if Wq.numel() != H * q_rows_per_head * d_in or Wk.numel() != H * k_rows_per_head * d_in:
+        raise ValueError("Wq must be [H * q_rows_per_head, d_in] and Wk [H * k_rows_per_head, d_in]")
+    if gamma is None:
+        gamma = torch.empty(H, dtype=torch.float32, device=smax.device)
+    if clipped is None:
+        clipped = torch.empty(H, dtype=torch.int32, device=smax.device)
+    status = lib.qk_clip_apply(smax.data_ptr(), H, tau, alpha, Wq.data_ptr(), Wk.data_ptr(),
+                               _dtype(Wq, "Wq"), d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
+                               gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
+    _check("qk_clip_apply", status)
+    return gamma, clipped
+
+
+def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1, momentum=0.95,
+                  tau=100.0, alpha=0.5, steps=NS_STEPS, coeffs=None, eps=NS_EPS):
+    """One MuonClip step over dicts of 2-D tensors, in place.
+
+    weights: name -> W (float32 or bfloat16); grads: name -> float32 G;
+    momenta: name -> float32 M (created as zeros when missing: M_0 = 0);
+    smax: float32 [H] max logits recorded by the forward; attention: dict with
+    'q', 'k' (weight names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head'.
+    Returns (gamma, clipped)."""
+    for name, W in weights.items():
+        M = momenta.get(name)
+        if M is None:
+            M = momenta[name] = torch.zeros(W.shape, dtype=torch.float32, device=W.device)
+        muonclip_momentum(M, grads[name], momentum)
+        rows, cols = W.shape
+        O = muon_ns_orthogonalize_batched(M, steps=steps, coeffs=coeffs, eps=eps,
+                                          out_scale=muon_out_scale(rows, cols), out_dtype=W.dtype)
+        muon_apply_update(W, O, lr, weight_decay)
+    return qk_clip_apply(smax, weights[attention["q"]], weights[attention["k"]],
+                         attention["q_rows_per_head"], attention["q_c_rows"], attention["k_rows_per_head"],
+                         tau, alpha)

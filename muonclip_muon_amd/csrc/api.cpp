@@ -1,0 +1,180 @@
+// C ABI of libmuonclip.so: argument validation and dispatch to the kernels.
+// Every check runs before anything is enqueued, so an invalid call touches
+// no output; see include/muonclip.h for the contract of each entry point.
+
+#include "muonclip.h"
+
+#include <math.h>
+
+#include "mc_internal.h"
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+inline bool valid_dtype(int d) { return d == MC_F32 || d == MC_BF16; }
+inline size_t dtype_size(int d) { return d == MC_BF16 ? 2 : 4; }
+inline mc_status_t from_hip(hipError_t e) { return e == hipSuccess ? MC_OK : MC_EHIP; }
+
+constexpr int64_t kNsMaxN = 16384;   // min(rows, cols)
+constexpr int64_t kNsMaxM = 65536;   // max(rows, cols)
+constexpr int32_t kNsMaxSteps = 64;
+constexpr int64_t kGridMax = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+int mc_abi_version(void) { return MC_ABI_VERSION; }
+
+const char* mc_status_string(int status) {
+  switch (status) {
+    case MC_OK: return "ok";
+    case MC_EINVAL: return "invalid argument";
+    case MC_ESHAPE: return "unsupported shape";
+    case MC_EDTYPE: return "unsupported dtype";
+    case MC_EALIGN: return "misaligned pointer";
+    case MC_EWORKSPACE: return "workspace missing or too small";
+    case MC_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+mc_status_t muonclip_momentum(float* M, const float* G, int64_t numel, float mu, void* stream) {
+  if (numel < 0) return MC_EINVAL;
+  if (numel == 0) return MC_OK;
+  if (!M || !G) return MC_EINVAL;
+  if (!isfinite(mu)) return MC_EINVAL;
+  if (!aligned(M, 4) || !aligned(G, 4)) return MC_EALIGN;
+  return from_hip(mc::launch_momentum(M, G, numel, mu, static_cast<hipStream_t>(stream)));
+}
+
+size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
+  if (batch < 0 || rows < 1 || cols < 1) return 0;
+  const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
+  if (n > kNsMaxN || m > kNsMaxM) return 0;
+  return mc::ns_geometry(batch, rows, cols).total;
+}
+
+mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t batch, int64_t rows,
+                                          int64_t cols, int64_t m_batch_stride, void* O, int o_dtype,
+                                          int64_t o_batch_stride, int32_t steps, const float* coeffs,
+                                          float eps, float out_scale, void* workspace,
+                                          size_t workspace_bytes, void* stream,
+                                          void* const* gemm_events) {
+  if (batch < 0 || rows < 1 || cols < 1) return MC_EINVAL;
+  if (!valid_dtype(m_dtype) || !valid_dtype(o_dtype)) return MC_EDTYPE;
+  const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
+  if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  if (batch == 0) return MC_OK;
+  if (!M || !O || !coeffs || !workspace) return MC_EINVAL;
+  if (steps < 1 || steps > kNsMaxSteps) return MC_EINVAL;
+  if (!(eps >= 0.0f) || !isfinite(eps) || !isfinite(out_scale)) return MC_EINVAL;
+  for (int i = 0; i < 3 * steps; ++i)
+    if (!isfinite(coeffs[i])) return MC_EINVAL;
+  if (batch > 1 && (m_batch_stride < rows * cols || o_batch_stride < rows * cols)) return MC_EINVAL;
+  if (!aligned(M, dtype_size(m_dtype)) || !aligned(O, dtype_size(o_dtype))) return MC_EALIGN;
+  if (!aligned(workspace, 256)) return MC_EALIGN;
+  const mc::NsGeometry g = mc::ns_geometry(batch, rows, cols);
+  if (workspace_bytes < g.total) return MC_EWORKSPACE;
+  const int64_t tiles = (g.n_pad / mc::kNsTile) * (g.m_pad / mc::kNsTile);
+  if (tiles * batch > kGridMax || batch > 65535 || g.sumsq_chunks > kGridMax) return MC_ESHAPE;
+  if (gemm_events)
+    for (int i = 0; i < 6 * steps; ++i)
+      if (!gemm_events[i]) return MC_EINVAL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const bool m_bf16 = m_dtype == MC_BF16, o_bf16 = o_dtype == MC_BF16;
+  hipError_t e = mc::launch_ns_norm(M, m_bf16, m_batch_stride, g, eps, ws, s);
+  if (e != hipSuccess) return MC_EHIP;
+  e = mc::launch_ns_prescale(M, m_bf16, m_batch_stride, g, ws, s);
+  if (e != hipSuccess) return MC_EHIP;
+
+  uint16_t* X = reinterpret_cast<uint16_t*>(ws + g.off_x0);
+  uint16_t* Xn = reinterpret_cast<uint16_t*>(ws + g.off_x1);
+  uint16_t* A = reinterpret_cast<uint16_t*>(ws + g.off_a);
+  uint16_t* B = reinterpret_cast<uint16_t*>(ws + g.off_b);
+  auto record = [&](int idx) -> hipError_t {
+    return gemm_events ? hipEventRecord(static_cast<hipEvent_t>(gemm_events[idx]), s) : hipSuccess;
+  };
+  for (int st = 0; st < steps; ++st) {
+    const float a = coeffs[3 * st], b = coeffs[3 * st + 1], c = coeffs[3 * st + 2];
+    const uint16_t* in0[3] = {X, A, B};
+    const uint16_t* in1[3] = {nullptr, nullptr, X};
+    uint16_t* out[3] = {A, B, Xn};
+    const float alpha[3] = {0.f, b, a}, beta[3] = {0.f, c, 0.f};
+    for (int gm = 0; gm < 3; ++gm) {
+      if ((e = record(2 * (3 * st + gm))) != hipSuccess) return MC_EHIP;
+      e = mc::launch_ns_gemm(gm, g, in0[gm], in1[gm], out[gm], alpha[gm], beta[gm], s);
+      if (e != hipSuccess) return MC_EHIP;
+      if ((e = record(2 * (3 * st + gm) + 1)) != hipSuccess) return MC_EHIP;
+    }
+    uint16_t* tmp = X;
+    X = Xn;
+    Xn = tmp;
+  }
+  return from_hip(mc::launch_ns_output(X, g, O, o_bf16, o_batch_stride, out_scale, s));
+}
+
+mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, int64_t numel,
+                              float lr, float weight_decay, void* stream) {
+  if (numel < 0) return MC_EINVAL;
+  if (!valid_dtype(w_dtype) || !valid_dtype(o_dtype)) return MC_EDTYPE;
+  if (numel == 0) return MC_OK;
+  if (!W || !O) return MC_EINVAL;
+  if (!isfinite(lr) || !isfinite(weight_decay)) return MC_EINVAL;
+  if (!aligned(W, dtype_size(w_dtype)) || !aligned(O, dtype_size(o_dtype))) return MC_EALIGN;
+  return from_hip(mc::launch_update(W, w_dtype == MC_BF16, O, o_dtype == MC_BF16, numel, lr,
+                                    weight_decay, static_cast<hipStream_t>(stream)));
+}
+
+mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype, int64_t B, int64_t H,
+                        int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
+                        int32_t accumulate, void* stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || d_c < 1 || d_r < 0) return MC_EINVAL;
+  if (!valid_dtype(dtype)) return MC_EDTYPE;
+  if (d_c + d_r > 512) return MC_ESHAPE;
+  if (H == 0) return MC_OK;
+  if (!smax) return MC_EINVAL;
+  if (H > 65535 || B > 65535 || (Sq + 63) / 64 > kGridMax) return MC_ESHAPE;
+  const bool empty = B == 0 || Sq == 0 || Sk == 0;
+  if (!empty) {
+    if (!Q || !Kc) return MC_EINVAL;
+    if ((d_r > 0) != (Kr != nullptr)) return MC_EINVAL;
+    const size_t es = dtype_size(dtype);
+    if (!aligned(Q, es) || !aligned(Kc, es) || (Kr && !aligned(Kr, es))) return MC_EALIGN;
+  }
+  if (!aligned(smax, 4)) return MC_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!accumulate) {
+    hipError_t e = mc::launch_maxlogit_init(smax, H, s);
+    if (e != hipSuccess) return MC_EHIP;
+  }
+  if (empty) return MC_OK;
+  return from_hip(mc::launch_maxlogit(Q, Kc, Kr, dtype == MC_BF16, B, H, Sq, Sk, d_c, d_r, smax, s));
+}
+
+mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+                          int w_dtype, int64_t d_in, int64_t q_rows_per_head, int64_t q_c_rows,
+                          int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
+                          void* stream) {
+  if (H < 0 || d_in < 1 || q_rows_per_head < 0 || q_c_rows < 0 || q_c_rows > q_rows_per_head ||
+      k_rows_per_head < 0)
+    return MC_EINVAL;
+  if (!valid_dtype(w_dtype)) return MC_EDTYPE;
+  if (!(tau > 0.0f) || !isfinite(tau) || !(alpha >= 0.0f && alpha <= 1.0f)) return MC_EINVAL;
+  if (H == 0) return MC_OK;
+  if (!smax) return MC_EINVAL;
+  if ((q_rows_per_head > 0 && !Wq) || (k_rows_per_head > 0 && !Wk)) return MC_EINVAL;
+  if (H > 65535) return MC_ESHAPE;
+  const size_t es = dtype_size(w_dtype);
+  if (!aligned(smax, 4) || (Wq && !aligned(Wq, es)) || (Wk && !aligned(Wk, es)) ||
+      (gamma_out && !aligned(gamma_out, 4)) || (clipped_out && !aligned(clipped_out, 4)))
+    return MC_EALIGN;
+  if ((q_rows_per_head + k_rows_per_head) * d_in / 8 / 1024 + 1 > kGridMax) return MC_ESHAPE;
+  return from_hip(mc::launch_qk_clip(smax, H, tau, alpha, Wq, Wk, w_dtype == MC_BF16, d_in,
+                                     q_rows_per_head, q_c_rows, k_rows_per_head, gamma_out,
+                                     clipped_out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

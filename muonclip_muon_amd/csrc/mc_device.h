@@ -1,0 +1,49 @@
+// Device-side helpers shared by the kernel translation units of libmuonclip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mc {
+
+// Native clang vector types (HIP's float4/uint4 are structs, which the
+// nontemporal and MFMA builtins do not accept).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bfloat16 <-> float32.  bfloat16 is the upper half of a binary32, so the
+// widening is a shift; the narrowing rounds to nearest, ties to even, and
+// keeps NaNs quiet.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> two packed bfloat16 in one dword (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Blocks of one launch are distributed round-robin over the 8 XCDs of an
+// MI355X (block b runs on XCD b % 8).  This remap makes consecutive logical
+// block ids land on the same XCD, so tiles that share operands share that
+// XCD's L2.  Identity when the grid does not divide evenly.
+__device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t bid, uint32_t nblocks) {
+  constexpr uint32_t kXcds = 8;
+  if (nblocks % kXcds != 0) return bid;
+  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
+}  // namespace mc

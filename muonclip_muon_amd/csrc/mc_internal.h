@@ -1,0 +1,63 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel
+// translation units.  Every launcher enqueues on `stream` and returns the
+// hipError_t of the launch; argument checking has already been done by the
+// ABI layer, so launchers assume valid, non-empty shapes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mc {
+
+// ---------------------------------------------------------------- momentum
+hipError_t launch_momentum(float* M, const float* G, int64_t numel, float mu, hipStream_t stream);
+
+// ---------------------------------------------------------------- update
+// w_bf16/o_bf16 select bfloat16 (true) or float32 (false) storage.
+hipError_t launch_update(void* W, bool w_bf16, const void* O, bool o_bf16, int64_t numel, float lr,
+                         float weight_decay, hipStream_t stream);
+
+// ---------------------------------------------------------------- Newton-Schulz
+// Padded internal geometry of one batch of matrices.  X is n x m with
+// n = min(rows, cols), m = max(rows, cols); both are padded to multiples of
+// the GEMM tile so no kernel needs a bounds check.  Padding is zero, which the
+// polynomial keeps zero.
+struct NsGeometry {
+  int64_t batch, rows, cols;
+  int64_t n, m;          // logical
+  int64_t n_pad, m_pad;  // padded to kNsTile
+  bool transposed;       // rows > cols: X = M^T
+  int64_t sumsq_chunks;  // partial sums per matrix
+  // byte offsets inside the workspace
+  size_t off_x0, off_x1, off_a, off_b, off_partials, off_invnorm, total;
+};
+constexpr int64_t kNsTile = 256;
+NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols);
+
+hipError_t launch_ns_norm(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
+                          float eps, char* ws, hipStream_t stream);
+hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride,
+                              const NsGeometry& g, char* ws, hipStream_t stream);
+// One GEMM of the polynomial step, on the whole batch:
+//   mode 0: A = X X^T          (in: X, out: A)
+//   mode 1: B = b A + c A A    (in: A, out: B)
+//   mode 2: X' = a X + B X     (in: B and X, out: X')
+hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
+                          uint16_t* out, float alpha, float beta, hipStream_t stream);
+hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
+                            int64_t o_batch_stride, float out_scale, hipStream_t stream);
+
+// ---------------------------------------------------------------- max logit
+hipError_t launch_maxlogit_init(float* smax, int64_t H, hipStream_t stream);
+// Returns hipErrorInvalidValue if no kernel covers the shape (caller checked).
+hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool bf16, int64_t B,
+                           int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
+                           hipStream_t stream);
+
+// ---------------------------------------------------------------- QK-Clip
+hipError_t launch_qk_clip(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+                          bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
+                          float* gamma_out, int32_t* clipped_out, hipStream_t stream);
+
+}  // namespace mc

@@ -1,0 +1,164 @@
+// QK-Clip: per-head rescale of the query/key projection rows.
+//
+// For a head h with S_max^h > tau, gamma = tau / S_max^h (computed on the
+// device: no host round trip per head), and in place
+//   W_q rows of the head's first q_c_rows       x gamma^alpha
+//   W_q rows of the rest of the head             x gamma
+//   W_k rows of the head                         x gamma^(1 - alpha)
+// ("Kimi K2 内部机制", MuonClip section: per-head gamma_h = min(1, tau/S_max^h),
+// W_q^h by gamma^alpha and W_k^h by gamma^(1-alpha), and the MLA table that
+// scales q^C and k^C by sqrt(gamma), q^R by gamma and leaves the shared k^R).
+//
+// A head's rows are two contiguous row blocks (W_q and W_k are row-major with
+// head-major rows), so the kernel streams them with 16-byte accesses.  Grid:
+// (chunks, H); every block of an unclipped head returns after reading one
+// float, so the launch costs only the clipped heads' bytes.
+//
+// The multiply is a single float op, rounded once to the storage type; FP
+// contraction is off so the result does not depend on the compiler.
+
+#include <math.h>
+
+#include "mc_device.h"
+#include "mc_internal.h"
+
+namespace mc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;  // 16-byte vectors per thread per block
+
+struct ClipFactors {
+  float q_c, q_r, k;
+  int32_t state;  // 1 clipped, 0 not, -1 NaN
+  float gamma;
+};
+
+__device__ __forceinline__ ClipFactors clip_factors(float s, float tau, float alpha) {
+  ClipFactors f;
+  if (s != s) {
+    f = {1.f, 1.f, 1.f, -1, 1.f};
+  } else if (s > tau) {  // strict: a head exactly at tau is not touched
+    const float g = tau / s;
+    float qa, ka;
+    if (alpha == 0.5f) {
+      qa = sqrtf(g);
+      ka = qa;
+    } else {
+      qa = powf(g, alpha);
+      ka = powf(g, 1.0f - alpha);
+    }
+    f = {qa, g, ka, 1, g};
+  } else {
+    f = {1.f, 1.f, 1.f, 0, 1.f};
+  }
+  return f;
+}
+
+__device__ __forceinline__ float scale_op(float w, float f) {
+#pragma clang fp contract(off)
+  return w * f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void scale_vec8(void* base, int64_t v, float f) {
+  if constexpr (BF16) {
+    u32x4* p = reinterpret_cast<u32x4*>(base) + v;
+    u32x4 a = *p;
+    a.x = pack_bf16x2(scale_op(bf16_lo(a.x), f), scale_op(bf16_hi(a.x), f));
+    a.y = pack_bf16x2(scale_op(bf16_lo(a.y), f), scale_op(bf16_hi(a.y), f));
+    a.z = pack_bf16x2(scale_op(bf16_lo(a.z), f), scale_op(bf16_hi(a.z), f));
+    a.w = pack_bf16x2(scale_op(bf16_lo(a.w), f), scale_op(bf16_hi(a.w), f));
+    *p = a;
+  } else {
+    f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * v;
+    f32x4 a = p[0], b = p[1];
+    a.x = scale_op(a.x, f); a.y = scale_op(a.y, f); a.z = scale_op(a.z, f); a.w = scale_op(a.w, f);
+    b.x = scale_op(b.x, f); b.y = scale_op(b.y, f); b.z = scale_op(b.z, f); b.w = scale_op(b.w, f);
+    p[0] = a;
+    p[1] = b;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void scale_one(void* base, int64_t i, float f) {
+  if constexpr (BF16) {
+    uint16_t* p = static_cast<uint16_t*>(base) + i;
+    *p = f32_to_bf16(scale_op(bf16_to_f32(*p), f));
+  } else {
+    float* p = static_cast<float*>(base) + i;
+    *p = scale_op(*p, f);
+  }
+}
+
+// VEC: every row block starts 16-byte aligned and d_in % 8 == 0, so the
+// element ranges below are whole 8-element vectors.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restrict__ smax, float tau,
+                                                          float alpha, void* __restrict__ Wq,
+                                                          void* __restrict__ Wk, int64_t d_in,
+                                                          int64_t qph, int64_t q_c_rows, int64_t kph,
+                                                          float* __restrict__ gamma_out,
+                                                          int32_t* __restrict__ clipped_out) {
+  const int64_t h = blockIdx.y;
+  const ClipFactors f = clip_factors(smax[h], tau, alpha);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (gamma_out) gamma_out[h] = f.gamma;
+    if (clipped_out) clipped_out[h] = f.state;
+  }
+  if (f.state != 1) return;
+
+  const size_t esz = BF16 ? 2 : 4;
+  char* q_base = static_cast<char*>(Wq) + static_cast<size_t>(h * qph * d_in) * esz;
+  char* k_base = static_cast<char*>(Wk) + static_cast<size_t>(h * kph * d_in) * esz;
+  const int64_t q_elems = qph * d_in, q_c_elems = q_c_rows * d_in, k_elems = kph * d_in;
+  const int64_t total = q_elems + k_elems;
+
+  if constexpr (VEC) {
+    const int64_t nvec = total / 8, q_vec = q_elems / 8, q_c_vec = q_c_elems / 8;
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kVecPerThread;
+    const int64_t v_end = min(nvec, (static_cast<int64_t>(blockIdx.x) + 1) * per_block);
+    for (int64_t v = blockIdx.x * per_block + threadIdx.x; v < v_end; v += kThreads) {
+      if (v < q_vec) scale_vec8<BF16>(q_base, v, v < q_c_vec ? f.q_c : f.q_r);
+      else scale_vec8<BF16>(k_base, v - q_vec, f.k);
+    }
+  } else {
+    const int64_t per_block = static_cast<int64_t>(kThreads) * kVecPerThread * 8;
+    const int64_t e_end = min(total, (static_cast<int64_t>(blockIdx.x) + 1) * per_block);
+    for (int64_t e = blockIdx.x * per_block + threadIdx.x; e < e_end; e += kThreads) {
+      if (e < q_elems) scale_one<BF16>(q_base, e, e < q_c_elems ? f.q_c : f.q_r);
+      else scale_one<BF16>(k_base, e - q_elems, f.k);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qk_clip(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+                          bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
+                          float* gamma_out, int32_t* clipped_out, hipStream_t stream) {
+  const size_t esz = w_bf16 ? 2 : 4;
+  const bool vec = (d_in % 8 == 0) && (reinterpret_cast<uintptr_t>(Wq) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(Wk) % 16 == 0) &&
+                   ((qph * d_in * static_cast<int64_t>(esz)) % 16 == 0) &&
+                   ((kph * d_in * static_cast<int64_t>(esz)) % 16 == 0);
+  const int64_t total = (qph + kph) * d_in;
+  const int64_t per_block = static_cast<int64_t>(kThreads) * kVecPerThread * 8;
+  int64_t chunks = (total + per_block - 1) / per_block;
+  if (chunks < 1) chunks = 1;
+  dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(H));
+#define MC_CLIP_LAUNCH(B, V)                                                                   \
+  hipLaunchKernelGGL((qk_clip_kernel<B, V>), grid, dim3(kThreads), 0, stream, smax, tau, alpha, \
+                     Wq, Wk, d_in, qph, q_c_rows, kph, gamma_out, clipped_out)
+  if (w_bf16) {
+    if (vec) MC_CLIP_LAUNCH(true, true);
+    else MC_CLIP_LAUNCH(true, false);
+  } else {
+    if (vec) MC_CLIP_LAUNCH(false, true);
+    else MC_CLIP_LAUNCH(false, false);
+  }
+#undef MC_CLIP_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace mc

@@ -1,0 +1,131 @@
+"""Host-side checks of libmuonclip.so (no GPU): it loads, exports every entry
+point include/muonclip.h declares, and rejects invalid arguments before any
+HIP call (argument validation never touches the device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muonclip.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"MC_API\s+[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def mc():
+    import muonclip_muon_amd
+    return muonclip_muon_amd
+
+
+def test_header_declares_the_entry_points():
+    names = set(_declared())
+    assert {"muonclip_momentum", "muon_ns_orthogonalize_batched", "muon_apply_update", "qk_maxlogit",
+            "qk_clip_apply", "muon_ns_workspace_bytes", "mc_abi_version", "mc_status_string"} <= names
+
+
+def test_library_exports_every_declared_symbol(mc):
+    for name in _declared():
+        assert hasattr(mc.lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mc.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(_declared())  # nothing internal leaks
+
+
+def test_abi_version_and_status_strings(mc):
+    text = open(HEADER).read()
+    assert mc.abi_version() == int(re.search(r"#define MC_ABI_VERSION (\d+)", text).group(1))
+    for code in range(7):
+        assert mc.lib.mc_status_string(code)
+    assert mc.lib.mc_status_string(99) == b"unknown status"
+
+
+def test_binding_constants_match_oracle_constants(mc):
+    # The product and the oracle each define the Newton-Schulz constants; they
+    # must agree (they share no code).
+    import oracle
+    assert tuple(mc.NS_COEFFS) == tuple(oracle.NS_COEFFS)
+    assert mc.NS_EPS == oracle.NS_EPS and mc.NS_STEPS == oracle.NS_STEPS
+
+
+EINVAL, ESHAPE, EDTYPE, EALIGN, EWORKSPACE = 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+
+
+def test_momentum_validation(mc):
+    L = mc.lib
+    assert L.muonclip_momentum(None, None, 0, 0.95, None) == 0  # empty: nothing enqueued
+    assert L.muonclip_momentum(None, FAKE, 8, 0.95, None) == EINVAL
+    assert L.muonclip_momentum(FAKE, FAKE, -1, 0.95, None) == EINVAL
+    assert L.muonclip_momentum(FAKE, FAKE, 8, float("nan"), None) == EINVAL
+    assert L.muonclip_momentum(ctypes.c_void_p(0x100002), FAKE, 8, 0.95, None) == EALIGN
+
+
+def test_ns_validation(mc):
+    L = mc.lib
+    coeffs = (ctypes.c_float * 15)(*([3.4445, -4.775, 2.0315] * 5))
+    ws_bytes = L.muon_ns_workspace_bytes(4, 256, 512)
+    assert ws_bytes > 0
+    assert L.muon_ns_workspace_bytes(4, 0, 512) == 0
+    assert L.muon_ns_workspace_bytes(1, 20000, 20000) == 0
+
+    def call(**kw):
+        a = dict(M=FAKE, m_dtype=1, batch=4, rows=256, cols=512, mstride=256 * 512, O=FAKE, o_dtype=1,
+                 ostride=256 * 512, steps=5, coeffs=coeffs, eps=1e-7, scale=1.0, ws=ctypes.c_void_p(0x200000),
+                 wsb=ws_bytes, stream=None, ev=None)
+        a.update(kw)
+        return L.muon_ns_orthogonalize_batched(a["M"], a["m_dtype"], a["batch"], a["rows"], a["cols"],
+                                               a["mstride"], a["O"], a["o_dtype"], a["ostride"], a["steps"],
+                                               a["coeffs"], a["eps"], a["scale"], a["ws"], a["wsb"],
+                                               a["stream"], a["ev"])
+    assert call(batch=0) == 0
+    assert call(rows=0) == EINVAL
+    assert call(m_dtype=7) == EDTYPE
+    assert call(rows=20000, cols=20000) == ESHAPE
+    assert call(M=None) == EINVAL
+    assert call(steps=0) == EINVAL
+    assert call(eps=-1.0) == EINVAL
+    assert call(mstride=10) == EINVAL
+    assert call(ws=ctypes.c_void_p(0x200010)) == EALIGN
+    assert call(wsb=ws_bytes - 1) == EWORKSPACE
+    bad = (ctypes.c_float * 15)(*([float("inf")] * 15))
+    assert call(coeffs=bad) == EINVAL
+
+
+def test_update_validation(mc):
+    L = mc.lib
+    assert L.muon_apply_update(FAKE, 1, FAKE, 1, 0, 0.02, 0.1, None) == 0
+    assert L.muon_apply_update(FAKE, 5, FAKE, 1, 8, 0.02, 0.1, None) == EDTYPE
+    assert L.muon_apply_update(None, 1, FAKE, 1, 8, 0.02, 0.1, None) == EINVAL
+    assert L.muon_apply_update(FAKE, 1, FAKE, 1, 8, float("inf"), 0.1, None) == EINVAL
+    assert L.muon_apply_update(ctypes.c_void_p(0x100001), 1, FAKE, 1, 8, 0.02, 0.1, None) == EALIGN
+
+
+def test_maxlogit_validation(mc):
+    L = mc.lib
+    assert L.qk_maxlogit(FAKE, FAKE, FAKE, 1, 1, 0, 8, 8, 128, 64, FAKE, 0, None) == 0  # H = 0
+    assert L.qk_maxlogit(FAKE, FAKE, None, 1, 1, 2, 8, 8, 128, 64, FAKE, 0, None) == EINVAL  # Kr missing
+    assert L.qk_maxlogit(FAKE, FAKE, FAKE, 1, 1, 2, 8, 8, 128, 0, FAKE, 0, None) == EINVAL  # Kr given, d_r 0
+    assert L.qk_maxlogit(FAKE, FAKE, None, 9, 1, 2, 8, 8, 64, 0, FAKE, 0, None) == EDTYPE
+    assert L.qk_maxlogit(FAKE, FAKE, None, 1, 1, 2, 8, 8, 600, 0, FAKE, 0, None) == ESHAPE
+    assert L.qk_maxlogit(FAKE, FAKE, None, 1, 1, 2, 8, 8, 64, 0, None, 0, None) == EINVAL
+    assert L.qk_maxlogit(ctypes.c_void_p(0x100001), FAKE, None, 1, 1, 2, 8, 8, 64, 0, FAKE, 0, None) == EALIGN
+
+
+def test_clip_validation(mc):
+    L = mc.lib
+    assert L.qk_clip_apply(FAKE, 0, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == 0
+    assert L.qk_clip_apply(FAKE, 4, 0.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert L.qk_clip_apply(FAKE, 4, float("inf"), 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert L.qk_clip_apply(FAKE, 4, 100.0, 1.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert L.qk_clip_apply(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 8, 4, None, None, None) == EINVAL
+    assert L.qk_clip_apply(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 4, 16, 6, 4, 4, None, None, None) == EDTYPE
+    assert L.qk_clip_apply(None, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert L.qk_clip_apply(FAKE, 4, 100.0, 0.5, ctypes.c_void_p(0x100001), FAKE, 1, 16, 6, 4, 4, None, None,
+                           None) == EALIGN
