@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark: one full MuonClip optimizer step for one MoE layer on one MI355X.
+
+Workload (synthetic, seeded, resident in HBM before timing):
+  * 384 experts x {gate 2048x7168, up 2048x7168, down 7168x2048} bf16 weights
+    ~N(0, 0.02) with float32 momentum and gradients ~N(0, 1e-4), plus the MLA
+    attention projections W_q 12288x7168, W_kc 8192x7168, W_kr 64x7168
+    (4 random heads x6 so they exceed tau);
+  * Q / K of 8 x 4096 tokens through those projections (64 heads, 128 + 64
+    head dim), computed before timing: the max logit is measured on them.
+One step = every row of the path, on one stream:
+  momentum (all matrices, one launch) -> per shape group and chunk of 64
+  matrices: Newton-Schulz x 5 with the Muon scale, decoupled-decay update ->
+  per-head max logit -> QK-Clip of W_q / W_kc.
+
+Prints one JSON line on stdout (progress goes to stderr).  `value` is the
+step's MFMA work (nominal Newton-Schulz GEMM flops 4n^2m + 2n^3 per matrix
+per iteration, plus 2 B H Sq Sk d for the max logit) divided by the step
+time.  `roofline` covers the dominant kernel, timed per launch with HIP
+events on the library's stream.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MuonClip step: NS + max-logit TFLOP/s (MFMA util), rescale GB/s"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0
+
+D_MODEL, D_EXPERT, N_HEADS, D_NOPE, D_ROPE = 7168, 2048, 64, 128, 64
+LR, WD, MU, TAU, ALPHA = 2e-4, 0.1, 0.95, 100.0, 0.5
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def ns_flops(rows, cols, steps):
+    n, m = min(rows, cols), max(rows, cols)
+    return steps * (4 * n * n * m + 2 * n ** 3)
+
+
+class Workload:
+    """Flat parameter buffers and the groups of equally shaped matrices."""
+
+    def __init__(self, torch, experts, device, seed):
+        import workloads
+        self.groups = []  # (name, offset (elements), count, rows, cols)
+        off = 0
+        for name, count, rows, cols in (("expert_gate_up", 2 * experts, D_EXPERT, D_MODEL),
+                                        ("expert_down", experts, D_MODEL, D_EXPERT),
+                                        ("attn_q", 1, N_HEADS * (D_NOPE + D_ROPE), D_MODEL),
+                                        ("attn_kc", 1, N_HEADS * D_NOPE, D_MODEL),
+                                        ("attn_kr", 1, D_ROPE, D_MODEL)):
+            self.groups.append((name, off, count, rows, cols))
+            off += count * rows * cols
+        self.numel = off
+        log(f"allocating {self.numel / 1e9:.2f} G parameters: W bf16 {2 * off / 1e9:.1f} GB, "
+            f"M and G float32 {8 * off / 1e9:.1f} GB")
+        self.W = torch.empty(off, dtype=torch.bfloat16, device=device)
+        self.M = torch.empty(off, dtype=torch.float32, device=device)
+        self.G = torch.empty(off, dtype=torch.float32, device=device)
+        gen = workloads.generator(seed, device)
+        chunk = 1 << 28
+        t0 = time.time()
+        for s in range(0, off, chunk):
+            e = min(off, s + chunk)
+            self.W[s:e] = workloads.normal((e - s,), 0.02, gen, device, torch.bfloat16)
+            self.M[s:e] = workloads.normal((e - s,), 1e-4, gen, device)
+            self.G[s:e] = workloads.normal((e - s,), 1e-4, gen, device)
+        torch.cuda.synchronize()
+        log(f"filled in {time.time() - t0:.1f} s")
+        # attention projections: the 4-hot-head MLA weights, and the forward's Q / K
+        Wq, Wkc, Wkr, hot = workloads.mla_weights(seed=seed + 1, device=device)
+        self.view("attn_q").copy_(Wq.view(1, *Wq.shape))
+        self.view("attn_kc").copy_(Wkc.view(1, *Wkc.shape))
+        self.view("attn_kr").copy_(Wkr.view(1, *Wkr.shape))
+        self.hot = hot
+        X = workloads.normal((8, 4096, D_MODEL), 1.0, workloads.generator(seed + 2, device), device,
+                             torch.bfloat16)
+        self.Q, self.Kc, self.Kr = workloads.mla_project(X, Wq, Wkc, Wkr, N_HEADS)
+        del X, Wq, Wkc, Wkr
+        torch.cuda.synchronize()
+
+    def group(self, name):
+        return next(g for g in self.groups if g[0] == name)
+
+    def view(self, name, buf=None, start=0, count=None):
+        _, off, n, rows, cols = self.group(name)
+        count = n - start if count is None else count
+        buf = self.W if buf is None else buf
+        s = off + start * rows * cols
+        return buf[s:s + count * rows * cols].view(count, rows, cols)
+
+
+def run(args):
+    import torch
+
+    import muonclip_muon_amd as mc
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    wl = Workload(torch, args.experts, dev, args.seed)
+    steps_ns = mc.NS_STEPS
+
+    chunk = args.chunk
+    ws_bytes = max(mc.muon_ns_workspace_bytes(min(chunk, n), r, c) for _, _, n, r, c in wl.groups)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o_elems = max(min(chunk, n) * r * c for _, _, n, r, c in wl.groups)
+    O_buf = torch.empty(o_elems, dtype=torch.bfloat16, device=dev)
+    smax = torch.empty(N_HEADS, dtype=torch.float32, device=dev)
+    gamma = torch.empty(N_HEADS, dtype=torch.float32, device=dev)
+    clipped = torch.empty(N_HEADS, dtype=torch.int32, device=dev)
+    B, H, Sq, dq = wl.Q.shape
+    Sk = wl.Kc.shape[2]
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # NS calls of one step, and per-call event pairs
+    ns_calls = []
+    for name, off, n, rows, cols in wl.groups:
+        for s in range(0, n, chunk):
+            ns_calls.append((name, s, min(chunk, n - s), rows, cols))
+    gemm_ev = [[ev() for _ in range(6 * steps_ns)] for _ in ns_calls]
+    call_ev = {k: (ev(), ev()) for k in ("momentum", "maxlogit", "clip")}
+    upd_ev = [(ev(), ev()) for _ in ns_calls]
+    ns_ev = [(ev(), ev()) for _ in ns_calls]
+
+    def step(timed):
+        e = call_ev["momentum"]
+        timed and e[0].record(stream)
+        mc.muonclip_momentum(wl.M, wl.G, MU)
+        timed and e[1].record(stream)
+        for k, (name, s, cnt, rows, cols) in enumerate(ns_calls):
+            M = wl.view(name, wl.M, s, cnt)
+            W = wl.view(name, wl.W, s, cnt)
+            O = O_buf[:cnt * rows * cols].view(cnt, rows, cols)
+            timed and ns_ev[k][0].record(stream)
+            mc.muon_ns_orthogonalize_batched(M, O, workspace=workspace, out_scale=mc.muon_out_scale(rows, cols),
+                                             gemm_events=gemm_ev[k] if timed else None)
+            timed and ns_ev[k][1].record(stream)
+            timed and upd_ev[k][0].record(stream)
+            mc.muon_apply_update(W, O, LR, WD)
+            timed and upd_ev[k][1].record(stream)
+        e = call_ev["maxlogit"]
+        timed and e[0].record(stream)
+        mc.qk_maxlogit(wl.Q, wl.Kc, wl.Kr, smax=smax)
+        timed and e[1].record(stream)
+        e = call_ev["clip"]
+        timed and e[0].record(stream)
+        mc.qk_clip_apply(smax, wl.view("attn_q")[0], wl.view("attn_kc")[0], D_NOPE + D_ROPE, D_NOPE, D_NOPE,
+                         TAU, ALPHA, gamma=gamma, clipped=clipped)
+        timed and e[1].record(stream)
+
+    log(f"{len(ns_calls)} Newton-Schulz calls per step; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # timed region: K steps bracketed by synchronisation
+    acc = {"momentum": 0.0, "maxlogit": 0.0, "clip": 0.0, "ns": 0.0, "update": 0.0}
+    gemm_ms = {0: [], 1: [], 2: []}
+    gemm_flops = {0: [], 1: [], 2: []}
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()  # read this step's events before re-recording them
+        for k in ("momentum", "maxlogit", "clip"):
+            acc[k] += call_ev[k][0].elapsed_time(call_ev[k][1])
+        for k, (name, s, cnt, rows, cols) in enumerate(ns_calls):
+            acc["ns"] += ns_ev[k][0].elapsed_time(ns_ev[k][1])
+            acc["update"] += upd_ev[k][0].elapsed_time(upd_ev[k][1])
+            n_, m_ = min(rows, cols), max(rows, cols)
+            per = {0: 2 * n_ * n_ * m_, 1: 2 * n_ ** 3, 2: 2 * n_ * n_ * m_}
+            for st in range(steps_ns):
+                for gm in range(3):
+                    a, b = gemm_ev[k][2 * (3 * st + gm)], gemm_ev[k][2 * (3 * st + gm) + 1]
+                    gemm_ms[gm].append(a.elapsed_time(b))
+                    gemm_flops[gm].append(per[gm] * cnt)
+        log(f"step {i + 1}/{args.steps} done")
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    K = args.steps
+    ms_per_step = total_ms / K
+
+    ns_fl = sum(ns_flops(r, c, steps_ns) * n for _, _, n, r, c in wl.groups)
+    ml_fl = 2.0 * B * H * Sq * Sk * dq
+    value = (ns_fl + ml_fl) / (ms_per_step * 1e-3) / 1e12
+    E = wl.numel
+    n_clip = int((clipped == 1).sum().item())
+    d_in = D_MODEL
+    rescale_bytes = 2 * n_clip * ((D_NOPE + D_ROPE) + D_NOPE) * d_in * 2  # read + write, bf16
+
+    # dominant kernel: the GEMM mode with the largest total time
+    dom = max(gemm_ms, key=lambda g: sum(gemm_ms[g]))
+    dom_launches = len(gemm_ms[dom])
+    dom_avg_ms = sum(gemm_ms[dom]) / dom_launches
+    dom_avg_flops = sum(gemm_flops[dom]) / dom_launches
+    achieved = dom_avg_flops / (dom_avg_ms * 1e-3) / 1e12
+    kernel_names = {0: "ns_gemm_kernel<0> (A = X X^T)", 1: "ns_gemm_kernel<1> (B = bA + cAA)",
+                    2: "ns_gemm_kernel<2> (X = aX + BX)"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "full MuonClip step, one MoE layer: 384 experts x (gate, up 2048x7168; down 7168x2048) "
+                        "+ W_q 12288x7168, W_kc 8192x7168, W_kr 64x7168; max logit over 8 x 4096 tokens, "
+                        "64 heads, d 128+64; QK-Clip tau 100",
+            "experts": args.experts,
+            "matrices": sum(g[2] for g in wl.groups),
+            "parameters": E,
+            "ns_iterations": steps_ns,
+            "ns_chunk": chunk,
+            "lr": LR, "weight_decay": WD, "mu": MU, "tau": TAU, "alpha": ALPHA,
+        },
+        "breakdown": {
+            "wall_s_timed_region": round(wall, 3),
+            "newton_schulz_ms": round(acc["ns"] / K, 3),
+            "newton_schulz_tflops": round(ns_fl / (acc["ns"] / K * 1e-3) / 1e12, 1),
+            "maxlogit_ms": round(acc["maxlogit"] / K, 4),
+            "maxlogit_tflops": round(ml_fl / (acc["maxlogit"] / K * 1e-3) / 1e12, 1),
+            "momentum_ms": round(acc["momentum"] / K, 3),
+            "momentum_gbps": round(12.0 * E / (acc["momentum"] / K * 1e-3) / 1e9, 1),
+            "update_ms": round(acc["update"] / K, 3),
+            "update_gbps": round(6.0 * E / (acc["update"] / K * 1e-3) / 1e9, 1),
+            "rescale_ms": round(acc["clip"] / K, 4),
+            "rescale_gbps": round(rescale_bytes / (acc["clip"] / K * 1e-3) / 1e9, 1),
+            "clipped_heads": n_clip,
+            "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
+                            for g in gemm_ms},
+        },
+        "roofline": {
+            "kernel": kernel_names[dom],
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_ms": round(dom_avg_ms, 4),
+            "algorithmic_flops_per_launch": dom_avg_flops,
+            "launches": dom_launches,
+        },
+    }
+    return out, wl
+
+
+def cpu_baseline(wl, torch):
+    """The fp64 oracle on a bounded sample of the same workload: one 2048x7168
+    and one 7168x2048 expert matrix (momentum, Newton-Schulz x5, update) and
+    the max logit of two heads over the full 8 x 4096 batch."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    mats = [wl.view("expert_gate_up", wl.M, 0, 1)[0], wl.view("expert_down", wl.M, 0, 1)[0]]
+    grads = [wl.view("expert_gate_up", wl.G, 0, 1)[0], wl.view("expert_down", wl.G, 0, 1)[0]]
+    ws = [wl.view("expert_gate_up", wl.W, 0, 1)[0], wl.view("expert_down", wl.W, 0, 1)[0]]
+    host = [(m.cpu().numpy(), g.cpu().numpy(), w.float().cpu().numpy().astype(np.float64))
+            for m, g, w in zip(mats, grads, ws)]
+    heads = [int(wl.hot[0]), (int(wl.hot[0]) + 1) % N_HEADS]
+    Qh = [wl.Q[:, h:h + 1].float().cpu().numpy() for h in heads]
+    Kch = [wl.Kc[:, h:h + 1].float().cpu().numpy() for h in heads]
+    Kr = wl.Kr.float().cpu().numpy()
+    t0 = time.perf_counter()
+    flops = 0.0
+    for M, G, W in host:
+        Mn = oracle.momentum_update(M, G, MU)
+        O = oracle.muon_orthogonalised_update(Mn.astype(np.float64))
+        oracle.apply_update(W, O, LR, WD, "bf16")
+        flops += ns_flops(*M.shape, oracle.NS_STEPS)
+    for q, k in zip(Qh, Kch):
+        oracle.max_logit(q, k, Kr)
+        flops += 2.0 * q.shape[0] * q.shape[2] * k.shape[2] * q.shape[3]
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "fp64 oracle: momentum + Newton-Schulz x5 + update of one 2048x7168 and one "
+                      "7168x2048 expert matrix, and the max logit of 2 heads over 8 x 4096 tokens; "
+                      "same flop accounting as value"}
+
+
+def copy_calibration():
+    """A plain 1 GiB device copy, repeated: the reference kernel for scaling
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 4 * n, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--experts", type=int, default=384)
+    ap.add_argument("--chunk", type=int, default=64, help="matrices per Newton-Schulz call")
+    ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: measured on one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(no multi-GPU path is implemented)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no ROCm GPU visible", file=sys.stderr)
+        sys.exit(1)
+    out, wl = run(args)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a CPU sample")
+        out["cpu_baseline"] = cpu_baseline(wl, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
