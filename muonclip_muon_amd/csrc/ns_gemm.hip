@@ -10,23 +10,33 @@
 //
 // Tiling: a 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output
 // tile; each wave owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 float32
-// accumulators per lane).  The K loop steps by 64 through a double-buffered
-// LDS stage of two 256 x 64 bf16 operand tiles (64 KB per stage); the next
-// stage's global loads are issued before the current stage's MFMAs.
+// accumulators per lane, held in AGPRs).  The K loop steps by 64 through two
+// LDS stages of 64 KB (two 256 x 64 bf16 operand tiles each).
 //
-// Operand layout in LDS: every operand tile is stored "K-contiguous": row r
-// (an output row or column index) holds 64 consecutive k as 8 units of
-// 16 bytes, unit u stored at position u ^ (r & 7) (XOR swizzle: the 8 lanes
-// that share a ds_read_b128 phase touch 8 different 16-byte bank groups).
-// Modes 0/1 read both operands K-contiguous from global memory.  In mode 2
-// the right operand X is row-major with K as its row index, so each thread
-// loads an 8 (k) x 8 (column) bf16 block, transposes it in registers with
-// v_perm_b32 and writes 8 K-contiguous rows.
+// Global -> LDS: global_load_lds_dwordx4 moves 16 bytes per lane straight into
+// LDS (lane l of a wave lands at the instruction's LDS base + 16 l), so the
+// next stage streams in without staging registers while the current stage's
+// MFMAs run; one s_waitcnt + barrier per K step publishes it.  Because the
+// LDS slot of each lane is fixed, the XOR swizzles below are applied on the
+// global side: each lane fetches the 16 bytes that belong in its slot.
+//
+// LDS layouts.
+//  * K-contiguous tiles (both operands of modes 0/1, the left operand of
+//    mode 2): row r (an output row or column index) holds 64 consecutive k as
+//    8 units of 16 bytes, unit u at position u ^ swizzle(r).  Fragment reads
+//    are ds_read_b128.
+//  * Mode 2's right operand is X itself, row-major with K as its row index.
+//    The tile is stored as it is in memory (64 k-rows x 256 columns, 32 units
+//    per row, unit u at u ^ 4 (k & 3)) and read with ds_read_b64_tr_b16,
+//    which hands each lane 4 consecutive k of one column: two of them make
+//    an MFMA operand.  (Measured on gfx950: within each 16-lane group, lane i
+//    receives element i % 4 of the 4 x 16-bit values addressed by lanes
+//    i / 4 + 4 e, e = 0..3.)
 //
 // MFMA operand roles: the MFMA "A" operand is the right-hand tile (output
-// columns j) and "B" is the left-hand tile (output rows i), so that each lane
-// ends up holding 4 consecutive j of one output row i per 4-register group:
-// the epilogue then reads and writes 8-byte runs.
+// columns j) and "B" is the left-hand tile (output rows i), so each lane ends
+// up holding 4 consecutive j of one output row i per 4-register group and the
+// epilogue reads and writes 8-byte runs.
 // Lane layout of v_mfma_f32_32x32x16_bf16 (measured on gfx950): A/B lane l
 // holds row/column l % 32, k = 8 * (l / 32) + [0, 8); result register r of
 // lane l is row 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32.
@@ -37,31 +47,173 @@
 namespace mc {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64, kThreads = 256;
-constexpr int kUnits = kBK / 8;  // 16-byte units per LDS row
+constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 256;
+constexpr int kStages = 5;                 // LDS stages in flight (prefetch distance kStages - 1)
+constexpr int kTileBytes = kBM * kBK * 2;  // 16 KB per operand tile
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kLoadsPerStage = 2 * (kTileBytes / 1024) / 4;  // DMA instructions per wave per stage
 
-struct Lds {
-  u32x4 p[2][kBM][kUnits];  // left operand rows (output rows i)
-  u32x4 q[2][kBN][kUnits];  // right operand rows (output columns j)
-};
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ u32x4 ld_global16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+// K-contiguous LDS tile: row r (an output row or column index) holds 32
+// consecutive k as 4 units of 16 bytes; unit u sits at u ^ swizzle(r).  Over
+// 16 consecutive rows the pair (r & 3, swizzle(r)) takes 16 distinct values,
+// so a ds_read_b128 of consecutive rows at one unit touches 16 different
+// 16-byte bank groups per 256 bytes.
+__device__ __forceinline__ int swizzle(int r) { return (r >> 2) & 3; }
+
+// Mode 2's X tile (32 k-rows x 256 columns, 32 units per row): unit u of
+// k-row r sits at u ^ xswz(r).  A transposed read touches rows r..r+3 and
+// r+8..r+11 in one 64-byte column segment; the XOR with 4 (r & 3) moves the
+// four rows to four different 64-byte bank slots.
+__device__ __forceinline__ int xswz(int r) { return 4 * (r & 3); }
+
+// One global_load_lds_dwordx4: 16 bytes from g_uniform + lane_off to LDS
+// address m0 + 16 * lane.  Written as inline asm so the compiler's waitcnt
+// insertion does not treat every later LDS read as a possible alias of the
+// in-flight copy (it would otherwise wait for the copy before each read);
+// completion is awaited explicitly (wait_vmem) before the barrier that
+// publishes a stage.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const char* g_uniform, uint32_t lane_off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n"
+               :
+               : "s"(lds_addr), "v"(lane_off), "s"(g_uniform)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// 8 x 8 bf16 transpose: v[r] holds row r (8 columns, 2 per dword); returns
-// w[c] holding column c (8 rows, 2 per dword, row 2j in the low half).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&v)[8], u32x4 (&w)[8]) {
+// Per-lane byte offsets of the tile loads.  The swizzle of a lane's row does
+// not depend on the 1 KB block it fills, so each lane has one offset per tile
+// and every load is "uniform base + lane offset" (SGPR-base addressing).
+//
+// K-contiguous 256 x 32 tile: wave w fills 1 KB blocks b = w + 4 jj, i.e.
+// rows 16 b .. 16 b + 15; lane l takes row 16 b + l / 4, slot l % 4, and
+// swizzle(row) = (l / 16) & 3 for every jj.
+__device__ __forceinline__ uint32_t kc_lane_offset(int64_t ld, int wave, int lane) {
+  const int r = 16 * wave + (lane >> 2);
+  const int u = (lane & 3) ^ ((lane >> 4) & 3);
+  return static_cast<uint32_t>((r * ld + 8 * u) * 2);
+}
+// Row-major 32 x 256 X tile: wave w fills blocks b = w + 4 jj, i.e. k-rows
+// 2 b, 2 b + 1; lane l takes row 2 b + l / 32, slot l % 32, and xswz(row) =
+// 4 ((2 w + l / 32) & 3) for every jj.
+__device__ __forceinline__ uint32_t x_lane_offset(int64_t ld, int wave, int lane) {
+  const int r = 2 * wave + (lane >> 5);
+  const int u = (lane & 31) ^ xswz(r);
+  return static_cast<uint32_t>((r * ld + 8 * u) * 2);
+}
+
+// Issue a K-contiguous tile (row 0 / column k0 at g, pitch ld elements).
+__device__ __forceinline__ void issue_kc_tile(const uint16_t* g, int64_t ld, uint32_t lane_off,
+                                              uint32_t lds, int wave) {
+  const char* base = reinterpret_cast<const char*>(g);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+  for (int jj = 0; jj < kTileBytes / 1024 / 4; ++jj)
+    load_lds16(base + static_cast<int64_t>(64 * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
+}
+// Issue a row-major X tile (k-row 0, column 0 at g, pitch ld).
+__device__ __forceinline__ void issue_x_tile(const uint16_t* g, int64_t ld, uint32_t lane_off,
+                                             uint32_t lds, int wave) {
+  const char* base = reinterpret_cast<const char*>(g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // low half from row 2j, high half from row 2j+1, column c
-      w[c][j] = __builtin_amdgcn_perm(v[2 * j + 1][c >> 1], v[2 * j][c >> 1], sel);
+  for (int jj = 0; jj < kTileBytes / 1024 / 4; ++jj)
+    load_lds16(base + static_cast<int64_t>(8 * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
+}
+
+// Per-lane LDS read addresses relative to a stage.  Everything else that
+// varies inside a stage (the 32-row MFMA tile, and for X tiles the k sub-step
+// and half) is a compile-time offset, so fragment reads are ds_read
+// instructions with immediate offsets from (this + stage base).
+struct FragAddr {
+  uint32_t p[2];  // left tile, per k16 sub-step
+  uint32_t q[4];  // right tile: per k16 sub-step (modes 0/1, q[0..1]) or per 32-column tile (mode 2)
+};
+
+template <int MODE>
+__device__ __forceinline__ FragAddr frag_addresses(int lane, int wm, int wn) {
+  FragAddr a;
+  const int frag_row = lane & 31, frag_half = lane >> 5, swz = swizzle(frag_row);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int unit = (2 * ks + frag_half) ^ swz;
+    a.p[ks] = (wm * 128 + frag_row) * 64 + unit * 16;
+    if constexpr (MODE != 2) a.q[ks] = kTileBytes + (wn * 128 + frag_row) * 64 + unit * 16;
+  }
+  if constexpr (MODE == 2) {
+    // lane l: group g = l / 16, i = l % 16; it addresses k-row 8 (g / 2) + i / 4
+    // (+ 16 ks + 4 h) and columns wn*128 + 32 x + 16 (g & 1) + 4 (i & 3) .. + 3
+    const int g = lane >> 4, i = lane & 15;
+    const int r = 8 * (g >> 1) + (i >> 2);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int col = wn * 128 + 32 * x + 16 * (g & 1) + 4 * (i & 3);
+      a.q[x] = kTileBytes + r * 512 + (((col >> 3) ^ xswz(r)) << 4) + (col & 7) * 2;
     }
+  }
+  return a;
+}
+
+// Fragment registers of one k16 sub-step.
+struct Frags {
+  bf16x8 a[4];  // right tile (output columns): MFMA "A" operand
+  bf16x8 b[4];  // left tile (output rows): MFMA "B" operand
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_frags(const FragAddr& fadr, uint32_t stage_base, int ks, Frags& f) {
+  const uint32_t pb = stage_base + fadr.p[ks];
+#pragma unroll
+  for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
+  if constexpr (MODE != 2) {
+    const uint32_t qb = stage_base + fadr.q[ks];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) f.a[x] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(qb + x * 2048));
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const uint32_t qb = stage_base + fadr.q[x] + ks * 8192;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(qb));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(qb + 2048));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+      f.a[x] = as_bf16x8(v);
+    }
+  }
+}
+
+__device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+      acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
+}
+
+// Scheduling pattern for one half step: 16 MFMAs with the reads of the next
+// sub-step spread between them (4 MFMAs, then a quarter of the reads).  Left
+// alone the scheduler moves every read next to its use, which exposes LDS
+// latency with one wave per SIMD.
+template <int MODE>
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+  constexpr int kReads = (MODE == 2) ? 12 : 8;  // DS reads per sub-step
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads / 4, 0);
   }
 }
 
@@ -70,31 +222,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
                     uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n,
                     int tiles_per_mat, float alpha, float beta) {
-  __shared__ Lds lds;
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
-  // ---- which matrix and tile
+  // ---- which matrix and tile.  Modes 0/1 produce symmetric matrices, so
+  // only tiles with ti <= tj are computed (row-major over the upper
+  // triangle); an off-diagonal tile is also written mirrored.
   const uint32_t bid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int mat = bid / tiles_per_mat;
-  const int t = bid % tiles_per_mat;
-  const int ti = t / tiles_n, tj = t % tiles_n;
+  int t = bid % tiles_per_mat;
+  int ti, tj;
+  if constexpr (MODE == 2) {
+    // column-major: tiles resident together on one XCD share X column panels
+    // (and all of B's few row panels), which keeps the K-slices in its L2
+    const int tiles_m = n_pad / kBM;
+    ti = t % tiles_m;
+    tj = t / tiles_m;
+  } else {
+    ti = 0;
+    while (t >= tiles_n - ti) {
+      t -= tiles_n - ti;
+      ++ti;
+    }
+    tj = ti + t;
+  }
   const int i0 = ti * kBM, j0 = tj * kBN;
 
-  // Left operand P (rows i, K-contiguous), right operand Q (rows j).
   const int64_t nn = static_cast<int64_t>(n_pad) * n_pad, nm = static_cast<int64_t>(n_pad) * m_pad;
-  const uint16_t* P;
-  const uint16_t* Q;
-  int ldp, K;
-  if constexpr (MODE == 0) {  // A = X X^T: P = Q = X (n_pad x m_pad)
+  const uint16_t* P;  // left operand rows (output rows i), K-contiguous
+  const uint16_t* Q;  // right operand: rows j K-contiguous (modes 0/1) or X (mode 2)
+  int64_t ldp;
+  int K;
+  if constexpr (MODE == 0) {
     P = in0 + mat * nm;
     Q = P;
     ldp = m_pad;
     K = m_pad;
-  } else if constexpr (MODE == 1) {  // B = b A + c A A^T: P = Q = A (n_pad x n_pad)
+  } else if constexpr (MODE == 1) {
     P = in0 + mat * nn;
     Q = P;
     ldp = n_pad;
     K = n_pad;
-  } else {  // X' = a X + B X: P = B (n_pad x n_pad), Q^T = X (n_pad x m_pad)
+  } else {
     P = in0 + mat * nn;
     Q = in1 + mat * nm;
     ldp = n_pad;
@@ -102,54 +272,24 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   }
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global -> register staging
-  // K-contiguous tile: thread loads unit tid%8 of rows tid/8 + 32*jj.
-  const int ld_unit = tid & 7, ld_row = tid >> 3;
-  // transposed tile (mode 2): k-chunk tid%8 (8 rows of X), column chunk tid/8.
-  const int tr_kc = tid & 7, tr_cc = tid >> 3;
-
-  u32x4 regP[8], regQ[8];
-
-  auto load_stage = [&](int k0) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      regP[jj] = ld_global16(P + static_cast<int64_t>(i0 + ld_row + 32 * jj) * ldp + k0 + 8 * ld_unit);
-    if constexpr (MODE != 2) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        regQ[jj] = ld_global16(Q + static_cast<int64_t>(j0 + ld_row + 32 * jj) * ldp + k0 + 8 * ld_unit);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        regQ[r] = ld_global16(Q + static_cast<int64_t>(k0 + 8 * tr_kc + r) * m_pad + j0 + 8 * tr_cc);
-    }
+  const uint32_t off_p = kc_lane_offset(ldp, wave, lane);
+  const uint32_t off_q = (MODE != 2) ? off_p : x_lane_offset(m_pad, wave, lane);
+  const int KT = K / kBK;
+  // Loads of K-step kt into stage kt % kStages.  Past the last step the last
+  // in-bounds tile is fetched again into a stage nobody reads, which keeps
+  // the number of loads in flight (and so the wait counts) fixed.
+  auto issue = [&](int kt) {
+    const int k0 = min(kt, KT - 1) * kBK;
+    const uint32_t sb = lds + (kt % kStages) * kStageBytes;
+    issue_kc_tile(P + i0 * ldp + k0, ldp, off_p, sb, wave);
+    if constexpr (MODE != 2) issue_kc_tile(Q + j0 * ldp + k0, ldp, off_q, sb + kTileBytes, wave);
+    else issue_x_tile(Q + static_cast<int64_t>(k0) * m_pad + j0, m_pad, off_q, sb + kTileBytes, wave);
   };
-
-  auto store_stage = [&](int s) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int row = ld_row + 32 * jj;
-      lds.p[s][row][ld_unit ^ (row & 7)] = regP[jj];
-    }
-    if constexpr (MODE != 2) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int row = ld_row + 32 * jj;
-        lds.q[s][row][ld_unit ^ (row & 7)] = regQ[jj];
-      }
-    } else {
-      u32x4 w[8];
-      transpose8x8(regQ, w);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int row = 8 * tr_cc + c;  // row & 7 == c
-        lds.q[s][row][tr_kc ^ c] = w[c];
-      }
-    }
-  };
+  const FragAddr fadr = frag_addresses<MODE>(lane, wm, wn);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -157,65 +297,117 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-  const int frag_row = lane & 31, frag_half = lane >> 5, swz = lane & 7;
-
-  auto compute_stage = [&](int s) {
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int unit = (2 * ks + frag_half) ^ swz;
-      bf16x8 fa[4], fb[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        fa[x] = as_bf16x8(lds.q[s][wn * 128 + x * 32 + frag_row][unit]);
-        fb[x] = as_bf16x8(lds.p[s][wm * 128 + x * 32 + frag_row][unit]);
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-    }
-  };
-
-  // ---- main loop: one barrier per K step
-  const int KT = K / kBK;
-  load_stage(0);
-  store_stage(0);
+  // ---- main loop: kStages - 1 K-steps in flight.  At step kt the stage of
+  // kt + kStages - 1 is refilled (it was last read at step kt - 1, before the
+  // barrier), stage kt is consumed, and the wait leaves only the loads of the
+  // kStages - 2 newest steps outstanding, so step kt + 1 is complete.  The
+  // two k16 sub-steps of a step are software-pipelined across the barrier:
+  // sub-step 1's fragments load under sub-step 0's MFMAs, and the next
+  // step's sub-step 0 fragments load under sub-step 1's MFMAs.
+  for (int s = 0; s < kStages - 1; ++s) issue(s);
+  wait_vmem<(kStages - 2) * kLoadsPerStage>();
   __syncthreads();
+  Frags f0, f1;
+  load_frags<MODE>(fadr, lds, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_stage((kt + 1) * kBK);
-    compute_stage(cur);
-    if (kt + 1 < KT) store_stage(cur ^ 1);
+    const uint32_t cur = lds + (kt % kStages) * kStageBytes;
+    const uint32_t nxt = lds + ((kt + 1) % kStages) * kStageBytes;
+    issue(kt + kStages - 1);
+    load_frags<MODE>(fadr, cur, 1, f1);
+    mfma_16(f0, acc);
+    interleave_reads_with_mfma<MODE>();
+    wait_vmem<(kStages - 2) * kLoadsPerStage>();
     __syncthreads();
+    // After the last step this reads a stage of redundant tiles; unused.
+    load_frags<MODE>(fadr, nxt, 0, f0);
+    mfma_16(f1, acc);
+    interleave_reads_with_mfma<MODE>();
   }
+  wait_vmem<0>();
 
-  // ---- epilogue: acc[x][y] holds C[i][j] for i = rows of tile y, j = rows of tile x
-  const int ldo = (MODE == 2) ? m_pad : n_pad;
+  // ---- epilogue, staged through LDS (free once every stage is consumed).
+  // Wave w owns the 128 x 128 sub-tile at rows i0 + 128 wm, columns
+  // j0 + 128 wn, staged at lds + 32 KB w: row ii at ii * 256 bytes, 16-byte
+  // unit u at position u ^ (ii & 15).  Global traffic is whole 256-byte rows:
+  //   modes 1/2: the epilogue operand sub-tile (A or X) is copied in by DMA;
+  //   every lane combines its accumulators with it (or just rounds, mode 0)
+  //   in place, in bf16;
+  //   the sub-tile is stored row by row, 16 bytes per lane;
+  //   modes 0/1, off-diagonal tiles: it is also stored mirrored, each lane
+  //   assembling 8 consecutive rows of one column with two transposed reads.
+  wait_vmem<0>();
+  __syncthreads();
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  const int64_t ldo = (MODE == 2) ? m_pad : n_pad;
   uint16_t* O = out + mat * ((MODE == 2) ? nm : nn);
-  const uint16_t* E = nullptr;  // epilogue operand (A for mode 1, X for mode 2)
-  if constexpr (MODE == 1) E = in0 + mat * nn;
-  if constexpr (MODE == 2) E = in1 + mat * nm;
+  const int i0w = i0 + wm * 128, j0w = j0 + wn * 128;
+  const uint32_t eb = lds + wave * 32768;
+  auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
+
+  if constexpr (MODE == 1 || MODE == 2) {
+    const uint16_t* E = ((MODE == 1) ? in0 + mat * nn : in1 + mat * nm) + static_cast<int64_t>(i0w) * ldo + j0w;
+    const char* ebase = reinterpret_cast<const char*>(E);
+#pragma unroll 4
+    for (int s = 0; s < 32; ++s) {
+      const int row = 4 * s + (lane >> 4);
+      const int u = (lane & 15) ^ (row & 15);
+      load_lds16(ebase, static_cast<uint32_t>((row * ldo + 8 * u) * 2), eb + 1024 * s);
+    }
+    wait_vmem<0>();
+  }
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
-    const int64_t i = i0 + wm * 128 + y * 32 + frag_row;
+    const int ii = y * 32 + frag_row;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t j = j0 + wn * 128 + x * 32 + 8 * g + 4 * frag_half;
+        const uint32_t a = st_addr(ii, 4 * x + g) + 8 * frag_half;
         float v0 = acc[x][y][4 * g + 0], v1 = acc[x][y][4 * g + 1];
         float v2 = acc[x][y][4 * g + 2], v3 = acc[x][y][4 * g + 3];
         if constexpr (MODE == 1 || MODE == 2) {
-          const u32x2 e = *reinterpret_cast<const u32x2*>(E + i * ldo + j);
+          const u32x2 e = *(const lds_u32x2_t*)(uintptr_t)a;
           const float sa = alpha, sb = (MODE == 1) ? beta : 1.0f;
           v0 = sa * bf16_lo(e.x) + sb * v0;
           v1 = sa * bf16_hi(e.x) + sb * v1;
           v2 = sa * bf16_lo(e.y) + sb * v2;
           v3 = sa * bf16_hi(e.y) + sb * v3;
         }
-        u32x2 o = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        *reinterpret_cast<u32x2*>(O + i * ldo + j) = o;
+        const u32x2 o = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        *(lds_u32x2_t*)(uintptr_t)a = o;
+      }
+    }
+  }
+  // direct store: 4 rows of 256 bytes per instruction
+  {
+    uint16_t* Ow = O + static_cast<int64_t>(i0w) * ldo + j0w;
+#pragma unroll 4
+    for (int s = 0; s < 32; ++s) {
+      const int row = 4 * s + (lane >> 4), u = lane & 15;
+      const u32x4 v = *(const lds_u32x4_t*)(uintptr_t)st_addr(row, u);
+      *reinterpret_cast<u32x4*>(Ow + static_cast<int64_t>(row) * ldo + 8 * u) = v;
+    }
+  }
+  if constexpr (MODE != 2) {
+    if (ti != tj) {
+      // mirrored store: out[j0w + jj][i0w + ii] = tile[ii][jj].  Instruction s
+      // covers rows ii = R .. R + 7 (R = 8 (s / 2)) and 64 columns; 16-lane
+      // group g takes columns C = 64 (s % 2) + 16 g .. + 15, lane i column C + i.
+      uint16_t* Ot = O + static_cast<int64_t>(j0w) * ldo + i0w;
+      const int g = lane >> 4, i = lane & 15;
+#pragma unroll 4
+      for (int s = 0; s < 32; ++s) {
+        const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
+        const int col = C + 4 * (i & 3);
+        const int r0 = R + (i >> 2), r1 = r0 + 4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(uintptr_t)(st_addr(r0, col >> 3) + (col & 7) * 2));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(uintptr_t)(st_addr(r1, col >> 3) + (col & 7) * 2));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+        *reinterpret_cast<u32x4*>(Ot + static_cast<int64_t>(C + i) * ldo + R) = v;
       }
     }
   }
@@ -228,7 +420,8 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
   const int n_pad = static_cast<int>(g.n_pad), m_pad = static_cast<int>(g.m_pad);
   const int tiles_m = n_pad / kBM;
   const int tiles_n = (mode == 2) ? m_pad / kBN : n_pad / kBN;
-  const int tiles_per_mat = tiles_m * tiles_n;
+  // modes 0/1: upper triangle only (symmetric results)
+  const int tiles_per_mat = (mode == 2) ? tiles_m * tiles_n : tiles_m * (tiles_m + 1) / 2;
   const int64_t blocks = static_cast<int64_t>(tiles_per_mat) * g.batch;
   dim3 grid(static_cast<unsigned>(blocks));
   switch (mode) {

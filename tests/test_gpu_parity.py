@@ -220,6 +220,8 @@ NS_CASES = [
     (1, 64, 7168, torch.float32, torch.bfloat16),   # the shared rotary key projection's shape
     (2, 512, 1792, torch.float32, torch.bfloat16),
     (1, 1, 40, torch.float32, torch.float32),
+    (1, 600, 1000, torch.float32, torch.bfloat16),  # 3 x 3 tile grid: mirrored off-diagonal tiles
+    (2, 1100, 700, torch.bfloat16, torch.float32),  # transposed, 3 x 3 grid, ragged padding
 ]
 
 
