@@ -282,12 +282,19 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // Loads of K-step kt into stage kt % kStages.  Past the last step the last
   // in-bounds tile is fetched again into a stage nobody reads, which keeps
   // the number of loads in flight (and so the wait counts) fixed.
-  auto issue = [&](int kt) {
+  auto issue_p = [&](int kt) {
     const int k0 = min(kt, KT - 1) * kBK;
-    const uint32_t sb = lds + (kt % kStages) * kStageBytes;
-    issue_kc_tile(P + i0 * ldp + k0, ldp, off_p, sb, wave);
-    if constexpr (MODE != 2) issue_kc_tile(Q + j0 * ldp + k0, ldp, off_q, sb + kTileBytes, wave);
-    else issue_x_tile(Q + static_cast<int64_t>(k0) * m_pad + j0, m_pad, off_q, sb + kTileBytes, wave);
+    issue_kc_tile(P + i0 * ldp + k0, ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
+  };
+  auto issue_q = [&](int kt) {
+    const int k0 = min(kt, KT - 1) * kBK;
+    const uint32_t sb = lds + (kt % kStages) * kStageBytes + kTileBytes;
+    if constexpr (MODE != 2) issue_kc_tile(Q + j0 * ldp + k0, ldp, off_q, sb, wave);
+    else issue_x_tile(Q + static_cast<int64_t>(k0) * m_pad + j0, m_pad, off_q, sb, wave);
+  };
+  auto issue = [&](int kt) {
+    issue_p(kt);
+    issue_q(kt);
   };
   const FragAddr fadr = frag_addresses<MODE>(lane, wm, wn);
 
@@ -312,12 +319,15 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   for (int kt = 0; kt < KT; ++kt) {
     const uint32_t cur = lds + (kt % kStages) * kStageBytes;
     const uint32_t nxt = lds + ((kt + 1) % kStages) * kStageBytes;
-    issue(kt + kStages - 1);
+    // The refill of stage kt + kStages - 1 is issued in two halves, one per
+    // half step, so no wave blocks on a burst of copies.
+    issue_p(kt + kStages - 1);
     load_frags<MODE>(fadr, cur, 1, f1);
     mfma_16(f0, acc);
     interleave_reads_with_mfma<MODE>();
-    wait_vmem<(kStages - 2) * kLoadsPerStage>();
+    wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerStage / 2>();
     __syncthreads();
+    issue_q(kt + kStages - 1);
     // After the last step this reads a stage of redundant tiles; unused.
     load_frags<MODE>(fadr, nxt, 0, f0);
     mfma_16(f1, acc);
