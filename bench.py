@@ -234,8 +234,8 @@ def run(args):
     dom_avg_ms = sum(gemm_ms[dom]) / dom_launches
     dom_avg_flops = sum(gemm_flops[dom]) / dom_launches
     achieved = dom_avg_flops / (dom_avg_ms * 1e-3) / 1e12
-    kernel_names = {0: "ns_gemm_kernel<0> (A = X X^T)", 1: "ns_gemm_kernel<1> (B = bA + cAA)",
-                    2: "ns_gemm_kernel<2> (X = aX + BX)"}
+    kernel_names = {0: "ns_gemm_kernel<0> (A = X X^T)", 1: "ns_gemm_kernel<1> (B' = aI + bA + cAA)",
+                    2: "ns_gemm_kernel<2> (X' = B'X)"}
 
     out = {
         "metric": METRIC,

@@ -106,9 +106,11 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  * not on the pages and are arguments here.  Pass out_scale =
  * sqrt(max(rows, cols)) * 0.2 for the pages' step.
  *
- * Arithmetic: the norm is accumulated in float32 (combined in double); X, A
- * and B are held in bfloat16 between the GEMMs, which run on bf16 MFMA with
- * float32 accumulation; each polynomial epilogue is float32, rounded once.
+ * Arithmetic: the norm is accumulated in float32 (combined in double); each
+ * step is evaluated as A = X X^T, B' = a_s I + b_s A + c_s A A, X <- B' X
+ * (the same polynomial, with a_s X folded into the last product); X, A and B'
+ * are held in bfloat16 between the GEMMs, which run on bf16 MFMA with float32
+ * accumulation, and each GEMM result is rounded once.
  *
  *   M              device, m_dtype (MC_F32 or MC_BF16); matrix b starts at
  *                  element b * m_batch_stride and is row-major rows x cols
@@ -121,7 +123,7 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  *   gemm_events    NULL, or host array of 6 * steps hipEvent_t (as void*):
  *                  events[2*(3s+g)] and events[2*(3s+g)+1] are recorded on
  *                  `stream` right before and after GEMM g of step s
- *                  (g = 0: X X^T, 1: b A + c A A, 2: a X + B X), for timing
+ *                  (g = 0: X X^T, 1: a I + b A + c A A, 2: B' X), for timing
  * Sizes: batch >= 0 (0 enqueues nothing); 1 <= rows, cols; min(rows, cols)
  * <= 16384 and max(rows, cols) <= 65536.
  * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EWORKSPACE, MC_EHIP.

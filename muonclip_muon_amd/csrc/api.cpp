@@ -99,13 +99,14 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   };
   for (int st = 0; st < steps; ++st) {
     const float a = coeffs[3 * st], b = coeffs[3 * st + 1], c = coeffs[3 * st + 2];
+    // X' = a X + (b A + c A^2) X = (a I + b A + c A^2) X
     const uint16_t* in0[3] = {X, A, B};
     const uint16_t* in1[3] = {nullptr, nullptr, X};
     uint16_t* out[3] = {A, B, Xn};
-    const float alpha[3] = {0.f, b, a}, beta[3] = {0.f, c, 0.f};
+    const float alpha[3] = {0.f, b, 0.f}, beta[3] = {0.f, c, 0.f}, diag[3] = {0.f, a, 0.f};
     for (int gm = 0; gm < 3; ++gm) {
       if ((e = record(2 * (3 * st + gm))) != hipSuccess) return MC_EHIP;
-      e = mc::launch_ns_gemm(gm, g, in0[gm], in1[gm], out[gm], alpha[gm], beta[gm], s);
+      e = mc::launch_ns_gemm(gm, g, in0[gm], in1[gm], out[gm], alpha[gm], beta[gm], diag[gm], s);
       if (e != hipSuccess) return MC_EHIP;
       if ((e = record(2 * (3 * st + gm) + 1)) != hipSuccess) return MC_EHIP;
     }

@@ -29,7 +29,8 @@ struct NsGeometry {
   int64_t n_pad, m_pad;  // padded to kNsTile
   bool transposed;       // rows > cols: X = M^T
   int64_t sumsq_chunks;  // partial sums per matrix
-  // byte offsets inside the workspace
+  // byte offsets inside the workspace: X (two ping-pong copies, n_pad x m_pad),
+  // A and B' (n_pad x n_pad), norm partials, 1/norm
   size_t off_x0, off_x1, off_a, off_b, off_partials, off_invnorm, total;
 };
 constexpr int64_t kNsTile = 256;
@@ -40,11 +41,12 @@ hipError_t launch_ns_norm(const void* M, bool m_bf16, int64_t m_batch_stride, co
 hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride,
                               const NsGeometry& g, char* ws, hipStream_t stream);
 // One GEMM of the polynomial step, on the whole batch:
-//   mode 0: A = X X^T          (in: X, out: A)
-//   mode 1: B = b A + c A A    (in: A, out: B)
-//   mode 2: X' = a X + B X     (in: B and X, out: X')
+//   mode 0: A = X X^T                          (in0: X, out: A)
+//   mode 1: B' = diag I + alpha A + beta A A   (in0: A, out: B')
+//   mode 2: X' = B' X                          (in0: B', in1: X, out: X')
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          uint16_t* out, float alpha, float beta, hipStream_t stream);
+                          uint16_t* out, float alpha, float beta, float diag, hipStream_t stream);
+// O_b = out_scale * X_b (rows <= cols) or X_b^T (rows > cols), rows x cols.
 hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
                             int64_t o_batch_stride, float out_scale, hipStream_t stream);
 

@@ -2,40 +2,47 @@
 //
 // One step of the odd polynomial p(X) = a X + b (X X^T) X + c (X X^T)^2 X is
 // three GEMMs on the zero-padded n_pad x m_pad bf16 state X:
-//   mode 0  A  = X X^T              K = m_pad   (out n_pad x n_pad)
-//   mode 1  B  = b A + c A A        K = n_pad   (A is symmetric, so A A = A A^T)
-//   mode 2  X' = a X + B X          K = n_pad   (out n_pad x m_pad)
+//   mode 0  A  = X X^T                    K = m_pad   (out n_pad x n_pad)
+//   mode 1  B' = a I + b A + c A A        K = n_pad   (A symmetric: A A = A^T A)
+//   mode 2  X' = B' X                     K = n_pad   (out n_pad x m_pad)
 // All three accumulate in float32 on v_mfma_f32_32x32x16_bf16 and round the
-// epilogue result once to bf16.
+// epilogue result once to bf16.  Folding a I into B' makes the third product
+// a plain GEMM (no re-read of X after its K loop); B' is then rounded once
+// with its diagonal included.  A and B' are symmetric, so modes 0/1 compute
+// only the tiles on and above the diagonal and write each off-diagonal tile
+// twice.
 //
 // Tiling: a 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output
 // tile; each wave owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 float32
-// accumulators per lane, held in AGPRs).  The K loop steps by 64 through two
-// LDS stages of 64 KB (two 256 x 64 bf16 operand tiles each).
+// accumulators per lane, held in AGPRs).  K advances 32 at a time through 5
+// LDS stages of 32 KB (two 16 KB operand tiles each).
 //
 // Global -> LDS: global_load_lds_dwordx4 moves 16 bytes per lane straight into
 // LDS (lane l of a wave lands at the instruction's LDS base + 16 l), so the
-// next stage streams in without staging registers while the current stage's
-// MFMAs run; one s_waitcnt + barrier per K step publishes it.  Because the
-// LDS slot of each lane is fixed, the XOR swizzles below are applied on the
-// global side: each lane fetches the 16 bytes that belong in its slot.
+// next stages stream in without staging registers while the current stage's
+// MFMAs run.  Because the LDS slot of each lane is fixed, the XOR swizzles
+// below are applied on the global side: each lane fetches the 16 bytes that
+// belong in its slot.
 //
-// LDS layouts.
-//  * K-contiguous tiles (both operands of modes 0/1, the left operand of
-//    mode 2): row r (an output row or column index) holds 64 consecutive k as
-//    8 units of 16 bytes, unit u at position u ^ swizzle(r).  Fragment reads
-//    are ds_read_b128.
-//  * Mode 2's right operand is X itself, row-major with K as its row index.
-//    The tile is stored as it is in memory (64 k-rows x 256 columns, 32 units
-//    per row, unit u at u ^ 4 (k & 3)) and read with ds_read_b64_tr_b16,
-//    which hands each lane 4 consecutive k of one column: two of them make
-//    an MFMA operand.  (Measured on gfx950: within each 16-lane group, lane i
-//    receives element i % 4 of the 4 x 16-bit values addressed by lanes
-//    i / 4 + 4 e, e = 0..3.)
+// Operand tiles, by the layout of the matrix they come from:
+//  * K-contiguous (mode 0: both operands are row panels of X): LDS row r (an
+//    output index) holds 32 consecutive k as 4 units of 16 bytes, unit u at
+//    u ^ swizzle(r); fragments are ds_read_b128.  One DMA instruction covers
+//    16 rows x 64 bytes.
+//  * K-rows (modes 1/2: A and B' are symmetric, so their row panels are the
+//    column panels the product needs, and X is row-major with K as its row
+//    index): 32 k-rows x 256 output indices, 512 bytes per row, unit u at
+//    u ^ 4 (r & 3).  One DMA instruction covers 2 rows x 512 bytes, which the
+//    LDS-DMA path moves about 45 % faster than 64-byte row segments
+//    (measured on MI355X, one CU: 81 vs 56 GB/s).  Fragments come from
+//    ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one column
+//    (measured on gfx950: within each 16-lane group, lane i receives element
+//    i % 4 of the 4 x 16-bit values addressed by lanes i / 4 + 4 e,
+//    e = 0..3); two of them make one 8-k MFMA operand.
 //
 // MFMA operand roles: the MFMA "A" operand is the right-hand tile (output
-// columns j) and "B" is the left-hand tile (output rows i), so each lane ends
-// up holding 4 consecutive j of one output row i per 4-register group and the
+// columns j) and "B" the left-hand tile (output rows i), so each lane ends up
+// holding 4 consecutive j of one output row i per 4-register group and the
 // epilogue reads and writes 8-byte runs.
 // Lane layout of v_mfma_f32_32x32x16_bf16 (measured on gfx950): A/B lane l
 // holds row/column l % 32, k = 8 * (l / 32) + [0, 8); result register r of
@@ -49,28 +56,28 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 256;
 constexpr int kStages = 5;                 // LDS stages in flight (prefetch distance kStages - 1)
-constexpr int kTileBytes = kBM * kBK * 2;  // 16 KB per operand tile
+constexpr int kTileBytes = kBK * kBN * 2;  // 16 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kLdsBytes = kStages * kStageBytes;
-constexpr int kLoadsPerStage = 2 * (kTileBytes / 1024) / 4;  // DMA instructions per wave per stage
+constexpr int kLoadsPerTile = kTileBytes / 1024 / 4;  // DMA instructions per wave per operand tile
+constexpr int kLoadsPerStage = 2 * kLoadsPerTile;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// K-contiguous LDS tile: row r (an output row or column index) holds 32
-// consecutive k as 4 units of 16 bytes; unit u sits at u ^ swizzle(r).  Over
-// 16 consecutive rows the pair (r & 3, swizzle(r)) takes 16 distinct values,
-// so a ds_read_b128 of consecutive rows at one unit touches 16 different
-// 16-byte bank groups per 256 bytes.
+// K-contiguous tile: unit u of row r sits at u ^ swizzle(r).  Over 16
+// consecutive rows the pair (r & 3, swizzle(r)) takes 16 distinct values, so
+// a ds_read_b128 of consecutive rows at one unit touches 16 different 16-byte
+// bank groups per 256 bytes.
 __device__ __forceinline__ int swizzle(int r) { return (r >> 2) & 3; }
 
-// Mode 2's X tile (32 k-rows x 256 columns, 32 units per row): unit u of
-// k-row r sits at u ^ xswz(r).  A transposed read touches rows r..r+3 and
-// r+8..r+11 in one 64-byte column segment; the XOR with 4 (r & 3) moves the
-// four rows to four different 64-byte bank slots.
+// K-rows tile: unit u of k-row r sits at u ^ xswz(r).  A transposed read
+// touches rows r..r+3 (and r+8..r+11) in one 64-byte column segment; the XOR
+// moves the four rows to four different 64-byte bank slots.
 __device__ __forceinline__ int xswz(int r) { return 4 * (r & 3); }
 
 // One global_load_lds_dwordx4: 16 bytes from g_uniform + lane_off to LDS
@@ -97,71 +104,77 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // Per-lane byte offsets of the tile loads.  The swizzle of a lane's row does
-// not depend on the 1 KB block it fills, so each lane has one offset per tile
-// and every load is "uniform base + lane offset" (SGPR-base addressing).
+// not depend on which 1 KB block it fills, so each lane has one offset per
+// tile and every load is "uniform base + lane offset" (SGPR-base addressing).
+// Wave w fills the 1 KB blocks b = w + 4 jj.
 //
-// K-contiguous 256 x 32 tile: wave w fills 1 KB blocks b = w + 4 jj, i.e.
-// rows 16 b .. 16 b + 15; lane l takes row 16 b + l / 4, slot l % 4, and
-// swizzle(row) = (l / 16) & 3 for every jj.
+// K-contiguous 256 x 32 tile: block b is rows 16 b .. 16 b + 15; lane l takes
+// row 16 b + l / 4, slot l % 4, and swizzle(row) = (l / 16) & 3 for every jj.
 __device__ __forceinline__ uint32_t kc_lane_offset(int64_t ld, int wave, int lane) {
   const int r = 16 * wave + (lane >> 2);
   const int u = (lane & 3) ^ ((lane >> 4) & 3);
   return static_cast<uint32_t>((r * ld + 8 * u) * 2);
 }
-// Row-major 32 x 256 X tile: wave w fills blocks b = w + 4 jj, i.e. k-rows
-// 2 b, 2 b + 1; lane l takes row 2 b + l / 32, slot l % 32, and xswz(row) =
-// 4 ((2 w + l / 32) & 3) for every jj.
-__device__ __forceinline__ uint32_t x_lane_offset(int64_t ld, int wave, int lane) {
+// K-rows 32 x 256 tile: block b is k-rows 2 b, 2 b + 1; lane l takes row
+// 2 b + l / 32, slot l % 32, and xswz(row) = 4 ((2 w + l / 32) & 3) for
+// every jj.
+__device__ __forceinline__ uint32_t kr_lane_offset(int64_t ld, int wave, int lane) {
   const int r = 2 * wave + (lane >> 5);
   const int u = (lane & 31) ^ xswz(r);
   return static_cast<uint32_t>((r * ld + 8 * u) * 2);
 }
 
-// Issue a K-contiguous tile (row 0 / column k0 at g, pitch ld elements).
-__device__ __forceinline__ void issue_kc_tile(const uint16_t* g, int64_t ld, uint32_t lane_off,
-                                              uint32_t lds, int wave) {
+// Issue one operand tile: K-contiguous (row 0, column k0 at g; block rows
+// advance by 64 per jj) or K-rows (k-row 0, column 0 at g; 8 rows per jj).
+template <bool KROWS>
+__device__ __forceinline__ void issue_tile(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
+                                           int wave) {
   const char* base = reinterpret_cast<const char*>(g);
+  constexpr int kRowsPerJ = KROWS ? 8 : 64;
 #pragma unroll
-  for (int jj = 0; jj < kTileBytes / 1024 / 4; ++jj)
-    load_lds16(base + static_cast<int64_t>(64 * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
-}
-// Issue a row-major X tile (k-row 0, column 0 at g, pitch ld).
-__device__ __forceinline__ void issue_x_tile(const uint16_t* g, int64_t ld, uint32_t lane_off,
-                                             uint32_t lds, int wave) {
-  const char* base = reinterpret_cast<const char*>(g);
-#pragma unroll
-  for (int jj = 0; jj < kTileBytes / 1024 / 4; ++jj)
-    load_lds16(base + static_cast<int64_t>(8 * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
+  for (int jj = 0; jj < kLoadsPerTile; ++jj)
+    load_lds16(base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
 }
 
-// Per-lane LDS read addresses relative to a stage.  Everything else that
-// varies inside a stage (the 32-row MFMA tile, and for X tiles the k sub-step
-// and half) is a compile-time offset, so fragment reads are ds_read
-// instructions with immediate offsets from (this + stage base).
+// K-rows tiles: per-lane LDS read address (relative to a stage) of the
+// fragment of 32-column MFMA tile x of an operand tile at tile_off, for
+// k-rows 0..7; the k sub-step (+8 KB), the upper four k (+2 KB) and the stage
+// are uniform offsets.  Lane l (16-lane group g = l / 16, i = l % 16)
+// addresses k-row 8 (g / 2) + i / 4 and columns
+// col_base + 32 x + 16 (g & 1) + 4 (i & 3) .. + 3.
+__device__ __forceinline__ uint32_t tr_addr(int tile_off, int col_base, int x, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int r = 8 * (g >> 1) + (i >> 2);
+  const int col = col_base + 32 * x + 16 * (g & 1) + 4 * (i & 3);
+  return tile_off + r * 512 + (((col >> 3) ^ xswz(r)) << 4) + (col & 7) * 2;
+}
+
+// Per-lane LDS read addresses relative to a stage; everything else that
+// varies inside a stage is a compile-time or uniform offset.
 struct FragAddr {
-  uint32_t p[2];  // left tile, per k16 sub-step
-  uint32_t q[4];  // right tile: per k16 sub-step (modes 0/1, q[0..1]) or per 32-column tile (mode 2)
+  uint32_t p[4];  // left tile: K-rows per 32-row MFMA tile y; K-contiguous per k16 sub-step (p[0..1])
+  uint32_t q[4];  // right tile: K-rows per 32-column MFMA tile x; K-contiguous per sub-step
 };
 
-template <int MODE>
+template <bool KROWS>
 __device__ __forceinline__ FragAddr frag_addresses(int lane, int wm, int wn) {
   FragAddr a;
-  const int frag_row = lane & 31, frag_half = lane >> 5, swz = swizzle(frag_row);
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int unit = (2 * ks + frag_half) ^ swz;
-    a.p[ks] = (wm * 128 + frag_row) * 64 + unit * 16;
-    if constexpr (MODE != 2) a.q[ks] = kTileBytes + (wn * 128 + frag_row) * 64 + unit * 16;
-  }
-  if constexpr (MODE == 2) {
-    // lane l: group g = l / 16, i = l % 16; it addresses k-row 8 (g / 2) + i / 4
-    // (+ 16 ks + 4 h) and columns wn*128 + 32 x + 16 (g & 1) + 4 (i & 3) .. + 3
-    const int g = lane >> 4, i = lane & 15;
-    const int r = 8 * (g >> 1) + (i >> 2);
+  if constexpr (KROWS) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      const int col = wn * 128 + 32 * x + 16 * (g & 1) + 4 * (i & 3);
-      a.q[x] = kTileBytes + r * 512 + (((col >> 3) ^ xswz(r)) << 4) + (col & 7) * 2;
+      a.p[x] = tr_addr(0, wm * 128, x, lane);
+      a.q[x] = tr_addr(kTileBytes, wn * 128, x, lane);
+    }
+  } else {
+    // lane l reads row l % 32 of each 32-row MFMA tile (+ 2 KB per tile),
+    // k = 8 (l / 32) + 16 ks .. + 7
+    const int frag_row = lane & 31, frag_half = lane >> 5, swz = swizzle(frag_row);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int unit = (2 * ks + frag_half) ^ swz;
+      a.p[ks] = (wm * 128 + frag_row) * 64 + unit * 16;
+      a.q[ks] = kTileBytes + (wn * 128 + frag_row) * 64 + unit * 16;
+      a.p[ks + 2] = a.q[ks + 2] = 0;
     }
   }
   return a;
@@ -173,25 +186,27 @@ struct Frags {
   bf16x8 b[4];  // left tile (output rows): MFMA "B" operand
 };
 
-template <int MODE>
+__device__ __forceinline__ bf16x8 tr_frag(uint32_t addr) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(addr));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(addr + 2048));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+  return as_bf16x8(v);
+}
+
+template <bool KROWS>
 __device__ __forceinline__ void load_frags(const FragAddr& fadr, uint32_t stage_base, int ks, Frags& f) {
-  const uint32_t pb = stage_base + fadr.p[ks];
+  if constexpr (KROWS) {
 #pragma unroll
-  for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
-  if constexpr (MODE != 2) {
-    const uint32_t qb = stage_base + fadr.q[ks];
+    for (int y = 0; y < 4; ++y) f.b[y] = tr_frag(stage_base + fadr.p[y] + ks * 8192);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) f.a[x] = tr_frag(stage_base + fadr.q[x] + ks * 8192);
+  } else {
+    const uint32_t pb = stage_base + fadr.p[ks], qb = stage_base + fadr.q[ks];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
 #pragma unroll
     for (int x = 0; x < 4; ++x) f.a[x] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(qb + x * 2048));
-  } else {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const uint32_t qb = stage_base + fadr.q[x] + ks * 8192;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(qb));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(qb + 2048));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
-      f.a[x] = as_bf16x8(v);
-    }
   }
 }
 
@@ -203,13 +218,13 @@ __device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
       acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
 }
 
-// Scheduling pattern for one half step: 16 MFMAs with the reads of the next
-// sub-step spread between them (4 MFMAs, then a quarter of the reads).  Left
-// alone the scheduler moves every read next to its use, which exposes LDS
-// latency with one wave per SIMD.
-template <int MODE>
+// Scheduling pattern for one half step: 16 MFMAs with the LDS reads of the
+// next sub-step spread between them (4 MFMAs, then a quarter of the reads).
+// Left alone the scheduler moves every read next to its use, which exposes
+// LDS latency with one wave per SIMD.
+template <bool KROWS>
 __device__ __forceinline__ void interleave_reads_with_mfma() {
-  constexpr int kReads = (MODE == 2) ? 12 : 8;  // DS reads per sub-step
+  constexpr int kReads = KROWS ? 16 : 8;  // DS reads per sub-step
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
@@ -217,25 +232,48 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
   }
 }
 
+// Mirrored store of a symmetric result: the wave's staged 128 x 128 bf16
+// sub-tile (row ii at eb + ii * 256, 16-byte unit u at position u ^ (ii & 15))
+// is written transposed: element (ii, jj) goes
+// to dst[jj * ld + ii].  Instruction s covers rows ii = R .. R + 7
+// (R = 8 (s / 2)) and 64 columns: 16-lane group g takes columns
+// C = 64 (s % 2) + 16 g .. + 15, lane i column C + i, which it assembles
+// from two transposed reads of 4 rows each.
+__device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int64_t ld, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll 4
+  for (int s = 0; s < 32; ++s) {
+    const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
+    const int col = C + 4 * (i & 3);
+    const int r0 = R + (i >> 2), r1 = r0 + 4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(uintptr_t)(eb + r0 * 256 + (((col >> 3) ^ (r0 & 15)) << 4) + (col & 7) * 2));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(uintptr_t)(eb + r1 * 256 + (((col >> 3) ^ (r1 & 15)) << 4) + (col & 7) * 2));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(C + i) * ld + R) = v;
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
-                    uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n,
-                    int tiles_per_mat, float alpha, float beta) {
+                    uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
+                    float alpha, float beta, float diag) {
+  constexpr bool kKRows = MODE != 0;
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
-  // ---- which matrix and tile.  Modes 0/1 produce symmetric matrices, so
-  // only tiles with ti <= tj are computed (row-major over the upper
-  // triangle); an off-diagonal tile is also written mirrored.
+  // ---- which matrix and tile.  Modes 0/1: the upper triangle (ti <= tj),
+  // row-major.  Mode 2: column-major, so tiles resident together on one XCD
+  // share X panels (and all of B's few panels) in that XCD's L2.
   const uint32_t bid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int mat = bid / tiles_per_mat;
   int t = bid % tiles_per_mat;
   int ti, tj;
   if constexpr (MODE == 2) {
-    // column-major: tiles resident together on one XCD share X column panels
-    // (and all of B's few row panels), which keeps the K-slices in its L2
     const int tiles_m = n_pad / kBM;
     ti = t % tiles_m;
     tj = t / tiles_m;
@@ -250,24 +288,29 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const int i0 = ti * kBM, j0 = tj * kBN;
 
   const int64_t nn = static_cast<int64_t>(n_pad) * n_pad, nm = static_cast<int64_t>(n_pad) * m_pad;
-  const uint16_t* P;  // left operand rows (output rows i), K-contiguous
-  const uint16_t* Q;  // right operand: rows j K-contiguous (modes 0/1) or X (mode 2)
-  int64_t ldp;
+  // Operand tile origins at k = 0 and their pitches.
+  //   mode 0: rows i0.. and j0.. of X, K-contiguous (pitch m_pad)
+  //   mode 1: k-rows of A at columns i0.. and j0.. (pitch n_pad)
+  //   mode 2: k-rows of B' at columns i0.. (pitch n_pad), of X at j0.. (m_pad)
+  const uint16_t* Pg;
+  const uint16_t* Qg;
+  int64_t ldp, ldq;
   int K;
   if constexpr (MODE == 0) {
-    P = in0 + mat * nm;
-    Q = P;
-    ldp = m_pad;
+    Pg = in0 + mat * nm + static_cast<int64_t>(i0) * m_pad;
+    Qg = in0 + mat * nm + static_cast<int64_t>(j0) * m_pad;
+    ldp = ldq = m_pad;
     K = m_pad;
   } else if constexpr (MODE == 1) {
-    P = in0 + mat * nn;
-    Q = P;
-    ldp = n_pad;
+    Pg = in0 + mat * nn + i0;
+    Qg = in0 + mat * nn + j0;
+    ldp = ldq = n_pad;
     K = n_pad;
   } else {
-    P = in0 + mat * nn;
-    Q = in1 + mat * nm;
+    Pg = in0 + mat * nn + i0;
+    Qg = in1 + mat * nm + j0;
     ldp = n_pad;
+    ldq = m_pad;
     K = n_pad;
   }
 
@@ -276,27 +319,24 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  const uint32_t off_p = kc_lane_offset(ldp, wave, lane);
-  const uint32_t off_q = (MODE != 2) ? off_p : x_lane_offset(m_pad, wave, lane);
+  const uint32_t off_p = kKRows ? kr_lane_offset(ldp, wave, lane) : kc_lane_offset(ldp, wave, lane);
+  const uint32_t off_q = (MODE == 2) ? kr_lane_offset(ldq, wave, lane) : off_p;
   const int KT = K / kBK;
   // Loads of K-step kt into stage kt % kStages.  Past the last step the last
   // in-bounds tile is fetched again into a stage nobody reads, which keeps
   // the number of loads in flight (and so the wait counts) fixed.
+  auto k_offset = [&](int kt, int64_t ld) -> int64_t {
+    const int64_t k0 = min(kt, KT - 1) * kBK;
+    return kKRows ? k0 * ld : k0;
+  };
   auto issue_p = [&](int kt) {
-    const int k0 = min(kt, KT - 1) * kBK;
-    issue_kc_tile(P + i0 * ldp + k0, ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
+    issue_tile<kKRows>(Pg + k_offset(kt, ldp), ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
   };
   auto issue_q = [&](int kt) {
-    const int k0 = min(kt, KT - 1) * kBK;
-    const uint32_t sb = lds + (kt % kStages) * kStageBytes + kTileBytes;
-    if constexpr (MODE != 2) issue_kc_tile(Q + j0 * ldp + k0, ldp, off_q, sb, wave);
-    else issue_x_tile(Q + static_cast<int64_t>(k0) * m_pad + j0, m_pad, off_q, sb, wave);
+    issue_tile<kKRows>(Qg + k_offset(kt, ldq), ldq, off_q, lds + (kt % kStages) * kStageBytes + kTileBytes,
+                       wave);
   };
-  auto issue = [&](int kt) {
-    issue_p(kt);
-    issue_q(kt);
-  };
-  const FragAddr fadr = frag_addresses<MODE>(lane, wm, wn);
+  const FragAddr fadr = frag_addresses<kKRows>(lane, wm, wn);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -306,45 +346,45 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 
   // ---- main loop: kStages - 1 K-steps in flight.  At step kt the stage of
   // kt + kStages - 1 is refilled (it was last read at step kt - 1, before the
-  // barrier), stage kt is consumed, and the wait leaves only the loads of the
-  // kStages - 2 newest steps outstanding, so step kt + 1 is complete.  The
-  // two k16 sub-steps of a step are software-pipelined across the barrier:
-  // sub-step 1's fragments load under sub-step 0's MFMAs, and the next
-  // step's sub-step 0 fragments load under sub-step 1's MFMAs.
-  for (int s = 0; s < kStages - 1; ++s) issue(s);
+  // barrier) in two halves, one per half step, so no wave blocks on a burst of
+  // copies; stage kt is consumed; the mid-step wait leaves only newer loads
+  // outstanding, so step kt + 1 is complete.  The two k16 sub-steps of a
+  // step are software-pipelined across the barrier: sub-step 1's fragments
+  // load under sub-step 0's MFMAs, and the next step's sub-step 0 fragments
+  // load under sub-step 1's MFMAs.
+  for (int s = 0; s < kStages - 1; ++s) {
+    issue_p(s);
+    issue_q(s);
+  }
   wait_vmem<(kStages - 2) * kLoadsPerStage>();
   __syncthreads();
   Frags f0, f1;
-  load_frags<MODE>(fadr, lds, 0, f0);
+  load_frags<kKRows>(fadr, lds, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
     const uint32_t cur = lds + (kt % kStages) * kStageBytes;
     const uint32_t nxt = lds + ((kt + 1) % kStages) * kStageBytes;
-    // The refill of stage kt + kStages - 1 is issued in two halves, one per
-    // half step, so no wave blocks on a burst of copies.
     issue_p(kt + kStages - 1);
-    load_frags<MODE>(fadr, cur, 1, f1);
+    load_frags<kKRows>(fadr, cur, 1, f1);
     mfma_16(f0, acc);
-    interleave_reads_with_mfma<MODE>();
-    wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerStage / 2>();
+    interleave_reads_with_mfma<kKRows>();
+    wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerTile>();
     __syncthreads();
     issue_q(kt + kStages - 1);
     // After the last step this reads a stage of redundant tiles; unused.
-    load_frags<MODE>(fadr, nxt, 0, f0);
+    load_frags<kKRows>(fadr, nxt, 0, f0);
     mfma_16(f1, acc);
-    interleave_reads_with_mfma<MODE>();
+    interleave_reads_with_mfma<kKRows>();
   }
-  wait_vmem<0>();
 
   // ---- epilogue, staged through LDS (free once every stage is consumed).
   // Wave w owns the 128 x 128 sub-tile at rows i0 + 128 wm, columns
   // j0 + 128 wn, staged at lds + 32 KB w: row ii at ii * 256 bytes, 16-byte
   // unit u at position u ^ (ii & 15).  Global traffic is whole 256-byte rows:
-  //   modes 1/2: the epilogue operand sub-tile (A or X) is copied in by DMA;
-  //   every lane combines its accumulators with it (or just rounds, mode 0)
-  //   in place, in bf16;
+  //   mode 1: the A sub-tile is copied in by DMA and every lane combines it
+  //   with its accumulators, b A + c (A A) (+ a on the diagonal), in place;
+  //   modes 0/2: every lane rounds its accumulators into place;
   //   the sub-tile is stored row by row, 16 bytes per lane;
-  //   modes 0/1, off-diagonal tiles: it is also stored mirrored, each lane
-  //   assembling 8 consecutive rows of one column with two transposed reads.
+  //   modes 0/1, off-diagonal tiles: it is also stored mirrored.
   wait_vmem<0>();
   __syncthreads();
   const int frag_row = lane & 31, frag_half = lane >> 5;
@@ -354,8 +394,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const uint32_t eb = lds + wave * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
 
-  if constexpr (MODE == 1 || MODE == 2) {
-    const uint16_t* E = ((MODE == 1) ? in0 + mat * nn : in1 + mat * nm) + static_cast<int64_t>(i0w) * ldo + j0w;
+  if constexpr (MODE == 1) {
+    const uint16_t* E = in0 + mat * nn + static_cast<int64_t>(i0w) * ldo + j0w;
     const char* ebase = reinterpret_cast<const char*>(E);
 #pragma unroll 4
     for (int s = 0; s < 32; ++s) {
@@ -365,7 +405,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     }
     wait_vmem<0>();
   }
-  typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
+  // a I lands on the wave's sub-tile only if it straddles the diagonal
+  const bool on_diag = MODE == 1 && i0w == j0w;
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
     const int ii = y * 32 + frag_row;
@@ -374,17 +415,18 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t a = st_addr(ii, 4 * x + g) + 8 * frag_half;
-        float v0 = acc[x][y][4 * g + 0], v1 = acc[x][y][4 * g + 1];
-        float v2 = acc[x][y][4 * g + 2], v3 = acc[x][y][4 * g + 3];
-        if constexpr (MODE == 1 || MODE == 2) {
+        float v[4] = {acc[x][y][4 * g + 0], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]};
+        if constexpr (MODE == 1) {
           const u32x2 e = *(const lds_u32x2_t*)(uintptr_t)a;
-          const float sa = alpha, sb = (MODE == 1) ? beta : 1.0f;
-          v0 = sa * bf16_lo(e.x) + sb * v0;
-          v1 = sa * bf16_hi(e.x) + sb * v1;
-          v2 = sa * bf16_lo(e.y) + sb * v2;
-          v3 = sa * bf16_hi(e.y) + sb * v3;
+          const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
+          const int jj0 = 32 * x + 8 * g + 4 * frag_half;  // column of v[0] within the sub-tile
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float scaled = alpha * ev[q] + beta * v[q];
+            v[q] = (on_diag && ii == jj0 + q) ? scaled + diag : scaled;
+          }
         }
-        const u32x2 o = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *(lds_u32x2_t*)(uintptr_t)a = o;
       }
     }
@@ -400,33 +442,14 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     }
   }
   if constexpr (MODE != 2) {
-    if (ti != tj) {
-      // mirrored store: out[j0w + jj][i0w + ii] = tile[ii][jj].  Instruction s
-      // covers rows ii = R .. R + 7 (R = 8 (s / 2)) and 64 columns; 16-lane
-      // group g takes columns C = 64 (s % 2) + 16 g .. + 15, lane i column C + i.
-      uint16_t* Ot = O + static_cast<int64_t>(j0w) * ldo + i0w;
-      const int g = lane >> 4, i = lane & 15;
-#pragma unroll 4
-      for (int s = 0; s < 32; ++s) {
-        const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
-        const int col = C + 4 * (i & 3);
-        const int r0 = R + (i >> 2), r1 = r0 + 4;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(uintptr_t)(st_addr(r0, col >> 3) + (col & 7) * 2));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(uintptr_t)(st_addr(r1, col >> 3) + (col & 7) * 2));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
-        *reinterpret_cast<u32x4*>(Ot + static_cast<int64_t>(C + i) * ldo + R) = v;
-      }
-    }
+    if (ti != tj) store_transposed(eb, O + static_cast<int64_t>(j0w) * n_pad + i0w, n_pad, lane);
   }
 }
 
 }  // namespace
 
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          uint16_t* out, float alpha, float beta, hipStream_t stream) {
+                          uint16_t* out, float alpha, float beta, float diag, hipStream_t stream) {
   const int n_pad = static_cast<int>(g.n_pad), m_pad = static_cast<int>(g.m_pad);
   const int tiles_m = n_pad / kBM;
   const int tiles_n = (mode == 2) ? m_pad / kBN : n_pad / kBN;
@@ -436,16 +459,16 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
   dim3 grid(static_cast<unsigned>(blocks));
   switch (mode) {
     case 0:
-      hipLaunchKernelGGL(ns_gemm_kernel<0>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad,
-                         m_pad, tiles_n, tiles_per_mat, alpha, beta);
+      hipLaunchKernelGGL(ns_gemm_kernel<0>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad,
+                         tiles_n, tiles_per_mat, alpha, beta, diag);
       break;
     case 1:
-      hipLaunchKernelGGL(ns_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad,
-                         m_pad, tiles_n, tiles_per_mat, alpha, beta);
+      hipLaunchKernelGGL(ns_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad,
+                         tiles_n, tiles_per_mat, alpha, beta, diag);
       break;
     default:
-      hipLaunchKernelGGL(ns_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad,
-                         m_pad, tiles_n, tiles_per_mat, alpha, beta);
+      hipLaunchKernelGGL(ns_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad,
+                         tiles_n, tiles_per_mat, alpha, beta, diag);
       break;
   }
   return hipGetLastError();

@@ -4,10 +4,12 @@
 //             then one block per matrix combines them in double in a fixed
 //             order (deterministic), giving inv_b = 1 / (||M_b||_F + eps).
 //   prescale  X_0 = bf16(inv_b * M_b), or of M_b^T when rows > cols, written
-//             into the zero-padded n_pad x m_pad workspace layout the GEMMs use.
+//             into the zero-padded n_pad x m_pad workspace layout the GEMMs
+//             use.
 //   output    O_b = out_scale * X (or X^T), cast to the output dtype.
-// The transposing variants go through a 64 x 64 LDS tile so both the read
-// and the write side are coalesced.
+// Both move 8-element runs (16-byte vectors where the row length and the
+// alignment allow); the transposing variants go through a 64 x 64 LDS tile so
+// both the read and the write side are coalesced.
 
 #include "mc_device.h"
 #include "mc_internal.h"
@@ -102,57 +104,74 @@ __global__ __launch_bounds__(kThreads) void invnorm_kernel(const float* __restri
   if (threadIdx.x == 0) invnorm[b] = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(eps)));
 }
 
-// Straight pre-scale (rows <= cols): X0[i][k] = bf16(inv * M[i][k]); one
-// thread per 8 consecutive k of the padded row.  grid (ceil(n_pad*m_pad/8/256), batch)
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void prescale_kernel(const void* __restrict__ M,
-                                                           int64_t batch_stride, int64_t n, int64_t m,
-                                                           int64_t n_pad, int64_t m_pad,
-                                                           const float* __restrict__ invnorm,
-                                                           uint16_t* __restrict__ X0) {
-  const int64_t b = blockIdx.y;
-  const int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per_row = m_pad / 8;
-  if (v >= n_pad * per_row) return;
-  const int64_t i = v / per_row, k = (v % per_row) * 8;
-  const float inv = invnorm[b];
-  const char* base = static_cast<const char*>(M) + static_cast<size_t>(b * batch_stride) * (BF16 ? 2 : 4);
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    x[e] = (i < n && k + e < m) ? load_elem<BF16>(base, i * m + k + e) * inv : 0.f;
-  u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-             pack_bf16x2(x[6], x[7])};
-  *reinterpret_cast<u32x4*>(X0 + static_cast<size_t>(b) * n_pad * m_pad + i * m_pad + k) = o;
-}
-
-// Transposing pre-scale (rows > cols): X0[i][k] = bf16(inv * M[k][i]) with M
-// rows x cols = m x n.  grid (m_pad/64, n_pad/64, batch); tile over (k, i).
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void prescale_t_kernel(const void* __restrict__ M,
-                                                             int64_t batch_stride, int64_t n,
-                                                             int64_t m, int64_t n_pad, int64_t m_pad,
-                                                             const float* __restrict__ invnorm,
-                                                             uint16_t* __restrict__ X0) {
+// Pre-scale.  M_b is R x C (rows x cols); it is scaled by
+// inv_b = 1 / (||M_b||_F + eps), rounded once to bf16 and written zero-padded
+// either as it is into S (R_pad x C_pad; rows <= cols: X_0 = M) or transposed
+// into T (C_pad x R_pad; rows > cols: X_0 = M^T); the other pointer is null.
+// grid (C_pad / 64, R_pad / 64, batch); each block reads one 64 x 64 tile in
+// 8-element runs (vector loads when VEC) and writes it straight from
+// registers or transposed through LDS.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void prescale_kernel(const void* __restrict__ M, int64_t batch_stride,
+                                                           int64_t R, int64_t C, int64_t R_pad,
+                                                           int64_t C_pad, const float* __restrict__ invnorm,
+                                                           uint16_t* __restrict__ S,
+                                                           uint16_t* __restrict__ T) {
   __shared__ float tile[kT][kT + 1];
   const int64_t b = blockIdx.z;
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kT, i0 = static_cast<int64_t>(blockIdx.y) * kT;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kT, r0 = static_cast<int64_t>(blockIdx.y) * kT;
   const float inv = invnorm[b];
   const char* base = static_cast<const char*>(M) + static_cast<size_t>(b * batch_stride) * (BF16 ? 2 : 4);
-  // read M[k0 + r][i0 + c] (row r of the tile is a row of M; M has n columns)
-  for (int t = threadIdx.x; t < kT * kT; t += kThreads) {
-    const int r = t / kT, c = t % kT;
-    const int64_t k = k0 + r, i = i0 + c;
-    tile[r][c] = (k < m && i < n) ? load_elem<BF16>(base, k * n + i) * inv : 0.f;
+  uint16_t* sb = S + static_cast<size_t>(b) * R_pad * C_pad;
+  uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
+  const int q = threadIdx.x & 7;  // 8-element run within a row
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = pass * 32 + (threadIdx.x >> 3);
+    const int64_t r = r0 + rr, c = c0 + 8 * q;
+    float x[8];
+    if constexpr (VEC) {
+      // C % 8 == 0: a run is wholly inside or wholly outside the matrix
+      if (r < R && c < C) {
+        if constexpr (BF16) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(base + (r * C + c) * 2);
+          x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+          x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+        } else {
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(base + (r * C + c) * 4);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(base + (r * C + c + 4) * 4);
+          x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+          x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= inv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (r < R && c + e < C) ? load_elem<BF16>(base, r * C + c + e) * inv : 0.f;
+    }
+    if (S != nullptr) {
+      const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                       pack_bf16x2(x[6], x[7])};
+      *reinterpret_cast<u32x4*>(sb + r * C_pad + c) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
+    }
   }
+  if (S != nullptr) return;
   __syncthreads();
-  // write X0[i0 + r][k0 + c .. +7] = tile[c..][r]
-  uint16_t* xb = X0 + static_cast<size_t>(b) * n_pad * m_pad;
-  for (int t = threadIdx.x; t < kT * kT / 8; t += kThreads) {
-    const int r = t / (kT / 8), c = (t % (kT / 8)) * 8;
-    u32x4 o = {pack_bf16x2(tile[c + 0][r], tile[c + 1][r]), pack_bf16x2(tile[c + 2][r], tile[c + 3][r]),
-               pack_bf16x2(tile[c + 4][r], tile[c + 5][r]), pack_bf16x2(tile[c + 6][r], tile[c + 7][r])};
-    *reinterpret_cast<u32x4*>(xb + (i0 + r) * m_pad + k0 + c) = o;
+  // T[c0 + cc][r0 + 8 q' .. + 7] = tile[8 q' ..][cc]
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cc = pass * 32 + (threadIdx.x >> 3);
+    const int rq = 8 * q;
+    const u32x4 o = {pack_bf16x2(tile[rq + 0][cc], tile[rq + 1][cc]), pack_bf16x2(tile[rq + 2][cc], tile[rq + 3][cc]),
+                     pack_bf16x2(tile[rq + 4][cc], tile[rq + 5][cc]), pack_bf16x2(tile[rq + 6][cc], tile[rq + 7][cc])};
+    *reinterpret_cast<u32x4*>(tb + (c0 + cc) * R_pad + r0 + rq) = o;
   }
 }
 
@@ -162,44 +181,104 @@ __device__ __forceinline__ void store_out(void* O, int64_t idx, float v) {
   else static_cast<float*>(O)[idx] = v;
 }
 
-// Straight output: O[r][c] = s * X[r][c], r < rows = n, c < cols = m.
-// grid (ceil(rows*cols/256), batch)
+// Output, element by element: O[r][c] = s * src[r][c] (src pitch sp).
+// grid (ceil(R * C / 256), batch)
 template <bool OBF16>
-__global__ __launch_bounds__(kThreads) void output_kernel(const uint16_t* __restrict__ X, int64_t n,
-                                                         int64_t m, int64_t n_pad, int64_t m_pad,
-                                                         void* __restrict__ O, int64_t o_stride,
-                                                         float s) {
+__global__ __launch_bounds__(kThreads) void output_kernel(const uint16_t* __restrict__ src, int64_t R,
+                                                         int64_t C, int64_t sp, int64_t src_stride,
+                                                         void* __restrict__ O, int64_t o_stride, float s) {
   const int64_t b = blockIdx.y;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= n * m) return;
-  const int64_t r = e / m, c = e % m;
-  const float x = bf16_to_f32(X[static_cast<size_t>(b) * n_pad * m_pad + r * m_pad + c]);
+  if (e >= R * C) return;
+  const int64_t r = e / C, c = e % C;
+  const float x = bf16_to_f32(src[b * src_stride + r * sp + c]);
   char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride) * (OBF16 ? 2 : 4);
   store_out<OBF16>(ob, e, x * s);
 }
 
-// Transposing output: O[r][c] = s * X[c][r], O is rows x cols = m x n.
-// grid (m_pad/64, n_pad/64, batch); tile over (c in X rows, r in X cols).
+// Output, 8 elements per thread (C % 8 == 0 and 16-byte aligned rows of O).
+// grid (ceil(R * C / 8 / 256), batch)
 template <bool OBF16>
-__global__ __launch_bounds__(kThreads) void output_t_kernel(const uint16_t* __restrict__ X, int64_t n,
-                                                           int64_t m, int64_t n_pad, int64_t m_pad,
+__global__ __launch_bounds__(kThreads) void output_vec_kernel(const uint16_t* __restrict__ src, int64_t R,
+                                                             int64_t C, int64_t sp, int64_t src_stride,
+                                                             void* __restrict__ O, int64_t o_stride,
+                                                             float s) {
+  const int64_t b = blockIdx.y;
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t per_row = C / 8;
+  if (v >= R * per_row) return;
+  const int64_t r = v / per_row, c = (v % per_row) * 8;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(src + b * src_stride + r * sp + c);
+  const float y[8] = {bf16_lo(x.x) * s, bf16_hi(x.x) * s, bf16_lo(x.y) * s, bf16_hi(x.y) * s,
+                      bf16_lo(x.z) * s, bf16_hi(x.z) * s, bf16_lo(x.w) * s, bf16_hi(x.w) * s};
+  char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride + r * C + c) * (OBF16 ? 2 : 4);
+  if constexpr (OBF16) {
+    const u32x4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                     pack_bf16x2(y[6], y[7])};
+    *reinterpret_cast<u32x4*>(ob) = o;
+  } else {
+    const f32x4 o0 = {y[0], y[1], y[2], y[3]}, o1 = {y[4], y[5], y[6], y[7]};
+    reinterpret_cast<f32x4*>(ob)[0] = o0;
+    reinterpret_cast<f32x4*>(ob)[1] = o1;
+  }
+}
+
+// Transposing output (rows > cols): O[r][c] = s * X[c][r], O is R x C =
+// m x n, X is n_pad x m_pad.  grid (R_pad / 64, C_pad / 64, batch): each block
+// reads 64 rows x 64 columns of X in 16-byte runs and writes the transposed
+// 64 x 64 block of O, in 8-element runs when VEC (C % 8 == 0 and 16-byte
+// aligned rows), else element by element.
+template <bool OBF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void output_t_kernel(const uint16_t* __restrict__ X, int64_t R,
+                                                           int64_t C, int64_t m_pad, int64_t src_stride,
                                                            void* __restrict__ O, int64_t o_stride,
                                                            float s) {
   __shared__ float tile[kT][kT + 1];
   const int64_t b = blockIdx.z;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kT, c0 = static_cast<int64_t>(blockIdx.y) * kT;
-  const uint16_t* xb = X + static_cast<size_t>(b) * n_pad * m_pad;
+  const uint16_t* xb = X + b * src_stride;
+  const int q = threadIdx.x & 7;
   // tile[cc][rr] = X[c0 + cc][r0 + rr]
-  for (int t = threadIdx.x; t < kT * kT; t += kThreads) {
-    const int cc = t / kT, rr = t % kT;
-    tile[cc][rr] = bf16_to_f32(xb[(c0 + cc) * m_pad + r0 + rr]);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cc = pass * 32 + (threadIdx.x >> 3);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + (c0 + cc) * m_pad + r0 + 8 * q);
+    tile[cc][8 * q + 0] = bf16_lo(v.x) * s;
+    tile[cc][8 * q + 1] = bf16_hi(v.x) * s;
+    tile[cc][8 * q + 2] = bf16_lo(v.y) * s;
+    tile[cc][8 * q + 3] = bf16_hi(v.y) * s;
+    tile[cc][8 * q + 4] = bf16_lo(v.z) * s;
+    tile[cc][8 * q + 5] = bf16_hi(v.z) * s;
+    tile[cc][8 * q + 6] = bf16_lo(v.w) * s;
+    tile[cc][8 * q + 7] = bf16_hi(v.w) * s;
   }
   __syncthreads();
   char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride) * (OBF16 ? 2 : 4);
-  for (int t = threadIdx.x; t < kT * kT; t += kThreads) {
-    const int rr = t / kT, cc = t % kT;
-    const int64_t r = r0 + rr, c = c0 + cc;
-    if (r < m && c < n) store_out<OBF16>(ob, r * n + c, tile[cc][rr] * s);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = pass * 32 + (threadIdx.x >> 3);
+    const int64_t r = r0 + rr, c = c0 + 8 * q;
+    if (r >= R) continue;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = tile[8 * q + e][rr];
+    if constexpr (VEC) {
+      if (c >= C) continue;  // C % 8 == 0: the run is wholly in or out
+      char* dst = ob + (r * C + c) * (OBF16 ? 2 : 4);
+      if constexpr (OBF16) {
+        const u32x4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                         pack_bf16x2(y[6], y[7])};
+        *reinterpret_cast<u32x4*>(dst) = o;
+      } else {
+        const f32x4 o0 = {y[0], y[1], y[2], y[3]}, o1 = {y[4], y[5], y[6], y[7]};
+        reinterpret_cast<f32x4*>(dst)[0] = o0;
+        reinterpret_cast<f32x4*>(dst)[1] = o1;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e < C) store_out<OBF16>(ob, r * C + c + e, y[e]);
+    }
   }
 }
 
@@ -227,48 +306,67 @@ hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride
                               const NsGeometry& g, char* ws, hipStream_t stream) {
   const float* invnorm = reinterpret_cast<const float*>(ws + g.off_invnorm);
   uint16_t* X0 = reinterpret_cast<uint16_t*>(ws + g.off_x0);
-  if (!g.transposed) {
-    const int64_t vecs = g.n_pad * g.m_pad / 8;
-    dim3 grid(static_cast<unsigned>((vecs + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
-    if (m_bf16)
-      hipLaunchKernelGGL(prescale_kernel<true>, grid, dim3(kThreads), 0, stream, M, m_batch_stride, g.n,
-                         g.m, g.n_pad, g.m_pad, invnorm, X0);
-    else
-      hipLaunchKernelGGL(prescale_kernel<false>, grid, dim3(kThreads), 0, stream, M, m_batch_stride,
-                         g.n, g.m, g.n_pad, g.m_pad, invnorm, X0);
+  // M is R x C = rows x cols; X_0 = M (straight) or M^T (transposed)
+  const int64_t R = g.rows, C = g.cols;
+  const int64_t R_pad = g.transposed ? g.m_pad : g.n_pad, C_pad = g.transposed ? g.n_pad : g.m_pad;
+  uint16_t* S = g.transposed ? nullptr : X0;
+  uint16_t* T = g.transposed ? X0 : nullptr;
+  const size_t esz = m_bf16 ? 2 : 4;
+  const bool vec = C % 8 == 0 && (g.batch == 1 || m_batch_stride % 8 == 0) &&
+                   reinterpret_cast<uintptr_t>(M) % (8 * esz) == 0;
+  dim3 grid(static_cast<unsigned>(C_pad / kT), static_cast<unsigned>(R_pad / kT), static_cast<unsigned>(g.batch));
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, m_batch_stride, R, C, R_pad, C_pad, invnorm,
+                       S, T);
+  };
+  if (m_bf16) {
+    if (vec) go(prescale_kernel<true, true>);
+    else go(prescale_kernel<true, false>);
   } else {
-    dim3 grid(static_cast<unsigned>(g.m_pad / kT), static_cast<unsigned>(g.n_pad / kT),
-              static_cast<unsigned>(g.batch));
-    if (m_bf16)
-      hipLaunchKernelGGL(prescale_t_kernel<true>, grid, dim3(kThreads), 0, stream, M, m_batch_stride,
-                         g.n, g.m, g.n_pad, g.m_pad, invnorm, X0);
-    else
-      hipLaunchKernelGGL(prescale_t_kernel<false>, grid, dim3(kThreads), 0, stream, M, m_batch_stride,
-                         g.n, g.m, g.n_pad, g.m_pad, invnorm, X0);
+    if (vec) go(prescale_kernel<false, true>);
+    else go(prescale_kernel<false, false>);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
                             int64_t o_batch_stride, float out_scale, hipStream_t stream) {
-  if (!g.transposed) {
-    const int64_t count = g.n * g.m;
-    dim3 grid(static_cast<unsigned>((count + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
-    if (o_bf16)
-      hipLaunchKernelGGL(output_kernel<true>, grid, dim3(kThreads), 0, stream, X, g.n, g.m, g.n_pad,
-                         g.m_pad, O, o_batch_stride, out_scale);
-    else
-      hipLaunchKernelGGL(output_kernel<false>, grid, dim3(kThreads), 0, stream, X, g.n, g.m, g.n_pad,
-                         g.m_pad, O, o_batch_stride, out_scale);
-  } else {
+  const int64_t R = g.rows, C = g.cols;
+  const int64_t src_stride = g.n_pad * g.m_pad;
+  const bool vec = C % 8 == 0 && (g.batch == 1 || o_batch_stride % 8 == 0) &&
+                   reinterpret_cast<uintptr_t>(O) % 16 == 0;
+  if (g.transposed) {
     dim3 grid(static_cast<unsigned>(g.m_pad / kT), static_cast<unsigned>(g.n_pad / kT),
               static_cast<unsigned>(g.batch));
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O, o_batch_stride,
+                         out_scale);
+    };
+    if (o_bf16) {
+      if (vec) go(output_t_kernel<true, true>);
+      else go(output_t_kernel<true, false>);
+    } else {
+      if (vec) go(output_t_kernel<false, true>);
+      else go(output_t_kernel<false, false>);
+    }
+  } else if (vec) {
+    const int64_t vecs = R * C / 8;
+    dim3 grid(static_cast<unsigned>((vecs + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
     if (o_bf16)
-      hipLaunchKernelGGL(output_t_kernel<true>, grid, dim3(kThreads), 0, stream, X, g.n, g.m, g.n_pad,
-                         g.m_pad, O, o_batch_stride, out_scale);
+      hipLaunchKernelGGL(output_vec_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O,
+                         o_batch_stride, out_scale);
     else
-      hipLaunchKernelGGL(output_t_kernel<false>, grid, dim3(kThreads), 0, stream, X, g.n, g.m,
-                         g.n_pad, g.m_pad, O, o_batch_stride, out_scale);
+      hipLaunchKernelGGL(output_vec_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride,
+                         O, o_batch_stride, out_scale);
+  } else {
+    const int64_t count = R * C;
+    dim3 grid(static_cast<unsigned>((count + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
+    if (o_bf16)
+      hipLaunchKernelGGL(output_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O,
+                         o_batch_stride, out_scale);
+    else
+      hipLaunchKernelGGL(output_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O,
+                         o_batch_stride, out_scale);
   }
   return hipGetLastError();
 }

@@ -222,6 +222,10 @@ NS_CASES = [
     (1, 1, 40, torch.float32, torch.float32),
     (1, 600, 1000, torch.float32, torch.bfloat16),  # 3 x 3 tile grid: mirrored off-diagonal tiles
     (2, 1100, 700, torch.bfloat16, torch.float32),  # transposed, 3 x 3 grid, ragged padding
+    # 16-byte vector and element-wise variants of the pre-scale and output copies
+    (2, 256, 1024, torch.bfloat16, torch.float32),  # bf16 M, vector loads; float32 O, vector stores
+    (1, 700, 96, torch.bfloat16, torch.bfloat16),   # transposed, vector paths
+    (1, 130, 50, torch.float32, torch.bfloat16),    # transposed, element-wise paths
 ]
 
 
@@ -238,6 +242,27 @@ def test_newton_schulz(mc, case):
         ref = oracle.muon_orthogonalised_update(f64(M[b]))
         err = rel_fro(f64(O[b]), ref)
         assert err <= 2e-2, (b, err)
+
+
+def test_newton_schulz_misaligned(mc):
+    """M and O that start one element past a 16-byte boundary (row length a
+    multiple of 8): the copies must fall back to element-wise access."""
+    say("newton-schulz misaligned")
+    batch, rows, cols = 2, 192, 320
+    g = workloads.generator(77, "cpu")
+    M = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32)
+    Mbuf = torch.zeros(batch * rows * cols + 1, device=DEV)
+    Mbuf[1:] = M.reshape(-1).to(DEV)
+    Obuf = torch.full((batch * rows * cols + 1,), 7.0, device=DEV, dtype=torch.bfloat16)
+    Mv = Mbuf[1:].view(batch, rows, cols)
+    Ov = Obuf[1:].view(batch, rows, cols)
+    scale = mc.muon_out_scale(rows, cols)
+    mc.muon_ns_orthogonalize_batched(Mv, Ov, out_scale=scale)
+    torch.cuda.synchronize()
+    assert Obuf[0].item() == 7.0
+    for b in range(batch):
+        ref = oracle.muon_orthogonalised_update(f64(M[b]))
+        assert rel_fro(f64(Ov[b]), ref) <= 2e-2
 
 
 def test_newton_schulz_zero_matrix(mc):
