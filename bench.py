@@ -138,7 +138,7 @@ def run(args):
     ws_bytes = max(mc.muon_ns_workspace_bytes(min(chunk, n), r, c) for _, _, n, r, c in wl.groups)
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     o_elems = max(min(chunk, n) * r * c for _, _, n, r, c in wl.groups)
-    O_buf = torch.empty(o_elems, dtype=torch.bfloat16, device=dev)
+    O_buf = torch.empty(o_elems if args.unfused else 1, dtype=torch.bfloat16, device=dev)
     smax = torch.empty(N_HEADS, dtype=torch.float32, device=dev)
     gamma = torch.empty(N_HEADS, dtype=torch.float32, device=dev)
     clipped = torch.empty(N_HEADS, dtype=torch.int32, device=dev)
@@ -159,15 +159,22 @@ def run(args):
     ns_ev = [(ev(), ev()) for _ in ns_calls]
 
     def step(timed):
-        e = call_ev["momentum"]
-        timed and e[0].record(stream)
-        mc.muonclip_momentum(wl.M, wl.G, MU)
-        timed and e[1].record(stream)
+        if args.unfused:
+            e = call_ev["momentum"]
+            timed and e[0].record(stream)
+            mc.muonclip_momentum(wl.M, wl.G, MU)
+            timed and e[1].record(stream)
         for k, (name, s, cnt, rows, cols) in enumerate(ns_calls):
             M = wl.view(name, wl.M, s, cnt)
             W = wl.view(name, wl.W, s, cnt)
-            O = O_buf[:cnt * rows * cols].view(cnt, rows, cols)
             timed and ns_ev[k][0].record(stream)
+            if not args.unfused:
+                # momentum, Newton-Schulz and update of the chunk in one call
+                mc.muon_momentum_ns_update_batched(M, wl.view(name, wl.G, s, cnt), W, LR, WD, MU,
+                                                   workspace=workspace, gemm_events=gemm_ev[k] if timed else None)
+                timed and ns_ev[k][1].record(stream)
+                continue
+            O = O_buf[:cnt * rows * cols].view(cnt, rows, cols)
             mc.muon_ns_orthogonalize_batched(M, O, workspace=workspace, out_scale=mc.muon_out_scale(rows, cols),
                                              gemm_events=gemm_ev[k] if timed else None)
             timed and ns_ev[k][1].record(stream)
@@ -200,11 +207,12 @@ def run(args):
     for i in range(args.steps):
         step(True)
         torch.cuda.synchronize()  # read this step's events before re-recording them
-        for k in ("momentum", "maxlogit", "clip"):
+        for k in ("momentum", "maxlogit", "clip") if args.unfused else ("maxlogit", "clip"):
             acc[k] += call_ev[k][0].elapsed_time(call_ev[k][1])
         for k, (name, s, cnt, rows, cols) in enumerate(ns_calls):
             acc["ns"] += ns_ev[k][0].elapsed_time(ns_ev[k][1])
-            acc["update"] += upd_ev[k][0].elapsed_time(upd_ev[k][1])
+            if args.unfused:
+                acc["update"] += upd_ev[k][0].elapsed_time(upd_ev[k][1])
             n_, m_ = min(rows, cols), max(rows, cols)
             per = {0: 2 * n_ * n_ * m_, 1: 2 * n_ ** 3, 2: 2 * n_ * n_ * m_}
             for st in range(steps_ns):
@@ -235,7 +243,33 @@ def run(args):
     dom_avg_flops = sum(gemm_flops[dom]) / dom_launches
     achieved = dom_avg_flops / (dom_avg_ms * 1e-3) / 1e12
     kernel_names = {0: "ns_gemm_kernel<0> (A = X X^T)", 1: "ns_gemm_kernel<1> (B' = aI + bA + cAA)",
-                    2: "ns_gemm_kernel<2> (X' = B'X)"}
+                    2: "ns_gemm_kernel<2> (X' = B'X)" if args.unfused else
+                    "ns_gemm_kernel<2, *> (X' = B'X; the last step's launch applies the update to W)"}
+
+    breakdown = {
+        "path": "three calls: momentum, Newton-Schulz, update" if args.unfused else
+                "fused call per chunk: momentum + Newton-Schulz + update (O not stored)",
+        "wall_s_timed_region": round(wall, 3),
+        ("newton_schulz_ms" if args.unfused else "momentum_ns_update_ms"): round(acc["ns"] / K, 3),
+        ("newton_schulz_tflops" if args.unfused else "momentum_ns_update_tflops"):
+            round(ns_fl / (acc["ns"] / K * 1e-3) / 1e12, 1),
+        "maxlogit_ms": round(acc["maxlogit"] / K, 4),
+        "maxlogit_tflops": round(ml_fl / (acc["maxlogit"] / K * 1e-3) / 1e12, 1),
+    }
+    if args.unfused:
+        breakdown.update({
+            "momentum_ms": round(acc["momentum"] / K, 3),
+            "momentum_gbps": round(12.0 * E / (acc["momentum"] / K * 1e-3) / 1e9, 1),
+            "update_ms": round(acc["update"] / K, 3),
+            "update_gbps": round(6.0 * E / (acc["update"] / K * 1e-3) / 1e9, 1),
+        })
+    breakdown.update({
+        "rescale_ms": round(acc["clip"] / K, 4),
+        "rescale_gbps": round(rescale_bytes / (acc["clip"] / K * 1e-3) / 1e9, 1),
+        "clipped_heads": n_clip,
+        "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
+                        for g in gemm_ms},
+    })
 
     out = {
         "metric": METRIC,
@@ -261,22 +295,7 @@ def run(args):
             "ns_chunk": chunk,
             "lr": LR, "weight_decay": WD, "mu": MU, "tau": TAU, "alpha": ALPHA,
         },
-        "breakdown": {
-            "wall_s_timed_region": round(wall, 3),
-            "newton_schulz_ms": round(acc["ns"] / K, 3),
-            "newton_schulz_tflops": round(ns_fl / (acc["ns"] / K * 1e-3) / 1e12, 1),
-            "maxlogit_ms": round(acc["maxlogit"] / K, 4),
-            "maxlogit_tflops": round(ml_fl / (acc["maxlogit"] / K * 1e-3) / 1e12, 1),
-            "momentum_ms": round(acc["momentum"] / K, 3),
-            "momentum_gbps": round(12.0 * E / (acc["momentum"] / K * 1e-3) / 1e9, 1),
-            "update_ms": round(acc["update"] / K, 3),
-            "update_gbps": round(6.0 * E / (acc["update"] / K * 1e-3) / 1e9, 1),
-            "rescale_ms": round(acc["clip"] / K, 4),
-            "rescale_gbps": round(rescale_bytes / (acc["clip"] / K * 1e-3) / 1e9, 1),
-            "clipped_heads": n_clip,
-            "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
-                            for g in gemm_ms},
-        },
+        "breakdown": breakdown,
         "roofline": {
             "kernel": kernel_names[dom],
             "bound": "mfma",
@@ -355,6 +374,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=64, help="matrices per Newton-Schulz call")
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="momentum, Newton-Schulz and update as three calls (O stored in bf16)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

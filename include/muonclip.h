@@ -13,9 +13,14 @@
  *   qk_maxlogit                    S_max^h from the forward's Q, K
  *   qk_clip_apply                  rescale W_q / W_k rows of heads over tau
  *
+ * or, for the Muon part, one fused call per shape group that does the first
+ * three without storing O:
+ *
+ *   muon_momentum_ns_update_batched  M <- mu M + G; W <- W - eta (s NS(M) + lambda W)
+ *
  * Conventions shared by every call:
  *  - Every tensor pointer is a DEVICE pointer owned by the caller, except
- *    `coeffs` of muon_ns_orthogonalize_batched, which is host memory.  The
+ *    `coeffs` of the Newton-Schulz calls, which is host memory.  The
  *    library never allocates device memory; scratch space is a caller
  *    workspace whose size a query function returns.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -149,6 +154,43 @@ MC_API mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int
  */
 MC_API mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, int64_t numel,
                               float lr, float weight_decay, void* stream);
+
+/*
+ * The Muon part of the step for a batch of equally shaped matrices, fused:
+ * for b in [0, batch), with M_b, G_b, W_b rows x cols at element offset
+ * b * batch_stride of M, G and W,
+ *   M_b <- fl32(fl32(mu * M_b) + G_b)                      (as muonclip_momentum)
+ *   O_b  = out_scale * NS(M_b)                             (as muon_ns_orthogonalize_batched)
+ *   W_b <- W_b - lr * (O_b + weight_decay * W_b)           (as muon_apply_update)
+ * (Algorithm 1 of "Kimi K2 内部机制", MuonClip section; the paper notes'
+ * muonclip_step pseudocode, section 3.2.)  The momentum is bit-identical to
+ * muonclip_momentum.  O is never stored: the last Newton-Schulz GEMM applies
+ * the update as it finishes each tile of X (rounded to bf16 as between steps;
+ * O = out_scale * X is formed in float32, not rounded to a storage type).
+ * The new M is converted to bf16 once, in the momentum pass, together
+ * with float32 partial sums of its squares; the normalisation
+ * 1 / (||M_b||_F + eps) is applied inside the first Newton-Schulz step (to
+ * X X^T squared and to the step's result), which equals normalising X_0 up
+ * to rounding.  Steps and coefficients as muon_ns_orthogonalize_batched.
+ *
+ *   M          device float32, in/out;  G: device float32
+ *   W          device, w_dtype (MC_F32 or MC_BF16), in/out
+ *   batch_stride  elements between consecutive matrices of M, G and W
+ *                 (>= rows * cols when batch > 1)
+ *   mu, lr, weight_decay, out_scale: finite; eps >= 0
+ *   workspace  device, >= muon_ns_workspace_bytes(batch, rows, cols) bytes,
+ *              256-byte aligned
+ *   gemm_events as muon_ns_orthogonalize_batched (the last step's third GEMM
+ *              includes the update)
+ * Sizes as muon_ns_orthogonalize_batched.
+ * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EWORKSPACE, MC_EHIP.
+ */
+MC_API mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, void* W, int w_dtype,
+                                                   int64_t batch, int64_t rows, int64_t cols,
+                                                   int64_t batch_stride, int32_t steps, const float* coeffs,
+                                                   float eps, float out_scale, float lr, float weight_decay,
+                                                   void* workspace, size_t workspace_bytes, void* stream,
+                                                   void* const* gemm_events);
 
 /*
  * Per-head max logit over a batch, the logits never stored:

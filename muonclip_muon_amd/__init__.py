@@ -30,6 +30,7 @@ __all__ = [
     "muon_ns_workspace_bytes",
     "muon_ns_orthogonalize_batched",
     "muon_apply_update",
+    "muon_momentum_ns_update_batched",
     "qk_maxlogit",
     "qk_clip_apply",
     "muon_out_scale",
@@ -78,6 +79,10 @@ def _load():
     L.muon_ns_orthogonalize_batched.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, vp, ctypes.c_int, i64,
                                                 i32, ctypes.POINTER(f32), f32, f32, vp, ctypes.c_size_t,
                                                 vp, ctypes.POINTER(vp)]
+    L.muon_momentum_ns_update_batched.restype = ctypes.c_int
+    L.muon_momentum_ns_update_batched.argtypes = [vp, vp, f32, vp, ctypes.c_int, i64, i64, i64, i64, i32,
+                                                  ctypes.POINTER(f32), f32, f32, f32, f32, vp, ctypes.c_size_t,
+                                                  vp, ctypes.POINTER(vp)]
     L.muon_apply_update.restype = ctypes.c_int
     L.muon_apply_update.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, f32, f32, vp]
     L.qk_maxlogit.restype = ctypes.c_int
@@ -139,6 +144,33 @@ def muon_out_scale(rows, cols):
     return math.sqrt(max(rows, cols)) * 0.2
 
 
+def _coeffs(steps, coeffs):
+    if coeffs is None:
+        coeffs = NS_COEFFS[:steps] if steps <= len(NS_COEFFS) else (NS_COEFFS[0],) * steps
+    flat = [float(x) for abc in coeffs for x in abc]
+    if len(flat) != 3 * steps:
+        raise ValueError("coeffs must hold `steps` (a, b, c) triples")
+    return (ctypes.c_float * len(flat))(*flat)
+
+
+def _workspace(workspace, batch, rows, cols, device):
+    need = lib.muon_ns_workspace_bytes(batch, rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return _dev(workspace, "workspace")
+
+
+def _events(gemm_events, steps, device, stream):
+    if gemm_events is None:
+        return None
+    if len(gemm_events) != 6 * steps:
+        raise ValueError("gemm_events needs 6 * steps events")
+    st = stream or torch.cuda.current_stream(device)
+    for e in gemm_events:  # torch creates events lazily; make sure each exists
+        e.record(st)
+    return (ctypes.c_void_p * len(gemm_events))(*[e.cuda_event for e in gemm_events])
+
+
 def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS_EPS, out_scale=1.0,
                                   workspace=None, out_dtype=None, gemm_events=None, stream=None):
     """O[b] = out_scale * NS(M[b]) for M of shape [rows, cols] or [batch, rows, cols].
@@ -159,24 +191,9 @@ def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS
     _dev(O, "O")
     if O.shape != M.shape:
         raise ValueError("O must have M's shape")
-    if coeffs is None:
-        coeffs = NS_COEFFS[:steps] if steps <= len(NS_COEFFS) else (NS_COEFFS[0],) * steps
-    flat = [float(x) for abc in coeffs for x in abc]
-    if len(flat) != 3 * steps:
-        raise ValueError("coeffs must hold `steps` (a, b, c) triples")
-    c_coeffs = (ctypes.c_float * len(flat))(*flat)
-    need = lib.muon_ns_workspace_bytes(batch, rows, cols)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=M.device)
-    _dev(workspace, "workspace")
-    ev = None
-    if gemm_events is not None:
-        if len(gemm_events) != 6 * steps:
-            raise ValueError("gemm_events needs 6 * steps events")
-        st = stream or torch.cuda.current_stream(M.device)
-        for e in gemm_events:  # torch creates events lazily; make sure each exists
-            e.record(st)
-        ev = (ctypes.c_void_p * len(gemm_events))(*[e.cuda_event for e in gemm_events])
+    c_coeffs = _coeffs(steps, coeffs)
+    workspace = _workspace(workspace, batch, rows, cols, M.device)
+    ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_ns_orthogonalize_batched(
         M.data_ptr(), _dtype(M, "M"), batch, rows, cols, rows * cols, O.data_ptr(), _dtype(O, "O"),
         rows * cols, steps, c_coeffs, eps, out_scale, workspace.data_ptr(), workspace.numel(),
@@ -193,6 +210,34 @@ def muon_apply_update(W, O, lr, weight_decay=0.1, stream=None):
     _check("muon_apply_update", lib.muon_apply_update(W.data_ptr(), _dtype(W, "W"), O.data_ptr(),
                                                       _dtype(O, "O"), W.numel(), lr, weight_decay,
                                                       _stream(W, stream)))
+    return W
+
+
+def muon_momentum_ns_update_batched(M, G, W, lr, weight_decay=0.1, mu=0.95, steps=NS_STEPS, coeffs=None,
+                                    eps=NS_EPS, out_scale=None, workspace=None, gemm_events=None, stream=None):
+    """Fused Muon step for [rows, cols] or [batch, rows, cols] tensors, in place:
+    M <- mu M + G; W <- W - lr * (out_scale * NS(M) + weight_decay * W).
+
+    M, G float32; W float32 or bfloat16, all the same shape.  ``out_scale``
+    defaults to muon_out_scale(rows, cols)."""
+    _dev(M, "M"), _dev(G, "G"), _dev(W, "W")
+    if M.dtype != torch.float32 or G.dtype != torch.float32:
+        raise ValueError("M and G must be float32")
+    if M.shape != G.shape or M.shape != W.shape:
+        raise ValueError("M, G and W must have the same shape")
+    M3 = M.unsqueeze(0) if M.dim() == 2 else M
+    if M3.dim() != 3:
+        raise ValueError("M must be [rows, cols] or [batch, rows, cols]")
+    batch, rows, cols = M3.shape
+    if out_scale is None:
+        out_scale = muon_out_scale(rows, cols)
+    c_coeffs = _coeffs(steps, coeffs)
+    workspace = _workspace(workspace, batch, rows, cols, M.device)
+    ev = _events(gemm_events, steps, M.device, stream)
+    status = lib.muon_momentum_ns_update_batched(
+        M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
+        c_coeffs, eps, out_scale, lr, weight_decay, workspace.data_ptr(), workspace.numel(), _stream(M, stream), ev)
+    _check("muon_momentum_ns_update_batched", status)
     return W
 
 
@@ -249,18 +294,23 @@ def qk_clip_apply(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=
 
 
 def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1, momentum=0.95,
-                  tau=100.0, alpha=0.5, steps=NS_STEPS, coeffs=None, eps=NS_EPS):
+                  tau=100.0, alpha=0.5, steps=NS_STEPS, coeffs=None, eps=NS_EPS, fused=False):
     """One MuonClip step over dicts of 2-D tensors, in place.
 
     weights: name -> W (float32 or bfloat16); grads: name -> float32 G;
     momenta: name -> float32 M (created as zeros when missing: M_0 = 0);
     smax: float32 [H] max logits recorded by the forward; attention: dict with
     'q', 'k' (weight names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head'.
+    fused: use muon_momentum_ns_update_batched instead of the three calls.
     Returns (gamma, clipped)."""
     for name, W in weights.items():
         M = momenta.get(name)
         if M is None:
             M = momenta[name] = torch.zeros(W.shape, dtype=torch.float32, device=W.device)
+        if fused:
+            muon_momentum_ns_update_batched(M, grads[name], W, lr, weight_decay, momentum, steps=steps,
+                                            coeffs=coeffs, eps=eps)
+            continue
         muonclip_momentum(M, grads[name], momentum)
         rows, cols = W.shape
         O = muon_ns_orthogonalize_batched(M, steps=steps, coeffs=coeffs, eps=eps,

@@ -55,6 +55,74 @@ size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
   return mc::ns_geometry(batch, rows, cols).total;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the Newton-Schulz entry points (shape, steps, coefficients,
+// eps, scale, workspace, events); fills g on success.
+mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, const float* coeffs, float eps,
+                     float out_scale, void* workspace, size_t workspace_bytes, void* const* gemm_events,
+                     mc::NsGeometry* g) {
+  const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
+  if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  if (!coeffs || !workspace) return MC_EINVAL;
+  if (steps < 1 || steps > kNsMaxSteps) return MC_EINVAL;
+  if (!(eps >= 0.0f) || !isfinite(eps) || !isfinite(out_scale)) return MC_EINVAL;
+  for (int i = 0; i < 3 * steps; ++i)
+    if (!isfinite(coeffs[i])) return MC_EINVAL;
+  if (!aligned(workspace, 256)) return MC_EALIGN;
+  *g = mc::ns_geometry(batch, rows, cols);
+  if (workspace_bytes < g->total) return MC_EWORKSPACE;
+  const int64_t tiles = (g->n_pad / mc::kNsTile) * (g->m_pad / mc::kNsTile);
+  if (tiles * batch > kGridMax || batch > 65535 || g->sumsq_chunks > kGridMax) return MC_ESHAPE;
+  if (gemm_events)
+    for (int i = 0; i < 6 * steps; ++i)
+      if (!gemm_events[i]) return MC_EINVAL;
+  return MC_OK;
+}
+
+// The steps' GEMMs, X_0 at off_x0.  X <- (a I + b A + c A^2) X with
+// A = X X^T.  inv0 (or null): the stored X_0 is to be scaled per matrix by
+// inv0 (applied inside the first step).  upd (or null): the last step
+// updates W instead of storing X.  Returns the buffer holding the final X.
+hipError_t run_ns_steps(const mc::NsGeometry& g, char* ws, int32_t steps, const float* coeffs, const float* inv0,
+                        const mc::NsUpdate* upd, hipStream_t s, void* const* gemm_events, uint16_t** x_final) {
+  uint16_t* X = reinterpret_cast<uint16_t*>(ws + g.off_x0);
+  uint16_t* Xn = reinterpret_cast<uint16_t*>(ws + g.off_x1);
+  uint16_t* A = reinterpret_cast<uint16_t*>(ws + g.off_a);
+  uint16_t* B = reinterpret_cast<uint16_t*>(ws + g.off_b);
+  auto record = [&](int idx) -> hipError_t {
+    return gemm_events ? hipEventRecord(static_cast<hipEvent_t>(gemm_events[idx]), s) : hipSuccess;
+  };
+  hipError_t e = hipSuccess;
+  for (int st = 0; st < steps; ++st) {
+    const float a = coeffs[3 * st], b = coeffs[3 * st + 1], c = coeffs[3 * st + 2];
+    const float* inv = st == 0 ? inv0 : nullptr;
+    const uint16_t* in0[3] = {X, A, B};
+    const uint16_t* in1[3] = {nullptr, nullptr, X};
+    uint16_t* out[3] = {A, B, Xn};
+    const float alpha[3] = {0.f, b, 0.f}, beta[3] = {0.f, c, 0.f}, diag[3] = {0.f, a, 0.f};
+    const float* invs[3] = {inv, nullptr, inv};
+    const mc::NsUpdate* upds[3] = {nullptr, nullptr, st == steps - 1 ? upd : nullptr};
+    for (int gm = 0; gm < 3; ++gm) {
+      if ((e = record(2 * (3 * st + gm))) != hipSuccess) return e;
+      e = mc::launch_ns_gemm(gm, g, in0[gm], in1[gm], out[gm], alpha[gm], beta[gm], diag[gm], invs[gm], upds[gm], s);
+      if (e != hipSuccess) return e;
+      if ((e = record(2 * (3 * st + gm) + 1)) != hipSuccess) return e;
+    }
+    uint16_t* tmp = X;
+    X = Xn;
+    Xn = tmp;
+  }
+  *x_final = X;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
 mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t batch, int64_t rows,
                                           int64_t cols, int64_t m_batch_stride, void* O, int o_dtype,
                                           int64_t o_batch_stride, int32_t steps, const float* coeffs,
@@ -63,24 +131,18 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
                                           void* const* gemm_events) {
   if (batch < 0 || rows < 1 || cols < 1) return MC_EINVAL;
   if (!valid_dtype(m_dtype) || !valid_dtype(o_dtype)) return MC_EDTYPE;
-  const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
-  if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  {
+    const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
+    if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  }
   if (batch == 0) return MC_OK;
-  if (!M || !O || !coeffs || !workspace) return MC_EINVAL;
-  if (steps < 1 || steps > kNsMaxSteps) return MC_EINVAL;
-  if (!(eps >= 0.0f) || !isfinite(eps) || !isfinite(out_scale)) return MC_EINVAL;
-  for (int i = 0; i < 3 * steps; ++i)
-    if (!isfinite(coeffs[i])) return MC_EINVAL;
+  if (!M || !O) return MC_EINVAL;
   if (batch > 1 && (m_batch_stride < rows * cols || o_batch_stride < rows * cols)) return MC_EINVAL;
   if (!aligned(M, dtype_size(m_dtype)) || !aligned(O, dtype_size(o_dtype))) return MC_EALIGN;
-  if (!aligned(workspace, 256)) return MC_EALIGN;
-  const mc::NsGeometry g = mc::ns_geometry(batch, rows, cols);
-  if (workspace_bytes < g.total) return MC_EWORKSPACE;
-  const int64_t tiles = (g.n_pad / mc::kNsTile) * (g.m_pad / mc::kNsTile);
-  if (tiles * batch > kGridMax || batch > 65535 || g.sumsq_chunks > kGridMax) return MC_ESHAPE;
-  if (gemm_events)
-    for (int i = 0; i < 6 * steps; ++i)
-      if (!gemm_events[i]) return MC_EINVAL;
+  mc::NsGeometry g;
+  const mc_status_t st = check_ns(batch, rows, cols, steps, coeffs, eps, out_scale, workspace, workspace_bytes,
+                                  gemm_events, &g);
+  if (st != MC_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -89,32 +151,39 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   if (e != hipSuccess) return MC_EHIP;
   e = mc::launch_ns_prescale(M, m_bf16, m_batch_stride, g, ws, s);
   if (e != hipSuccess) return MC_EHIP;
-
-  uint16_t* X = reinterpret_cast<uint16_t*>(ws + g.off_x0);
-  uint16_t* Xn = reinterpret_cast<uint16_t*>(ws + g.off_x1);
-  uint16_t* A = reinterpret_cast<uint16_t*>(ws + g.off_a);
-  uint16_t* B = reinterpret_cast<uint16_t*>(ws + g.off_b);
-  auto record = [&](int idx) -> hipError_t {
-    return gemm_events ? hipEventRecord(static_cast<hipEvent_t>(gemm_events[idx]), s) : hipSuccess;
-  };
-  for (int st = 0; st < steps; ++st) {
-    const float a = coeffs[3 * st], b = coeffs[3 * st + 1], c = coeffs[3 * st + 2];
-    // X' = a X + (b A + c A^2) X = (a I + b A + c A^2) X
-    const uint16_t* in0[3] = {X, A, B};
-    const uint16_t* in1[3] = {nullptr, nullptr, X};
-    uint16_t* out[3] = {A, B, Xn};
-    const float alpha[3] = {0.f, b, 0.f}, beta[3] = {0.f, c, 0.f}, diag[3] = {0.f, a, 0.f};
-    for (int gm = 0; gm < 3; ++gm) {
-      if ((e = record(2 * (3 * st + gm))) != hipSuccess) return MC_EHIP;
-      e = mc::launch_ns_gemm(gm, g, in0[gm], in1[gm], out[gm], alpha[gm], beta[gm], diag[gm], s);
-      if (e != hipSuccess) return MC_EHIP;
-      if ((e = record(2 * (3 * st + gm) + 1)) != hipSuccess) return MC_EHIP;
-    }
-    uint16_t* tmp = X;
-    X = Xn;
-    Xn = tmp;
-  }
+  uint16_t* X = nullptr;
+  if (run_ns_steps(g, ws, steps, coeffs, nullptr, nullptr, s, gemm_events, &X) != hipSuccess) return MC_EHIP;
   return from_hip(mc::launch_ns_output(X, g, O, o_bf16, o_batch_stride, out_scale, s));
+}
+
+mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, void* W, int w_dtype,
+                                            int64_t batch, int64_t rows, int64_t cols, int64_t batch_stride,
+                                            int32_t steps, const float* coeffs, float eps, float out_scale,
+                                            float lr, float weight_decay, void* workspace,
+                                            size_t workspace_bytes, void* stream, void* const* gemm_events) {
+  if (batch < 0 || rows < 1 || cols < 1) return MC_EINVAL;
+  if (!valid_dtype(w_dtype)) return MC_EDTYPE;
+  {
+    const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
+    if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  }
+  if (batch == 0) return MC_OK;
+  if (!M || !G || !W) return MC_EINVAL;
+  if (batch > 1 && batch_stride < rows * cols) return MC_EINVAL;
+  if (!isfinite(mu) || !isfinite(lr) || !isfinite(weight_decay)) return MC_EINVAL;
+  if (!aligned(M, 4) || !aligned(G, 4) || !aligned(W, dtype_size(w_dtype))) return MC_EALIGN;
+  mc::NsGeometry g;
+  const mc_status_t st = check_ns(batch, rows, cols, steps, coeffs, eps, out_scale, workspace, workspace_bytes,
+                                  gemm_events, &g);
+  if (st != MC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (mc::launch_momentum_prescale(M, G, batch_stride, mu, g, eps, ws, s) != hipSuccess) return MC_EHIP;
+  const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
+  mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, out_scale, lr, weight_decay};
+  uint16_t* X = nullptr;
+  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events, &X));
 }
 
 mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, int64_t numel,

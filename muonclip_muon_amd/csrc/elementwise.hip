@@ -4,10 +4,9 @@
 // Both stream their operands once (momentum: 12 bytes per element; update:
 // 4 + 2 + ... bytes per element depending on dtypes) with 16-byte vector
 // accesses, a grid-stride loop and no reuse, so they are bound by HBM.
-// Arithmetic is written as separate float operations with FP contraction
-// switched off in the function that does them (clang otherwise fuses a
-// multiply and an add, even __fmul_rn/__fadd_rn from the HIP headers, into
-// v_fma_f32): momentum must equal float32 multiply-then-add bit for bit.
+// The arithmetic (momentum_op, update_op) is separate float operations with FP
+// contraction switched off: momentum must equal float32 multiply-then-add bit
+// for bit.
 
 #include "mc_device.h"
 #include "mc_internal.h"
@@ -23,13 +22,6 @@ __host__ int grid_for(int64_t work_items) {
   if (blocks > 256 * 16) blocks = 256 * 16;
   if (blocks < 1) blocks = 1;
   return static_cast<int>(blocks);
-}
-
-// M <- fl32(fl32(mu * M) + G)
-__device__ __forceinline__ float momentum_op(float m, float g, float mu) {
-#pragma clang fp contract(off)
-  const float scaled = mu * m;
-  return scaled + g;
 }
 
 __global__ __launch_bounds__(kThreads) void momentum_vec4_kernel(f32x4* __restrict__ M,
@@ -53,15 +45,6 @@ __global__ __launch_bounds__(kThreads) void momentum_scalar_kernel(float* __rest
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride)
     M[i] = momentum_op(M[i], G[i], mu);
-}
-
-// W' = W - lr * (O + wd * W), as t = wd*W; u = O + t; v = lr*u; W - v.
-__device__ __forceinline__ float update_op(float w, float o, float lr, float wd) {
-#pragma clang fp contract(off)
-  const float t = wd * w;
-  const float u = o + t;
-  const float v = lr * u;
-  return w - v;
 }
 
 __device__ __forceinline__ void load8_f32(const float* p, float (&v)[8]) {

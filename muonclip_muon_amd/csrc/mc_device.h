@@ -39,6 +39,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// The rounding of the element-wise steps, shared by every kernel that applies
+// them.  Each is a chain of separate float32 operations, each rounded once,
+// with FP contraction switched off (clang otherwise fuses a multiply and an
+// add, even __fmul_rn/__fadd_rn from the HIP headers, into v_fma_f32).
+//   momentum: M <- fl32(fl32(mu * M) + G)
+__device__ __forceinline__ float momentum_op(float m, float g, float mu) {
+#pragma clang fp contract(off)
+  const float scaled = mu * m;
+  return scaled + g;
+}
+//   update: W' = W - lr * (O + wd * W), as t = wd*W; u = O + t; v = lr*u; W - v
+__device__ __forceinline__ float update_op(float w, float o, float lr, float wd) {
+#pragma clang fp contract(off)
+  const float t = wd * w;
+  const float u = o + t;
+  const float v = lr * u;
+  return w - v;
+}
+
 // Blocks of one launch are distributed round-robin over the 8 XCDs of an
 // MI355X (block b runs on XCD b % 8).  This remap makes consecutive logical
 // block ids land on the same XCD, so tiles that share operands share that

@@ -28,7 +28,8 @@ struct NsGeometry {
   int64_t n, m;          // logical
   int64_t n_pad, m_pad;  // padded to kNsTile
   bool transposed;       // rows > cols: X = M^T
-  int64_t sumsq_chunks;  // partial sums per matrix
+  int64_t sumsq_chunks;    // partial sums per matrix of the stand-alone norm
+  int64_t prescale_tiles;  // 64 x 64 tiles per matrix of the pre-scale (fused norm partials)
   // byte offsets inside the workspace: X (two ping-pong copies, n_pad x m_pad),
   // A and B' (n_pad x n_pad), norm partials, 1/norm
   size_t off_x0, off_x1, off_a, off_b, off_partials, off_invnorm, total;
@@ -40,12 +41,29 @@ hipError_t launch_ns_norm(const void* M, bool m_bf16, int64_t m_batch_stride, co
                           float eps, char* ws, hipStream_t stream);
 hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride,
                               const NsGeometry& g, char* ws, hipStream_t stream);
+// Fused: M <- mu M + G in place (float32, batch matrices of rows x cols at
+// batch_stride), X_0 = bf16(M) unscaled at off_x0, and 1 / (||M||_F + eps)
+// per matrix at off_invnorm (to be applied by the first step's GEMMs).
+hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
+                                    const NsGeometry& g, float eps, char* ws, hipStream_t stream);
+// In-place update applied by the last step's X' = B' X instead of storing X':
+// W_b <- W_b - lr * (out_scale * X'_b (transposed back for a tall matrix) +
+// wd * W_b), W_b rows x cols at W + b * w_stride, float32 or bf16.
+struct NsUpdate {
+  void* W;
+  bool w_bf16;
+  int64_t w_stride;
+  float out_scale, lr, wd;
+};
 // One GEMM of the polynomial step, on the whole batch:
 //   mode 0: A = X X^T                          (in0: X, out: A)
 //   mode 1: B' = diag I + alpha A + beta A A   (in0: A, out: B')
-//   mode 2: X' = B' X                          (in0: B', in1: X, out: X')
+//   mode 2: X' = B' X                          (in0: B', in1: X, out: X', or upd)
+// inv (device, per matrix, or null): X is inv_b times the stored X (the first
+// step of the fused path); mode 0 scales A by inv_b^2, mode 2 X' by inv_b.
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          uint16_t* out, float alpha, float beta, float diag, hipStream_t stream);
+                          uint16_t* out, float alpha, float beta, float diag, const float* inv,
+                          const NsUpdate* upd, hipStream_t stream);
 // O_b = out_scale * X_b (rows <= cols) or X_b^T (rows > cols), rows x cols.
 hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
                             int64_t o_batch_stride, float out_scale, hipStream_t stream);

@@ -89,9 +89,15 @@ __device__ __forceinline__ int xswz(int r) { return 4 * (r & 3); }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(const char* g_uniform, uint32_t lane_off, uint32_t lds_addr) {
+  // the base is wave-uniform by construction; readfirstlane lets the compiler
+  // keep it in SGPRs where it cannot prove that itself
+  const uint64_t a = reinterpret_cast<uintptr_t>(g_uniform);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const char* base = reinterpret_cast<const char*>(lo | (hi << 32));
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n"
                :
-               : "s"(lds_addr), "v"(lane_off), "s"(g_uniform)
+               : "s"(lds_addr), "v"(lane_off), "s"(base)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -256,11 +262,23 @@ __device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int
   }
 }
 
-template <int MODE>
+// Fused in-place update of the last step (mode 2): W is n x m (or m x n when
+// transposed, i.e. the matrix was iterated on as its transpose).
+struct UpdArgs {
+  void* W;
+  int64_t w_stride;  // elements between matrices
+  int n, m;          // logical X shape
+  int transposed;
+  float out_scale, lr, wd;
+};
+
+// UPD: 0 = store X' (or A, B'); 1 = update bf16 W; 2 = update float32 W.
+template <int MODE, int UPD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
                     uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
-                    float alpha, float beta, float diag) {
+                    float alpha, float beta, float diag, const float* __restrict__ inv, UpdArgs ua) {
+  static_assert(UPD == 0 || MODE == 2, "only X' = B' X can apply the update");
   constexpr bool kKRows = MODE != 0;
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   typedef __attribute__((address_space(3))) char lds_char_t;
@@ -385,12 +403,15 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   //   modes 0/2: every lane rounds its accumulators into place;
   //   the sub-tile is stored row by row, 16 bytes per lane;
   //   modes 0/1, off-diagonal tiles: it is also stored mirrored.
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  const int i0w = i0 + wm * 128, j0w = j0 + wn * 128;
+  // X is inv_b times the stored X in the first step of the fused path
+  const float xs = (inv != nullptr) ? inv[mat] : 1.0f;
+
   wait_vmem<0>();
   __syncthreads();
-  const int frag_row = lane & 31, frag_half = lane >> 5;
   const int64_t ldo = (MODE == 2) ? m_pad : n_pad;
   uint16_t* O = out + mat * ((MODE == 2) ? nm : nn);
-  const int i0w = i0 + wm * 128, j0w = j0 + wn * 128;
   const uint32_t eb = lds + wave * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
 
@@ -416,6 +437,14 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       for (int g = 0; g < 4; ++g) {
         const uint32_t a = st_addr(ii, 4 * x + g) + 8 * frag_half;
         float v[4] = {acc[x][y][4 * g + 0], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]};
+        if constexpr (MODE == 0) {
+          const float s2 = xs * xs;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] *= s2;
+        } else if constexpr (MODE == 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] *= xs;
+        }
         if constexpr (MODE == 1) {
           const u32x2 e = *(const lds_u32x2_t*)(uintptr_t)a;
           const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
@@ -430,6 +459,94 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         *(lds_u32x2_t*)(uintptr_t)a = o;
       }
     }
+  }
+  if constexpr (UPD != 0) {
+    // Fused update instead of storing X': W <- W - lr * (out_scale * X' + wd * W)
+    // with X' rounded to bf16 as between steps; W is n x m, or m x n for a
+    // matrix iterated on as its transpose.  Each lane handles 8 elements of
+    // one W row per pass: 16-byte accesses, 256-byte row segments per 16
+    // lanes (straight) or the mirrored-store pattern (transposed); runs that
+    // leave the matrix (padding) or are misaligned go element by element.
+    constexpr int kEsz = (UPD == 1) ? 2 : 4;
+    char* Wb = static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz;
+    const int64_t wcols = ua.transposed ? ua.n : ua.m;
+    const bool vec = wcols % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
+    auto update8 = [&](int64_t wrow, int64_t wcol, int valid, const float (&x)[8]) {
+      if (valid <= 0) return;
+      const int64_t idx = wrow * wcols + wcol;
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = ua.out_scale * x[e];
+      if (vec && valid == 8) {
+        if constexpr (UPD == 1) {
+          u32x4* p = reinterpret_cast<u32x4*>(Wb + idx * 2);
+          u32x4 w = *p;
+          w.x = pack_bf16x2(update_op(bf16_lo(w.x), o[0], ua.lr, ua.wd), update_op(bf16_hi(w.x), o[1], ua.lr, ua.wd));
+          w.y = pack_bf16x2(update_op(bf16_lo(w.y), o[2], ua.lr, ua.wd), update_op(bf16_hi(w.y), o[3], ua.lr, ua.wd));
+          w.z = pack_bf16x2(update_op(bf16_lo(w.z), o[4], ua.lr, ua.wd), update_op(bf16_hi(w.z), o[5], ua.lr, ua.wd));
+          w.w = pack_bf16x2(update_op(bf16_lo(w.w), o[6], ua.lr, ua.wd), update_op(bf16_hi(w.w), o[7], ua.lr, ua.wd));
+          *p = w;
+        } else {
+          f32x4* p = reinterpret_cast<f32x4*>(Wb + idx * 4);
+          f32x4 a = p[0], b = p[1];
+          a.x = update_op(a.x, o[0], ua.lr, ua.wd);
+          a.y = update_op(a.y, o[1], ua.lr, ua.wd);
+          a.z = update_op(a.z, o[2], ua.lr, ua.wd);
+          a.w = update_op(a.w, o[3], ua.lr, ua.wd);
+          b.x = update_op(b.x, o[4], ua.lr, ua.wd);
+          b.y = update_op(b.y, o[5], ua.lr, ua.wd);
+          b.z = update_op(b.z, o[6], ua.lr, ua.wd);
+          b.w = update_op(b.w, o[7], ua.lr, ua.wd);
+          p[0] = a;
+          p[1] = b;
+        }
+      } else {
+        for (int e = 0; e < valid; ++e) {
+          if constexpr (UPD == 1) {
+            uint16_t* p = reinterpret_cast<uint16_t*>(Wb) + idx + e;
+            *p = f32_to_bf16(update_op(bf16_to_f32(*p), o[e], ua.lr, ua.wd));
+          } else {
+            float* p = reinterpret_cast<float*>(Wb) + idx + e;
+            *p = update_op(*p, o[e], ua.lr, ua.wd);
+          }
+        }
+      }
+    };
+    auto unpack8 = [](u32x4 v, float (&x)[8]) {
+      x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+      x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+    };
+    if (!ua.transposed) {
+#pragma unroll 2
+      for (int s = 0; s < 32; ++s) {
+        const int row = 4 * s + (lane >> 4), u = lane & 15;
+        const int i = i0w + row, j = j0w + 8 * u;
+        float x[8];
+        unpack8(*(const lds_u32x4_t*)(uintptr_t)st_addr(row, u), x);
+        update8(i, j, i < ua.n ? min(8, ua.m - j) : 0, x);
+      }
+    } else {
+      // lane takes column jj = C + (lane % 16) and rows ii = R .. R + 7 of the
+      // staged tile (two transposed reads), i.e. 8 consecutive elements of W
+      // row j0w + jj
+      const int g = lane >> 4, il = lane & 15;
+#pragma unroll 2
+      for (int s = 0; s < 32; ++s) {
+        const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
+        const int col = C + 4 * (il & 3);
+        const int r0 = R + (il >> 2), r1 = r0 + 4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(uintptr_t)(eb + r0 * 256 + (((col >> 3) ^ (r0 & 15)) << 4) + (col & 7) * 2));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(uintptr_t)(eb + r1 * 256 + (((col >> 3) ^ (r1 & 15)) << 4) + (col & 7) * 2));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        float x[8];
+        unpack8(u32x4{l2.x, l2.y, h2.x, h2.y}, x);
+        const int j = j0w + C + il, i = i0w + R;
+        update8(j, i, j < ua.m ? min(8, ua.n - i) : 0, x);
+      }
+    }
+    return;
   }
   // direct store: 4 rows of 256 bytes per instruction
   {
@@ -449,7 +566,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 }  // namespace
 
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          uint16_t* out, float alpha, float beta, float diag, hipStream_t stream) {
+                          uint16_t* out, float alpha, float beta, float diag, const float* inv,
+                          const NsUpdate* upd, hipStream_t stream) {
   const int n_pad = static_cast<int>(g.n_pad), m_pad = static_cast<int>(g.m_pad);
   const int tiles_m = n_pad / kBM;
   const int tiles_n = (mode == 2) ? m_pad / kBN : n_pad / kBN;
@@ -457,20 +575,26 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
   const int tiles_per_mat = (mode == 2) ? tiles_m * tiles_n : tiles_m * (tiles_m + 1) / 2;
   const int64_t blocks = static_cast<int64_t>(tiles_per_mat) * g.batch;
   dim3 grid(static_cast<unsigned>(blocks));
-  switch (mode) {
-    case 0:
-      hipLaunchKernelGGL(ns_gemm_kernel<0>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad,
-                         tiles_n, tiles_per_mat, alpha, beta, diag);
-      break;
-    case 1:
-      hipLaunchKernelGGL(ns_gemm_kernel<1>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad,
-                         tiles_n, tiles_per_mat, alpha, beta, diag);
-      break;
-    default:
-      hipLaunchKernelGGL(ns_gemm_kernel<2>, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad,
-                         tiles_n, tiles_per_mat, alpha, beta, diag);
-      break;
+  UpdArgs ua{};
+  if (upd != nullptr) {
+    ua.W = upd->W;
+    ua.w_stride = upd->w_stride;
+    ua.n = static_cast<int>(g.n);
+    ua.m = static_cast<int>(g.m);
+    ua.transposed = g.transposed ? 1 : 0;
+    ua.out_scale = upd->out_scale;
+    ua.lr = upd->lr;
+    ua.wd = upd->wd;
   }
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad, tiles_n, tiles_per_mat,
+                       alpha, beta, diag, inv, ua);
+  };
+  if (mode == 0) go(ns_gemm_kernel<0, 0>);
+  else if (mode == 1) go(ns_gemm_kernel<1, 0>);
+  else if (upd == nullptr) go(ns_gemm_kernel<2, 0>);
+  else if (upd->w_bf16) go(ns_gemm_kernel<2, 1>);
+  else go(ns_gemm_kernel<2, 2>);
   return hipGetLastError();
 }
 

@@ -7,6 +7,10 @@
 //             into the zero-padded n_pad x m_pad workspace layout the GEMMs
 //             use.
 //   output    O_b = out_scale * X (or X^T), cast to the output dtype.
+//   momentum + pre-scale (the fused step): M_b <- mu M_b + G_b in place, and
+//             in the same pass X_0 = bf16(M_b) unscaled plus per-tile partial
+//             sums of squares of the new M_b; the 1 / (||M_b||_F + eps) is
+//             applied inside the first Newton-Schulz step's GEMM epilogues.
 // Both move 8-element runs (16-byte vectors where the row length and the
 // alignment allow); the transposing variants go through a 64 x 64 LDS tile so
 // both the read and the write side are coalesced.
@@ -36,6 +40,7 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   g.n_pad = round_up(g.n, kNsTile);
   g.m_pad = round_up(g.m, kNsTile);
   g.sumsq_chunks = (rows * cols + kNormChunk - 1) / kNormChunk;
+  g.prescale_tiles = (g.n_pad / kT) * (g.m_pad / kT);
   const size_t xb = static_cast<size_t>(batch) * g.n_pad * g.m_pad * 2;
   const size_t ab = static_cast<size_t>(batch) * g.n_pad * g.n_pad * 2;
   size_t off = 0;
@@ -43,7 +48,8 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   g.off_x1 = off; off = align256(off + xb);
   g.off_a = off; off = align256(off + ab);
   g.off_b = off; off = align256(off + ab);
-  g.off_partials = off; off = align256(off + static_cast<size_t>(batch * g.sumsq_chunks) * 4);
+  const int64_t partials = g.sumsq_chunks > g.prescale_tiles ? g.sumsq_chunks : g.prescale_tiles;
+  g.off_partials = off; off = align256(off + static_cast<size_t>(batch * partials) * 4);
   g.off_invnorm = off; off = align256(off + static_cast<size_t>(batch) * 4);
   g.total = off;
   return g;
@@ -165,6 +171,95 @@ __global__ __launch_bounds__(kThreads) void prescale_kernel(const void* __restri
   if (S != nullptr) return;
   __syncthreads();
   // T[c0 + cc][r0 + 8 q' .. + 7] = tile[8 q' ..][cc]
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cc = pass * 32 + (threadIdx.x >> 3);
+    const int rq = 8 * q;
+    const u32x4 o = {pack_bf16x2(tile[rq + 0][cc], tile[rq + 1][cc]), pack_bf16x2(tile[rq + 2][cc], tile[rq + 3][cc]),
+                     pack_bf16x2(tile[rq + 4][cc], tile[rq + 5][cc]), pack_bf16x2(tile[rq + 6][cc], tile[rq + 7][cc])};
+    *reinterpret_cast<u32x4*>(tb + (c0 + cc) * R_pad + r0 + rq) = o;
+  }
+}
+
+// Fused momentum and pre-scale.  M_b, G_b are R x C float32 (rows x cols);
+// M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the stand-alone
+// momentum), and the new M_b is written unscaled as bf16 into S (R_pad x
+// C_pad) or transposed into T (C_pad x R_pad), zero-padded, as in
+// prescale_kernel.  Each block also writes the float32 sum of squares of its
+// tile's new M values to partials[b * tiles + tile].
+// grid (C_pad / 64, R_pad / 64, batch).
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __restrict__ M,
+                                                                    const float* __restrict__ G,
+                                                                    int64_t batch_stride, float mu, int64_t R,
+                                                                    int64_t C, int64_t R_pad, int64_t C_pad,
+                                                                    uint16_t* __restrict__ S,
+                                                                    uint16_t* __restrict__ T,
+                                                                    float* __restrict__ partials) {
+  __shared__ float tile[kT][kT + 1];
+  __shared__ float red[kThreads / 64];
+  const int64_t b = blockIdx.z;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kT, r0 = static_cast<int64_t>(blockIdx.y) * kT;
+  float* mb = M + b * batch_stride;
+  const float* gb = G + b * batch_stride;
+  uint16_t* sb = S + static_cast<size_t>(b) * R_pad * C_pad;
+  uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
+  const int q = threadIdx.x & 7;
+  float ss = 0.f;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int rr = pass * 32 + (threadIdx.x >> 3);
+    const int64_t r = r0 + rr, c = c0 + 8 * q;
+    float x[8];
+    if constexpr (VEC) {
+      // C % 8 == 0: a run is wholly inside or wholly outside the matrix
+      if (r < R && c < C) {
+        f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
+        const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
+        f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
+        const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
+        m0.x = momentum_op(m0.x, g0.x, mu);
+        m0.y = momentum_op(m0.y, g0.y, mu);
+        m0.z = momentum_op(m0.z, g0.z, mu);
+        m0.w = momentum_op(m0.w, g0.w, mu);
+        m1.x = momentum_op(m1.x, g1.x, mu);
+        m1.y = momentum_op(m1.y, g1.y, mu);
+        m1.z = momentum_op(m1.z, g1.z, mu);
+        m1.w = momentum_op(m1.w, g1.w, mu);
+        __builtin_nontemporal_store(m0, mp);
+        __builtin_nontemporal_store(m1, mp + 1);
+        x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
+        x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = 0.f;
+        if (r < R && c + e < C) {
+          const float m = momentum_op(mb[r * C + c + e], gb[r * C + c + e], mu);
+          mb[r * C + c + e] = m;
+          x[e] = m;
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    if (S != nullptr) {
+      const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                       pack_bf16x2(x[6], x[7])};
+      *reinterpret_cast<u32x4*>(sb + r * C_pad + c) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
+    }
+  }
+  // block_sum's barrier also publishes the tile
+  const float tile_ss = block_sum(ss, red);
+  if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = tile_ss;
+  if (S != nullptr) return;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int cc = pass * 32 + (threadIdx.x >> 3);
@@ -326,6 +421,31 @@ hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride
     if (vec) go(prescale_kernel<false, true>);
     else go(prescale_kernel<false, false>);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
+                                    const NsGeometry& g, float eps, char* ws, hipStream_t stream) {
+  float* partials = reinterpret_cast<float*>(ws + g.off_partials);
+  float* invnorm = reinterpret_cast<float*>(ws + g.off_invnorm);
+  uint16_t* X0 = reinterpret_cast<uint16_t*>(ws + g.off_x0);
+  const int64_t R = g.rows, C = g.cols;
+  const int64_t R_pad = g.transposed ? g.m_pad : g.n_pad, C_pad = g.transposed ? g.n_pad : g.m_pad;
+  uint16_t* S = g.transposed ? nullptr : X0;
+  uint16_t* T = g.transposed ? X0 : nullptr;
+  const bool vec = C % 8 == 0 && (g.batch == 1 || batch_stride % 8 == 0) &&
+                   reinterpret_cast<uintptr_t>(M) % 32 == 0 && reinterpret_cast<uintptr_t>(G) % 32 == 0;
+  dim3 grid(static_cast<unsigned>(C_pad / kT), static_cast<unsigned>(R_pad / kT), static_cast<unsigned>(g.batch));
+  if (vec)
+    hipLaunchKernelGGL(momentum_prescale_kernel<true>, grid, dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C,
+                       R_pad, C_pad, S, T, partials);
+  else
+    hipLaunchKernelGGL(momentum_prescale_kernel<false>, grid, dim3(kThreads), 0, stream, M, G, batch_stride, mu, R,
+                       C, R_pad, C_pad, S, T, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(invnorm_kernel, dim3(static_cast<unsigned>(g.batch)), dim3(kThreads), 0, stream, partials,
+                     g.prescale_tiles, eps, invnorm);
   return hipGetLastError();
 }
 

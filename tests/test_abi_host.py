@@ -27,7 +27,8 @@ def mc():
 def test_header_declares_the_entry_points():
     names = set(_declared())
     assert {"muonclip_momentum", "muon_ns_orthogonalize_batched", "muon_apply_update", "qk_maxlogit",
-            "qk_clip_apply", "muon_ns_workspace_bytes", "mc_abi_version", "mc_status_string"} <= names
+            "qk_clip_apply", "muon_ns_workspace_bytes", "mc_abi_version", "mc_status_string",
+            "muon_momentum_ns_update_batched"} <= names
 
 
 def test_library_exports_every_declared_symbol(mc):
@@ -96,6 +97,37 @@ def test_ns_validation(mc):
     assert call(wsb=ws_bytes - 1) == EWORKSPACE
     bad = (ctypes.c_float * 15)(*([float("inf")] * 15))
     assert call(coeffs=bad) == EINVAL
+
+
+def test_fused_validation(mc):
+    L = mc.lib
+    coeffs = (ctypes.c_float * 15)(*([3.4445, -4.775, 2.0315] * 5))
+    ws_bytes = L.muon_ns_workspace_bytes(4, 256, 512)
+
+    def call(**kw):
+        a = dict(M=FAKE, G=FAKE, mu=0.95, W=FAKE, w_dtype=1, batch=4, rows=256, cols=512, stride=256 * 512,
+                 steps=5, coeffs=coeffs, eps=1e-7, scale=4.5, lr=0.02, wd=0.1, ws=ctypes.c_void_p(0x200000),
+                 wsb=ws_bytes, stream=None, ev=None)
+        a.update(kw)
+        return L.muon_momentum_ns_update_batched(a["M"], a["G"], a["mu"], a["W"], a["w_dtype"], a["batch"],
+                                                 a["rows"], a["cols"], a["stride"], a["steps"], a["coeffs"],
+                                                 a["eps"], a["scale"], a["lr"], a["wd"], a["ws"], a["wsb"],
+                                                 a["stream"], a["ev"])
+    assert call(batch=0) == 0
+    assert call(cols=0) == EINVAL
+    assert call(w_dtype=3) == EDTYPE
+    assert call(rows=70000, cols=8) == ESHAPE
+    assert call(G=None) == EINVAL
+    assert call(W=None) == EINVAL
+    assert call(stride=100) == EINVAL
+    assert call(mu=float("nan")) == EINVAL
+    assert call(lr=float("inf")) == EINVAL
+    assert call(steps=65) == EINVAL
+    assert call(coeffs=None) == EINVAL
+    assert call(M=ctypes.c_void_p(0x100002)) == EALIGN
+    assert call(W=ctypes.c_void_p(0x100001)) == EALIGN
+    assert call(ws=ctypes.c_void_p(0x200080)) == EALIGN
+    assert call(wsb=ws_bytes - 1) == EWORKSPACE
 
 
 def test_update_validation(mc):

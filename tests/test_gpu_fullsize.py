@@ -140,3 +140,35 @@ def test_maxlogit_long_context_32k(mc):
         say("  oracle head", h)
         ref = oracle.max_logit(f64(L.Q[:, h:h + 1]), f64(L.Kc[:, h:h + 1]), Kr_h, block=4096)[0]
         assert rel_err(s[h], ref) <= 1e-4
+
+
+@pytest.mark.parametrize("shape", [(64, 2048, 7168), (8, 7168, 2048)])
+def test_fused_expert_batch(mc, shape):
+    """The fused momentum + Newton-Schulz + update call at the benchmark's chunk
+    shapes (64 gate/up experts; 8 down-projection experts, iterated on the
+    transpose): sampled momentum elements bit-exact, and W_t - W_{t-1} of two
+    matrices against the oracle (lr 1 so that the update, not the bf16
+    rounding of W, dominates the difference)."""
+    batch, rows, cols = shape
+    say("full size fused:", shape)
+    gen = workloads.generator(31 + rows, DEV)
+    M = workloads.normal(shape, 1e-4, gen, DEV)
+    G = workloads.normal(shape, 1e-4, gen, DEV)
+    W = workloads.normal(shape, 0.02, gen, DEV, torch.bfloat16)
+    idx_t = torch.from_numpy(_sample(M.numel(), 1 << 20, 3)).to(DEV)
+    m0 = M.view(-1)[idx_t].cpu().numpy()
+    g0 = G.view(-1)[idx_t].cpu().numpy()
+    picks = (0, batch - 1)
+    M_pick = {b: M[b].clone() for b in picks}
+    G_pick = {b: G[b].clone() for b in picks}
+    W_pick = {b: W[b].clone() for b in picks}
+    mc.muon_momentum_ns_update_batched(M, G, W, 1.0, 0.1, 0.95)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(M.view(-1)[idx_t].cpu().numpy(), oracle.momentum_update(m0, g0, 0.95))
+    for b in picks:
+        say("  oracle step of matrix", b)
+        Mn = oracle.momentum_update(M_pick[b].cpu().numpy(), G_pick[b].cpu().numpy(), 0.95)
+        W0 = f64(W_pick[b])
+        ref = oracle.apply_update(W0, oracle.muon_orthogonalised_update(Mn.astype(np.float64)), 1.0, 0.1, "bf16")
+        err = rel_fro(f64(W[b]) - W0, ref - W0)
+        assert err <= 2e-2, (b, err)

@@ -265,6 +265,65 @@ def test_newton_schulz_misaligned(mc):
         assert rel_fro(f64(Ov[b]), ref) <= 2e-2
 
 
+FUSED_CASES = [
+    # (batch, rows, cols, W dtype, NS steps)
+    (2, 256, 512, torch.bfloat16, 5),   # vector paths throughout
+    (3, 200, 328, torch.float32, 5),    # ragged padding; cols % 8 != 0: element-wise momentum pass
+    (2, 300, 200, torch.bfloat16, 5),   # rows > cols: iterated on M^T, W updated transposed
+    (1, 130, 50, torch.float32, 5),     # tall and ragged
+    (2, 257, 330, torch.bfloat16, 5),   # cols % 4 != 0: element-wise W update
+    (1, 600, 1000, torch.bfloat16, 1),  # one step: the normalising step is also the updating one
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES)
+def test_fused_momentum_ns_update(mc, case):
+    """muon_momentum_ns_update_batched against the oracle's momentum (bit-exact),
+    Newton-Schulz and update.  lr is large for bf16 W so that the update, not
+    W's own rounding, dominates W_t - W_{t-1}."""
+    batch, rows, cols, wdt, steps = case
+    say("fused momentum + NS + update", case)
+    g = workloads.generator(90 + rows + cols, "cpu")
+    M0 = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32)
+    G = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32)
+    W0 = workloads.normal((batch, rows, cols), 0.02, g, "cpu", wdt)
+    lr = 1.0 if wdt == torch.bfloat16 else 0.02
+    coeffs = mc.NS_COEFFS[:steps]
+    M, W = M0.to(DEV), W0.to(DEV)
+    mc.muon_momentum_ns_update_batched(M, G.to(DEV), W, lr, 0.1, 0.95, steps=steps, coeffs=coeffs)
+    torch.cuda.synchronize()
+    M_ref = oracle.momentum_update(M0.numpy(), G.numpy(), 0.95)
+    np.testing.assert_array_equal(M.cpu().numpy(), M_ref)
+    wname = "bf16" if wdt == torch.bfloat16 else "f32"
+    for b in range(batch):
+        O_ref = oracle.muon_orthogonalised_update(M_ref[b].astype(np.float64), coeffs=coeffs)
+        W_ref = oracle.apply_update(f64(W0[b]), O_ref, lr, 0.1, wname)
+        d_gpu = f64(W[b]) - f64(W0[b])
+        d_ref = W_ref - f64(W0[b])
+        err = rel_fro(d_gpu, d_ref)
+        assert err <= 2e-2, (b, err)
+
+
+def test_fused_matches_separate_calls(mc):
+    """The fused call and momentum + NS + update as three calls agree to the
+    Newton-Schulz tolerance (same M bit for bit)."""
+    say("fused vs separate calls")
+    batch, rows, cols = 2, 512, 1024
+    g = workloads.generator(5150, "cpu")
+    M0 = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32).to(DEV)
+    G = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32).to(DEV)
+    W0 = workloads.normal((batch, rows, cols), 0.02, g, "cpu", torch.float32).to(DEV)
+    M1, W1 = M0.clone(), W0.clone()
+    mc.muon_momentum_ns_update_batched(M1, G, W1, 0.02, 0.1, 0.95)
+    M2, W2 = M0.clone(), W0.clone()
+    mc.muonclip_momentum(M2, G, 0.95)
+    O = mc.muon_ns_orthogonalize_batched(M2, out_scale=mc.muon_out_scale(rows, cols), out_dtype=torch.float32)
+    mc.muon_apply_update(W2, O, 0.02, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(M1, M2)
+    assert rel_fro(f64(W1 - W0), f64(W2 - W0)) <= 2e-2
+
+
 def test_newton_schulz_zero_matrix(mc):
     say("newton-schulz zero")
     O = mc.muon_ns_orthogonalize_batched(torch.zeros(2, 64, 128, device=DEV), out_scale=2.0)
