@@ -2,8 +2,9 @@
 // accumulation and the decoupled weight-decay update.
 //
 // Both stream their operands once (momentum: 12 bytes per element; update:
-// 4 + 2 + ... bytes per element depending on dtypes) with 16-byte vector
-// accesses, a grid-stride loop and no reuse, so they are bound by HBM.
+// 4 + 2 + ... bytes per element depending on dtypes) with 16-byte
+// non-temporal vector accesses, one vector per thread and no reuse, so they
+// are bound by HBM.
 // The arithmetic (momentum_op, update_op) is separate float operations with FP
 // contraction switched off: momentum must equal float32 multiply-then-add bit
 // for bit.
@@ -17,9 +18,12 @@ namespace {
 constexpr int kThreads = 256;
 
 __host__ int grid_for(int64_t work_items) {
-  // Enough blocks to fill 256 CUs several times over; the loop covers the rest.
+  // One work item per thread (the loop then runs once): measured on MI355X,
+  // a grid that covers the whole array streams about 20 % faster than a
+  // grid-stride loop over a few thousand blocks (6.5 vs 5.1-5.4 TB/s for
+  // the momentum).  The loop only covers arrays beyond the grid limit.
   int64_t blocks = (work_items + kThreads - 1) / kThreads;
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks > 0x7fffffff) blocks = 0x7fffffff;
   if (blocks < 1) blocks = 1;
   return static_cast<int>(blocks);
 }

@@ -24,21 +24,25 @@
 // below are applied on the global side: each lane fetches the 16 bytes that
 // belong in its slot.
 //
-// Operand tiles, by the layout of the matrix they come from:
-//  * K-contiguous (mode 0: both operands are row panels of X): LDS row r (an
-//    output index) holds 32 consecutive k as 4 units of 16 bytes, unit u at
-//    u ^ swizzle(r); fragments are ds_read_b128.  One DMA instruction covers
-//    16 rows x 64 bytes.
-//  * K-rows (modes 1/2: A and B' are symmetric, so their row panels are the
-//    column panels the product needs, and X is row-major with K as its row
-//    index): 32 k-rows x 256 output indices, 512 bytes per row, unit u at
-//    u ^ 4 (r & 3).  One DMA instruction covers 2 rows x 512 bytes, which the
-//    LDS-DMA path moves about 45 % faster than 64-byte row segments
-//    (measured on MI355X, one CU: 81 vs 56 GB/s).  Fragments come from
-//    ds_read_b64_tr_b16, which hands each lane 4 consecutive k of one column
-//    (measured on gfx950: within each 16-lane group, lane i receives element
-//    i % 4 of the 4 x 16-bit values addressed by lanes i / 4 + 4 e,
-//    e = 0..3); two of them make one 8-k MFMA operand.
+// Operand tiles.  The left tile is always K-contiguous in LDS: row r (an
+// output index) holds 32 consecutive k as 4 units of 16 bytes, unit u at
+// u ^ swizzle(r), read with ds_read_b128.  It comes from
+//  * X itself for X X^T (row panels of X, 16 rows x 64 bytes per DMA
+//    instruction), or
+//  * A or B' for the other two products, which this file stores in a blocked
+//    layout (256 x 32 blocks, row-major inside): a K-contiguous 256 x 32 tile
+//    of A or B' is one contiguous 16 KB block.  A and B' are symmetric, so
+//    their row panels are the column panels the products need.
+// The right tile is the same kind of tile for X X^T and A A; for B' X it is a
+// "K-rows" tile of X (row-major with K as its row index): 32 k-rows x 256
+// output indices, 2 rows x 512 bytes per DMA instruction, unit u of row r at
+// u ^ 4 (r & 3), and fragments come from ds_read_b64_tr_b16, which hands
+// each lane 4 consecutive k of one column (measured on gfx950: within each
+// 16-lane group, lane i receives element i % 4 of the 4 x 16-bit values
+// addressed by lanes i / 4 + 4 e, e = 0..3); two of them make one 8-k MFMA
+// operand.  Measured on MI355X: ds_read_b128 fragments stall the MFMA
+// pipeline about 2.5 x less per K step than transposed b64 reads, and a
+// contiguous 1 KB DMA instruction is the fastest LDS-DMA pattern.
 //
 // MFMA operand roles: the MFMA "A" operand is the right-hand tile (output
 // columns j) and "B" the left-hand tile (output rows i), so each lane ends up
@@ -156,32 +160,32 @@ __device__ __forceinline__ uint32_t tr_addr(int tile_off, int col_base, int x, i
 }
 
 // Per-lane LDS read addresses relative to a stage; everything else that
-// varies inside a stage is a compile-time or uniform offset.
+// varies inside a stage is a compile-time or uniform offset.  The left tile
+// is always K-contiguous (p[ks] per k16 sub-step, + 2 KB per 32-row MFMA
+// tile); the right tile is K-contiguous (q[ks], modes 0/1) or K-rows (q[x]
+// per 32-column MFMA tile, mode 2).
 struct FragAddr {
-  uint32_t p[4];  // left tile: K-rows per 32-row MFMA tile y; K-contiguous per k16 sub-step (p[0..1])
-  uint32_t q[4];  // right tile: K-rows per 32-column MFMA tile x; K-contiguous per sub-step
+  uint32_t p[2];
+  uint32_t q[4];
 };
 
-template <bool KROWS>
+template <bool Q_KROWS>
 __device__ __forceinline__ FragAddr frag_addresses(int lane, int wm, int wn) {
   FragAddr a;
-  if constexpr (KROWS) {
+  // K-contiguous: lane l reads row l % 32 of each 32-row MFMA tile,
+  // k = 8 (l / 32) + 16 ks .. + 7
+  const int frag_row = lane & 31, frag_half = lane >> 5, swz = swizzle(frag_row);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      a.p[x] = tr_addr(0, wm * 128, x, lane);
-      a.q[x] = tr_addr(kTileBytes, wn * 128, x, lane);
-    }
+  for (int ks = 0; ks < 2; ++ks) {
+    const int unit = (2 * ks + frag_half) ^ swz;
+    a.p[ks] = (wm * 128 + frag_row) * 64 + unit * 16;
+    if constexpr (!Q_KROWS) a.q[ks] = kTileBytes + (wn * 128 + frag_row) * 64 + unit * 16;
+  }
+  if constexpr (Q_KROWS) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) a.q[x] = tr_addr(kTileBytes, wn * 128, x, lane);
   } else {
-    // lane l reads row l % 32 of each 32-row MFMA tile (+ 2 KB per tile),
-    // k = 8 (l / 32) + 16 ks .. + 7
-    const int frag_row = lane & 31, frag_half = lane >> 5, swz = swizzle(frag_row);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int unit = (2 * ks + frag_half) ^ swz;
-      a.p[ks] = (wm * 128 + frag_row) * 64 + unit * 16;
-      a.q[ks] = kTileBytes + (wn * 128 + frag_row) * 64 + unit * 16;
-      a.p[ks + 2] = a.q[ks + 2] = 0;
-    }
+    a.q[2] = a.q[3] = 0;
   }
   return a;
 }
@@ -200,17 +204,16 @@ __device__ __forceinline__ bf16x8 tr_frag(uint32_t addr) {
   return as_bf16x8(v);
 }
 
-template <bool KROWS>
+template <bool Q_KROWS>
 __device__ __forceinline__ void load_frags(const FragAddr& fadr, uint32_t stage_base, int ks, Frags& f) {
-  if constexpr (KROWS) {
+  const uint32_t pb = stage_base + fadr.p[ks];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) f.b[y] = tr_frag(stage_base + fadr.p[y] + ks * 8192);
+  for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
+  if constexpr (Q_KROWS) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) f.a[x] = tr_frag(stage_base + fadr.q[x] + ks * 8192);
   } else {
-    const uint32_t pb = stage_base + fadr.p[ks], qb = stage_base + fadr.q[ks];
-#pragma unroll
-    for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
+    const uint32_t qb = stage_base + fadr.q[ks];
 #pragma unroll
     for (int x = 0; x < 4; ++x) f.a[x] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(qb + x * 2048));
   }
@@ -228,9 +231,9 @@ __device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
 // next sub-step spread between them (4 MFMAs, then a quarter of the reads).
 // Left alone the scheduler moves every read next to its use, which exposes
 // LDS latency with one wave per SIMD.
-template <bool KROWS>
+template <bool Q_KROWS>
 __device__ __forceinline__ void interleave_reads_with_mfma() {
-  constexpr int kReads = KROWS ? 16 : 8;  // DS reads per sub-step
+  constexpr int kReads = Q_KROWS ? 12 : 8;  // DS reads per sub-step
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
@@ -238,14 +241,25 @@ __device__ __forceinline__ void interleave_reads_with_mfma() {
   }
 }
 
+// Blocked layout of the n_pad x n_pad matrices A and B' (internal to a call):
+// 256 x 32 blocks, row-major inside, block (r / 256, c / 32) at element
+// ((r / 256) * nkb + c / 32) * 8192 with nkb = n_pad / 32.  A K-contiguous
+// 256 x 32 operand tile of A or B' (rows r0.., k-block kb) is then one
+// contiguous 16 KB block, which the LDS DMA reads fastest.
+__device__ __forceinline__ int64_t blk_off(int r, int c, int nkb) {
+  return (static_cast<int64_t>(r >> 8) * nkb + (c >> 5)) * 8192 + (r & 255) * 32 + (c & 31);
+}
+
 // Mirrored store of a symmetric result: the wave's staged 128 x 128 bf16
 // sub-tile (row ii at eb + ii * 256, 16-byte unit u at position u ^ (ii & 15))
-// is written transposed: element (ii, jj) goes
-// to dst[jj * ld + ii].  Instruction s covers rows ii = R .. R + 7
+// is written transposed: element (ii, jj) goes to row r0d + jj, column
+// c0d + ii.  Instruction s covers rows ii = R .. R + 7
 // (R = 8 (s / 2)) and 64 columns: 16-lane group g takes columns
 // C = 64 (s % 2) + 16 g .. + 15, lane i column C + i, which it assembles
 // from two transposed reads of 4 rows each.
-__device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int64_t ld, int lane) {
+// dst is the matrix base; (r0, c0) the destination of staged element (0, 0)
+// after the transposition; the destination is blocked.
+__device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int r0d, int c0d, int nkb, int lane) {
   const int g = lane >> 4, i = lane & 15;
 #pragma unroll 4
   for (int s = 0; s < 32; ++s) {
@@ -258,7 +272,7 @@ __device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int
         (lds_s16x4_t*)(uintptr_t)(eb + r1 * 256 + (((col >> 3) ^ (r1 & 15)) << 4) + (col & 7) * 2));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
-    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(C + i) * ld + R) = v;
+    *reinterpret_cast<u32x4*>(dst + blk_off(r0d + C + i, c0d + R, nkb)) = v;
   }
 }
 
@@ -279,7 +293,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
                     uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
                     float alpha, float beta, float diag, const float* __restrict__ inv, UpdArgs ua) {
   static_assert(UPD == 0 || MODE == 2, "only X' = B' X can apply the update");
-  constexpr bool kKRows = MODE != 0;
+  constexpr bool kQKRows = MODE == 2;      // right operand X as K-rows tiles
+  constexpr bool kBlockedOut = MODE != 2;  // A, B' results in the blocked layout
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
@@ -306,29 +321,35 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const int i0 = ti * kBM, j0 = tj * kBN;
 
   const int64_t nn = static_cast<int64_t>(n_pad) * n_pad, nm = static_cast<int64_t>(n_pad) * m_pad;
-  // Operand tile origins at k = 0 and their pitches.
-  //   mode 0: rows i0.. and j0.. of X, K-contiguous (pitch m_pad)
-  //   mode 1: k-rows of A at columns i0.. and j0.. (pitch n_pad)
-  //   mode 2: k-rows of B' at columns i0.. (pitch n_pad), of X at j0.. (m_pad)
+  const int nkb = n_pad / kBK;  // k-blocks per row of the blocked layout
+  // Operand tiles at k = 0, their row pitch and the step between K-steps.
+  //   mode 0: rows i0.. and j0.. of X, K-contiguous (pitch m_pad, step 32)
+  //   mode 1: blocks of A at rows i0.. and j0.. (pitch 32, step one block)
+  //   mode 2: blocks of B' at rows i0.. (symmetric: rows are columns), and
+  //           k-rows of X at columns j0.. (pitch m_pad, step 32 rows)
   const uint16_t* Pg;
   const uint16_t* Qg;
-  int64_t ldp, ldq;
+  int64_t ldp, ldq, kstep_p, kstep_q;
   int K;
   if constexpr (MODE == 0) {
     Pg = in0 + mat * nm + static_cast<int64_t>(i0) * m_pad;
     Qg = in0 + mat * nm + static_cast<int64_t>(j0) * m_pad;
     ldp = ldq = m_pad;
+    kstep_p = kstep_q = kBK;
     K = m_pad;
   } else if constexpr (MODE == 1) {
-    Pg = in0 + mat * nn + i0;
-    Qg = in0 + mat * nn + j0;
-    ldp = ldq = n_pad;
+    Pg = in0 + mat * nn + blk_off(i0, 0, nkb);
+    Qg = in0 + mat * nn + blk_off(j0, 0, nkb);
+    ldp = ldq = kBK;
+    kstep_p = kstep_q = kBM * kBK;
     K = n_pad;
   } else {
-    Pg = in0 + mat * nn + i0;
+    Pg = in0 + mat * nn + blk_off(i0, 0, nkb);
     Qg = in1 + mat * nm + j0;
-    ldp = n_pad;
+    ldp = kBK;
+    kstep_p = kBM * kBK;
     ldq = m_pad;
+    kstep_q = static_cast<int64_t>(kBK) * m_pad;
     K = n_pad;
   }
 
@@ -337,24 +358,20 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  const uint32_t off_p = kKRows ? kr_lane_offset(ldp, wave, lane) : kc_lane_offset(ldp, wave, lane);
-  const uint32_t off_q = (MODE == 2) ? kr_lane_offset(ldq, wave, lane) : off_p;
+  const uint32_t off_p = kc_lane_offset(ldp, wave, lane);
+  const uint32_t off_q = kQKRows ? kr_lane_offset(ldq, wave, lane) : kc_lane_offset(ldq, wave, lane);
   const int KT = K / kBK;
   // Loads of K-step kt into stage kt % kStages.  Past the last step the last
   // in-bounds tile is fetched again into a stage nobody reads, which keeps
   // the number of loads in flight (and so the wait counts) fixed.
-  auto k_offset = [&](int kt, int64_t ld) -> int64_t {
-    const int64_t k0 = min(kt, KT - 1) * kBK;
-    return kKRows ? k0 * ld : k0;
-  };
   auto issue_p = [&](int kt) {
-    issue_tile<kKRows>(Pg + k_offset(kt, ldp), ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
+    issue_tile<false>(Pg + min(kt, KT - 1) * kstep_p, ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
   };
   auto issue_q = [&](int kt) {
-    issue_tile<kKRows>(Qg + k_offset(kt, ldq), ldq, off_q, lds + (kt % kStages) * kStageBytes + kTileBytes,
-                       wave);
+    issue_tile<kQKRows>(Qg + min(kt, KT - 1) * kstep_q, ldq, off_q,
+                        lds + (kt % kStages) * kStageBytes + kTileBytes, wave);
   };
-  const FragAddr fadr = frag_addresses<kKRows>(lane, wm, wn);
+  const FragAddr fadr = frag_addresses<kQKRows>(lane, wm, wn);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -377,21 +394,21 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   wait_vmem<(kStages - 2) * kLoadsPerStage>();
   __syncthreads();
   Frags f0, f1;
-  load_frags<kKRows>(fadr, lds, 0, f0);
+  load_frags<kQKRows>(fadr, lds, 0, f0);
   for (int kt = 0; kt < KT; ++kt) {
     const uint32_t cur = lds + (kt % kStages) * kStageBytes;
     const uint32_t nxt = lds + ((kt + 1) % kStages) * kStageBytes;
     issue_p(kt + kStages - 1);
-    load_frags<kKRows>(fadr, cur, 1, f1);
+    load_frags<kQKRows>(fadr, cur, 1, f1);
     mfma_16(f0, acc);
-    interleave_reads_with_mfma<kKRows>();
+    interleave_reads_with_mfma<kQKRows>();
     wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerTile>();
     __syncthreads();
     issue_q(kt + kStages - 1);
     // After the last step this reads a stage of redundant tiles; unused.
-    load_frags<kKRows>(fadr, nxt, 0, f0);
+    load_frags<kQKRows>(fadr, nxt, 0, f0);
     mfma_16(f1, acc);
-    interleave_reads_with_mfma<kKRows>();
+    interleave_reads_with_mfma<kQKRows>();
   }
 
   // ---- epilogue, staged through LDS (free once every stage is consumed).
@@ -416,13 +433,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
 
   if constexpr (MODE == 1) {
-    const uint16_t* E = in0 + mat * nn + static_cast<int64_t>(i0w) * ldo + j0w;
-    const char* ebase = reinterpret_cast<const char*>(E);
+    // the A sub-tile, from the blocked layout (64-byte runs, 16 per 4 rows)
+    const char* ebase = reinterpret_cast<const char*>(in0 + mat * nn);
 #pragma unroll 4
     for (int s = 0; s < 32; ++s) {
       const int row = 4 * s + (lane >> 4);
       const int u = (lane & 15) ^ (row & 15);
-      load_lds16(ebase, static_cast<uint32_t>((row * ldo + 8 * u) * 2), eb + 1024 * s);
+      load_lds16(ebase, static_cast<uint32_t>(blk_off(i0w + row, j0w + 8 * u, nkb) * 2), eb + 1024 * s);
     }
     wait_vmem<0>();
   }
@@ -555,11 +572,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     for (int s = 0; s < 32; ++s) {
       const int row = 4 * s + (lane >> 4), u = lane & 15;
       const u32x4 v = *(const lds_u32x4_t*)(uintptr_t)st_addr(row, u);
-      *reinterpret_cast<u32x4*>(Ow + static_cast<int64_t>(row) * ldo + 8 * u) = v;
+      uint16_t* dst = kBlockedOut ? O + blk_off(i0w + row, j0w + 8 * u, nkb)
+                                  : Ow + static_cast<int64_t>(row) * ldo + 8 * u;
+      *reinterpret_cast<u32x4*>(dst) = v;
     }
   }
   if constexpr (MODE != 2) {
-    if (ti != tj) store_transposed(eb, O + static_cast<int64_t>(j0w) * n_pad + i0w, n_pad, lane);
+    if (ti != tj) store_transposed(eb, O, j0w, i0w, nkb, lane);
   }
 }
 
