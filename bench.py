@@ -198,8 +198,8 @@ def run(args):
 
     # timed region: K steps bracketed by synchronisation
     acc = {"momentum": 0.0, "maxlogit": 0.0, "clip": 0.0, "ns": 0.0, "update": 0.0}
-    gemm_ms = {0: [], 1: [], 2: []}
-    gemm_flops = {0: [], 1: [], 2: []}
+    gemm_ms = {0: [], 1: [], 2: []} if args.unfused else {0: [], 1: [], 2: [], "2u": []}
+    gemm_flops = {k: [] for k in gemm_ms}
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -218,8 +218,10 @@ def run(args):
             for st in range(steps_ns):
                 for gm in range(3):
                     a, b = gemm_ev[k][2 * (3 * st + gm)], gemm_ev[k][2 * (3 * st + gm) + 1]
-                    gemm_ms[gm].append(a.elapsed_time(b))
-                    gemm_flops[gm].append(per[gm] * cnt)
+                    # the fused path's last B'X launch also applies the update to W
+                    key = "2u" if (gm == 2 and st == steps_ns - 1 and not args.unfused) else gm
+                    gemm_ms[key].append(a.elapsed_time(b))
+                    gemm_flops[key].append(per[gm] * cnt)
         log(f"step {i + 1}/{args.steps} done")
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -242,9 +244,9 @@ def run(args):
     dom_avg_ms = sum(gemm_ms[dom]) / dom_launches
     dom_avg_flops = sum(gemm_flops[dom]) / dom_launches
     achieved = dom_avg_flops / (dom_avg_ms * 1e-3) / 1e12
-    kernel_names = {0: "ns_gemm_kernel<0> (A = X X^T)", 1: "ns_gemm_kernel<1> (B' = aI + bA + cAA)",
-                    2: "ns_gemm_kernel<2> (X' = B'X)" if args.unfused else
-                    "ns_gemm_kernel<2, *> (X' = B'X; the last step's launch applies the update to W)"}
+    kernel_names = {0: "ns_gemm_kernel<0, 0> (A = X X^T)", 1: "ns_gemm_kernel<1, 0> (B' = aI + bA + cAA)",
+                    2: "ns_gemm_kernel<2, 0> (X' = B'X)",
+                    "2u": "ns_gemm_kernel<2, 1> (last step: X' = B'X applied as the update of bf16 W)"}
 
     breakdown = {
         "path": "three calls: momentum, Newton-Schulz, update" if args.unfused else

@@ -2,16 +2,19 @@
 // with the logit matrix never written anywhere ("Kimi K2 内部机制", MuonClip
 // section, core maths: max over the batch and over all token pairs).
 //
-// bf16 path (d in {64, 128, 192}, d_c and d_r multiples of 8):
-//   A 512-thread workgroup (8 wave64s) owns 512 query rows of one (b, h); each
-//   wave keeps its 64 rows of Q as MFMA fragments in registers for the whole
-//   kernel and streams every key row of (b, h) through a double-buffered LDS
-//   stage of 64 keys x d.  Per key block a wave issues 2 x 2 x (d/16)
-//   v_mfma_f32_32x32x16_bf16 and folds the 64 x 64 float32 logits into a
-//   16-register running max.  The key row is assembled in LDS from the
-//   head's own part Kc[b,h,j] and the shared rotary part Kr[b,j] (MLA).
-//   Consecutive workgroups of one (b, h) are kept on one XCD so the key
-//   stream is read from that XCD's L2.
+// bf16 path (d_c in {64, 128, 192} and d_r in {0, 64}, d <= 192, Sk >= 64):
+//   A 256-thread workgroup (4 wave64s, one per SIMD) owns 512 query rows of
+//   one (b, h); each wave keeps its 128 rows of Q as MFMA fragments in
+//   registers for the whole kernel, so every key fragment read from LDS feeds
+//   4 MFMAs.  Every key row of (b, h) streams through 4 LDS stages of 64 keys
+//   x d, filled by LDS DMA (global_load_lds, per-lane 64-bit addresses) three
+//   blocks ahead, one barrier per block; Kc and Kr rows land in two regions
+//   of the stage, so each DMA instruction reads whole rows of one source.  Per key block a wave issues
+//   4 x 2 x (d/16) v_mfma_f32_32x32x16_bf16 and folds the 128 x 64 float32
+//   logits into a 16-register running max.  The key row is assembled in LDS
+//   from the head's own part Kc[b,h,j] and the shared rotary part Kr[b,j]
+//   (MLA).  Consecutive workgroups of one (b, h) are kept on one XCD so the
+//   key stream is read from that XCD's L2.
 // float32 path (any other shape, either dtype): a plain LDS-tiled FMA kernel.
 //
 // Both finish with a workgroup max and one atomic max per workgroup into
@@ -41,136 +44,186 @@ __global__ void init_kernel(float* smax, int64_t H) {
 }
 
 // ------------------------------------------------------------------ bf16 MFMA
-constexpr int kMfmaThreads = 512;
-constexpr int kRowsPerWave = 64;
+constexpr int kMfmaThreads = 256;
+constexpr int kRowsPerWave = 128;
 constexpr int kRowsPerBlock = kRowsPerWave * (kMfmaThreads / 64);  // 512
 constexpr int kKeys = 64;                                          // key rows per LDS stage
+constexpr int kKeyStages = 4;                                      // prefetch distance 3
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int D>
-__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// One global_load_lds_dwordx4: 16 bytes from g_uniform + lane_off to LDS
+// address m0 + 16 * lane.  Inline asm so the compiler does not wait for the
+// copy before unrelated LDS reads; the copy is awaited with an explicit vmcnt
+// wait before the barrier that publishes the stage.  The lane offsets stay
+// constant for the whole kernel (the moving part is the uniform base), so no
+// register an in-flight copy reads is ever overwritten.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const char* g_uniform, uint32_t lane_off, uint32_t lds_addr) {
+  const uint64_t a = reinterpret_cast<uintptr_t>(g_uniform);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const char* base = reinterpret_cast<const char*>(lo | (hi << 32));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n"
+               :
+               : "s"(lds_addr), "v"(lane_off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Key stage: the 64 key rows' own parts (Kc, DC elements each) in one region
+// and their shared rotary parts (Kr, DR each) in another, each row-major; a
+// 16-byte unit u of row r sits at position u ^ (r & 7) of its row (a
+// permutation inside each aligned group of 8 units), so a fragment read of 32
+// consecutive rows at one unit spreads over 8 bank groups.  Every DMA
+// instruction then reads whole rows of one source: 1 KB = 1024 / (2 DC) rows
+// of Kc, or 1024 / (2 DR) rows of Kr.
+template <int DC, int DR>
+__global__ __launch_bounds__(kMfmaThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
-                          const uint16_t* __restrict__ Kr, int H, int Sq, int Sk, int d_c,
-                          int blocks_per_bh, float* __restrict__ smax, float scale) {
-  constexpr int kUnits = D / 8;   // 16-byte units per key row
-  constexpr int kSteps = D / 16;  // MFMA k-steps
-  constexpr int kStageUnits = kKeys * kUnits;
-  constexpr int kLoadsPerThread = (kStageUnits + kMfmaThreads - 1) / kMfmaThreads;
-  __shared__ u32x4 ks[2][kKeys][kUnits];
+                          const uint16_t* __restrict__ Kr, int H, int Sq, int Sk, int blocks_per_bh,
+                          float* __restrict__ smax, float scale) {
+  constexpr int D = DC + DR;
+  constexpr int kUc = DC / 8, kUr = DR / 8;        // 16-byte units per row and part
+  constexpr int kSteps = D / 16;                   // MFMA k-steps
+  constexpr int kKcBytes = kKeys * DC * 2, kKrBytes = kKeys * DR * 2;
+  constexpr int kStageBytes = kKcBytes + kKrBytes;
+  constexpr int kLoadsC = kKcBytes / 1024 / 4, kLoadsR = kKrBytes / 1024 / 4;  // per wave
+  constexpr int kLoads = kLoadsC + kLoadsR;
+  static_assert(DC % 64 == 0 && DR % 64 == 0, "parts of 64-element multiples");
+  __shared__ __attribute__((aligned(1024))) char smem[kKeyStages * kStageBytes];
   __shared__ float red[kMfmaThreads / 64];
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
   const uint32_t bid = xcd_grouped_block(blockIdx.x, gridDim.x);
   const int bh = bid / blocks_per_bh;
   const int ib = bid % blocks_per_bh;
   const int b = bh / H, h = bh % H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int frag_row = lane & 31, frag_half = lane >> 5;
-  const int d_r = D - d_c, uc = d_c / 8;
 
   const uint16_t* Qbh = Q + (static_cast<int64_t>(b) * H + h) * Sq * D;
-  const uint16_t* Kcbh = Kc + (static_cast<int64_t>(b) * H + h) * Sk * d_c;
-  const uint16_t* Krb = Kr ? Kr + static_cast<int64_t>(b) * Sk * d_r : nullptr;
+  const char* Kcbh = reinterpret_cast<const char*>(Kc + (static_cast<int64_t>(b) * H + h) * Sk * DC);
+  const char* Krb = reinterpret_cast<const char*>(Kr ? Kr + static_cast<int64_t>(b) * Sk * DR : Kc);
 
-  // ---- this wave's 64 query rows as MFMA "A" fragments (row = lane % 32)
+  // ---- this wave's 128 query rows as MFMA "A" fragments (row = lane % 32).
+  // Tails need no masking: a query row past Sq repeats row Sq - 1, and the
+  // last key block is the last 64 keys (it may overlap the previous one), so
+  // every logit computed is one of the real ones and the maximum is exact.
   const int row_base = ib * kRowsPerBlock + wave * kRowsPerWave;
-  bf16x8 qf[2][kSteps];
-  bool row_ok[2];
+  bf16x8 qf[4][kSteps];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int i = row_base + t * 32 + frag_row;
-    row_ok[t] = i < Sq;
+  for (int t = 0; t < 4; ++t) {
+    const int i = min(row_base + t * 32 + frag_row, Sq - 1);
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok[t]) v = *reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half);
-      qf[t][s] = as_bf16x8(v);
-    }
+    for (int s = 0; s < kSteps; ++s)
+      qf[t][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half));
   }
-  // Rows this lane's accumulator registers cover (for masking the row tail):
-  // register r of tile t is row 8*(r/4) + 4*frag_half + r%4 of that 32-row tile.
-  const bool any_row_tail = row_base + kRowsPerWave > Sq;
+  // Q is in registers before any key copy starts: otherwise the compiler,
+  // which cannot tell the copies from these loads, waits on the copies in
+  // flight before the first use of each Q register inside the loop.  The
+  // empty asm statements consume every Q register (forcing the loads to
+  // complete) and, being volatile, stay ahead of the copies' asm.
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) asm volatile("" : : "v"(qf[t][s]));
 
-  // ---- key staging: unit u of key row r goes to ks[s][r][u ^ (r & 7)]
-  u32x4 stage[kLoadsPerThread];
-  auto load_keys = [&](int j0) {
+  // ---- key loads.  DMA instruction l of this wave fills 1 KB at region
+  // offset 1024 (wave + 4 l); its lane slot p = 64 (wave + 4 l) + lane holds
+  // row r = p / units, unit (p % units) ^ (r & 7).  Lane offsets are relative
+  // to key row j0 of the block, which moves with the uniform base.
+  uint32_t off_c[kLoadsC > 0 ? kLoadsC : 1], off_r[kLoadsR > 0 ? kLoadsR : 1];
 #pragma unroll
-    for (int l = 0; l < kLoadsPerThread; ++l) {
-      const int idx = tid + l * kMfmaThreads;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (idx < kStageUnits) {
-        const int r = idx / kUnits, u = idx % kUnits, j = j0 + r;
-        if (j < Sk) {
-          if (u < uc) v = *reinterpret_cast<const u32x4*>(Kcbh + static_cast<int64_t>(j) * d_c + 8 * u);
-          else v = *reinterpret_cast<const u32x4*>(Krb + static_cast<int64_t>(j) * d_r + 8 * (u - uc));
-        }
-      }
-      stage[l] = v;
-    }
-  };
-  auto store_keys = [&](int s) {
+  for (int l = 0; l < kLoadsC; ++l) {
+    const int p = 64 * (wave + 4 * l) + lane;
+    const int r = p / kUc, u = (p % kUc) ^ (r & 7);
+    off_c[l] = static_cast<uint32_t>((r * DC + 8 * u) * 2);
+  }
 #pragma unroll
-    for (int l = 0; l < kLoadsPerThread; ++l) {
-      const int idx = tid + l * kMfmaThreads;
-      if (idx < kStageUnits) {
-        const int r = idx / kUnits, u = idx % kUnits;
-        ks[s][r][u ^ (r & 7)] = stage[l];
-      }
-    }
+  for (int l = 0; l < kLoadsR; ++l) {
+    const int p = 64 * (wave + 4 * l) + lane;
+    const int r = p / kUr, u = (p % kUr) ^ (r & 7);
+    off_r[l] = static_cast<uint32_t>((r * DR + 8 * u) * 2);
+  }
+  const int NJ = (Sk + kKeys - 1) / kKeys;
+  auto issue = [&](int jb) {
+    const int64_t j0 = min(min(jb, NJ - 1) * kKeys, Sk - kKeys);
+    const uint32_t st = lds + (jb % kKeyStages) * kStageBytes;
+#pragma unroll
+    for (int l = 0; l < kLoadsC; ++l) load_lds16(Kcbh + j0 * DC * 2, off_c[l], st + 1024 * (wave + 4 * l));
+#pragma unroll
+    for (int l = 0; l < kLoadsR; ++l)
+      load_lds16(Krb + j0 * DR * 2, off_r[l], st + kKcBytes + 1024 * (wave + 4 * l));
   };
 
   f32x16 run;
 #pragma unroll
   for (int r = 0; r < 16; ++r) run[r] = -INFINITY;
 
-  const int NJ = (Sk + kKeys - 1) / kKeys;
-  load_keys(0);
-  store_keys(0);
-  __syncthreads();
+  for (int s = 0; s < kKeyStages - 1; ++s) issue(s);
   for (int jb = 0; jb < NJ; ++jb) {
-    const int cur = jb & 1;
-    if (jb + 1 < NJ) load_keys((jb + 1) * kKeys);
+    // block jb's loads are older than the 2 newer stages in flight
+    wait_vmem<(kKeyStages - 2) * kLoads>();
+    __syncthreads();
+    // the stage of block jb - 1 is free now: refill it with block jb + 3
+    issue(jb + kKeyStages - 1);
+    const uint32_t cur = lds + (jb % kKeyStages) * kStageBytes;
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u) acc[t][u] = f32x16{};
+    // key fragments one k-step ahead: the two reads of step s + 1 are issued
+    // before the 8 MFMAs of step s, so LDS latency hides behind them
+    auto read_kf = [&](int s, bf16x8 (&kf)[2]) {
+      const int unit = 2 * s + frag_half;  // of the full row of D
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = u * 32 + frag_row;
+        // 2 s < DC / 8 decides the part at compile time (both parts hold an
+        // even number of units)
+        const uint32_t a = (2 * s < kUc) ? cur + row * (2 * DC) + 16 * (unit ^ (row & 7))
+                                         : cur + kKcBytes + row * (2 * DR) + 16 * ((unit - kUc) ^ (row & 7));
+        kf[u] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
+      }
+    };
+    bf16x8 kfa[2], kfb[2];
+    read_kf(0, kfa);
+    // schedule: reads(0), then per step s: reads(s + 1), MFMAs(s)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int unit = (2 * s + frag_half) ^ (lane & 7);
-      bf16x8 kf[2];
+      bf16x8 (&kc)[2] = (s & 1) ? kfb : kfa;
+      bf16x8 (&kn)[2] = (s & 1) ? kfa : kfb;
+      if (s + 1 < kSteps) read_kf(s + 1, kn);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) kf[u] = as_bf16x8(ks[cur][u * 32 + frag_row][unit]);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[u], acc[t][u], 0, 0, 0);
-    }
-
-    // mask the tails: key column j = jb*64 + u*32 + lane%32; query rows per register
-    const bool key_tail = (jb + 1) * kKeys > Sk;
-    if (key_tail || any_row_tail) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bool col_ok = jb * kKeys + u * 32 + frag_row < Sk;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = row_base + t * 32 + 8 * (r >> 2) + 4 * frag_half + (r & 3);
-            if (!col_ok || i >= Sq) acc[t][u][r] = -INFINITY;
-          }
-        }
+          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kc[u], acc[t][u], 0, 0, 0);
+      if (s + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      run[r] = fmaxf(fmaxf(run[r], fmaxf(acc[0][0][r], acc[0][1][r])), fmaxf(acc[1][0][r], acc[1][1][r]));
-
-    if (jb + 1 < NJ) store_keys(cur ^ 1);
-    __syncthreads();
+    for (int r = 0; r < 16; ++r) {
+      const float m01 = fmaxf(fmaxf(acc[0][0][r], acc[0][1][r]), fmaxf(acc[1][0][r], acc[1][1][r]));
+      const float m23 = fmaxf(fmaxf(acc[2][0][r], acc[2][1][r]), fmaxf(acc[3][0][r], acc[3][1][r]));
+      run[r] = fmaxf(run[r], fmaxf(m01, m23));
+    }
   }
+  wait_vmem<0>();  // the redundant prefetches past the last block
 
   // ---- workgroup max, one atomic per workgroup
   float m = run[0];
@@ -255,16 +308,15 @@ __global__ __launch_bounds__(kGenThreads) void maxlogit_generic_kernel(
   }
 }
 
-template <int D>
+template <int DC, int DR>
 hipError_t launch_mfma(const void* Q, const void* Kc, const void* Kr, int64_t B, int64_t H, int64_t Sq,
-                       int64_t Sk, int64_t d_c, float* smax, float scale, hipStream_t stream) {
+                       int64_t Sk, float* smax, float scale, hipStream_t stream) {
   const int64_t blocks_per_bh = (Sq + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t blocks = blocks_per_bh * B * H;
-  hipLaunchKernelGGL((maxlogit_mfma_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(kMfmaThreads),
+  hipLaunchKernelGGL((maxlogit_mfma_kernel<DC, DR>), dim3(static_cast<unsigned>(blocks)), dim3(kMfmaThreads),
                      0, stream, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(Kc),
                      static_cast<const uint16_t*>(Kr), static_cast<int>(H), static_cast<int>(Sq),
-                     static_cast<int>(Sk), static_cast<int>(d_c), static_cast<int>(blocks_per_bh), smax,
-                     scale);
+                     static_cast<int>(Sk), static_cast<int>(blocks_per_bh), smax, scale);
   return hipGetLastError();
 }
 
@@ -284,15 +336,17 @@ hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool b
   const bool aligned16 = (reinterpret_cast<uintptr_t>(Q) % 16 == 0) &&
                          (reinterpret_cast<uintptr_t>(Kc) % 16 == 0) &&
                          (Kr == nullptr || reinterpret_cast<uintptr_t>(Kr) % 16 == 0);
-  const bool mfma_ok = bf16 && aligned16 && d_c % 8 == 0 && d_r % 8 == 0 &&
-                       (d == 64 || d == 128 || d == 192) && Sq <= INT32_MAX &&
-                       Sk <= INT32_MAX && B * H * ((Sq + kRowsPerBlock - 1) / kRowsPerBlock) <= INT32_MAX;
+  // MFMA kernel shapes: parts of 64-element multiples, d <= 192, at least one
+  // full key block (the last block is the last 64 keys)
+  const bool mfma_ok = bf16 && aligned16 && Sk >= kKeys && Sq <= INT32_MAX && Sk <= INT32_MAX &&
+                       B * H * ((Sq + kRowsPerBlock - 1) / kRowsPerBlock) <= INT32_MAX &&
+                       (Kr != nullptr || d_r == 0);
   if (mfma_ok) {
-    switch (d) {
-      case 64: return launch_mfma<64>(Q, Kc, Kr, B, H, Sq, Sk, d_c, smax, scale, stream);
-      case 128: return launch_mfma<128>(Q, Kc, Kr, B, H, Sq, Sk, d_c, smax, scale, stream);
-      default: return launch_mfma<192>(Q, Kc, Kr, B, H, Sq, Sk, d_c, smax, scale, stream);
-    }
+    if (d_c == 64 && d_r == 0) return launch_mfma<64, 0>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
+    if (d_c == 128 && d_r == 0) return launch_mfma<128, 0>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
+    if (d_c == 192 && d_r == 0) return launch_mfma<192, 0>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
+    if (d_c == 64 && d_r == 64) return launch_mfma<64, 64>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
+    if (d_c == 128 && d_r == 64) return launch_mfma<128, 64>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
   }
   dim3 grid(static_cast<unsigned>((Sq + kGenTile - 1) / kGenTile), static_cast<unsigned>(H),
             static_cast<unsigned>(B));
