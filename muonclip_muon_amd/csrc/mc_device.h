@@ -58,6 +58,14 @@ __device__ __forceinline__ float update_op(float w, float o, float lr, float wd)
   return w - v;
 }
 
+// Layout of the Newton-Schulz state X (n_pad x m_pad bf16) in the workspace:
+// column panels of 256, each n_pad x 256 row-major, so a 32 x 256 K-rows tile
+// (the right operand of B' X) is one contiguous 16 KB run and a row panel of
+// X X^T reads 64-byte runs at a 512-byte pitch.  Element offset of (r, c):
+__host__ __device__ __forceinline__ int64_t x_off(int64_t r, int64_t c, int64_t n_pad) {
+  return (c >> 8) * n_pad * 256 + r * 256 + (c & 255);
+}
+
 // Blocks of one launch are distributed round-robin over the 8 XCDs of an
 // MI355X (block b runs on XCD b % 8).  This remap makes consecutive logical
 // block ids land on the same XCD, so tiles that share operands share that

@@ -228,16 +228,27 @@ __device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
 }
 
 // Scheduling pattern for one half step: 16 MFMAs with the LDS reads of the
-// next sub-step spread between them (4 MFMAs, then a quarter of the reads).
-// Left alone the scheduler moves every read next to its use, which exposes
-// LDS latency with one wave per SIMD.
+// next sub-step spread between them.  Left alone the scheduler moves every
+// read next to its use, which exposes LDS latency with one wave per SIMD.
+// Patterns picked by a sweep on MI355X (64 x 2048 x 7168): B' X (12 reads)
+// one read after every second MFMA for the first 8 reads, 3.5 % faster than
+// groups of 4; the all-b128 products (8 reads) two reads after each of the
+// first four MFMA pairs.
 template <bool Q_KROWS>
 __device__ __forceinline__ void interleave_reads_with_mfma() {
-  constexpr int kReads = Q_KROWS ? 12 : 8;  // DS reads per sub-step
+  if constexpr (Q_KROWS) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kReads / 4, 0);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
 }
 
@@ -322,20 +333,23 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 
   const int64_t nn = static_cast<int64_t>(n_pad) * n_pad, nm = static_cast<int64_t>(n_pad) * m_pad;
   const int nkb = n_pad / kBK;  // k-blocks per row of the blocked layout
-  // Operand tiles at k = 0, their row pitch and the step between K-steps.
-  //   mode 0: rows i0.. and j0.. of X, K-contiguous (pitch m_pad, step 32)
+  // Operand tiles at k = 0, their row pitch and the step between K-steps
+  // (X in the column-panel layout, see x_off; A and B' blocked).
+  //   mode 0: rows i0.. and j0.. of X, K-contiguous: 64-byte runs at the
+  //           panel's 512-byte pitch; a new panel every 8 K-steps
   //   mode 1: blocks of A at rows i0.. and j0.. (pitch 32, step one block)
   //   mode 2: blocks of B' at rows i0.. (symmetric: rows are columns), and
-  //           k-rows of X at columns j0.. (pitch m_pad, step 32 rows)
+  //           k-rows of X in panel j0 / 256: one contiguous 16 KB run per step
+  const int64_t panel = static_cast<int64_t>(n_pad) * 256;
   const uint16_t* Pg;
   const uint16_t* Qg;
   int64_t ldp, ldq, kstep_p, kstep_q;
   int K;
   if constexpr (MODE == 0) {
-    Pg = in0 + mat * nm + static_cast<int64_t>(i0) * m_pad;
-    Qg = in0 + mat * nm + static_cast<int64_t>(j0) * m_pad;
-    ldp = ldq = m_pad;
-    kstep_p = kstep_q = kBK;
+    Pg = in0 + mat * nm + static_cast<int64_t>(i0) * 256;
+    Qg = in0 + mat * nm + static_cast<int64_t>(j0) * 256;
+    ldp = ldq = 256;
+    kstep_p = kstep_q = 0;  // see k_ofs
     K = m_pad;
   } else if constexpr (MODE == 1) {
     Pg = in0 + mat * nn + blk_off(i0, 0, nkb);
@@ -345,13 +359,22 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     K = n_pad;
   } else {
     Pg = in0 + mat * nn + blk_off(i0, 0, nkb);
-    Qg = in1 + mat * nm + j0;
+    Qg = in1 + mat * nm + tj * panel;
     ldp = kBK;
     kstep_p = kBM * kBK;
-    ldq = m_pad;
-    kstep_q = static_cast<int64_t>(kBK) * m_pad;
+    ldq = 256;
+    kstep_q = kBK * 256;
     K = n_pad;
   }
+  // element offset of K-step kt from the operand origin
+  auto k_ofs = [&](int kt, int64_t kstep) -> int64_t {
+    if constexpr (MODE == 0) {
+      const int k0 = kt * kBK;
+      return (k0 >> 8) * panel + (k0 & 255);
+    } else {
+      return kt * kstep;
+    }
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -365,10 +388,10 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // in-bounds tile is fetched again into a stage nobody reads, which keeps
   // the number of loads in flight (and so the wait counts) fixed.
   auto issue_p = [&](int kt) {
-    issue_tile<false>(Pg + min(kt, KT - 1) * kstep_p, ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
+    issue_tile<false>(Pg + k_ofs(min(kt, KT - 1), kstep_p), ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
   };
   auto issue_q = [&](int kt) {
-    issue_tile<kQKRows>(Qg + min(kt, KT - 1) * kstep_q, ldq, off_q,
+    issue_tile<kQKRows>(Qg + k_ofs(min(kt, KT - 1), kstep_q), ldq, off_q,
                         lds + (kt % kStages) * kStageBytes + kTileBytes, wave);
   };
   const FragAddr fadr = frag_addresses<kQKRows>(lane, wm, wn);
@@ -427,7 +450,6 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 
   wait_vmem<0>();
   __syncthreads();
-  const int64_t ldo = (MODE == 2) ? m_pad : n_pad;
   uint16_t* O = out + mat * ((MODE == 2) ? nm : nn);
   const uint32_t eb = lds + wave * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
@@ -488,67 +510,32 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     char* Wb = static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz;
     const int64_t wcols = ua.transposed ? ua.n : ua.m;
     const bool vec = wcols % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
-    auto update8 = [&](int64_t wrow, int64_t wcol, int valid, const float (&x)[8]) {
-      if (valid <= 0) return;
-      const int64_t idx = wrow * wcols + wcol;
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = ua.out_scale * x[e];
-      if (vec && valid == 8) {
-        if constexpr (UPD == 1) {
-          u32x4* p = reinterpret_cast<u32x4*>(Wb + idx * 2);
-          u32x4 w = *p;
-          w.x = pack_bf16x2(update_op(bf16_lo(w.x), o[0], ua.lr, ua.wd), update_op(bf16_hi(w.x), o[1], ua.lr, ua.wd));
-          w.y = pack_bf16x2(update_op(bf16_lo(w.y), o[2], ua.lr, ua.wd), update_op(bf16_hi(w.y), o[3], ua.lr, ua.wd));
-          w.z = pack_bf16x2(update_op(bf16_lo(w.z), o[4], ua.lr, ua.wd), update_op(bf16_hi(w.z), o[5], ua.lr, ua.wd));
-          w.w = pack_bf16x2(update_op(bf16_lo(w.w), o[6], ua.lr, ua.wd), update_op(bf16_hi(w.w), o[7], ua.lr, ua.wd));
-          *p = w;
-        } else {
-          f32x4* p = reinterpret_cast<f32x4*>(Wb + idx * 4);
-          f32x4 a = p[0], b = p[1];
-          a.x = update_op(a.x, o[0], ua.lr, ua.wd);
-          a.y = update_op(a.y, o[1], ua.lr, ua.wd);
-          a.z = update_op(a.z, o[2], ua.lr, ua.wd);
-          a.w = update_op(a.w, o[3], ua.lr, ua.wd);
-          b.x = update_op(b.x, o[4], ua.lr, ua.wd);
-          b.y = update_op(b.y, o[5], ua.lr, ua.wd);
-          b.z = update_op(b.z, o[6], ua.lr, ua.wd);
-          b.w = update_op(b.w, o[7], ua.lr, ua.wd);
-          p[0] = a;
-          p[1] = b;
-        }
-      } else {
-        for (int e = 0; e < valid; ++e) {
-          if constexpr (UPD == 1) {
-            uint16_t* p = reinterpret_cast<uint16_t*>(Wb) + idx + e;
-            *p = f32_to_bf16(update_op(bf16_to_f32(*p), o[e], ua.lr, ua.wd));
-          } else {
-            float* p = reinterpret_cast<float*>(Wb) + idx + e;
-            *p = update_op(*p, o[e], ua.lr, ua.wd);
-          }
-        }
-      }
-    };
     auto unpack8 = [](u32x4 v, float (&x)[8]) {
       x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
       x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
     };
-    if (!ua.transposed) {
-#pragma unroll 2
-      for (int s = 0; s < 32; ++s) {
-        const int row = 4 * s + (lane >> 4), u = lane & 15;
-        const int i = i0w + row, j = j0w + 8 * u;
-        float x[8];
-        unpack8(*(const lds_u32x4_t*)(uintptr_t)st_addr(row, u), x);
-        update8(i, j, i < ua.n ? min(8, ua.m - j) : 0, x);
+    // Pass s: straight W, lane takes staged row 4 s + lane / 16, unit
+    // lane % 16 (W row i0w + row, 8 columns); transposed W, lane takes staged
+    // column jj = C + lane % 16 and rows R .. R + 7 (two transposed reads),
+    // i.e. 8 consecutive elements of W row j0w + jj.
+    const int g = lane >> 4, il = lane & 15;
+    auto pos = [&](int s, int64_t& wrow, int64_t& wcol, int& valid) {
+      if (!ua.transposed) {
+        const int row = 4 * s + g;
+        wrow = i0w + row;
+        wcol = j0w + 8 * il;
+        valid = wrow < ua.n ? min(8, ua.m - static_cast<int>(wcol)) : 0;
+      } else {
+        const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
+        wrow = j0w + C + il;
+        wcol = i0w + R;
+        valid = wrow < ua.m ? min(8, ua.n - static_cast<int>(wcol)) : 0;
       }
-    } else {
-      // lane takes column jj = C + (lane % 16) and rows ii = R .. R + 7 of the
-      // staged tile (two transposed reads), i.e. 8 consecutive elements of W
-      // row j0w + jj
-      const int g = lane >> 4, il = lane & 15;
-#pragma unroll 2
-      for (int s = 0; s < 32; ++s) {
+    };
+    auto read_x = [&](int s, float (&x)[8]) {
+      if (!ua.transposed) {
+        unpack8(*(const lds_u32x4_t*)(uintptr_t)st_addr(4 * s + g, il), x);
+      } else {
         const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
         const int col = C + 4 * (il & 3);
         const int r0 = R + (il >> 2), r1 = r0 + 4;
@@ -557,23 +544,82 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4_t*)(uintptr_t)(eb + r1 * 256 + (((col >> 3) ^ (r1 & 15)) << 4) + (col & 7) * 2));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        float x[8];
         unpack8(u32x4{l2.x, l2.y, h2.x, h2.y}, x);
-        const int j = j0w + C + il, i = i0w + R;
-        update8(j, i, j < ua.m ? min(8, ua.n - i) : 0, x);
+      }
+    };
+    // Batches of 8 passes: all W loads of a batch are issued before any of
+    // its updates, so the read latency is paid once per batch, not per pass.
+    constexpr int kBatch = 8;
+    constexpr int kWords = (UPD == 1) ? 1 : 2;  // 16-byte words per 8 elements
+    for (int s0 = 0; s0 < 32; s0 += kBatch) {
+      u32x4 wbuf[kBatch][kWords];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        int64_t wrow, wcol;
+        int valid;
+        pos(s0 + e, wrow, wcol, valid);
+        if (vec && valid == 8) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(Wb + (wrow * wcols + wcol) * kEsz);
+#pragma unroll
+          for (int w = 0; w < kWords; ++w) wbuf[e][w] = p[w];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        int64_t wrow, wcol;
+        int valid;
+        pos(s0 + e, wrow, wcol, valid);
+        // read with every lane active: a transposed read hands each lane data
+        // addressed by other lanes, which an inactive lane does not provide
+        float x[8], o[8];
+        read_x(s0 + e, x);
+        if (valid <= 0) continue;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = ua.out_scale * x[q];
+        const int64_t idx = wrow * wcols + wcol;
+        if (vec && valid == 8) {
+          u32x4* p = reinterpret_cast<u32x4*>(Wb + idx * kEsz);
+          if constexpr (UPD == 1) {
+            u32x4 w = wbuf[e][0];
+            w.x = pack_bf16x2(update_op(bf16_lo(w.x), o[0], ua.lr, ua.wd), update_op(bf16_hi(w.x), o[1], ua.lr, ua.wd));
+            w.y = pack_bf16x2(update_op(bf16_lo(w.y), o[2], ua.lr, ua.wd), update_op(bf16_hi(w.y), o[3], ua.lr, ua.wd));
+            w.z = pack_bf16x2(update_op(bf16_lo(w.z), o[4], ua.lr, ua.wd), update_op(bf16_hi(w.z), o[5], ua.lr, ua.wd));
+            w.w = pack_bf16x2(update_op(bf16_lo(w.w), o[6], ua.lr, ua.wd), update_op(bf16_hi(w.w), o[7], ua.lr, ua.wd));
+            p[0] = w;
+          } else {
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              f32x4 v = __builtin_bit_cast(f32x4, wbuf[e][w]);
+              v.x = update_op(v.x, o[4 * w + 0], ua.lr, ua.wd);
+              v.y = update_op(v.y, o[4 * w + 1], ua.lr, ua.wd);
+              v.z = update_op(v.z, o[4 * w + 2], ua.lr, ua.wd);
+              v.w = update_op(v.w, o[4 * w + 3], ua.lr, ua.wd);
+              p[w] = __builtin_bit_cast(u32x4, v);
+            }
+          }
+        } else {
+          for (int q = 0; q < valid; ++q) {
+            if constexpr (UPD == 1) {
+              uint16_t* pw = reinterpret_cast<uint16_t*>(Wb) + idx + q;
+              *pw = f32_to_bf16(update_op(bf16_to_f32(*pw), o[q], ua.lr, ua.wd));
+            } else {
+              float* pw = reinterpret_cast<float*>(Wb) + idx + q;
+              *pw = update_op(*pw, o[q], ua.lr, ua.wd);
+            }
+          }
+        }
       }
     }
     return;
   }
   // direct store: 4 rows of 256 bytes per instruction
   {
-    uint16_t* Ow = O + static_cast<int64_t>(i0w) * ldo + j0w;
 #pragma unroll 4
     for (int s = 0; s < 32; ++s) {
       const int row = 4 * s + (lane >> 4), u = lane & 15;
       const u32x4 v = *(const lds_u32x4_t*)(uintptr_t)st_addr(row, u);
       uint16_t* dst = kBlockedOut ? O + blk_off(i0w + row, j0w + 8 * u, nkb)
-                                  : Ow + static_cast<int64_t>(row) * ldo + 8 * u;
+                                  : O + x_off(i0w + row, j0w + 8 * u, n_pad);
       *reinterpret_cast<u32x4*>(dst) = v;
     }
   }

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void prescale_kernel(const void* __restri
     if (S != nullptr) {
       const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                        pack_bf16x2(x[6], x[7])};
-      *reinterpret_cast<u32x4*>(sb + r * C_pad + c) = o;
+      *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = o;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void prescale_kernel(const void* __restri
     const int rq = 8 * q;
     const u32x4 o = {pack_bf16x2(tile[rq + 0][cc], tile[rq + 1][cc]), pack_bf16x2(tile[rq + 2][cc], tile[rq + 3][cc]),
                      pack_bf16x2(tile[rq + 4][cc], tile[rq + 5][cc]), pack_bf16x2(tile[rq + 6][cc], tile[rq + 7][cc])};
-    *reinterpret_cast<u32x4*>(tb + (c0 + cc) * R_pad + r0 + rq) = o;
+    *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = o;
   }
 }
 
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
     if (S != nullptr) {
       const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                        pack_bf16x2(x[6], x[7])};
-      *reinterpret_cast<u32x4*>(sb + r * C_pad + c) = o;
+      *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = o;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
     const int rq = 8 * q;
     const u32x4 o = {pack_bf16x2(tile[rq + 0][cc], tile[rq + 1][cc]), pack_bf16x2(tile[rq + 2][cc], tile[rq + 3][cc]),
                      pack_bf16x2(tile[rq + 4][cc], tile[rq + 5][cc]), pack_bf16x2(tile[rq + 6][cc], tile[rq + 7][cc])};
-    *reinterpret_cast<u32x4*>(tb + (c0 + cc) * R_pad + r0 + rq) = o;
+    *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = o;
   }
 }
 
@@ -276,17 +276,17 @@ __device__ __forceinline__ void store_out(void* O, int64_t idx, float v) {
   else static_cast<float*>(O)[idx] = v;
 }
 
-// Output, element by element: O[r][c] = s * src[r][c] (src pitch sp).
+// Output, element by element: O[r][c] = s * X[r][c] (X in the panel layout).
 // grid (ceil(R * C / 256), batch)
 template <bool OBF16>
 __global__ __launch_bounds__(kThreads) void output_kernel(const uint16_t* __restrict__ src, int64_t R,
-                                                         int64_t C, int64_t sp, int64_t src_stride,
+                                                         int64_t C, int64_t n_pad, int64_t src_stride,
                                                          void* __restrict__ O, int64_t o_stride, float s) {
   const int64_t b = blockIdx.y;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (e >= R * C) return;
   const int64_t r = e / C, c = e % C;
-  const float x = bf16_to_f32(src[b * src_stride + r * sp + c]);
+  const float x = bf16_to_f32(src[b * src_stride + x_off(r, c, n_pad)]);
   char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride) * (OBF16 ? 2 : 4);
   store_out<OBF16>(ob, e, x * s);
 }
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel(const uint16_t* __rest
 // grid (ceil(R * C / 8 / 256), batch)
 template <bool OBF16>
 __global__ __launch_bounds__(kThreads) void output_vec_kernel(const uint16_t* __restrict__ src, int64_t R,
-                                                             int64_t C, int64_t sp, int64_t src_stride,
+                                                             int64_t C, int64_t n_pad, int64_t src_stride,
                                                              void* __restrict__ O, int64_t o_stride,
                                                              float s) {
   const int64_t b = blockIdx.y;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void output_vec_kernel(const uint16_t* __
   const int64_t per_row = C / 8;
   if (v >= R * per_row) return;
   const int64_t r = v / per_row, c = (v % per_row) * 8;
-  const u32x4 x = *reinterpret_cast<const u32x4*>(src + b * src_stride + r * sp + c);
+  const u32x4 x = *reinterpret_cast<const u32x4*>(src + b * src_stride + x_off(r, c, n_pad));
   const float y[8] = {bf16_lo(x.x) * s, bf16_hi(x.x) * s, bf16_lo(x.y) * s, bf16_hi(x.y) * s,
                       bf16_lo(x.z) * s, bf16_hi(x.z) * s, bf16_lo(x.w) * s, bf16_hi(x.w) * s};
   char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride + r * C + c) * (OBF16 ? 2 : 4);
@@ -319,13 +319,13 @@ __global__ __launch_bounds__(kThreads) void output_vec_kernel(const uint16_t* __
 }
 
 // Transposing output (rows > cols): O[r][c] = s * X[c][r], O is R x C =
-// m x n, X is n_pad x m_pad.  grid (R_pad / 64, C_pad / 64, batch): each block
+// m x n, X is n_pad x m_pad in the panel layout.  grid (R_pad / 64, C_pad / 64, batch): each block
 // reads 64 rows x 64 columns of X in 16-byte runs and writes the transposed
 // 64 x 64 block of O, in 8-element runs when VEC (C % 8 == 0 and 16-byte
 // aligned rows), else element by element.
 template <bool OBF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void output_t_kernel(const uint16_t* __restrict__ X, int64_t R,
-                                                           int64_t C, int64_t m_pad, int64_t src_stride,
+                                                           int64_t C, int64_t n_pad, int64_t src_stride,
                                                            void* __restrict__ O, int64_t o_stride,
                                                            float s) {
   __shared__ float tile[kT][kT + 1];
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void output_t_kernel(const uint16_t* __re
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int cc = pass * 32 + (threadIdx.x >> 3);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + (c0 + cc) * m_pad + r0 + 8 * q);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + x_off(c0 + cc, r0 + 8 * q, n_pad));
     tile[cc][8 * q + 0] = bf16_lo(v.x) * s;
     tile[cc][8 * q + 1] = bf16_hi(v.x) * s;
     tile[cc][8 * q + 2] = bf16_lo(v.y) * s;
@@ -459,7 +459,7 @@ hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, boo
     dim3 grid(static_cast<unsigned>(g.m_pad / kT), static_cast<unsigned>(g.n_pad / kT),
               static_cast<unsigned>(g.batch));
     auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O, o_batch_stride,
+      hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O, o_batch_stride,
                          out_scale);
     };
     if (o_bf16) {
@@ -473,19 +473,19 @@ hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, boo
     const int64_t vecs = R * C / 8;
     dim3 grid(static_cast<unsigned>((vecs + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
     if (o_bf16)
-      hipLaunchKernelGGL(output_vec_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O,
+      hipLaunchKernelGGL(output_vec_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O,
                          o_batch_stride, out_scale);
     else
-      hipLaunchKernelGGL(output_vec_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride,
+      hipLaunchKernelGGL(output_vec_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride,
                          O, o_batch_stride, out_scale);
   } else {
     const int64_t count = R * C;
     dim3 grid(static_cast<unsigned>((count + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
     if (o_bf16)
-      hipLaunchKernelGGL(output_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O,
+      hipLaunchKernelGGL(output_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O,
                          o_batch_stride, out_scale);
     else
-      hipLaunchKernelGGL(output_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.m_pad, src_stride, O,
+      hipLaunchKernelGGL(output_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O,
                          o_batch_stride, out_scale);
   }
   return hipGetLastError();
