@@ -146,6 +146,15 @@ __device__ __forceinline__ void issue_tile(const uint16_t* g, int64_t ld, uint32
     load_lds16(base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
 }
 
+// One of the kLoadsPerTile DMA instructions of an operand tile.
+template <bool KROWS>
+__device__ __forceinline__ void issue_tile_part(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
+                                                int wave, int jj) {
+  constexpr int kRowsPerJ = KROWS ? 8 : 64;
+  load_lds16(reinterpret_cast<const char*>(g) + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off,
+             lds + 1024 * (wave + 4 * jj));
+}
+
 // K-rows tiles: per-lane LDS read address (relative to a stage) of the
 // fragment of 32-column MFMA tile x of an operand tile at tile_off, for
 // k-rows 0..7; the k sub-step (+8 KB), the upper four k (+2 KB) and the stage
@@ -219,37 +228,19 @@ __device__ __forceinline__ void load_frags(const FragAddr& fadr, uint32_t stage_
   }
 }
 
-__device__ __forceinline__ void mfma_16(const Frags& f, f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y)
-      acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[x], f.b[y], acc[x][y], 0, 0, 0);
+// Part g of a sub-step's fragments: left tile y = g and right tile x = g.
+template <bool Q_KROWS>
+__device__ __forceinline__ void load_frags_part(const FragAddr& fadr, uint32_t stage_base, int ks, int g,
+                                                Frags& f) {
+  f.b[g] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.p[ks] + g * 2048));
+  if constexpr (Q_KROWS) f.a[g] = tr_frag(stage_base + fadr.q[g] + ks * 8192);
+  else f.a[g] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.q[ks] + g * 2048));
 }
 
-// Scheduling pattern for one half step: 16 MFMAs with the LDS reads of the
-// next sub-step spread between them.  Left alone the scheduler moves every
-// read next to its use, which exposes LDS latency with one wave per SIMD.
-// Patterns picked by a sweep on MI355X (64 x 2048 x 7168): B' X (12 reads)
-// one read after every second MFMA for the first 8 reads, 3.5 % faster than
-// groups of 4; the all-b128 products (8 reads) two reads after each of the
-// first four MFMA pairs.
-template <bool Q_KROWS>
-__device__ __forceinline__ void interleave_reads_with_mfma() {
-  if constexpr (Q_KROWS) {
+// The 4 MFMAs of right tile x = g.
+__device__ __forceinline__ void mfma_4(const Frags& f, int g, f32x16 (&acc)[4][4]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-  }
+  for (int y = 0; y < 4; ++y) acc[g][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[g], f.b[y], acc[g][y], 0, 0, 0);
 }
 
 // Blocked layout of the n_pad x n_pad matrices A and B' (internal to a call):
@@ -418,20 +409,36 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   __syncthreads();
   Frags f0, f1;
   load_frags<kQKRows>(fadr, lds, 0, f0);
+  // One half step: the 16 MFMAs of fragments fc in 4 groups (right tile
+  // x = g), each preceded by one DMA instruction of the refill and followed
+  // by part g of the next sub-step's fragment reads into fn.  The DMA asm
+  // statements fence the scheduler, so copies and reads stay spread over the
+  // half step instead of bunching up: a DMA instruction the memory pipeline
+  // cannot take yet stalls the in-order issue of everything behind it.
+  // Inside a group the scheduler orders MFMAs and reads itself (measured
+  // best of six fixed patterns on MI355X).
+  auto half = [&](const Frags& fc, Frags& fn, uint32_t rd_stage, int rd_ks, auto&& dma) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      dma(g);
+      mfma_4(fc, g, acc);
+      load_frags_part<kQKRows>(fadr, rd_stage, rd_ks, g, fn);
+    }
+  };
   for (int kt = 0; kt < KT; ++kt) {
     const uint32_t cur = lds + (kt % kStages) * kStageBytes;
     const uint32_t nxt = lds + ((kt + 1) % kStages) * kStageBytes;
-    issue_p(kt + kStages - 1);
-    load_frags<kQKRows>(fadr, cur, 1, f1);
-    mfma_16(f0, acc);
-    interleave_reads_with_mfma<kQKRows>();
+    const int kr = min(kt + kStages - 1, KT - 1);
+    const uint32_t refill = lds + ((kt + kStages - 1) % kStages) * kStageBytes;
+    half(f0, f1, cur, 1, [&](int jj) {
+      issue_tile_part<false>(Pg + k_ofs(kr, kstep_p), ldp, off_p, refill, wave, jj);
+    });
     wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerTile>();
     __syncthreads();
-    issue_q(kt + kStages - 1);
     // After the last step this reads a stage of redundant tiles; unused.
-    load_frags<kQKRows>(fadr, nxt, 0, f0);
-    mfma_16(f1, acc);
-    interleave_reads_with_mfma<kQKRows>();
+    half(f1, f0, nxt, 0, [&](int jj) {
+      issue_tile_part<kQKRows>(Qg + k_ofs(kr, kstep_q), ldq, off_q, refill + kTileBytes, wave, jj);
+    });
   }
 
   // ---- epilogue, staged through LDS (free once every stage is consumed).
