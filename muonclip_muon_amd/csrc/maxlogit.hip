@@ -157,14 +157,16 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     off_r[l] = static_cast<uint32_t>((r * DR + 8 * u) * 2);
   }
   const int NJ = (Sk + kKeys - 1) / kKeys;
-  auto issue = [&](int jb) {
+  // DMA instruction l (of kLoads) of block jb: Kc parts first, then Kr
+  auto issue_part = [&](int jb, int l) {
     const int64_t j0 = min(min(jb, NJ - 1) * kKeys, Sk - kKeys);
     const uint32_t st = lds + (jb % kKeyStages) * kStageBytes;
+    if (l < kLoadsC) load_lds16(Kcbh + j0 * DC * 2, off_c[l], st + 1024 * (wave + 4 * l));
+    else load_lds16(Krb + j0 * DR * 2, off_r[l - kLoadsC], st + kKcBytes + 1024 * (wave + 4 * (l - kLoadsC)));
+  };
+  auto issue = [&](int jb) {
 #pragma unroll
-    for (int l = 0; l < kLoadsC; ++l) load_lds16(Kcbh + j0 * DC * 2, off_c[l], st + 1024 * (wave + 4 * l));
-#pragma unroll
-    for (int l = 0; l < kLoadsR; ++l)
-      load_lds16(Krb + j0 * DR * 2, off_r[l], st + kKcBytes + 1024 * (wave + 4 * l));
+    for (int l = 0; l < kLoads; ++l) issue_part(jb, l);
   };
 
   f32x16 run;
@@ -176,8 +178,9 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // block jb's loads are older than the 2 newer stages in flight
     wait_vmem<(kKeyStages - 2) * kLoads>();
     __syncthreads();
-    // the stage of block jb - 1 is free now: refill it with block jb + 3
-    issue(jb + kKeyStages - 1);
+    // the stage of block jb - 1 is free now: its refill with block jb + 3 is
+    // spread over the k-steps below (one DMA instruction every few steps), so
+    // a copy the memory pipeline cannot take yet never stalls a burst of MFMAs
     const uint32_t cur = lds + (jb % kKeyStages) * kStageBytes;
 
     f32x16 acc[4][2];
@@ -199,22 +202,22 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         kf[u] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
       }
     };
-    bf16x8 kfa[2], kfb[2];
-    read_kf(0, kfa);
-    // schedule: reads(0), then per step s: reads(s + 1), MFMAs(s)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // three fragment buffers: the reads of step s + 2 go out with step s, so
+    // they have a whole step of MFMAs to land wherever the scheduler puts them
+    bf16x8 kf[3][2];
+    read_kf(0, kf[0]);
+    if (kSteps > 1) read_kf(1, kf[1]);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      bf16x8 (&kc)[2] = (s & 1) ? kfb : kfa;
-      bf16x8 (&kn)[2] = (s & 1) ? kfa : kfb;
-      if (s + 1 < kSteps) read_kf(s + 1, kn);
+      if (s + 2 < kSteps) read_kf(s + 2, kf[(s + 2) % 3]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kc[u], acc[t][u], 0, 0, 0);
-      if (s + 1 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[s % 3][u], acc[t][u], 0, 0, 0);
+      // between steps: one DMA instruction of the refill every few steps
+      constexpr int kEvery = (kSteps + kLoads - 1) / kLoads;
+      if (s % kEvery == 0 && s / kEvery < kLoads) issue_part(jb + kKeyStages - 1, s / kEvery);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
