@@ -29,7 +29,7 @@ struct NsGeometry {
   int64_t n_pad, m_pad;  // padded to kNsTile
   bool transposed;       // rows > cols: X = M^T
   int64_t sumsq_chunks;    // partial sums per matrix of the stand-alone norm
-  int64_t prescale_tiles;  // 64 x 64 tiles per matrix of the pre-scale (fused norm partials)
+  int64_t prescale_tiles;  // 4096-element blocks per matrix of the fused pre-scale (norm partials)
   // byte offsets inside the workspace: X (two ping-pong copies, n_pad x m_pad),
   // A and B' (n_pad x n_pad), norm partials, 1/norm
   size_t off_x0, off_x1, off_a, off_b, off_partials, off_invnorm, total;

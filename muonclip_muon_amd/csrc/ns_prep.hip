@@ -270,6 +270,57 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
   }
 }
 
+// The same for rows <= cols with 16-byte aligned rows (the common case),
+// with row strips instead of square tiles: a block covers 16 rows x 256
+// columns (one column panel of X), so every row segment it reads is 1 KB of
+// M and of G and every X_0 segment it writes is 512 contiguous bytes.
+// grid (C_pad / 256, R_pad / 16, batch); 4096 elements per block, like the
+// 64 x 64 tiles, so the partial-sum count per matrix is the same.
+__global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
+    float* __restrict__ M, const float* __restrict__ G, int64_t batch_stride, float mu, int64_t R, int64_t C,
+    int64_t R_pad, int64_t C_pad, uint16_t* __restrict__ X0, float* __restrict__ partials) {
+  __shared__ float red[kThreads / 64];
+  const int64_t b = blockIdx.z;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + 8 * (threadIdx.x & 31);
+  float* mb = M + b * batch_stride;
+  const float* gb = G + b * batch_stride;
+  uint16_t* xb = X0 + static_cast<size_t>(b) * R_pad * C_pad;
+  float ss = 0.f;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t r = static_cast<int64_t>(blockIdx.y) * 16 + pass * 8 + (threadIdx.x >> 5);
+    float x[8];
+    if (r < R && c < C) {  // C % 8 == 0: a run is wholly inside or outside
+      f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
+      const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
+      f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
+      const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
+      m0.x = momentum_op(m0.x, g0.x, mu);
+      m0.y = momentum_op(m0.y, g0.y, mu);
+      m0.z = momentum_op(m0.z, g0.z, mu);
+      m0.w = momentum_op(m0.w, g0.w, mu);
+      m1.x = momentum_op(m1.x, g1.x, mu);
+      m1.y = momentum_op(m1.y, g1.y, mu);
+      m1.z = momentum_op(m1.z, g1.z, mu);
+      m1.w = momentum_op(m1.w, g1.w, mu);
+      __builtin_nontemporal_store(m0, mp);
+      __builtin_nontemporal_store(m1, mp + 1);
+      x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
+      x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7])};
+    *reinterpret_cast<u32x4*>(xb + x_off(r, c, R_pad)) = o;
+  }
+  const float block_ss = block_sum(ss, red);
+  if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = block_ss;
+}
+
 template <bool OBF16>
 __device__ __forceinline__ void store_out(void* O, int64_t idx, float v) {
   if constexpr (OBF16) static_cast<uint16_t*>(O)[idx] = f32_to_bf16(v);
@@ -436,7 +487,12 @@ hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stri
   const bool vec = C % 8 == 0 && (g.batch == 1 || batch_stride % 8 == 0) &&
                    reinterpret_cast<uintptr_t>(M) % 32 == 0 && reinterpret_cast<uintptr_t>(G) % 32 == 0;
   dim3 grid(static_cast<unsigned>(C_pad / kT), static_cast<unsigned>(R_pad / kT), static_cast<unsigned>(g.batch));
-  if (vec)
+  if (vec && S != nullptr)
+    hipLaunchKernelGGL(momentum_prescale_rows_kernel,
+                       dim3(static_cast<unsigned>(C_pad / 256), static_cast<unsigned>(R_pad / 16),
+                            static_cast<unsigned>(g.batch)),
+                       dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C, R_pad, C_pad, S, partials);
+  else if (vec)
     hipLaunchKernelGGL(momentum_prescale_kernel<true>, grid, dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C,
                        R_pad, C_pad, S, T, partials);
   else
