@@ -37,6 +37,17 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source additions.  maxlogit.hip: MFMA results in VGPRs (the query
+# fragments then sit in AGPRs, which MFMA reads directly), so the running max
+# reads the logits without a v_accvgpr_read per value; and no NaN semantics
+# for float operations, so fmaxf becomes a bare v_max3_f32 instead of first
+# quieting each operand (the hardware maximum still skips quiet NaNs, and the
+# file tests for NaN on the bits).
+SOURCE_FLAGS = {
+    "maxlogit.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+}
+
+
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -46,7 +57,7 @@ def _hipcc():
 
 def _compile(hipcc, src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

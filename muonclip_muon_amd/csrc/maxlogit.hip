@@ -7,14 +7,16 @@
 //   one (b, h); each wave keeps its 128 rows of Q as MFMA fragments in
 //   registers for the whole kernel, so every key fragment read from LDS feeds
 //   4 MFMAs.  Every key row of (b, h) streams through 4 LDS stages of 64 keys
-//   x d, filled by LDS DMA (global_load_lds, per-lane 64-bit addresses) three
-//   blocks ahead, one barrier per block; Kc and Kr rows land in two regions
-//   of the stage, so each DMA instruction reads whole rows of one source.  Per key block a wave issues
-//   4 x 2 x (d/16) v_mfma_f32_32x32x16_bf16 and folds the 128 x 64 float32
-//   logits into a 16-register running max.  The key row is assembled in LDS
-//   from the head's own part Kc[b,h,j] and the shared rotary part Kr[b,j]
-//   (MLA).  Consecutive workgroups of one (b, h) are kept on one XCD so the
-//   key stream is read from that XCD's L2.
+//   x d, filled by LDS DMA (global_load_lds) three blocks ahead, one barrier
+//   per block; Kc and Kr rows land in two regions of the stage, so each DMA
+//   instruction reads whole rows of one source.  A key block is two phases of
+//   32 keys; per phase a wave issues 4 x (d/16) v_mfma_f32_32x32x16_bf16 into
+//   one of two accumulator sets while the 128 x 32 logits of the other set
+//   (the previous phase) are folded into a 16-register running max between
+//   the MFMAs.  The key row is assembled in LDS from the head's own part
+//   Kc[b,h,j] and the shared rotary part Kr[b,j] (MLA).  Consecutive
+//   workgroups of one (b, h) are kept on one XCD so the key stream is read
+//   from that XCD's L2.
 // float32 path (any other shape, either dtype): a plain LDS-tiled FMA kernel.
 //
 // Both finish with a workgroup max and one atomic max per workgroup into
@@ -33,7 +35,9 @@ namespace {
 // Float atomic max through integer atomics: for x >= 0 the int order of the
 // bits is the float order; for x < 0 the unsigned order is reversed.
 __device__ __forceinline__ void atomic_max_float(float* addr, float x) {
-  if (x != x) return;
+  // NaN test on the bits: this file is compiled without NaN semantics for
+  // float comparisons (see the running max below)
+  if ((__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u) return;
   if (__float_as_int(x) >= 0) atomicMax(reinterpret_cast<int*>(addr), __float_as_int(x));
   else atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(x));
 }
@@ -169,62 +173,93 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int l = 0; l < kLoads; ++l) issue_part(jb, l);
   };
 
-  f32x16 run;
+  // ---- main loop.  A key block is two phases of 32 keys (u = 0, 1); a
+  // phase is kSteps k-steps of 4 MFMAs (one per 32-row query tile t) into
+  // acc[t][u].  The two halves double-buffer the logits: while phase u runs
+  // its MFMAs, the 64 logits per lane of the other half (the phase before)
+  // are folded into the running max a few rows per step, so the VALU work
+  // issues between MFMAs instead of after them.  This file is built with MFMA
+  // results in VGPRs and without NaN semantics for float operations, so a
+  // fold is one v_max3_f32 per two logits, read straight from the MFMA result
+  // registers.  Key fragments are read two
+  // steps ahead through 4 buffers (the flat step count per block is a
+  // multiple of 4, so buffer indices repeat every block); the reads of the
+  // next block's first two steps go out under this block's last two steps,
+  // after the barrier that publishes its stage.
+  constexpr int kBlockSteps = 2 * kSteps;
+  constexpr int kBarrierStep = kBlockSteps - 2;
+  constexpr int kEvery = (kBlockSteps + kLoads - 1) / kLoads;  // steps between refill DMAs
+  // refill DMAs of this block issued before its barrier
+  constexpr int kIssuedBefore = ((kBarrierStep - 1) / kEvery + 1) < kLoads ? ((kBarrierStep - 1) / kEvery + 1) : kLoads;
+  static_assert(kBlockSteps % 4 == 0, "fragment buffers repeat every block");
+  static_assert(kSteps >= 3, "the fold is spread over steps 1 .. kSteps - 1");
+
+  // fragment of flat step f (phase f / kSteps, k-step f % kSteps) of a stage
+  auto read_kf = [&](uint32_t stage, int f) -> bf16x8 {
+    const int u = f / kSteps, s = f % kSteps;
+    const int unit = 2 * s + frag_half;  // of the full row of D
+    const int row = u * 32 + frag_row;
+    // 2 s < DC / 8 decides the part at compile time (both parts hold an even
+    // number of units)
+    const uint32_t a = (2 * s < kUc) ? stage + row * (2 * DC) + 16 * (unit ^ (row & 7))
+                                     : stage + kKcBytes + row * (2 * DR) + 16 * ((unit - kUc) ^ (row & 7));
+    return as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
+  };
+
+  f32x16 run, acc[4][2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) run[r] = -INFINITY;
+  // the half folded during the very first phase holds no logits yet
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t][1] = run;
 
   for (int s = 0; s < kKeyStages - 1; ++s) issue(s);
-  for (int jb = 0; jb < NJ; ++jb) {
-    // block jb's loads are older than the 2 newer stages in flight
-    wait_vmem<(kKeyStages - 2) * kLoads>();
-    __syncthreads();
-    // the stage of block jb - 1 is free now: its refill with block jb + 3 is
-    // spread over the k-steps below (one DMA instruction every few steps), so
-    // a copy the memory pipeline cannot take yet never stalls a burst of MFMAs
-    const uint32_t cur = lds + (jb % kKeyStages) * kStageBytes;
+  // block 0's loads are older than the 2 newer stages in flight
+  wait_vmem<(kKeyStages - 2) * kLoads>();
+  __syncthreads();
+  bf16x8 kf[4];
+  kf[0] = read_kf(lds, 0);
+  kf[1] = read_kf(lds, 1);
 
-    f32x16 acc[4][2];
+  for (int jb = 0; jb < NJ; ++jb) {
+    const uint32_t cur = lds + (jb % kKeyStages) * kStageBytes;
+    const uint32_t nxt = lds + ((jb + 1) % kKeyStages) * kStageBytes;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) acc[t][u] = f32x16{};
-    // key fragments one k-step ahead: the two reads of step s + 1 are issued
-    // before the 8 MFMAs of step s, so LDS latency hides behind them
-    auto read_kf = [&](int s, bf16x8 (&kf)[2]) {
-      const int unit = 2 * s + frag_half;  // of the full row of D
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = u * 32 + frag_row;
-        // 2 s < DC / 8 decides the part at compile time (both parts hold an
-        // even number of units)
-        const uint32_t a = (2 * s < kUc) ? cur + row * (2 * DC) + 16 * (unit ^ (row & 7))
-                                         : cur + kKcBytes + row * (2 * DR) + 16 * ((unit - kUc) ^ (row & 7));
-        kf[u] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
+    for (int f = 0; f < kBlockSteps; ++f) {
+      const int u = f / kSteps, s = f % kSteps;
+      if (f == kBarrierStep) {
+        // block jb + 1 has landed (only block jb + 2 and this block's
+        // refills are newer); every read of this block's stage has been
+        // issued, so after the barrier its stage may be refilled as well
+        wait_vmem<kLoads + kIssuedBefore>();
+        __syncthreads();
       }
-    };
-    // three fragment buffers: the reads of step s + 2 go out with step s, so
-    // they have a whole step of MFMAs to land wherever the scheduler puts them
-    bf16x8 kf[3][2];
-    read_kf(0, kf[0]);
-    if (kSteps > 1) read_kf(1, kf[1]);
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      if (s + 2 < kSteps) read_kf(s + 2, kf[(s + 2) % 3]);
+      const int g = f + 2;
+      kf[g % 4] = (g < kBlockSteps) ? read_kf(cur, g) : read_kf(nxt, g - kBlockSteps);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
+        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[f % 4], s == 0 ? f32x16{} : acc[t][u],
+                                                            0, 0, 0);
+      // fold rows r of the other half whose turn is this step: rows spread
+      // evenly over steps 1 .. kSteps - 1 (step 0 leaves the last MFMAs of
+      // the other half time to finish)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][s], kf[s % 3][u], acc[t][u], 0, 0, 0);
-      // between steps: one DMA instruction of the refill every few steps
-      constexpr int kEvery = (kSteps + kLoads - 1) / kLoads;
-      if (s % kEvery == 0 && s / kEvery < kLoads) issue_part(jb + kKeyStages - 1, s / kEvery);
+      for (int r = 0; r < 16; ++r) {
+        if (s == 1 + r * (kSteps - 1) / 16) {
+          const int o = 1 - u;
+          run[r] = fmaxf(fmaxf(run[r], acc[0][o][r]), acc[1][o][r]);
+          run[r] = fmaxf(fmaxf(run[r], acc[2][o][r]), acc[3][o][r]);
+        }
+      }
+      // one DMA instruction of the refill (block jb + 3) every kEvery steps
+      if (f % kEvery == 0 && f / kEvery < kLoads) issue_part(jb + kKeyStages - 1, f / kEvery);
     }
+  }
+  // the last phase's half
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float m01 = fmaxf(fmaxf(acc[0][0][r], acc[0][1][r]), fmaxf(acc[1][0][r], acc[1][1][r]));
-      const float m23 = fmaxf(fmaxf(acc[2][0][r], acc[2][1][r]), fmaxf(acc[3][0][r], acc[3][1][r]));
-      run[r] = fmaxf(run[r], fmaxf(m01, m23));
-    }
+  for (int r = 0; r < 16; ++r) {
+    run[r] = fmaxf(fmaxf(run[r], acc[0][1][r]), acc[1][1][r]);
+    run[r] = fmaxf(fmaxf(run[r], acc[2][1][r]), acc[3][1][r]);
   }
   wait_vmem<0>();  // the redundant prefetches past the last block
 
