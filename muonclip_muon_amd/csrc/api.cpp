@@ -224,10 +224,10 @@ mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype
   return from_hip(mc::launch_maxlogit(Q, Kc, Kr, dtype == MC_BF16, B, H, Sq, Sk, d_c, d_r, smax, s));
 }
 
-mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
-                          int w_dtype, int64_t d_in, int64_t q_rows_per_head, int64_t q_c_rows,
-                          int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
-                          void* stream) {
+static mc_status_t qk_clip_common(const float* smax, int64_t H, bool total_clip, float tau, float alpha,
+                                  void* Wq, void* Wk, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
+                                  int64_t q_c_rows, int64_t k_rows_per_head, float* gamma_out,
+                                  int32_t* clipped_out, void* stream) {
   if (H < 0 || d_in < 1 || q_rows_per_head < 0 || q_c_rows < 0 || q_c_rows > q_rows_per_head ||
       k_rows_per_head < 0)
     return MC_EINVAL;
@@ -242,9 +242,25 @@ mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, 
       (gamma_out && !aligned(gamma_out, 4)) || (clipped_out && !aligned(clipped_out, 4)))
     return MC_EALIGN;
   if ((q_rows_per_head + k_rows_per_head) * d_in / 8 / 1024 + 1 > kGridMax) return MC_ESHAPE;
-  return from_hip(mc::launch_qk_clip(smax, H, tau, alpha, Wq, Wk, w_dtype == MC_BF16, d_in,
+  return from_hip(mc::launch_qk_clip(smax, H, total_clip, tau, alpha, Wq, Wk, w_dtype == MC_BF16, d_in,
                                      q_rows_per_head, q_c_rows, k_rows_per_head, gamma_out,
                                      clipped_out, static_cast<hipStream_t>(stream)));
+}
+
+mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+                          int w_dtype, int64_t d_in, int64_t q_rows_per_head, int64_t q_c_rows,
+                          int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
+                          void* stream) {
+  return qk_clip_common(smax, H, false, tau, alpha, Wq, Wk, w_dtype, d_in, q_rows_per_head, q_c_rows,
+                        k_rows_per_head, gamma_out, clipped_out, stream);
+}
+
+mc_status_t qk_clip_apply_total(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+                                int w_dtype, int64_t d_in, int64_t q_rows_per_head, int64_t q_c_rows,
+                                int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
+                                void* stream) {
+  return qk_clip_common(smax, H, true, tau, alpha, Wq, Wk, w_dtype, d_in, q_rows_per_head, q_c_rows,
+                        k_rows_per_head, gamma_out, clipped_out, stream);
 }
 
 }  // extern "C"

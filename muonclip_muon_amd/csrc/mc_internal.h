@@ -76,7 +76,7 @@ hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool b
                            hipStream_t stream);
 
 // ---------------------------------------------------------------- QK-Clip
-hipError_t launch_qk_clip(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float tau, float alpha, void* Wq, void* Wk,
                           bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
                           float* gamma_out, int32_t* clipped_out, hipStream_t stream);
 

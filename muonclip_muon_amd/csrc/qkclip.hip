@@ -9,6 +9,11 @@
 // W_q^h by gamma^alpha and W_k^h by gamma^(1-alpha), and the MLA table that
 // scales q^C and k^C by sqrt(gamma), q^R by gamma and leaves the shared k^R).
 //
+// Total clip (the variant the same section describes before per-head clip):
+// one gamma = tau / S_max from S_max = max_h S_max^h (NaN heads skipped; all
+// NaN leaves everything untouched), applied to every head with the same
+// split when S_max > tau.  Each block reduces the H values itself.
+//
 // A head's rows are two contiguous row blocks (W_q and W_k are row-major with
 // head-major rows), so the kernel streams them with 16-byte accesses.  Grid:
 // (chunks, H); every block of an unclipped head returns after reading one
@@ -91,17 +96,32 @@ __device__ __forceinline__ void scale_one(void* base, int64_t i, float f) {
   }
 }
 
+// max over smax[0 .. H) skipping NaNs (NaN only if all are NaN), the same
+// value in every thread of the block
+__device__ float block_max_all(const float* __restrict__ smax, int64_t H) {
+  __shared__ float red[kThreads / 64];
+  float m = __builtin_nanf("");
+  for (int64_t i = threadIdx.x; i < H; i += kThreads) m = fmaxf(m, smax[i]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
+}
+
 // VEC: every row block starts 16-byte aligned and d_in % 8 == 0, so the
-// element ranges below are whole 8-element vectors.
+// element ranges below are whole 8-element vectors.  total_clip: one gamma
+// from the largest S_max of all heads.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restrict__ smax, float tau,
-                                                          float alpha, void* __restrict__ Wq,
+__global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restrict__ smax, int64_t H, bool total_clip,
+                                                          float tau, float alpha, void* __restrict__ Wq,
                                                           void* __restrict__ Wk, int64_t d_in,
                                                           int64_t qph, int64_t q_c_rows, int64_t kph,
                                                           float* __restrict__ gamma_out,
                                                           int32_t* __restrict__ clipped_out) {
   const int64_t h = blockIdx.y;
-  const ClipFactors f = clip_factors(smax[h], tau, alpha);
+  const ClipFactors f = clip_factors(total_clip ? block_max_all(smax, H) : smax[h], tau, alpha);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (gamma_out) gamma_out[h] = f.gamma;
     if (clipped_out) clipped_out[h] = f.state;
@@ -134,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t launch_qk_clip(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
+hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float tau, float alpha, void* Wq, void* Wk,
                           bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
                           float* gamma_out, int32_t* clipped_out, hipStream_t stream) {
   const size_t esz = w_bf16 ? 2 : 4;
@@ -148,7 +168,7 @@ hipError_t launch_qk_clip(const float* smax, int64_t H, float tau, float alpha, 
   if (chunks < 1) chunks = 1;
   dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(H));
 #define MC_CLIP_LAUNCH(B, V)                                                                   \
-  hipLaunchKernelGGL((qk_clip_kernel<B, V>), grid, dim3(kThreads), 0, stream, smax, tau, alpha, \
+  hipLaunchKernelGGL((qk_clip_kernel<B, V>), grid, dim3(kThreads), 0, stream, smax, H, total_clip, tau, alpha, \
                      Wq, Wk, d_in, qph, q_c_rows, kph, gamma_out, clipped_out)
   if (w_bf16) {
     if (vec) MC_CLIP_LAUNCH(true, true);
