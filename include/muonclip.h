@@ -246,6 +246,25 @@ MC_API mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float 
                           int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
                           void* stream);
 
+/*
+ * qk_clip_apply_total -- the total-clip variant: one gamma for all heads.
+ *
+ * S = max_h smax[h] (NaN entries skipped); if S > tau, gamma = tau / S and
+ * every head's rows are rescaled exactly as qk_clip_apply rescales a clipped
+ * head (q_c_rows x gamma^alpha, the rest of the head's W_q rows x gamma, W_k
+ * rows x gamma^(1-alpha)); otherwise nothing is touched.  Defined in
+ * "Kimi K2 内部机制", MuonClip section: the naive form that clips all heads
+ * together with gamma = min(1, tau / S_max), S_max = max_h S_max^h, before
+ * the per-head gamma_h replaces it (the Zhihu answer also names the change
+ * from total clip to per-head clip).  gamma_out / clipped_out get the same
+ * value for every head (clipped 1 or 0; -1 when every smax is NaN).
+ * Arguments, layouts and errors as for qk_clip_apply.
+ */
+MC_API mc_status_t qk_clip_apply_total(const float* smax, int64_t H, float tau, float alpha, void* Wq,
+                                       void* Wk, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
+                                       int64_t q_c_rows, int64_t k_rows_per_head, float* gamma_out,
+                                       int32_t* clipped_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step runs in the library's HIP kernels.
 PyTorch supplies device memory and the current stream.  The library must be
-built first (``python -m muonclip_muon_amd.build``); importing this package
+built first (``python muonclip_muon_amd/build.py``); importing this package
 without it raises, and no function here has a CPU fallback.
 
 Functions take torch tensors on a ROCm device and call the C ABI of
@@ -33,6 +33,7 @@ __all__ = [
     "muon_momentum_ns_update_batched",
     "qk_maxlogit",
     "qk_clip_apply",
+    "qk_clip_apply_total",
     "muon_out_scale",
     "muonclip_step",
 ]
@@ -63,7 +64,7 @@ class MuonClipError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m muonclip_muon_amd.build` (hipcc, gfx950). "
+            f"{LIB_PATH} is not built; run `python muonclip_muon_amd/build.py` (hipcc, gfx950). "
             "There is no fallback implementation.")
     L = ctypes.CDLL(LIB_PATH)
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
@@ -89,6 +90,8 @@ def _load():
     L.qk_maxlogit.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp, i32, vp]
     L.qk_clip_apply.restype = ctypes.c_int
     L.qk_clip_apply.argtypes = [vp, i64, f32, f32, vp, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp]
+    L.qk_clip_apply_total.restype = ctypes.c_int
+    L.qk_clip_apply_total.argtypes = L.qk_clip_apply.argtypes
     return L
 
 
@@ -275,6 +278,20 @@ def qk_clip_apply(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=
     """Rescale the W_q / W_k rows of every head with smax > tau, in place.
 
     Returns (gamma [H] float32, clipped [H] int32)."""
+    return _qk_clip("qk_clip_apply", smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, alpha,
+                    gamma, clipped, stream)
+
+
+def qk_clip_apply_total(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=100.0, alpha=0.5,
+                        gamma=None, clipped=None, stream=None):
+    """Total clip: one gamma = tau / max_h smax[h] for every head when that max exceeds tau.
+
+    Returns (gamma [H] float32, clipped [H] int32), the same value for every head."""
+    return _qk_clip("qk_clip_apply_total", smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau,
+                    alpha, gamma, clipped, stream)
+
+
+def _qk_clip(fn, smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, alpha, gamma, clipped, stream):
     _dev(smax, "smax"), _dev(Wq, "Wq"), _dev(Wk, "Wk")
     H = smax.numel()
     if Wq.dtype != Wk.dtype:
@@ -286,10 +303,10 @@ def qk_clip_apply(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=
         gamma = torch.empty(H, dtype=torch.float32, device=smax.device)
     if clipped is None:
         clipped = torch.empty(H, dtype=torch.int32, device=smax.device)
-    status = lib.qk_clip_apply(smax.data_ptr(), H, tau, alpha, Wq.data_ptr(), Wk.data_ptr(),
-                               _dtype(Wq, "Wq"), d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
-                               gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
-    _check("qk_clip_apply", status)
+    status = getattr(lib, fn)(smax.data_ptr(), H, tau, alpha, Wq.data_ptr(), Wk.data_ptr(),
+                              _dtype(Wq, "Wq"), d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
+                              gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
+    _check(fn, status)
     return gamma, clipped
 
 

@@ -1,6 +1,8 @@
 """Build libmuonclip.so in-tree with hipcc for gfx950.
 
-    python -m muonclip_muon_amd.build        # or muonclip_muon_amd.build.build()
+    python muonclip_muon_amd/build.py        # or __graft_entry__.build()
+
+(Run as a script, not with -m: importing the package loads the library.)
 
 Each translation unit under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into muonclip_muon_amd/libmuonclip.so.  Always

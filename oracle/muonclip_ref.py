@@ -62,6 +62,7 @@ __all__ = [
     "max_logit_bruteforce",
     "clip_factors",
     "qk_clip",
+    "qk_clip_total",
     "project_heads",
     "muonclip_step",
 ]
@@ -274,6 +275,25 @@ def qk_clip(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head,
         k0 = h * k_rows_per_head
         Wk[k0:k0 + k_rows_per_head] = round_to(Wk[k0:k0 + k_rows_per_head] * g**(1.0 - alpha), w_dtype)
     return Wq, Wk, gamma, clipped
+
+
+def qk_clip_total(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head,
+                  tau=TAU, alpha=ALPHA, w_dtype="bf16"):
+    """Total clip: one gamma for all heads; fp64, rounded once.
+
+    The naive form of the internals deep dive ("all heads clipped together"):
+    ``gamma = min(1, tau / S_max)`` with ``S_max = max_h S_max^h``, and every
+    head scaled like a clipped head of ``qk_clip`` (same MHA / MLA split).
+    Readings: a NaN S_max^h is skipped in the max (only an all-NaN input gives
+    a NaN S_max, which touches nothing and flags -1); the strict ``> tau`` of
+    per-head clip.  Returns (Wq', Wk', gamma, clipped), gamma and clipped
+    repeated per head.
+    """
+    smax = np.asarray(smax, dtype=np.float64)
+    numeric = smax[smax == smax]
+    s_all = numeric.max() if numeric.size else float("nan")
+    return qk_clip(np.full(smax.shape, s_all), Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head,
+                   tau=tau, alpha=alpha, w_dtype=w_dtype)
 
 
 def project_heads(X, W, n_heads):

@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = set(_declared())
     assert {"muonclip_momentum", "muon_ns_orthogonalize_batched", "muon_apply_update", "qk_maxlogit",
             "qk_clip_apply", "muon_ns_workspace_bytes", "mc_abi_version", "mc_status_string",
-            "muon_momentum_ns_update_batched"} <= names
+            "muon_momentum_ns_update_batched", "qk_clip_apply_total"} <= names
 
 
 def test_library_exports_every_declared_symbol(mc):
@@ -150,14 +150,15 @@ def test_maxlogit_validation(mc):
     assert L.qk_maxlogit(ctypes.c_void_p(0x100001), FAKE, None, 1, 1, 2, 8, 8, 64, 0, FAKE, 0, None) == EALIGN
 
 
-def test_clip_validation(mc):
-    L = mc.lib
-    assert L.qk_clip_apply(FAKE, 0, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == 0
-    assert L.qk_clip_apply(FAKE, 4, 0.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
-    assert L.qk_clip_apply(FAKE, 4, float("inf"), 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
-    assert L.qk_clip_apply(FAKE, 4, 100.0, 1.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
-    assert L.qk_clip_apply(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 8, 4, None, None, None) == EINVAL
-    assert L.qk_clip_apply(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 4, 16, 6, 4, 4, None, None, None) == EDTYPE
-    assert L.qk_clip_apply(None, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
-    assert L.qk_clip_apply(FAKE, 4, 100.0, 0.5, ctypes.c_void_p(0x100001), FAKE, 1, 16, 6, 4, 4, None, None,
-                           None) == EALIGN
+@pytest.mark.parametrize("fn", ["qk_clip_apply", "qk_clip_apply_total"])
+def test_clip_validation(mc, fn):
+    f = getattr(mc.lib, fn)
+    assert f(FAKE, 0, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == 0
+    assert f(FAKE, 4, 0.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert f(FAKE, 4, float("inf"), 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert f(FAKE, 4, 100.0, 1.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert f(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 8, 4, None, None, None) == EINVAL
+    assert f(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 4, 16, 6, 4, 4, None, None, None) == EDTYPE
+    assert f(None, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
+    assert f(FAKE, 4, 100.0, 0.5, ctypes.c_void_p(0x100001), FAKE, 1, 16, 6, 4, 4, None, None,
+             None) == EALIGN

@@ -141,6 +141,36 @@ def test_qk_clip_mha_general_alpha(mc):
     assert f32_ulp_diff(Wkd.cpu().numpy(), rk).max() <= 4
 
 
+@pytest.mark.parametrize("wdt", [torch.bfloat16, torch.float32])
+def test_qk_clip_total(mc, wdt):
+    say("qk_clip total", wdt)
+    H, dc, dr, d_in = 8, 8, 4, 136
+    qph, kph = dc + dr, dc
+    g = workloads.generator(11, "cpu")
+    Wq = workloads.normal((H * qph, d_in), 0.02, g, "cpu", wdt)
+    Wk = workloads.normal((H * kph, d_in), 0.02, g, "cpu", wdt)
+    wname = "bf16" if wdt == torch.bfloat16 else "f32"
+    ibits = torch.int16 if wname == "bf16" else torch.int32
+    nan = float("nan")
+    for vals in ([523.25, 100.0, nan, -3.0, 1e4, 99.99, 100.0001, 250.0],  # largest 1e4: all clipped
+                 [100.0, 3.0, -5.0, 99.0, 1.0, 2.0, 3.0, 4.0],             # largest at tau: none
+                 [nan] * 8):                                               # all NaN: none, flagged
+        smax = torch.tensor(vals, dtype=torch.float32)
+        Wqd, Wkd = Wq.to(DEV), Wk.to(DEV)
+        gamma, clipped = mc.qk_clip_apply_total(smax.to(DEV), Wqd, Wkd, qph, dc, kph, tau=100.0, alpha=0.5)
+        torch.cuda.synchronize()
+        rq, rk, rg, rc = oracle.qk_clip_total(f64(smax), f64(Wq), f64(Wk), qph, dc, kph, 100.0, 0.5, wname)
+        assert clipped.cpu().tolist() == rc.tolist()
+        assert rel_err(gamma.cpu().numpy(), rg).max() <= 1e-6
+        for got, ref, src in ((Wqd, rq, Wq), (Wkd, rk, Wk)):
+            if rc[0] != 1:
+                assert torch.equal(got.cpu().view(ibits), src.view(ibits))
+            elif wname == "bf16":
+                assert bf16_ulp_diff(bf16_bits(got), oracle.bf16_bits(ref)).max() <= 1
+            else:
+                assert f32_ulp_diff(got.cpu().numpy(), ref).max() <= 2
+
+
 # ------------------------------------------------------------------ max logit --
 MAXLOGIT_CASES = [
     # (dtype, B, H, Sq, Sk, d_c, d_r): MFMA path (d in 64/128/192) and generic path

@@ -189,3 +189,99 @@ def test_full_step_composition(rng):
     np.testing.assert_array_equal(new_w["q"][:dh], oracle.round_to_bf16(Wq1[:dh] * math.sqrt(1 / 3)))
     np.testing.assert_array_equal(new_w["q"][dh:], Wq1[dh:])
     assert list(clipped) == [1, 0]
+
+
+# ------------------------------------------------------------- total clip ----
+def test_total_clip_brings_the_largest_head_to_tau_and_scales_all_heads(rng):
+    # Total clip: one gamma = tau / max_h S^h for every head.  Recomputed on the
+    # clipped weights, the largest head max equals tau, every head's logits
+    # (so every S^h) scale by the same gamma, and the shared rotary key stays.
+    H, dc, dr, d_in = 4, 8, 4, 16
+    X = rng.standard_normal((2, 10, d_in))
+    Wq, Wkc, Wkr = _mla_weights(rng, H, dc, dr, d_in)
+    Wq[(dc + dr):2 * (dc + dr)] *= 20.0  # head 1 far over tau
+    Wkc[dc:2 * dc] *= 20.0
+    Q, Kc, Kr = _mla_qk(X, Wq, Wkc, Wkr, H)
+    S = oracle.max_logit(Q, Kc, Kr)
+    tau = float(np.sort(S)[-2]) * 1.5  # only head 1 above tau
+    Wq2, Wkc2, gamma, clipped = oracle.qk_clip_total(S, Wq, Wkc, dc + dr, dc, dc, tau=tau, w_dtype="f64")
+    assert list(clipped) == [1, 1, 1, 1]
+    assert np.all(gamma == tau / S.max())
+    Q2, Kc2, Kr2 = _mla_qk(X, Wq2, Wkc2, Wkr, H)
+    S2 = oracle.max_logit(Q2, Kc2, Kr2)
+    assert S2.max() == pytest.approx(tau, rel=1e-12)
+    np.testing.assert_allclose(S2, gamma * S, rtol=1e-12)
+    np.testing.assert_array_equal(Kr2, Kr)
+    for h in range(H):
+        full = Q[0, h] @ np.concatenate([Kc[0, h], Kr[0]], 1).T
+        full2 = Q2[0, h] @ np.concatenate([Kc2[0, h], Kr2[0]], 1).T
+        np.testing.assert_allclose(full2, gamma[h] * full, rtol=1e-12, atol=1e-12)
+
+
+def test_total_clip_below_tau_nan_and_single_head(rng):
+    Wq = oracle.round_to_bf16(rng.standard_normal((4 * 6, 8)) * 0.02)
+    Wk = oracle.round_to_bf16(rng.standard_normal((4 * 4, 8)) * 0.02)
+    # largest head exactly at tau: nothing touched (strict >), bit for bit
+    Wq2, Wk2, gamma, clipped = oracle.qk_clip_total(np.array([100.0, 3.0, -5.0, 99.0]), Wq, Wk, 6, 4, 4)
+    assert list(clipped) == [0] * 4 and np.all(gamma == 1.0)
+    np.testing.assert_array_equal(Wq2, Wq)
+    np.testing.assert_array_equal(Wk2, Wk)
+    # a NaN head is skipped in the max; gamma = 1/4 makes the result exact
+    Wq2, Wk2, gamma, clipped = oracle.qk_clip_total(np.array([np.nan, 400.0, 3.0, 50.0]), Wq, Wk, 6, 4, 4,
+                                                    w_dtype="f64")
+    assert list(clipped) == [1] * 4 and np.all(gamma == 0.25)
+    for h in range(4):
+        np.testing.assert_array_equal(Wq2[6 * h:6 * h + 4], Wq[6 * h:6 * h + 4] * 0.5)
+        np.testing.assert_array_equal(Wq2[6 * h + 4:6 * h + 6], Wq[6 * h + 4:6 * h + 6] * 0.25)
+        np.testing.assert_array_equal(Wk2[4 * h:4 * h + 4], Wk[4 * h:4 * h + 4] * 0.5)
+    # every head NaN: nothing touched, flagged
+    Wq2, Wk2, gamma, clipped = oracle.qk_clip_total(np.full(4, np.nan), Wq, Wk, 6, 4, 4)
+    assert list(clipped) == [-1] * 4
+    np.testing.assert_array_equal(Wq2, Wq)
+    # one head: total clip is per-head clip
+    a = oracle.qk_clip_total(np.array([523.25]), Wq[:6], Wk[:4], 6, 4, 4)
+    b = oracle.qk_clip(np.array([523.25]), Wq[:6], Wk[:4], 6, 4, 4)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------------- rotary q^R, k^R ----
+def _rotate_pairs(x, positions, base=10000.0):
+    # a position-dependent rotation of consecutive pairs (RoPE-style); any
+    # orthogonal map per position serves the invariance below
+    d = x.shape[-1]
+    freq = base ** (-np.arange(0, d, 2) / d)
+    ang = positions[:, None] * freq[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def test_clip_with_rotated_rotary_parts(rng):
+    # The rotary parts q^R and k^R are rotated by position before the logits.
+    # The rotation is linear, so scaling W_qr by gamma scales every rotated
+    # q^R by gamma, and the clipped head's recomputed max is tau again; the
+    # rotation lives upstream of the max logit (it rotates its inputs).
+    H, dc, dr, d_in, S_len = 3, 8, 4, 16, 12
+    X = rng.standard_normal((2, S_len, d_in))
+    Wq, Wkc, Wkr = _mla_weights(rng, H, dc, dr, d_in)
+    Wq[:dc + dr] *= 20.0
+    Wkc[:dc] *= 20.0
+    pos = np.arange(S_len, dtype=np.float64)
+
+    def rotated(Wq_, Wkc_):
+        Q, Kc, Kr = _mla_qk(X, Wq_, Wkc_, Wkr, H)
+        Q = Q.copy()
+        Q[..., dc:] = _rotate_pairs(Q[..., dc:], pos)
+        return Q, Kc, _rotate_pairs(Kr, pos)
+
+    Q, Kc, Kr = rotated(Wq, Wkc)
+    S = oracle.max_logit(Q, Kc, Kr)
+    tau = float(np.sort(S)[-2]) * 1.5
+    Wq2, Wkc2, gamma, clipped = oracle.qk_clip(S, Wq, Wkc, dc + dr, dc, dc, tau=tau, w_dtype="f64")
+    assert list(clipped) == [1, 0, 0]
+    S2 = oracle.max_logit(*rotated(Wq2, Wkc2))
+    assert S2[0] == pytest.approx(tau, rel=1e-12)
+    np.testing.assert_array_equal(S2[1:], S[1:])
