@@ -26,6 +26,10 @@ What it computes, and where the pages define it:
 * Per-head max logit ``S_max^h = (1/sqrt(d)) max_{X in B} max_{i,j} Q_i^h K_j^h^T``:
   internals deep dive, "核心数学" (core maths).  The paper-notes page prints
   1/d there, which is the same formula with the square root lost in extraction.
+* Attention forward ``O^h = softmax(Q^h K^h^T / sqrt(d)) V^h`` with the max
+  logit of the same logits as a by-product (the internals deep dive: S_max
+  is already computed in the forward; the paper notes, section 3.2: the
+  per-head max logit comes from the attention forward), optionally causal.
 * ``gamma_h = min(1, tau / S_max^h)``, only heads with ``S_max^h > tau`` touched;
   MHA split ``W_q^h <- gamma^alpha W_q^h``, ``W_k^h <- gamma^(1-alpha) W_k^h``;
   MLA split (table "MLA 的特殊处理"): head-specific q^C and k^C by sqrt(gamma),
@@ -60,6 +64,8 @@ __all__ = [
     "apply_update",
     "max_logit",
     "max_logit_bruteforce",
+    "attention_forward",
+    "attention_forward_bruteforce",
     "clip_factors",
     "qk_clip",
     "qk_clip_total",
@@ -222,6 +228,79 @@ def max_logit_bruteforce(Q, Kc, Kr=None):
                         best = s
         out.append(best * (1.0 / math.sqrt(d)))  # (1/sqrt(d)) x max, as printed
     return np.array(out)
+
+
+# --------------------------------------------------------------------------
+# Attention forward with the max logit as a by-product
+# --------------------------------------------------------------------------
+def _causal_allowed(Sq, Sk):
+    """Key j is visible to query i when j <= i + (Sk - Sq) (the queries are the
+    last Sq positions of the Sk keys; Sq == Sk is the usual square mask)."""
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    return j <= i + (Sk - Sq)
+
+
+def attention_forward(Q, Kc, Kr, V, causal=False):
+    """``O^h = softmax(Q^h K^h^T / sqrt(d)) V^h`` per batch element and head, fp64.
+
+    Q [B, H, Sq, d], Kc [B, H, Sk, d_c], Kr [B, Sk, d_r] or None (MHA),
+    V [B, H, Sk, d_v]; K^h = [Kc^h || Kr] as in ``max_logit``.  The logits are
+    ``Q K^T / sqrt(d)``; with ``causal`` the keys a query may not see (see
+    ``_causal_allowed``) are left out of the softmax and of the max.  Returns
+    (O [B, H, Sq, d_v], lse [B, H, Sq] = log sum_j exp(logit_ij),
+    smax [H] = max over b, i and visible j of the logits).  The softmax is
+    taken as exp(logit - row max) / sum, its plain definition.
+    """
+    Q = np.asarray(Q)
+    B, H, Sq, d = Q.shape
+    V = np.asarray(V)
+    Sk, d_v = V.shape[2], V.shape[3]
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, H, Sq, d_v))
+    lse = np.zeros((B, H, Sq))
+    smax = np.full(H, -np.inf)
+    allowed = _causal_allowed(Sq, Sk) if causal else np.ones((Sq, Sk), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            q = np.asarray(Q[b, h], dtype=np.float64)
+            k = _head_keys(Kc, Kr, b, h)
+            logits = (q @ k.T) * scale
+            logits = np.where(allowed, logits, -np.inf)
+            m = logits.max(axis=1)
+            p = np.exp(logits - m[:, None])
+            l = p.sum(axis=1)
+            O[b, h] = (p / l[:, None]) @ np.asarray(V[b, h], dtype=np.float64)
+            lse[b, h] = m + np.log(l)
+            smax[h] = max(smax[h], m.max())
+    return O, lse, smax
+
+
+def attention_forward_bruteforce(Q, Kc, Kr, V, causal=False):
+    """Pure-Python loops over (b, h, i, j) of the same definition; tiny inputs only."""
+    Q = np.asarray(Q, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, Sq, d = Q.shape
+    Sk, d_v = V.shape[2], V.shape[3]
+    O = np.zeros((B, H, Sq, d_v))
+    smax = [-math.inf] * H
+    for b in range(B):
+        for h in range(H):
+            k = _head_keys(Kc, Kr, b, h)
+            for i in range(Sq):
+                logits = []
+                for j in range(Sk):
+                    if causal and j > i + (Sk - Sq):
+                        continue
+                    s = sum(float(Q[b, h, i, t]) * float(k[j, t]) for t in range(d)) / math.sqrt(d)
+                    logits.append((j, s))
+                m = max(s for _, s in logits)
+                smax[h] = max(smax[h], m)
+                w = [(j, math.exp(s - m)) for j, s in logits]
+                tot = sum(x for _, x in w)
+                for c in range(d_v):
+                    O[b, h, i, c] = sum(x * float(V[b, h, j, c]) for j, x in w) / tot
+    return O, np.array(smax)
 
 
 # --------------------------------------------------------------------------
