@@ -13,6 +13,9 @@
  *   qk_maxlogit                    S_max^h from the forward's Q, K
  *   qk_clip_apply                  rescale W_q / W_k rows of heads over tau
  *
+ * or, where the forward itself runs here, S_max comes out of the attention
+ * forward (attention_fwd_maxlogit) instead of a separate qk_maxlogit pass.
+ *
  * or, for the Muon part, one fused call per shape group that does the first
  * three without storing O:
  *
@@ -216,6 +219,37 @@ MC_API mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, flo
 MC_API mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype, int64_t B, int64_t H,
                         int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
                         int32_t accumulate, void* stream);
+
+/*
+ * attention_fwd_maxlogit -- attention forward with the per-head max logit as
+ * a by-product (the logits are never written anywhere):
+ *   O[b,h,i,:] = sum_j softmax_j(L[b,h,i,j]) V[b,h,j,:],
+ *   L[b,h,i,j] = Q[b,h,i,:] . K[b,h,j,:] / sqrt(d_c + d_r),
+ *   smax[h]    = max over b, i and visible j of L[b,h,i,j],
+ *   lse[b,h,i] = log sum_j exp(L[b,h,i,j])   (natural log),
+ * K as in qk_maxlogit (MLA: [Kc || shared Kr]; MHA: Kr = NULL, d_r = 0).
+ * causal != 0: query i sees key j only when j <= i + Sk - Sq (the queries are
+ * the last Sq positions; requires Sq <= Sk); hidden keys are left out of the
+ * softmax and of the max.  Defined in "Kimi K2 内部机制", MuonClip section
+ * (S_max is already computed in the forward) and the attention formula of
+ * the paper notes ("Kimi K2: Open Agentic Intelligence", section 3.2).
+ *
+ *   Q   [B, H, Sq, d_c + d_r]   Kc [B, H, Sk, d_c]   Kr [B, Sk, d_r] or NULL
+ *   V   [B, H, Sk, d_v]         O  [B, H, Sq, d_v]  (all bf16, row-major, device)
+ *   lse_out   device float32 [B, H, Sq] or NULL
+ *   smax_out  device float32 [H]; initialised to -inf first unless
+ *             accumulate != 0 (then maxed into, for a batch split over calls)
+ * O is computed in float32 (softmax weights rounded to bf16 for the second
+ * product) and rounded once to bf16.
+ * Supported: dtype MC_BF16 (else MC_EDTYPE); (d_c, d_r, d_v) = (128, 64, 128)
+ * (Kimi K2's MLA head) or (64, 0, 64) (else MC_ESHAPE); Sk >= 64 unless the
+ * call is empty; Q, Kc, Kr, V 16-byte aligned, O 8-byte aligned (MC_EALIGN).
+ * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EHIP.
+ */
+MC_API mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr, const void* V,
+                                          int dtype, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t d_c,
+                                          int64_t d_r, int64_t d_v, int32_t causal, void* O, float* lse_out,
+                                          float* smax_out, int32_t accumulate, void* stream);
 
 /*
  * QK-Clip: for each head h with smax[h] > tau, gamma = tau / smax[h] and

@@ -34,6 +34,7 @@ __all__ = [
     "qk_maxlogit",
     "qk_clip_apply",
     "qk_clip_apply_total",
+    "attention_fwd_maxlogit",
     "muon_out_scale",
     "muonclip_step",
 ]
@@ -90,6 +91,9 @@ def _load():
     L.qk_maxlogit.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, vp, i32, vp]
     L.qk_clip_apply.restype = ctypes.c_int
     L.qk_clip_apply.argtypes = [vp, i64, f32, f32, vp, vp, ctypes.c_int, i64, i64, i64, i64, vp, vp, vp]
+    L.attention_fwd_maxlogit.restype = ctypes.c_int
+    L.attention_fwd_maxlogit.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i32, vp,
+                                         vp, vp, i32, vp]
     L.qk_clip_apply_total.restype = ctypes.c_int
     L.qk_clip_apply_total.argtypes = L.qk_clip_apply.argtypes
     return L
@@ -271,6 +275,34 @@ def qk_maxlogit(Q, Kc, Kr=None, smax=None, accumulate=False, stream=None):
                              _stream(Q, stream))
     _check("qk_maxlogit", status)
     return smax
+
+
+def attention_fwd_maxlogit(Q, Kc, Kr, V, causal=False, O=None, lse=None, smax=None, accumulate=False,
+                           stream=None):
+    """Attention forward of bf16 Q [B,H,Sq,d], Kc [B,H,Sk,d_c], Kr [B,Sk,d_r] or None, V [B,H,Sk,d_v].
+
+    Returns (O [B,H,Sq,d_v] bf16, smax [H] float32) and, when an `lse` tensor
+    [B,H,Sq] float32 is passed, fills it with the row log-sum-exp."""
+    for t, n in ((Q, "Q"), (Kc, "Kc"), (V, "V")):
+        _dev(t, n)
+    if Kr is not None:
+        _dev(Kr, "Kr")
+    B, H, Sq, d = Q.shape
+    Sk, d_c, d_v = Kc.shape[2], Kc.shape[3], V.shape[3]
+    d_r = Kr.shape[2] if Kr is not None else 0
+    if d != d_c + d_r or V.shape[:3] != (B, H, Sk) or Kc.shape[:2] != (B, H) or (
+            Kr is not None and Kr.shape[:2] != (B, Sk)):
+        raise ValueError("inconsistent attention shapes")
+    if O is None:
+        O = torch.empty((B, H, Sq, d_v), dtype=Q.dtype, device=Q.device)
+    if smax is None:
+        smax = torch.empty(H, dtype=torch.float32, device=Q.device)
+    status = lib.attention_fwd_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
+                                        V.data_ptr(), _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, d_v,
+                                        int(bool(causal)), O.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                        smax.data_ptr(), int(bool(accumulate)), _stream(Q, stream))
+    _check("attention_fwd_maxlogit", status)
+    return O, smax
 
 
 def qk_clip_apply(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=100.0, alpha=0.5,

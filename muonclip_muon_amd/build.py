@@ -22,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuonclip.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "elementwise.hip", "qkclip.hip", "ns_prep.hip", "ns_gemm.hip", "maxlogit.hip"]
+SOURCES = ["api.cpp", "elementwise.hip", "qkclip.hip", "ns_prep.hip", "ns_gemm.hip", "maxlogit.hip",
+           "attention.hip"]
 
 COMMON_FLAGS = [
     "-O3",

@@ -224,6 +224,33 @@ mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype
   return from_hip(mc::launch_maxlogit(Q, Kc, Kr, dtype == MC_BF16, B, H, Sq, Sk, d_c, d_r, smax, s));
 }
 
+mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr, const void* V, int dtype,
+                                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r,
+                                   int64_t d_v, int32_t causal, void* O, float* lse_out, float* smax_out,
+                                   int32_t accumulate, void* stream) {
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || d_c < 0 || d_r < 0 || d_v < 0) return MC_EINVAL;
+  if (!valid_dtype(dtype)) return MC_EDTYPE;
+  if (dtype != MC_BF16) return MC_EDTYPE;
+  if (!mc::attention_fwd_supported(d_c, d_r, d_v)) return MC_ESHAPE;
+  if (!Q || !Kc || !V || !O || !smax_out || (d_r > 0 && !Kr)) return MC_EINVAL;
+  if (H > 65535 || Sq > INT32_MAX || Sk > INT32_MAX) return MC_ESHAPE;
+  const bool empty = B == 0 || H == 0 || Sq == 0;
+  if (!empty && Sk < 64) return MC_ESHAPE;
+  if (causal && Sq > Sk) return MC_ESHAPE;
+  if (B * H * ((Sq + 255) / 256) > kGridMax) return MC_ESHAPE;
+  if (!aligned(Q, 16) || !aligned(Kc, 16) || (Kr && !aligned(Kr, 16)) || !aligned(V, 16) || !aligned(O, 8) ||
+      !aligned(smax_out, 4) || (lse_out && !aligned(lse_out, 4)))
+    return MC_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!accumulate) {
+    hipError_t e = mc::launch_maxlogit_init(smax_out, H, s);
+    if (e != hipSuccess) return MC_EHIP;
+  }
+  if (empty) return MC_OK;
+  return from_hip(mc::launch_attention_fwd(Q, Kc, Kr, V, B, H, Sq, Sk, d_c, d_r, d_v, causal != 0, O, lse_out,
+                                           smax_out, s));
+}
+
 static mc_status_t qk_clip_common(const float* smax, int64_t H, bool total_clip, float tau, float alpha,
                                   void* Wq, void* Wk, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
                                   int64_t q_c_rows, int64_t k_rows_per_head, float* gamma_out,

@@ -1,0 +1,392 @@
+// Attention forward with the per-head max logit as a by-product:
+//   O[b,h,i] = sum_j softmax_j(Q[b,h,i] . K[b,h,j] / sqrt(d)) V[b,h,j],
+//   S_max^h  = max_{b,i,j} Q[b,h,i] . K[b,h,j] / sqrt(d)   (visible j only),
+// with K[b,h,j] = [Kc[b,h,j] || Kr[b,j]] (MLA: the rotary key is shared by all
+// heads) or Kc alone (MHA), and an optional causal mask (query i sees key j
+// when j <= i + Sk - Sq).  "Kimi K2 内部机制", MuonClip section: S_max is
+// already computed in the forward; the paper notes (section 3.2) read the
+// per-head max logit from the attention forward.  The logits never leave
+// registers; the running row maximum of the softmax is the max logit.
+//
+// bf16, (d_c, d_r, d_v) in {(128, 64, 128), (64, 0, 64)}, Sk >= 64.
+// A 256-thread workgroup (4 wave64s) owns 256 query rows of one (b, h); each
+// wave keeps its 64 rows of Q as MFMA fragments in registers.  Keys and
+// values stream through 3 LDS stages of 64 keys (K rows and V rows, filled by
+// LDS DMA two blocks ahead, one barrier per block).  A block is two phases of
+// 32 keys; per phase and wave:
+//   S = K Q^T     2 x (d/16) v_mfma_f32_32x32x16_bf16 (keys as the MFMA rows,
+//                 so each lane holds 16 keys of one query row);
+//   softmax       row max over the lane's 16 keys and the other half-wave's
+//                 16 (one lane swap), p = 2^(s log2(e)/sqrt(d) - m) in float32,
+//                 rounded to bf16 for the second product; the row sum stays a
+//                 per-lane partial until the end;
+//   O += V^T P    (d_v/32) x 2 x 2 MFMAs (d as the MFMA rows), P straight from
+//                 the registers of S: the MFMA k order is permuted to the
+//                 order in which S holds the keys, and the V fragments are
+//                 read in that order with ds_read_b64_tr_b16.
+// The reference point m of the exponentials follows the row maximum lazily:
+// it moves (and O and the row sum are rescaled by 2^(m_old - m_new)) only
+// when a block's maximum exceeds it by more than 8 (p <= 256), which keeps the
+// result exact up to rounding and makes the rescale rare.  The true row
+// maximum is tracked separately for S_max.
+//
+// Tails: a query row past Sq repeats row Sq - 1 and is not stored; the last
+// key block is the last 64 keys (in bounds) with the keys of the previous
+// block masked out.  Workgroups whose rows cannot see a key block under the
+// causal mask stop before it.
+
+#include <math.h>
+
+#include "mc_device.h"
+#include "mc_internal.h"
+
+namespace mc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerWave = 64;
+constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / 64);  // 256
+constexpr int kKeys = 64;                                     // keys per LDS stage
+constexpr int kStages = 3;                                    // prefetch distance 2
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the reference may lag the row max
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One global_load_lds_dwordx4: 16 bytes from g_uniform + lane_off to LDS
+// address m0 + 16 * lane; completion is awaited with an explicit vmcnt wait
+// before the barrier that publishes the stage.
+__device__ __forceinline__ void load_lds16(const char* g_uniform, uint32_t lane_off, uint32_t lds_addr) {
+  const uint64_t a = reinterpret_cast<uintptr_t>(g_uniform);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const char* base = reinterpret_cast<const char*>(lo | (hi << 32));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2\n"
+               :
+               : "s"(lds_addr), "v"(lane_off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__device__ __forceinline__ void atomic_max_float(float* addr, float x) {
+  if ((__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u) return;
+  if (__float_as_int(x) >= 0) atomicMax(reinterpret_cast<int*>(addr), __float_as_int(x));
+  else atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(x));
+}
+
+// x of this lane and of lane l ^ 32 (the other half-wave), with
+// v_permlane32_swap: the swap of the upper half of its first operand with the
+// lower half of its second leaves, with both operands x, the two values in
+// the two results.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// LDS layout of a stage: K rows (the Kc part, then the Kr part, each its own
+// row-major region; 16-byte unit u of row r at position u ^ (r & 7)), then V
+// rows (row-major, unit u of row r at u ^ vswz(r)).  vswz spreads the 4 rows a
+// transposed read touches (rows r .. r + 3, r % 4 == 0) over different banks.
+template <int DV>
+__device__ __forceinline__ int vswz(int r) {
+  return DV == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+template <int DC, int DR, int DV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
+                          const uint16_t* __restrict__ Kr, const uint16_t* __restrict__ V, int H, int Sq,
+                          int Sk, int blocks_per_bh, int causal, float c_log2, float inv_sqrt_d,
+                          uint16_t* __restrict__ O, float* __restrict__ lse, float* __restrict__ smax) {
+  constexpr int D = DC + DR;
+  constexpr int kUc = DC / 8, kUr = DR / 8, kUv = DV / 8;  // 16-byte units per row
+  constexpr int kSteps = D / 16;                           // k16 steps of S = K Q^T
+  constexpr int kDt = DV / 32;                             // 32-row MFMA tiles of O
+  constexpr int kKcBytes = kKeys * DC * 2, kKrBytes = kKeys * DR * 2, kVBytes = kKeys * DV * 2;
+  constexpr int kStageBytes = kKcBytes + kKrBytes + kVBytes;
+  constexpr int kLoadsC = kKcBytes / 4096, kLoadsR = kKrBytes / 4096, kLoadsV = kVBytes / 4096;  // per wave
+  constexpr int kLoads = kLoadsC + kLoadsR + kLoadsV;
+  static_assert(DC % 64 == 0 && DR % 64 == 0 && (DV == 64 || DV == 128), "supported head dims");
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+  __shared__ float red[kThreads / 64];
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
+
+  const uint32_t bid = xcd_grouped_block(blockIdx.x, gridDim.x);
+  const int bh = bid / blocks_per_bh;
+  const int ib = bid % blocks_per_bh;
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+
+  const int64_t bh64 = static_cast<int64_t>(b) * H + h;
+  const uint16_t* Qbh = Q + bh64 * Sq * D;
+  const char* Kcbh = reinterpret_cast<const char*>(Kc + bh64 * Sk * DC);
+  const char* Krb = reinterpret_cast<const char*>(DR > 0 ? Kr + static_cast<int64_t>(b) * Sk * DR : Kc);
+  const char* Vbh = reinterpret_cast<const char*>(V + bh64 * Sk * DV);
+  const int off = Sk - Sq;  // causal: query i sees keys j <= i + off
+
+  // ---- this wave's 64 query rows as MFMA "B" fragments (column = lane % 32)
+  const int row_base = ib * kRowsPerBlock + wave * kRowsPerWave;
+  bf16x8 qf[2][kSteps];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = min(row_base + t * 32 + frag_row, Sq - 1);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      qf[t][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half));
+  }
+  // Q in registers before any copy starts (the copies' asm is opaque to the
+  // compiler, which would otherwise wait on them before each use of Q)
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) asm volatile("" : : "v"(qf[t][s]));
+
+  // ---- key / value loads: DMA instruction l of this wave fills 1 KB at
+  // region offset 1024 (wave + 4 l); lane slot p = 64 (wave + 4 l) + lane holds
+  // row p / units, unit (p % units) ^ swizzle(row).  Every region has rows of
+  // 128 or 256 bytes, so 4 KB further (l + 1) is a whole number of rows that
+  // leaves the row's swizzle unchanged: one lane offset per region, and the
+  // 4 KB steps go into the uniform base.
+  auto lane_off = [&](int units, int row_elems, int kind) -> uint32_t {
+    const int p = 64 * wave + lane;
+    const int r = p / units;
+    const int u = (p % units) ^ (kind == 2 ? vswz<DV>(r) : (r & 7));
+    return static_cast<uint32_t>((r * row_elems + 8 * u) * 2);
+  };
+  const uint32_t lo_c = lane_off(kUc, DC, 0), lo_r = lane_off(kUr > 0 ? kUr : 1, DR, 1), lo_v = lane_off(kUv, DV, 2);
+  const int NJ = (Sk + kKeys - 1) / kKeys;
+  // key blocks this workgroup needs: all, or up to the last key its last row sees
+  int nj = NJ;
+  if (causal) {
+    const int last_row = min(ib * kRowsPerBlock + kRowsPerBlock - 1, Sq - 1);
+    nj = min(NJ, (min(Sk - 1, last_row + off)) / kKeys + 1);
+  }
+  auto block_start = [&](int jb) { return min(min(jb, NJ - 1) * kKeys, Sk - kKeys); };
+  auto issue = [&](int jb) {
+    const int64_t j0 = block_start(jb);
+    const uint32_t st = lds + (jb % kStages) * kStageBytes;
+#pragma unroll
+    for (int l = 0; l < kLoadsC; ++l) load_lds16(Kcbh + j0 * DC * 2 + 4096 * l, lo_c, st + 1024 * (wave + 4 * l));
+#pragma unroll
+    for (int l = 0; l < kLoadsR; ++l)
+      load_lds16(Krb + j0 * DR * 2 + 4096 * l, lo_r, st + kKcBytes + 1024 * (wave + 4 * l));
+#pragma unroll
+    for (int l = 0; l < kLoadsV; ++l)
+      load_lds16(Vbh + j0 * DV * 2 + 4096 * l, lo_v, st + kKcBytes + kKrBytes + 1024 * (wave + 4 * l));
+  };
+
+  // running state per query tile t (this lane's row i = row_base + 32 t + lane % 32)
+  f32x16 oacc[kDt][2];
+#pragma unroll
+  for (int a = 0; a < kDt; ++a)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) oacc[a][t] = f32x16{};
+  float m_ref[2] = {-INFINITY, -INFINITY};   // reference of the exponentials (log2 units)
+  float m_true[2] = {-INFINITY, -INFINITY};  // true row max of the raw logits
+  float l_sum[2] = {0.f, 0.f};               // this lane's part of the row sum
+  int row_i[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) row_i[t] = min(row_base + t * 32 + frag_row, Sq - 1);
+
+  // Per-lane LDS read offsets with everything that is a compile-time constant
+  // left out: K fragments (row lane % 32, unit 2 s + half) repeat their
+  // swizzle every 4 k-steps (the XOR touches the low 3 bits of the unit), so
+  // 4 offsets per K part cover every step (+128 bytes per 4 steps, + 32 rows
+  // per phase); V transposed reads depend on the column tile only (the
+  // phase, k16 step and upper rows are whole multiples of 4 rows).
+  uint32_t kc_off[4], kr_off[4], v_off[kDt];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const int unit = 2 * s4 + frag_half;
+    kc_off[s4] = frag_row * (2 * DC) + 16 * (unit ^ (frag_row & 7));
+    kr_off[s4] = kKcBytes + frag_row * (2 * DR) + 16 * (unit ^ (frag_row & 7));
+  }
+  {
+    const int g = lane >> 4, il = lane & 15;
+    const int r = 4 * (g >> 1) + (il >> 2);
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const int col = 32 * dt + 16 * (g & 1) + 4 * (il & 3);
+      v_off[dt] = kKcBytes + kKrBytes + r * (2 * DV) + (((col >> 3) ^ vswz<DV>(r)) << 4) + (col & 7) * 2;
+    }
+  }
+
+  issue(0);
+  issue(1);
+  for (int jb = 0; jb < nj; ++jb) {
+    wait_vmem<kLoads>();  // block jb landed; only block jb + 1 is newer
+    __syncthreads();
+    issue(jb + 2);  // into the stage of block jb - 1, which every wave has finished
+    const uint32_t cur = lds + (jb % kStages) * kStageBytes;
+    const int j0 = block_start(jb);
+    const int j_lo = jb * kKeys;  // keys below this were in earlier blocks
+    // masks only where some key of the block is hidden from some row of the wave
+    const bool need_mask = (j0 < j_lo) || (causal && j0 + kKeys - 1 > row_base + off);
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // ---- S = K Q^T for keys 32 u .. 32 u + 31 of the block
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        // 2 s < DC / 8 decides the part at compile time
+        const int sp = (2 * s < kUc) ? s : s - kUc / 2;  // k-step within the part
+        const uint32_t a = (2 * s < kUc) ? cur + kc_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DC)
+                                         : cur + kr_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DR);
+        const bf16x8 kf = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][s], sacc[t], 0, 0, 0);
+      }
+      // ---- softmax of the 32 keys: register r holds key
+      // j0 + 32 u + 8 (r / 4) + 4 half + r % 4 of row row_i[t]
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 32 * u + 8 * (r >> 2) + 4 * frag_half + (r & 3);
+            if (j < j_lo || (causal && j > row_i[t] + off)) sacc[t][r] = -INFINITY;
+          }
+        }
+        float mb = sacc[t][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mb = fmaxf(mb, sacc[t][r]);
+        {
+          float a, c;
+          halves(mb, a, c);
+          mb = fmaxf(a, c);
+        }
+        m_true[t] = fmaxf(m_true[t], mb);
+        const float mb2 = mb * c_log2;
+        if (mb2 > m_ref[t] + kRescaleSlack) {
+          // per-row move of the reference; O and the row sum follow below
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[t] - mb2);
+          l_sum[t] *= alpha;
+#pragma unroll
+          for (int a = 0; a < kDt; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[a][t][r] *= alpha;
+          m_ref[t] = mb2;
+        }
+        // a row that has seen no visible key yet keeps p = 0 (no inf - inf)
+        const float mr = m_ref[t] == -INFINITY ? 0.f : m_ref[t];
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], c_log2, -mr));
+          l_sum[t] += p[r];
+        }
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16) {
+          const u32x4 w = {pack_bf16x2(p[8 * t16 + 0], p[8 * t16 + 1]), pack_bf16x2(p[8 * t16 + 2], p[8 * t16 + 3]),
+                           pack_bf16x2(p[8 * t16 + 4], p[8 * t16 + 5]), pack_bf16x2(p[8 * t16 + 6], p[8 * t16 + 7])};
+          pf[t][t16] = as_bf16x8(w);
+        }
+      }
+      // ---- O += V^T P: k16 step t16 covers keys 16 t16 .. + 15 of the phase
+      // in the order S holds them: half h's slots e = 0..3 are keys 4 h + e,
+      // slots 4..7 keys 8 + 4 h + e - 4.  Lane (16-lane group g, i) of a
+      // transposed read addresses V row 4 (g / 2) + i / 4 (+ 8 for slots
+      // 4..7), columns 32 dt + 16 (g & 1) + 4 (i & 3) .. + 3.
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) {
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) {
+          const uint32_t a = cur + v_off[dt] + (32 * u + 16 * t16) * (2 * DV);
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * (2 * DV)));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 vf = as_bf16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            oacc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][t16], oacc[dt][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  wait_vmem<0>();  // the prefetches past the last block
+
+  // ---- epilogue: O = acc / row sum (both half-waves' parts), LSE, S_max
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float la, lb;
+    halves(l_sum[t], la, lb);
+    const float l_tot = la + lb;
+    const float inv = 1.0f / l_tot;
+    const int i = row_base + t * 32 + frag_row;
+    if (i < Sq) {
+      uint16_t* orow = O + (bh64 * Sq + i) * DV;
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = 32 * dt + 8 * g4 + 4 * frag_half;
+          const u32x2 w = {pack_bf16x2(oacc[dt][t][4 * g4 + 0] * inv, oacc[dt][t][4 * g4 + 1] * inv),
+                           pack_bf16x2(oacc[dt][t][4 * g4 + 2] * inv, oacc[dt][t][4 * g4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d) = w;
+        }
+      if (lse != nullptr && frag_half == 0) lse[bh64 * Sq + i] = (m_ref[t] + log2f(l_tot)) * (1.0f / kLog2e);
+    }
+  }
+  float m = fmaxf(m_true[0], m_true[1]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float w = red[0];
+    for (int k = 1; k < kThreads / 64; ++k) w = fmaxf(w, red[k]);
+    if (w != -INFINITY) atomic_max_float(&smax[h], w * inv_sqrt_d);
+  }
+}
+
+template <int DC, int DR, int DV>
+hipError_t launch(const void* Q, const void* Kc, const void* Kr, const void* V, int64_t B, int64_t H,
+                  int64_t Sq, int64_t Sk, bool causal, void* O, float* lse, float* smax, hipStream_t stream) {
+  const int64_t blocks_per_bh = (Sq + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t blocks = blocks_per_bh * B * H;
+  const double d = static_cast<double>(DC + DR);
+  const float c_log2 = static_cast<float>(1.4426950408889634 / sqrt(d));
+  const float inv_sqrt_d = static_cast<float>(1.0 / sqrt(d));
+  hipLaunchKernelGGL((attention_fwd_kernel<DC, DR, DV>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(Kc),
+                     static_cast<const uint16_t*>(Kr), static_cast<const uint16_t*>(V), static_cast<int>(H),
+                     static_cast<int>(Sq), static_cast<int>(Sk), static_cast<int>(blocks_per_bh), causal ? 1 : 0,
+                     c_log2, inv_sqrt_d, static_cast<uint16_t*>(O), lse, smax);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_fwd_supported(int64_t d_c, int64_t d_r, int64_t d_v) {
+  return (d_c == 128 && d_r == 64 && d_v == 128) || (d_c == 64 && d_r == 0 && d_v == 64);
+}
+
+hipError_t launch_attention_fwd(const void* Q, const void* Kc, const void* Kr, const void* V, int64_t B,
+                                int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, int64_t d_v,
+                                bool causal, void* O, float* lse, float* smax, hipStream_t stream) {
+  if (d_c == 128 && d_r == 64 && d_v == 128)
+    return launch<128, 64, 128>(Q, Kc, Kr, V, B, H, Sq, Sk, causal, O, lse, smax, stream);
+  if (d_c == 64 && d_r == 0 && d_v == 64)
+    return launch<64, 0, 64>(Q, Kc, Kr, V, B, H, Sq, Sk, causal, O, lse, smax, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mc

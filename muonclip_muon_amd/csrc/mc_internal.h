@@ -75,6 +75,12 @@ hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool b
                            int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
                            hipStream_t stream);
 
+// ------------------------------------------------------ attention forward
+bool attention_fwd_supported(int64_t d_c, int64_t d_r, int64_t d_v);
+hipError_t launch_attention_fwd(const void* Q, const void* Kc, const void* Kr, const void* V, int64_t B,
+                                int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, int64_t d_v,
+                                bool causal, void* O, float* lse, float* smax, hipStream_t stream);
+
 // ---------------------------------------------------------------- QK-Clip
 hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float tau, float alpha, void* Wq, void* Wk,
                           bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
