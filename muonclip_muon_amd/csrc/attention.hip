@@ -47,7 +47,7 @@ constexpr int kThreads = 256;
 constexpr int kRowsPerWave = 64;
 constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / 64);  // 256
 constexpr int kKeys = 64;                                     // keys per LDS stage
-constexpr int kStages = 3;                                    // prefetch distance 2
+constexpr int kStages = 4;                                    // prefetch distance 3
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference may lag the row max
 
@@ -121,7 +121,6 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   constexpr int kLoads = kLoadsC + kLoadsR + kLoadsV;
   static_assert(DC % 64 == 0 && DR % 64 == 0 && (DV == 64 || DV == 128), "supported head dims");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
-  __shared__ float red[kThreads / 64];
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
@@ -151,11 +150,12 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       qf[t][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half));
   }
   // Q in registers before any copy starts (the copies' asm is opaque to the
-  // compiler, which would otherwise wait on them before each use of Q)
+  // compiler, which would otherwise wait on them before each use of Q), and
+  // in AGPRs, which MFMA reads directly: the VGPRs hold the softmax.
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) asm volatile("" : : "v"(qf[t][s]));
+    for (int s = 0; s < kSteps; ++s) asm volatile("" : "+a"(qf[t][s]));
 
   // ---- key / value loads: DMA instruction l of this wave fills 1 KB at
   // region offset 1024 (wave + 4 l); lane slot p = 64 (wave + 4 l) + lane holds
@@ -227,100 +227,145 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
   }
 
-  issue(0);
-  issue(1);
-  for (int jb = 0; jb < nj; ++jb) {
-    wait_vmem<kLoads>();  // block jb landed; only block jb + 1 is newer
-    __syncthreads();
-    issue(jb + 2);  // into the stage of block jb - 1, which every wave has finished
-    const uint32_t cur = lds + (jb % kStages) * kStageBytes;
-    const int j0 = block_start(jb);
-    const int j_lo = jb * kKeys;  // keys below this were in earlier blocks
-    // masks only where some key of the block is hidden from some row of the wave
-    const bool need_mask = (j0 < j_lo) || (causal && j0 + kKeys - 1 > row_base + off);
-
+  // ---- the three parts of a phase
+  // S = K Q^T for keys 32 u .. + 31 of the stage at st
+  auto qk = [&](uint32_t st, int u, f32x16 (&S)[2]) {
+    S[0] = f32x16{};
+    S[1] = f32x16{};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // ---- S = K Q^T for keys 32 u .. 32 u + 31 of the block
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    for (int s = 0; s < kSteps; ++s) {
+      // 2 s < DC / 8 decides the part at compile time
+      const int sp = (2 * s < kUc) ? s : s - kUc / 2;  // k-step within the part
+      const uint32_t a = (2 * s < kUc) ? st + kc_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DC)
+                                       : st + kr_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DR);
+      const bf16x8 kf = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        // 2 s < DC / 8 decides the part at compile time
-        const int sp = (2 * s < kUc) ? s : s - kUc / 2;  // k-step within the part
-        const uint32_t a = (2 * s < kUc) ? cur + kc_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DC)
-                                         : cur + kr_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DR);
-        const bf16x8 kf = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
+      for (int t = 0; t < 2; ++t) S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][s], S[t], 0, 0, 0);
+    }
+  };
+  // softmax of one phase: register r of S[t] holds key j0 + 32 u + 8 (r / 4) +
+  // 4 half + r % 4 of row row_i[t].  Writes the bf16 weights and the factor
+  // alpha by which O must be rescaled before they are added.
+  auto softmax = [&](f32x16 (&S)[2], bf16x8 (&pf)[2][2], float (&alpha)[2], bool mask, int j0, int j_lo,
+                     int u) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][s], sacc[t], 0, 0, 0);
-      }
-      // ---- softmax of the 32 keys: register r holds key
-      // j0 + 32 u + 8 (r / 4) + 4 half + r % 4 of row row_i[t]
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (need_mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * u + 8 * (r >> 2) + 4 * frag_half + (r & 3);
-            if (j < j_lo || (causal && j > row_i[t] + off)) sacc[t][r] = -INFINITY;
-          }
-        }
-        float mb = sacc[t][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mb = fmaxf(mb, sacc[t][r]);
-        {
-          float a, c;
-          halves(mb, a, c);
-          mb = fmaxf(a, c);
-        }
-        m_true[t] = fmaxf(m_true[t], mb);
-        const float mb2 = mb * c_log2;
-        if (mb2 > m_ref[t] + kRescaleSlack) {
-          // per-row move of the reference; O and the row sum follow below
-          const float alpha = __builtin_amdgcn_exp2f(m_ref[t] - mb2);
-          l_sum[t] *= alpha;
-#pragma unroll
-          for (int a = 0; a < kDt; ++a)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[a][t][r] *= alpha;
-          m_ref[t] = mb2;
-        }
-        // a row that has seen no visible key yet keeps p = 0 (no inf - inf)
-        const float mr = m_ref[t] == -INFINITY ? 0.f : m_ref[t];
-        float p[16];
+    for (int t = 0; t < 2; ++t) {
+      if (mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], c_log2, -mr));
-          l_sum[t] += p[r];
-        }
-#pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16) {
-          const u32x4 w = {pack_bf16x2(p[8 * t16 + 0], p[8 * t16 + 1]), pack_bf16x2(p[8 * t16 + 2], p[8 * t16 + 3]),
-                           pack_bf16x2(p[8 * t16 + 4], p[8 * t16 + 5]), pack_bf16x2(p[8 * t16 + 6], p[8 * t16 + 7])};
-          pf[t][t16] = as_bf16x8(w);
+          const int j = j0 + 32 * u + 8 * (r >> 2) + 4 * frag_half + (r & 3);
+          S[t][r] = (j < j_lo || (causal && j > row_i[t] + off)) ? -INFINITY : S[t][r];
         }
       }
-      // ---- O += V^T P: k16 step t16 covers keys 16 t16 .. + 15 of the phase
-      // in the order S holds them: half h's slots e = 0..3 are keys 4 h + e,
-      // slots 4..7 keys 8 + 4 h + e - 4.  Lane (16-lane group g, i) of a
-      // transposed read addresses V row 4 (g / 2) + i / 4 (+ 8 for slots
-      // 4..7), columns 32 dt + 16 (g & 1) + 4 (i & 3) .. + 3.
+      float mb = fmaxf(fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])),
+                       fmaxf(fmaxf(S[t][4], S[t][5]), fmaxf(S[t][6], S[t][7])));
+      mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(S[t][8], S[t][9]), fmaxf(S[t][10], S[t][11])),
+                           fmaxf(fmaxf(S[t][12], S[t][13]), fmaxf(S[t][14], S[t][15]))));
+      {
+        float x, y;
+        halves(mb, x, y);
+        mb = fmaxf(x, y);
+      }
+      m_true[t] = fmaxf(m_true[t], mb);
+      // the reference moves only when the block's max passes it by the slack
+      const float mb2 = mb * c_log2;
+      const float m_new = (mb2 > m_ref[t] + kRescaleSlack) ? mb2 : m_ref[t];
+      alpha[t] = (m_new == m_ref[t]) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[t] - m_new);
+      m_ref[t] = m_new;
+      // a row that has seen no visible key yet keeps p = 0 (no inf - inf)
+      const float mr = m_new == -INFINITY ? 0.f : m_new;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[t][r], c_log2, -mr));
+      float q[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) q[r] = p[2 * r] + p[2 * r + 1];
+      const float sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+      l_sum[t] = fmaf(l_sum[t], alpha[t], sum);
 #pragma unroll
       for (int t16 = 0; t16 < 2; ++t16) {
-#pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-          const uint32_t a = cur + v_off[dt] + (32 * u + 16 * t16) * (2 * DV);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * (2 * DV)));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const bf16x8 vf = as_bf16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            oacc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][t16], oacc[dt][t], 0, 0, 0);
-        }
+        const u32x4 w = {pack_bf16x2(p[8 * t16 + 0], p[8 * t16 + 1]), pack_bf16x2(p[8 * t16 + 2], p[8 * t16 + 3]),
+                         pack_bf16x2(p[8 * t16 + 4], p[8 * t16 + 5]), pack_bf16x2(p[8 * t16 + 6], p[8 * t16 + 7])};
+        pf[t][t16] = as_bf16x8(w);
       }
     }
+  };
+  // O = alpha O (rare: a wave-uniform branch) and O += V^T P for keys
+  // 32 u .. + 31 of the stage at st.  k16 step t16 covers keys 16 t16 .. + 15
+  // of the phase in the order S holds them: half h's slots e = 0..3 are keys
+  // 4 h + e, slots 4..7 keys 8 + 4 h + e - 4.  Lane (16-lane group g, i) of a
+  // transposed read addresses V row 4 (g / 2) + i / 4 (+ 8 for slots 4..7),
+  // columns 32 dt + 16 (g & 1) + 4 (i & 3) .. + 3.
+  auto pv = [&](uint32_t st, int u, const bf16x8 (&pf)[2][2], const float (&alpha)[2]) {
+    if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+      for (int a = 0; a < kDt; ++a)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[a][t][r] *= alpha[t];
+    }
+#pragma unroll
+    for (int t16 = 0; t16 < 2; ++t16) {
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        const uint32_t a = st + v_off[dt] + (32 * u + 16 * t16) * (2 * DV);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * (2 * DV)));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 vf = as_bf16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          oacc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][t16], oacc[dt][t], 0, 0, 0);
+      }
+    }
+  };
+  // masks only where some key of the phase is hidden from some row of the wave
+  auto needs_mask = [&](int jb, int u) {
+    const int j0 = block_start(jb), j_lo = jb * kKeys;
+    return (j0 + 32 * u < j_lo) || (causal && j0 + 32 * u + 31 > row_base + off);
+  };
+
+  // ---- main loop, software-pipelined by one phase: the S of the next phase
+  // is computed while the current phase's softmax runs (independent work for
+  // the MFMA and vector units), then the current phase's O += V^T P.  Block
+  // jb uses stage jb % 4 (its own K and V) and, in its second phase, the K
+  // of stage jb + 1; the barrier between its phases publishes stage jb + 1
+  // and frees stage jb - 1 (last read in phase 2 jb - 1), which is refilled
+  // with block jb + 3.
+  f32x16 sA[2], sB[2];
+  bf16x8 pf[2][2];
+  float alpha[2];
+  for (int s0 = 0; s0 < kStages - 1; ++s0) issue(s0);
+  wait_vmem<(kStages - 2) * kLoads>();  // block 0 landed
+  __syncthreads();
+  qk(lds, 0, sA);
+  for (int jb = 0; jb < nj; ++jb) {
+    const uint32_t st = lds + (jb % kStages) * kStageBytes;
+    const uint32_t st1 = lds + ((jb + 1) % kStages) * kStageBytes;
+    const int j0 = block_start(jb), j_lo = jb * kKeys;
+    // phase 0: S of phase 1 (same stage) with the softmax of phase 0
+    if (needs_mask(jb, 0)) {
+      qk(st, 1, sB);
+      softmax(sA, pf, alpha, true, j0, j_lo, 0);
+    } else {
+      qk(st, 1, sB);
+      softmax(sA, pf, alpha, false, j0, j_lo, 0);
+    }
+    pv(st, 0, pf, alpha);
+    wait_vmem<kLoads>();  // block jb + 1 landed; only block jb + 2 is newer
+    __syncthreads();
+    issue(jb + kStages - 1);
+    // phase 1: S of the next block's phase 0 (past the last block a redundant
+    // copy of it) with the softmax of phase 1
+    if (needs_mask(jb, 1)) {
+      qk(st1, 0, sA);
+      softmax(sB, pf, alpha, true, j0, j_lo, 1);
+    } else {
+      qk(st1, 0, sA);
+      softmax(sB, pf, alpha, false, j0, j_lo, 1);
+    }
+    pv(st, 1, pf, alpha);
   }
   wait_vmem<0>();  // the prefetches past the last block
 
@@ -348,6 +393,9 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   }
   float m = fmaxf(m_true[0], m_true[1]);
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  // the stages are free: every copy has landed and every wave is past its reads
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
   if (lane == 0) red[wave] = m;
   __syncthreads();
   if (tid == 0) {
