@@ -48,6 +48,7 @@ COMMON_FLAGS = [
 # file tests for NaN on the bits).
 SOURCE_FLAGS = {
     "maxlogit.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "attention.hip": ["-fno-honor-nans"],
 }
 
 

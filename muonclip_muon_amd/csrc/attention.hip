@@ -227,6 +227,9 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
   }
 
+  f32x16 sA[2], sB[2];
+  bf16x8 pf[2][2];
+  float alpha[2];
   // ---- the three parts of a phase
   // S = K Q^T for keys 32 u .. + 31 of the stage at st
   auto qk = [&](uint32_t st, int u, f32x16 (&S)[2]) {
@@ -243,52 +246,57 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       for (int t = 0; t < 2; ++t) S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][s], S[t], 0, 0, 0);
     }
   };
-  // softmax of one phase: register r of S[t] holds key j0 + 32 u + 8 (r / 4) +
-  // 4 half + r % 4 of row row_i[t].  Writes the bf16 weights and the factor
-  // alpha by which O must be rescaled before they are added.
-  auto softmax = [&](f32x16 (&S)[2], bf16x8 (&pf)[2][2], float (&alpha)[2], bool mask, int j0, int j_lo,
-                     int u) {
+  // Softmax of one phase as a list of small work items, so it can be spread
+  // between the MFMAs of the next phase's S (see qk_softmax).  Register r of
+  // S[t] holds key j0 + 32 u + 8 (r / 4) + 4 half + r % 4 of row row_i[t].
+  // Items: [mask t0 lo, t0 hi, t1 lo, t1 hi] (masked phases only), max t0,
+  // max t1, reference t0, reference t1, then 8 exponential pairs per t.  Each
+  // pair is packed to bf16 at once and added to a partial row sum.
+  float mb[2], psum[2], mr[2];
+  auto softmax_item = [&](f32x16 (&S)[2], bool mask, int j0, int j_lo, int u, int item) {
+    if (mask) {
+      if (item < 4) {
+        const int t = item >> 1, r0 = 8 * (item & 1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = r0; r < r0 + 8; ++r) {
           const int j = j0 + 32 * u + 8 * (r >> 2) + 4 * frag_half + (r & 3);
           S[t][r] = (j < j_lo || (causal && j > row_i[t] + off)) ? -INFINITY : S[t][r];
         }
+        return;
       }
-      float mb = fmaxf(fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])),
-                       fmaxf(fmaxf(S[t][4], S[t][5]), fmaxf(S[t][6], S[t][7])));
-      mb = fmaxf(mb, fmaxf(fmaxf(fmaxf(S[t][8], S[t][9]), fmaxf(S[t][10], S[t][11])),
-                           fmaxf(fmaxf(S[t][12], S[t][13]), fmaxf(S[t][14], S[t][15]))));
-      {
-        float x, y;
-        halves(mb, x, y);
-        mb = fmaxf(x, y);
-      }
-      m_true[t] = fmaxf(m_true[t], mb);
-      // the reference moves only when the block's max passes it by the slack
-      const float mb2 = mb * c_log2;
-      const float m_new = (mb2 > m_ref[t] + kRescaleSlack) ? mb2 : m_ref[t];
+      item -= 4;
+    }
+    if (item < 2) {  // row max over this lane's 16 keys
+      const int t = item;
+      mb[t] = fmaxf(fmaxf(fmaxf(fmaxf(S[t][0], S[t][1]), fmaxf(S[t][2], S[t][3])),
+                          fmaxf(fmaxf(S[t][4], S[t][5]), fmaxf(S[t][6], S[t][7]))),
+                    fmaxf(fmaxf(fmaxf(S[t][8], S[t][9]), fmaxf(S[t][10], S[t][11])),
+                          fmaxf(fmaxf(S[t][12], S[t][13]), fmaxf(S[t][14], S[t][15]))));
+      return;
+    }
+    if (item < 4) {  // the other half-wave's keys; move the reference lazily
+      const int t = item - 2;
+      float x, y;
+      halves(mb[t], x, y);
+      const float m = fmaxf(x, y);
+      m_true[t] = fmaxf(m_true[t], m);
+      const float m2 = m * c_log2;
+      const float m_new = (m2 > m_ref[t] + kRescaleSlack) ? m2 : m_ref[t];
       alpha[t] = (m_new == m_ref[t]) ? 1.0f : __builtin_amdgcn_exp2f(m_ref[t] - m_new);
       m_ref[t] = m_new;
       // a row that has seen no visible key yet keeps p = 0 (no inf - inf)
-      const float mr = m_new == -INFINITY ? 0.f : m_new;
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(S[t][r], c_log2, -mr));
-      float q[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) q[r] = p[2 * r] + p[2 * r + 1];
-      const float sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
-      l_sum[t] = fmaf(l_sum[t], alpha[t], sum);
-#pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) {
-        const u32x4 w = {pack_bf16x2(p[8 * t16 + 0], p[8 * t16 + 1]), pack_bf16x2(p[8 * t16 + 2], p[8 * t16 + 3]),
-                         pack_bf16x2(p[8 * t16 + 4], p[8 * t16 + 5]), pack_bf16x2(p[8 * t16 + 6], p[8 * t16 + 7])};
-        pf[t][t16] = as_bf16x8(w);
-      }
+      mr[t] = m_new == -INFINITY ? 0.f : m_new;
+      psum[t] = 0.f;
+      return;
     }
+    item -= 4;  // exponential pair: t = item / 8, registers 2 (item % 8), + 1
+    const int t = item >> 3, r = 2 * (item & 7);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[t][r], c_log2, -mr[t]));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[t][r + 1], c_log2, -mr[t]));
+    psum[t] += p0 + p1;
+    u32x4 w = __builtin_bit_cast(u32x4, pf[t][r >> 3]);
+    w[(r & 7) >> 1] = pack_bf16x2(p0, p1);
+    pf[t][r >> 3] = __builtin_bit_cast(bf16x8, w);
   };
   // O = alpha O (rare: a wave-uniform branch) and O += V^T P for keys
   // 32 u .. + 31 of the stage at st.  k16 step t16 covers keys 16 t16 .. + 15
@@ -320,6 +328,41 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       }
     }
   };
+  // S of the next phase with the softmax of the current one, interleaved by
+  // hand (the scheduler otherwise puts every MFMA first): per k-step, the two
+  // MFMAs each followed by the softmax items of that slot, fenced so the
+  // order stays; K fragments are read two steps ahead.  Then the row sums.
+  auto qk_softmax = [&](uint32_t st, int u_next, f32x16 (&Sn)[2], f32x16 (&Sc)[2], bool mask, int j0, int j_lo,
+                        int u) {
+    constexpr int kSlots = 2 * kSteps;
+    const int n_items = (mask ? 4 : 0) + 4 + 16;
+    auto kaddr = [&](int s) -> uint32_t {
+      const int sp = (2 * s < kUc) ? s : s - kUc / 2;  // k-step within the part
+      return (2 * s < kUc) ? st + kc_off[sp & 3] + 128 * (sp >> 2) + u_next * 32 * (2 * DC)
+                           : st + kr_off[sp & 3] + 128 * (sp >> 2) + u_next * 32 * (2 * DR);
+    };
+    bf16x8 kf[3];
+    kf[0] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)kaddr(0));
+    if (kSteps > 1) kf[1] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)kaddr(1));
+    Sn[0] = f32x16{};
+    Sn[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      if (s + 2 < kSteps) kf[(s + 2) % 3] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)kaddr(s + 2));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        Sn[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % 3], qf[t][s], Sn[t], 0, 0, 0);
+        const int slot = 2 * s + t;
+        // items i with i * kSlots / n_items == slot
+#pragma unroll
+        for (int i = 0; i < 24; ++i)
+          if (i < n_items && (i * kSlots) / n_items == slot) softmax_item(Sc, mask, j0, j_lo, u, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) l_sum[t] = fmaf(l_sum[t], alpha[t], psum[t]);  // per lane until the end
+  };
   // masks only where some key of the phase is hidden from some row of the wave
   auto needs_mask = [&](int jb, int u) {
     const int j0 = block_start(jb), j_lo = jb * kKeys;
@@ -333,38 +376,31 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // of stage jb + 1; the barrier between its phases publishes stage jb + 1
   // and frees stage jb - 1 (last read in phase 2 jb - 1), which is refilled
   // with block jb + 3.
-  f32x16 sA[2], sB[2];
-  bf16x8 pf[2][2];
-  float alpha[2];
   for (int s0 = 0; s0 < kStages - 1; ++s0) issue(s0);
   wait_vmem<(kStages - 2) * kLoads>();  // block 0 landed
   __syncthreads();
   qk(lds, 0, sA);
   for (int jb = 0; jb < nj; ++jb) {
+    // O stays in AGPRs across the iteration: without this the compiler keeps
+    // a VGPR copy of it for the (rare) rescale and refreshes it every block
+#pragma unroll
+    for (int a = 0; a < kDt; ++a)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) asm volatile("" : "+a"(oacc[a][t]));
     const uint32_t st = lds + (jb % kStages) * kStageBytes;
     const uint32_t st1 = lds + ((jb + 1) % kStages) * kStageBytes;
     const int j0 = block_start(jb), j_lo = jb * kKeys;
     // phase 0: S of phase 1 (same stage) with the softmax of phase 0
-    if (needs_mask(jb, 0)) {
-      qk(st, 1, sB);
-      softmax(sA, pf, alpha, true, j0, j_lo, 0);
-    } else {
-      qk(st, 1, sB);
-      softmax(sA, pf, alpha, false, j0, j_lo, 0);
-    }
+    if (needs_mask(jb, 0)) qk_softmax(st, 1, sB, sA, true, j0, j_lo, 0);
+    else qk_softmax(st, 1, sB, sA, false, j0, j_lo, 0);
     pv(st, 0, pf, alpha);
     wait_vmem<kLoads>();  // block jb + 1 landed; only block jb + 2 is newer
     __syncthreads();
     issue(jb + kStages - 1);
     // phase 1: S of the next block's phase 0 (past the last block a redundant
     // copy of it) with the softmax of phase 1
-    if (needs_mask(jb, 1)) {
-      qk(st1, 0, sA);
-      softmax(sB, pf, alpha, true, j0, j_lo, 1);
-    } else {
-      qk(st1, 0, sA);
-      softmax(sB, pf, alpha, false, j0, j_lo, 1);
-    }
+    if (needs_mask(jb, 1)) qk_softmax(st1, 0, sA, sB, true, j0, j_lo, 1);
+    else qk_softmax(st1, 0, sA, sB, false, j0, j_lo, 1);
     pv(st, 1, pf, alpha);
   }
   wait_vmem<0>();  // the prefetches past the last block
