@@ -120,6 +120,7 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   constexpr int kLoadsC = kKcBytes / 4096, kLoadsR = kKrBytes / 4096, kLoadsV = kVBytes / 4096;  // per wave
   constexpr int kLoads = kLoadsC + kLoadsR + kLoadsV;
   static_assert(DC % 64 == 0 && DR % 64 == 0 && (DV == 64 || DV == 128), "supported head dims");
+  static_assert(kLoads <= kSteps, "one block's copies fit one phase, one every other slot");
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
@@ -178,17 +179,23 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     nj = min(NJ, (min(Sk - 1, last_row + off)) / kKeys + 1);
   }
   auto block_start = [&](int jb) { return min(min(jb, NJ - 1) * kKeys, Sk - kKeys); };
-  auto issue = [&](int jb) {
+  // DMA instruction l (of kLoads: the Kc parts, the Kr parts, the V parts) of block jb
+  auto issue_part = [&](int jb, int l) {
     const int64_t j0 = block_start(jb);
     const uint32_t st = lds + (jb % kStages) * kStageBytes;
+    if (l < kLoadsC) {
+      load_lds16(Kcbh + j0 * DC * 2 + 4096 * l, lo_c, st + 1024 * (wave + 4 * l));
+    } else if (l < kLoadsC + kLoadsR) {
+      const int m = l - kLoadsC;
+      load_lds16(Krb + j0 * DR * 2 + 4096 * m, lo_r, st + kKcBytes + 1024 * (wave + 4 * m));
+    } else {
+      const int m = l - kLoadsC - kLoadsR;
+      load_lds16(Vbh + j0 * DV * 2 + 4096 * m, lo_v, st + kKcBytes + kKrBytes + 1024 * (wave + 4 * m));
+    }
+  };
+  auto issue = [&](int jb) {
 #pragma unroll
-    for (int l = 0; l < kLoadsC; ++l) load_lds16(Kcbh + j0 * DC * 2 + 4096 * l, lo_c, st + 1024 * (wave + 4 * l));
-#pragma unroll
-    for (int l = 0; l < kLoadsR; ++l)
-      load_lds16(Krb + j0 * DR * 2 + 4096 * l, lo_r, st + kKcBytes + 1024 * (wave + 4 * l));
-#pragma unroll
-    for (int l = 0; l < kLoadsV; ++l)
-      load_lds16(Vbh + j0 * DV * 2 + 4096 * l, lo_v, st + kKcBytes + kKrBytes + 1024 * (wave + 4 * l));
+    for (int l = 0; l < kLoads; ++l) issue_part(jb, l);
   };
 
   // running state per query tile t (this lane's row i = row_base + 32 t + lane % 32)
@@ -304,6 +311,15 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // 4 h + e, slots 4..7 keys 8 + 4 h + e - 4.  Lane (16-lane group g, i) of a
   // transposed read addresses V row 4 (g / 2) + i / 4 (+ 8 for slots 4..7),
   // columns 32 dt + 16 (g & 1) + 4 (i & 3) .. + 3.
+  // V fragment of k16 step t16 and column tile dt of phase u (two transposed reads)
+  auto read_vf = [&](uint32_t st, int u, int t16, int dt) -> bf16x8 {
+    const uint32_t a = st + v_off[dt] + (32 * u + 16 * t16) * (2 * DV);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * (2 * DV)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return as_bf16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
+  };
+  bf16x8 vpre[kDt];  // the phase's t16 = 0 fragments, read under the QK MFMAs
   auto pv = [&](uint32_t st, int u, const bf16x8 (&pf)[2][2], const float (&alpha)[2]) {
     if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
 #pragma unroll
@@ -317,11 +333,7 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int t16 = 0; t16 < 2; ++t16) {
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
-        const uint32_t a = st + v_off[dt] + (32 * u + 16 * t16) * (2 * DV);
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * (2 * DV)));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const bf16x8 vf = as_bf16x8(u32x4{l2.x, l2.y, h2.x, h2.y});
+        const bf16x8 vf = t16 == 0 ? vpre[dt] : read_vf(st, u, 1, dt);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           oacc[dt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[t][t16], oacc[dt][t], 0, 0, 0);
@@ -332,8 +344,11 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // hand (the scheduler otherwise puts every MFMA first): per k-step, the two
   // MFMAs each followed by the softmax items of that slot, fenced so the
   // order stays; K fragments are read two steps ahead.  Then the row sums.
+  // st_v / u: the current phase (its V fragments of k16 step 0 are read in
+  // the last slots); dma_block >= 0: that block's copies go out one every
+  // other slot.
   auto qk_softmax = [&](uint32_t st, int u_next, f32x16 (&Sn)[2], f32x16 (&Sc)[2], bool mask, int j0, int j_lo,
-                        int u) {
+                        int u, uint32_t st_v, int dma_block) {
     constexpr int kSlots = 2 * kSteps;
     const int n_items = (mask ? 4 : 0) + 4 + 16;
     auto kaddr = [&](int s) -> uint32_t {
@@ -357,6 +372,8 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int i = 0; i < 24; ++i)
           if (i < n_items && (i * kSlots) / n_items == slot) softmax_item(Sc, mask, j0, j_lo, u, i);
+        if (dma_block >= 0 && (slot & 1) == 0 && slot / 2 < kLoads) issue_part(dma_block, slot / 2);
+        if (slot >= kSlots - kDt) vpre[slot - (kSlots - kDt)] = read_vf(st_v, u, 0, slot - (kSlots - kDt));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -391,16 +408,17 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const uint32_t st1 = lds + ((jb + 1) % kStages) * kStageBytes;
     const int j0 = block_start(jb), j_lo = jb * kKeys;
     // phase 0: S of phase 1 (same stage) with the softmax of phase 0
-    if (needs_mask(jb, 0)) qk_softmax(st, 1, sB, sA, true, j0, j_lo, 0);
-    else qk_softmax(st, 1, sB, sA, false, j0, j_lo, 0);
+    if (needs_mask(jb, 0)) qk_softmax(st, 1, sB, sA, true, j0, j_lo, 0, st, -1);
+    else qk_softmax(st, 1, sB, sA, false, j0, j_lo, 0, st, -1);
     pv(st, 0, pf, alpha);
     wait_vmem<kLoads>();  // block jb + 1 landed; only block jb + 2 is newer
     __syncthreads();
-    issue(jb + kStages - 1);
     // phase 1: S of the next block's phase 0 (past the last block a redundant
     // copy of it) with the softmax of phase 1
-    if (needs_mask(jb, 1)) qk_softmax(st1, 0, sA, sB, true, j0, j_lo, 1);
-    else qk_softmax(st1, 0, sA, sB, false, j0, j_lo, 1);
+    // block jb + 3's copies (into the stage freed by the barrier) go out
+    // under this phase's MFMAs
+    if (needs_mask(jb, 1)) qk_softmax(st1, 0, sA, sB, true, j0, j_lo, 1, st, jb + kStages - 1);
+    else qk_softmax(st1, 0, sA, sB, false, j0, j_lo, 1, st, jb + kStages - 1);
     pv(st, 1, pf, alpha);
   }
   wait_vmem<0>();  // the prefetches past the last block
