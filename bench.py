@@ -36,7 +36,7 @@ METRIC = "MuonClip step: NS + max-logit TFLOP/s (MFMA util), rescale GB/s"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0
 
-D_MODEL, D_EXPERT, N_HEADS, D_NOPE, D_ROPE = 7168, 2048, 64, 128, 64
+D_MODEL, D_EXPERT, N_HEADS, D_NOPE, D_ROPE, D_V = 7168, 2048, 64, 128, 64, 128
 LR, WD, MU, TAU, ALPHA = 2e-4, 0.1, 0.95, 100.0, 0.5
 
 
@@ -110,6 +110,9 @@ class Workload:
                              torch.bfloat16)
         self.Q, self.Kc, self.Kr = workloads.mla_project(X, Wq, Wkc, Wkr, N_HEADS)
         del X, Wq, Wkc, Wkr
+        # values for the forward that yields the max logit as a by-product
+        self.V = workloads.normal((8, N_HEADS, 4096, D_V), 1.0, workloads.generator(seed + 3, device), device,
+                                  torch.bfloat16)
         torch.cuda.synchronize()
 
     def group(self, name):
@@ -238,6 +241,29 @@ def run(args):
     d_in = D_MODEL
     rescale_bytes = 2 * n_clip * ((D_NOPE + D_ROPE) + D_NOPE) * d_in * 2  # read + write, bf16
 
+    # The attention forward that yields the same max logit as a by-product
+    # (outside the step: the optimizer step reads S_max; where the forward
+    # runs here, this replaces the stand-alone pass).  Timed on the step's
+    # stream, 3 launches each, plain and causal.
+    fwd = {}
+    for causal in (False, True):
+        smax_f = torch.empty(N_HEADS, dtype=torch.float32, device=dev)
+        mc.attention_fwd_maxlogit(wl.Q, wl.Kc, wl.Kr, wl.V, causal=causal, smax=smax_f)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(3):
+            O_f, _ = mc.attention_fwd_maxlogit(wl.Q, wl.Kc, wl.Kr, wl.V, causal=causal, smax=smax_f)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 3
+        fl = 2.0 * B * H * Sq * Sk * (dq + D_V) * ((Sq + 1) / (2.0 * Sq) if causal else 1.0)
+        key = "causal" if causal else "full"
+        fwd[key + "_ms"] = round(ms, 4)
+        fwd[key + "_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
+        if not causal:
+            fwd["smax_rel_diff_vs_standalone"] = float(((smax_f - smax).abs() / smax.abs()).max().item())
+        del O_f
+
     # dominant kernel: the GEMM mode with the largest total time
     dom = max(gemm_ms, key=lambda g: sum(gemm_ms[g]))
     dom_launches = len(gemm_ms[dom])
@@ -271,6 +297,9 @@ def run(args):
         "clipped_heads": n_clip,
         "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
                         for g in gemm_ms},
+        "attention_forward_with_max_logit": dict(
+            fwd, note="outside the step: softmax(QK^T/sqrt(d))V with d_v 128 on the same Q/K, S_max as a by-product; "
+                      "flops 2 B H Sq Sk (192 + 128), causal counts the visible half"),
     })
 
     out = {
