@@ -26,7 +26,8 @@
 //                 read in that order with ds_read_b64_tr_b16.
 // The reference point m of the exponentials follows the row maximum lazily:
 // it moves (and O and the row sum are rescaled by 2^(m_old - m_new)) only
-// when a block's maximum exceeds it by more than 8 (p <= 256), which keeps the
+// when a block's maximum exceeds it by more than 32 (so p <= 2^32, and the row
+// sums stay far from the float32 and bf16 range limits), which keeps the
 // result exact up to rounding and makes the rescale rare.  The true row
 // maximum is tracked separately for S_max.
 //
@@ -49,7 +50,7 @@ constexpr int kRowsPerBlock = kRowsPerWave * (kThreads / 64);  // 256
 constexpr int kKeys = 64;                                     // keys per LDS stage
 constexpr int kStages = 4;                                    // prefetch distance 3
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units the reference may lag the row max
+constexpr float kRescaleSlack = 32.0f;  // log2 units the reference may lag the row max
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
