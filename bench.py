@@ -410,8 +410,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: measured on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(no multi-GPU path is implemented)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
