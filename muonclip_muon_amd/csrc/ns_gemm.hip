@@ -554,9 +554,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         unpack8(u32x4{l2.x, l2.y, h2.x, h2.y}, x);
       }
     };
-    // Batches of 8 passes: all W loads of a batch are issued before any of
+    // Batches of 16 passes: all W loads of a batch are issued before any of
     // its updates, so the read latency is paid once per batch, not per pass.
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     constexpr int kWords = (UPD == 1) ? 1 : 2;  // 16-byte words per 8 elements
     for (int s0 = 0; s0 < 32; s0 += kBatch) {
       u32x4 wbuf[kBatch][kWords];
