@@ -264,6 +264,32 @@ def run(args):
             fwd["smax_rel_diff_vs_standalone"] = float(((smax_f - smax).abs() / smax.abs()).max().item())
         del O_f
 
+    # Self-measured ceilings on this GPU (measurement aids, outside the step):
+    # the MFMA rate with register operands only (random and zero operands:
+    # the clock the chip holds depends on how many bits switch), and a plain
+    # device copy through the workspace (no longer needed at this point).
+    probes = {}
+    for zero in (False, True):
+        p_out, p_fl = mc.probe_mfma_bf16(1024, 20000, zero_operands=zero, device=dev)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        mc.probe_mfma_bf16(1024, 20000, zero_operands=zero, out=p_out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        probes["mfma_bf16_zero_operands_tflops" if zero else "mfma_bf16_random_operands_tflops"] = round(
+            p_fl / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    half_ws = (workspace.numel() // 2) // (1 << 20) * (1 << 20)
+    cp_src, cp_dst = workspace[:half_ws], workspace[half_ws:2 * half_ws]
+    mc.probe_copy(cp_src, cp_dst)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(5):
+        mc.probe_copy(cp_src, cp_dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    probes["copy_gbps"] = round(2.0 * half_ws * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    probes["copy_bytes"] = half_ws
+
     # dominant kernel: the GEMM mode with the largest total time
     dom = max(gemm_ms, key=lambda g: sum(gemm_ms[g]))
     dom_launches = len(gemm_ms[dom])
@@ -297,6 +323,10 @@ def run(args):
         "clipped_heads": n_clip,
         "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
                         for g in gemm_ms},
+        "probes": dict(probes, dominant_gemm_frac_of_mfma_probe=round(
+            achieved / probes["mfma_bf16_random_operands_tflops"], 3),
+            note="self-measured ceilings: MFMA-only loop on register operands, plain 16-byte copy "
+                 "(read + write bytes)"),
         "attention_forward_with_max_logit": dict(
             fwd, note="outside the step: softmax(QK^T/sqrt(d))V with d_v 128 on the same Q/K, S_max as a by-product; "
                       "flops 2 B H Sq Sk (192 + 128), causal counts the visible half"),

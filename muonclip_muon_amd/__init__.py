@@ -27,6 +27,8 @@ __all__ = [
     "lib",
     "abi_version",
     "muonclip_momentum",
+    "probe_mfma_bf16",
+    "probe_copy",
     "muon_ns_workspace_bytes",
     "muon_ns_orthogonalize_batched",
     "muon_apply_update",
@@ -96,6 +98,10 @@ def _load():
                                          vp, vp, i32, vp]
     L.qk_clip_apply_total.restype = ctypes.c_int
     L.qk_clip_apply_total.argtypes = L.qk_clip_apply.argtypes
+    L.mc_probe_mfma_bf16.restype = ctypes.c_int
+    L.mc_probe_mfma_bf16.argtypes = [i64, i64, ctypes.c_int, vp, vp]
+    L.mc_probe_copy.restype = ctypes.c_int
+    L.mc_probe_copy.argtypes = [vp, vp, i64, vp]
     return L
 
 
@@ -340,6 +346,29 @@ def _qk_clip(fn, smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, 
                               gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
     _check(fn, status)
     return gamma, clipped
+
+
+def probe_mfma_bf16(workgroups, iters, zero_operands=False, out=None, device=None, stream=None):
+    """Enqueue the MFMA ceiling probe (measurement aid, include/muonclip_probe.h).
+
+    Returns (out, flop) with flop = workgroups * 4 * iters * 16 * 32768."""
+    if out is None:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device=device or "cuda")
+    _dev(out, "out")
+    _check("mc_probe_mfma_bf16", lib.mc_probe_mfma_bf16(workgroups, iters, 1 if zero_operands else 0,
+                                                        out.data_ptr(), _stream(out, stream)))
+    return out, workgroups * 4 * iters * 16 * 32768
+
+
+def probe_copy(src, dst, stream=None):
+    """Enqueue the copy probe dst <- src over src's bytes (measurement aid)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check("mc_probe_copy", lib.mc_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src, stream)))
+    return dst
 
 
 def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1, momentum=0.95,

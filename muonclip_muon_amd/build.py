@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libmuonclip.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "elementwise.hip", "qkclip.hip", "ns_prep.hip", "ns_gemm.hip", "maxlogit.hip",
-           "attention.hip"]
+           "attention.hip", "probe.hip"]
 
 COMMON_FLAGS = [
     "-O3",

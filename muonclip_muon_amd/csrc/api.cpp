@@ -3,6 +3,7 @@
 // no output; see include/muonclip.h for the contract of each entry point.
 
 #include "muonclip.h"
+#include "muonclip_probe.h"
 
 #include <math.h>
 
@@ -288,6 +289,24 @@ mc_status_t qk_clip_apply_total(const float* smax, int64_t H, float tau, float a
                                 void* stream) {
   return qk_clip_common(smax, H, true, tau, alpha, Wq, Wk, w_dtype, d_in, q_rows_per_head, q_c_rows,
                         k_rows_per_head, gamma_out, clipped_out, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+mc_status_t mc_probe_mfma_bf16(int64_t workgroups, int64_t iters, int zero_operands, float* out, void* stream) {
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (int64_t{1} << 30)) return MC_EINVAL;
+  if (!out || !aligned(out, 4)) return MC_EINVAL;
+  return from_hip(mc::launch_mfma_probe(workgroups, iters, zero_operands != 0, out, static_cast<hipStream_t>(stream)));
+}
+
+mc_status_t mc_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return MC_EINVAL;
+  if (bytes == 0) return MC_OK;
+  if (!src || !dst) return MC_EINVAL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MC_EALIGN;
+  return from_hip(mc::launch_copy_probe(src, dst, bytes, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -86,4 +86,8 @@ hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float t
                           bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
                           float* gamma_out, int32_t* clipped_out, hipStream_t stream);
 
+// Measurement aids (probe.hip).
+hipError_t launch_mfma_probe(int64_t workgroups, int64_t iters, bool zero_operands, float* out, hipStream_t stream);
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 }  // namespace mc

@@ -1,8 +1,10 @@
 """Host-side checks of libmuonclip.so (no GPU): it loads, exports every entry
-point include/muonclip.h declares, and rejects invalid arguments before any
-HIP call (argument validation never touches the device)."""
+point include/*.h declares (the step in muonclip.h, the measurement aids in
+muonclip_probe.h), and rejects invalid arguments before any HIP call
+(argument validation never touches the device)."""
 
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -11,10 +13,11 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "muonclip.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return re.findall(r"MC_API\s+[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text)
 
 
@@ -28,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = set(_declared())
     assert {"muonclip_momentum", "muon_ns_orthogonalize_batched", "muon_apply_update", "qk_maxlogit",
             "qk_clip_apply", "muon_ns_workspace_bytes", "mc_abi_version", "mc_status_string",
-            "muon_momentum_ns_update_batched", "qk_clip_apply_total"} <= names
+            "muon_momentum_ns_update_batched", "qk_clip_apply_total", "attention_fwd_maxlogit",
+            "mc_probe_mfma_bf16", "mc_probe_copy"} <= names
 
 
 def test_library_exports_every_declared_symbol(mc):
@@ -162,3 +166,18 @@ def test_clip_validation(mc, fn):
     assert f(None, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
     assert f(FAKE, 4, 100.0, 0.5, ctypes.c_void_p(0x100001), FAKE, 1, 16, 6, 4, 4, None, None,
              None) == EALIGN
+
+
+def test_probe_validation(mc):
+    L = mc.lib
+    assert L.mc_probe_mfma_bf16(0, 10, 0, FAKE, None) == EINVAL
+    assert L.mc_probe_mfma_bf16(65537, 10, 0, FAKE, None) == EINVAL
+    assert L.mc_probe_mfma_bf16(8, 0, 0, FAKE, None) == EINVAL
+    assert L.mc_probe_mfma_bf16(8, (1 << 30) + 1, 0, FAKE, None) == EINVAL
+    assert L.mc_probe_mfma_bf16(8, 10, 0, None, None) == EINVAL
+    assert L.mc_probe_mfma_bf16(8, 10, 0, ctypes.c_void_p(0x100002), None) == EINVAL
+    assert L.mc_probe_copy(FAKE, FAKE, 0, None) == 0  # empty: nothing enqueued
+    assert L.mc_probe_copy(FAKE, FAKE, -16, None) == EINVAL
+    assert L.mc_probe_copy(FAKE, FAKE, 24, None) == EINVAL
+    assert L.mc_probe_copy(None, FAKE, 16, None) == EINVAL
+    assert L.mc_probe_copy(ctypes.c_void_p(0x100008), FAKE, 16, None) == EALIGN
