@@ -296,9 +296,9 @@ def run(args):
     dom_avg_ms = sum(gemm_ms[dom]) / dom_launches
     dom_avg_flops = sum(gemm_flops[dom]) / dom_launches
     achieved = dom_avg_flops / (dom_avg_ms * 1e-3) / 1e12
-    kernel_names = {0: "ns_gemm_kernel<0, 0> (A = X X^T)", 1: "ns_gemm_kernel<1, 0> (B' = aI + bA + cAA)",
-                    2: "ns_gemm_kernel<2, 0> (X' = B'X)",
-                    "2u": "ns_gemm_kernel<2, 1> (last step: X' = B'X applied as the update of bf16 W)"}
+    kernel_names = {0: "ns_gemm_kernel<0, 0, *> (A = X X^T)", 1: "ns_gemm_kernel<1, 0, false> (B' = aI + bA + cAA)",
+                    2: "ns_gemm_kernel<2, 0, *> (X' = B'X)",
+                    "2u": "ns_gemm_kernel<2, 1, *> (last step: X' = B'X applied as the update of bf16 W)"}
 
     breakdown = {
         "path": "three calls: momentum, Newton-Schulz, update" if args.unfused else

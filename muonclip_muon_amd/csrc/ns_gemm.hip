@@ -289,7 +289,9 @@ struct UpdArgs {
 };
 
 // UPD: 0 = store X' (or A, B'); 1 = update bf16 W; 2 = update float32 W.
-template <int MODE, int UPD>
+// SCALED: the launch carries 1 / ||M|| per matrix (the first Newton-Schulz
+// step of the fused path); otherwise the epilogue has no multiply.
+template <int MODE, int UPD, bool SCALED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
                     uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
@@ -483,11 +485,11 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       for (int g = 0; g < 4; ++g) {
         const uint32_t a = st_addr(ii, 4 * x + g) + 8 * frag_half;
         float v[4] = {acc[x][y][4 * g + 0], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]};
-        if constexpr (MODE == 0) {
+        if constexpr (MODE == 0 && SCALED) {
           const float s2 = xs * xs;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] *= s2;
-        } else if constexpr (MODE == 2) {
+        } else if constexpr (MODE == 2 && SCALED) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] *= xs;
         }
@@ -662,11 +664,12 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad, tiles_n, tiles_per_mat,
                        alpha, beta, diag, inv, ua);
   };
-  if (mode == 0) go(ns_gemm_kernel<0, 0>);
-  else if (mode == 1) go(ns_gemm_kernel<1, 0>);
-  else if (upd == nullptr) go(ns_gemm_kernel<2, 0>);
-  else if (upd->w_bf16) go(ns_gemm_kernel<2, 1>);
-  else go(ns_gemm_kernel<2, 2>);
+  const bool sc = inv != nullptr;
+  if (mode == 0) sc ? go(ns_gemm_kernel<0, 0, true>) : go(ns_gemm_kernel<0, 0, false>);
+  else if (mode == 1) go(ns_gemm_kernel<1, 0, false>);
+  else if (upd == nullptr) sc ? go(ns_gemm_kernel<2, 0, true>) : go(ns_gemm_kernel<2, 0, false>);
+  else if (upd->w_bf16) sc ? go(ns_gemm_kernel<2, 1, true>) : go(ns_gemm_kernel<2, 1, false>);
+  else sc ? go(ns_gemm_kernel<2, 2, true>) : go(ns_gemm_kernel<2, 2, false>);
   return hipGetLastError();
 }
 
