@@ -264,6 +264,27 @@ def run(args):
             fwd["smax_rel_diff_vs_standalone"] = float(((smax_f - smax).abs() / smax.abs()).max().item())
         del O_f
 
+    # Newton-Schulz alone on one chunk of 64 expert matrices (2048 x 7168):
+    # norm, pre-scale, 5 iterations and the bf16 output, no momentum or update.
+    ns_name, _, ns_n, ns_rows, ns_cols = wl.groups[0]
+    ns_cnt = min(64, ns_n)
+    M_ns = wl.view(ns_name, wl.M, 0, ns_cnt)
+    O_ns = torch.empty((ns_cnt, ns_rows, ns_cols), dtype=torch.bfloat16, device=dev)
+    mc.muon_ns_orthogonalize_batched(M_ns, O_ns, workspace=workspace, out_scale=mc.muon_out_scale(ns_rows, ns_cols))
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(3):
+        mc.muon_ns_orthogonalize_batched(M_ns, O_ns, workspace=workspace,
+                                         out_scale=mc.muon_out_scale(ns_rows, ns_cols))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ns_only_ms = e0.elapsed_time(e1) / 3
+    ns_only = {"shape": f"{ns_cnt} x {ns_rows} x {ns_cols}", "ms": round(ns_only_ms, 3),
+               "tflops_nominal": round(ns_flops(ns_rows, ns_cols, steps_ns) * ns_cnt / (ns_only_ms * 1e-3) / 1e12, 1),
+               "note": "muon_ns_orthogonalize_batched alone: norm, pre-scale, 5 iterations, bf16 output; "
+                       "nominal flops 4n^2m + 2n^3 per matrix per iteration"}
+    del O_ns
+
     # Self-measured ceilings on this GPU (measurement aids, outside the step):
     # the MFMA rate with register operands only (random and zero operands:
     # the clock the chip holds depends on how many bits switch), and a plain
@@ -323,6 +344,7 @@ def run(args):
         "clipped_heads": n_clip,
         "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
                         for g in gemm_ms},
+        "newton_schulz_only": ns_only,
         "probes": dict(probes, dominant_gemm_frac_of_mfma_probe=round(
             achieved / probes["mfma_bf16_random_operands_tflops"], 3),
             note="self-measured ceilings: MFMA-only loop on register operands, plain 16-byte copy "

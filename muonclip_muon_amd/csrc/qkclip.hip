@@ -15,9 +15,13 @@
 // split when S_max > tau.  Each block reduces the H values itself.
 //
 // A head's rows are two contiguous row blocks (W_q and W_k are row-major with
-// head-major rows), so the kernel streams them with 16-byte accesses.  Grid:
-// (chunks, H); every block of an unclipped head returns after reading one
-// float, so the launch costs only the clipped heads' bytes.
+// head-major rows), so the kernels stream them with 16-byte accesses.
+// Compact kernel (H up to 1024): every block reads the H values of S_max,
+// lists the clipped heads with their factors in LDS, and the grid, sized for
+// the case where every head is clipped, shares out only the listed heads'
+// elements, so few clipped heads still spread over every CU and no block is
+// launched just to find its head unclipped.  Larger H: a grid of
+// (chunks, H) whose blocks of unclipped heads return after reading one float.
 //
 // The multiply is a single float op, rounded once to the storage type; FP
 // contraction is off so the result does not depend on the compiler.
@@ -152,6 +156,79 @@ __global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restri
   }
 }
 
+
+constexpr int kCompactMaxHeads = 1024;
+constexpr int kCompactMaxBlocks = 2048;
+
+// The clipped heads, their factors and the head count, identical in every
+// block.  Block 0 also writes gamma_out / clipped_out for every head.
+struct ClipList {
+  int head[kCompactMaxHeads];
+  float q_c[kCompactMaxHeads], q_r[kCompactMaxHeads], k[kCompactMaxHeads];
+  int wave_count[kThreads / 64];
+};
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* __restrict__ smax, int H,
+                                                                  bool total_clip, float tau, float alpha,
+                                                                  void* __restrict__ Wq, void* __restrict__ Wk,
+                                                                  int64_t d_in, int64_t qph, int64_t q_c_rows,
+                                                                  int64_t kph, float* __restrict__ gamma_out,
+                                                                  int32_t* __restrict__ clipped_out) {
+  __shared__ ClipList L;
+  const float s_all = total_clip ? block_max_all(smax, H) : 0.0f;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int count = 0;  // the same in every thread
+  for (int base = 0; base < H; base += kThreads) {
+    const int h = base + static_cast<int>(threadIdx.x);
+    ClipFactors f = {1.f, 1.f, 1.f, 0, 1.f};
+    if (h < H) f = clip_factors(total_clip ? s_all : smax[h], tau, alpha);
+    if (blockIdx.x == 0 && h < H) {
+      if (gamma_out) gamma_out[h] = f.gamma;
+      if (clipped_out) clipped_out[h] = f.state;
+    }
+    const bool c = h < H && f.state == 1;
+    const uint64_t m = __ballot(c);
+    if (lane == 0) L.wave_count[w] = __popcll(m);
+    __syncthreads();
+    int slot = count + __popcll(m & ((uint64_t{1} << lane) - 1));
+    int round = 0;
+    for (int i = 0; i < kThreads / 64; ++i) {
+      if (i < w) slot += L.wave_count[i];
+      round += L.wave_count[i];
+    }
+    if (c) {
+      L.head[slot] = h;
+      L.q_c[slot] = f.q_c;
+      L.q_r[slot] = f.q_r;
+      L.k[slot] = f.k;
+    }
+    count += round;
+    __syncthreads();
+  }
+  if (count == 0) return;
+
+  const size_t esz = BF16 ? 2 : 4;
+  const int64_t unit = VEC ? 8 : 1;  // elements per work item
+  const int64_t q_items = qph * d_in / unit, q_c_items = q_c_rows * d_in / unit;
+  const int64_t per_head = q_items + kph * d_in / unit;
+  const int64_t total = count * per_head;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total; v += stride) {
+    const int idx = static_cast<int>(v / per_head);
+    const int64_t off = v - idx * per_head;
+    const int64_t h = L.head[idx];
+    char* q_base = static_cast<char*>(Wq) + static_cast<size_t>(h * qph * d_in) * esz;
+    char* k_base = static_cast<char*>(Wk) + static_cast<size_t>(h * kph * d_in) * esz;
+    if constexpr (VEC) {
+      if (off < q_items) scale_vec8<BF16>(q_base, off, off < q_c_items ? L.q_c[idx] : L.q_r[idx]);
+      else scale_vec8<BF16>(k_base, off - q_items, L.k[idx]);
+    } else {
+      if (off < q_items) scale_one<BF16>(q_base, off, off < q_c_items ? L.q_c[idx] : L.q_r[idx]);
+      else scale_one<BF16>(k_base, off - q_items, L.k[idx]);
+    }
+  }
+}
 }  // namespace
 
 hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float tau, float alpha, void* Wq, void* Wk,
@@ -163,6 +240,27 @@ hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float t
                    ((qph * d_in * static_cast<int64_t>(esz)) % 16 == 0) &&
                    ((kph * d_in * static_cast<int64_t>(esz)) % 16 == 0);
   const int64_t total = (qph + kph) * d_in;
+  if (H <= kCompactMaxHeads) {
+    // grid for every head clipped: one work item per thread, at most
+    // kCompactMaxBlocks blocks (then each thread loops)
+    const int64_t items = H * (vec ? total / 8 : total);
+    int64_t blocks = (items + kThreads - 1) / kThreads;
+    if (blocks > kCompactMaxBlocks) blocks = kCompactMaxBlocks;
+    if (blocks < 1) blocks = 1;
+#define MC_CLIP_COMPACT(B, V)                                                                                     \
+  hipLaunchKernelGGL((qk_clip_compact_kernel<B, V>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
+                     smax, static_cast<int>(H), total_clip, tau, alpha, Wq, Wk, d_in, qph, q_c_rows, kph, gamma_out,   \
+                     clipped_out)
+    if (w_bf16) {
+      if (vec) MC_CLIP_COMPACT(true, true);
+      else MC_CLIP_COMPACT(true, false);
+    } else {
+      if (vec) MC_CLIP_COMPACT(false, true);
+      else MC_CLIP_COMPACT(false, false);
+    }
+#undef MC_CLIP_COMPACT
+    return hipGetLastError();
+  }
   const int64_t per_block = static_cast<int64_t>(kThreads) * kVecPerThread * 8;
   int64_t chunks = (total + per_block - 1) / per_block;
   if (chunks < 1) chunks = 1;

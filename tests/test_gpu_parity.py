@@ -141,6 +141,32 @@ def test_qk_clip_mha_general_alpha(mc):
     assert f32_ulp_diff(Wkd.cpu().numpy(), rk).max() <= 4
 
 
+@pytest.mark.parametrize("H", [300, 1024, 1100])
+def test_qk_clip_many_heads(mc, H):
+    """Head lists longer than one 256-thread round (compact kernel up to 1024
+    heads) and the per-head grid beyond that; about a third of the heads
+    clipped, some NaN."""
+    say("qk_clip heads", H)
+    qph, q_c, kph, d_in = 3, 2, 2, 64
+    g = workloads.generator(12, "cpu")
+    Wq = workloads.normal((H * qph, d_in), 0.02, g, "cpu", torch.bfloat16)
+    Wk = workloads.normal((H * kph, d_in), 0.02, g, "cpu", torch.bfloat16)
+    smax = torch.rand(H, generator=g) * 150.0
+    smax[::97] = float("nan")
+    Wqd, Wkd = Wq.to(DEV), Wk.to(DEV)
+    gamma, clipped = mc.qk_clip_apply(smax.to(DEV), Wqd, Wkd, qph, q_c, kph, tau=100.0, alpha=0.5)
+    torch.cuda.synchronize()
+    rq, rk, rg, rc = oracle.qk_clip(f64(smax), f64(Wq), f64(Wk), qph, q_c, kph, 100.0, 0.5, "bf16")
+    assert clipped.cpu().tolist() == rc.tolist()
+    assert 0 < int((rc == 1).sum()) < H
+    assert rel_err(gamma.cpu().numpy(), rg).max() <= 1e-6
+    assert bf16_ulp_diff(bf16_bits(Wqd), oracle.bf16_bits(rq)).max() <= 1
+    assert bf16_ulp_diff(bf16_bits(Wkd), oracle.bf16_bits(rk)).max() <= 1
+    for got, src, rows in ((Wqd, Wq, qph), (Wkd, Wk, kph)):
+        keep = torch.from_numpy(rc != 1).repeat_interleave(rows)
+        assert torch.equal(got.cpu()[keep].view(torch.int16), src[keep].view(torch.int16))
+
+
 @pytest.mark.parametrize("wdt", [torch.bfloat16, torch.float32])
 def test_qk_clip_total(mc, wdt):
     say("qk_clip total", wdt)
