@@ -162,6 +162,12 @@ def run(args):
     ns_ev = [(ev(), ev()) for _ in ns_calls]
 
     def step(timed):
+        # S_max^h comes from the forward pass that precedes the optimizer step
+        # (measured at the weights before the update, applied after it)
+        e = call_ev["maxlogit"]
+        timed and e[0].record(stream)
+        mc.qk_maxlogit(wl.Q, wl.Kc, wl.Kr, smax=smax)
+        timed and e[1].record(stream)
         if args.unfused:
             e = call_ev["momentum"]
             timed and e[0].record(stream)
@@ -184,10 +190,6 @@ def run(args):
             timed and upd_ev[k][0].record(stream)
             mc.muon_apply_update(W, O, LR, WD)
             timed and upd_ev[k][1].record(stream)
-        e = call_ev["maxlogit"]
-        timed and e[0].record(stream)
-        mc.qk_maxlogit(wl.Q, wl.Kc, wl.Kr, smax=smax)
-        timed and e[1].record(stream)
         e = call_ev["clip"]
         timed and e[0].record(stream)
         mc.qk_clip_apply(smax, wl.view("attn_q")[0], wl.view("attn_kc")[0], D_NOPE + D_ROPE, D_NOPE, D_NOPE,
