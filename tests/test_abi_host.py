@@ -181,3 +181,41 @@ def test_probe_validation(mc):
     assert L.mc_probe_copy(FAKE, FAKE, 24, None) == EINVAL
     assert L.mc_probe_copy(None, FAKE, 16, None) == EINVAL
     assert L.mc_probe_copy(ctypes.c_void_p(0x100008), FAKE, 16, None) == EALIGN
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include "muonclip.h"
+#include "muonclip_probe.h"
+
+int main(void) {
+  /* plain C99 against the C ABI: version, status strings, validation paths
+     (no device pointer is ever dereferenced: every call fails its checks
+     or is empty) */
+  if (mc_abi_version() != MC_ABI_VERSION) return 1;
+  if (mc_status_string(MC_EINVAL) == NULL) return 2;
+  if (muonclip_momentum(NULL, NULL, 0, 0.95f, NULL) != MC_OK) return 3;
+  if (muonclip_momentum(NULL, NULL, 8, 0.95f, NULL) != MC_EINVAL) return 4;
+  if (muon_ns_workspace_bytes(1, 0, 8) != 0) return 5;
+  if (muon_ns_workspace_bytes(4, 256, 512) == 0) return 6;
+  if (qk_clip_apply(NULL, 0, 100.0f, 0.5f, NULL, NULL, MC_BF16, 64, 3, 2, 2, NULL, NULL, NULL) != MC_OK) return 7;
+  if (mc_probe_copy(NULL, NULL, 24, NULL) != MC_EINVAL) return 8;
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+def test_headers_compile_as_c_and_link(mc, tmp_path):
+    """The public headers are plain C: a C99 client compiles with -Wall
+    -Werror, links against the library and runs its validation paths."""
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(mc.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), "-L", libdir, "-lmuonclip", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
