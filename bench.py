@@ -266,6 +266,24 @@ def run(args):
             fwd["smax_rel_diff_vs_standalone"] = float(((smax_f - smax).abs() / smax.abs()).max().item())
         del O_f
 
+    # Long-context max logit (outside the step): 1 x 32768 tokens, 64 heads,
+    # the same MLA projections with no hot head (S about 18, nothing clipped)
+    import workloads
+    L32 = workloads.mla_logits(seed=args.seed + 4, device=dev, batch=1, seq=32768, n_hot=0)
+    smax_l = torch.empty(N_HEADS, dtype=torch.float32, device=dev)
+    mc.qk_maxlogit(L32.Q, L32.Kc, L32.Kr, smax=smax_l)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(3):
+        mc.qk_maxlogit(L32.Q, L32.Kc, L32.Kr, smax=smax_l)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ml_long_ms = e0.elapsed_time(e1) / 3
+    ml_long = {"shape": "1 x 64 heads x 32768 x 32768, d 128 + 64", "ms": round(ml_long_ms, 3),
+               "tflops": round(2.0 * 32768 * 32768 * 64 * (D_NOPE + D_ROPE) / (ml_long_ms * 1e-3) / 1e12, 1),
+               "max_s": round(float(smax_l.max().item()), 2)}
+    del L32
+
     # Newton-Schulz alone on one chunk of 64 expert matrices (2048 x 7168):
     # norm, pre-scale, 5 iterations and the bf16 output, no momentum or update.
     ns_name, _, ns_n, ns_rows, ns_cols = wl.groups[0]
@@ -347,6 +365,7 @@ def run(args):
         "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
                         for g in gemm_ms},
         "newton_schulz_only": ns_only,
+        "maxlogit_long_context": ml_long,
         "probes": dict(probes, dominant_gemm_frac_of_mfma_probe=round(
             achieved / probes["mfma_bf16_random_operands_tflops"], 3),
             note="self-measured ceilings: MFMA-only loop on register operands, plain 16-byte copy "
