@@ -12,10 +12,13 @@
 // only the tiles on and above the diagonal and write each off-diagonal tile
 // twice.
 //
-// Tiling: a 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output
-// tile; each wave owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 float32
-// accumulators per lane, held in AGPRs).  K advances 32 at a time through 5
-// LDS stages of 32 KB (two 16 KB operand tiles each).
+// Tiling: a 512-thread workgroup (8 wave64s, 2 x 4, two per SIMD) owns a
+// 256 x 256 output tile; each wave owns 128 x 64 = 4 x 2 MFMA tiles of
+// 32 x 32 (128 float32 accumulators per lane).  K advances 32 at a time
+// through 5 LDS stages of 32 KB (two 16 KB operand tiles each).  Two waves
+// per SIMD read a third more fragment bytes from LDS than four waves of
+// 128 x 128 would, but each hides the other's LDS and barrier waits behind
+// its MFMAs (measured: 1-3 % faster, results bit-identical).
 //
 // Global -> LDS: global_load_lds_dwordx4 moves 16 bytes per lane straight into
 // LDS (lane l of a wave lands at the instruction's LDS base + 16 l), so the
@@ -58,12 +61,15 @@
 namespace mc {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 32, kThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;  // 2 x 4 waves, 2 per SIMD
+constexpr int kWaveCols = kBN / 4;                   // 64 output columns per wave
+constexpr int kCT = kWaveCols / 32;                  // 32-column MFMA tiles per wave
 constexpr int kStages = 5;                 // LDS stages in flight (prefetch distance kStages - 1)
 constexpr int kTileBytes = kBK * kBN * 2;  // 16 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kLdsBytes = kStages * kStageBytes;
-constexpr int kLoadsPerTile = kTileBytes / 1024 / 4;  // DMA instructions per wave per operand tile
+constexpr int kLoadsPerTile = kTileBytes / 1024 / kWaves;  // DMA instructions per wave per operand tile
 constexpr int kLoadsPerStage = 2 * kLoadsPerTile;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -116,7 +122,7 @@ __device__ __forceinline__ void wait_vmem() {
 // Per-lane byte offsets of the tile loads.  The swizzle of a lane's row does
 // not depend on which 1 KB block it fills, so each lane has one offset per
 // tile and every load is "uniform base + lane offset" (SGPR-base addressing).
-// Wave w fills the 1 KB blocks b = w + 4 jj.
+// Wave w fills the 1 KB blocks b = w + 8 jj.
 //
 // K-contiguous 256 x 32 tile: block b is rows 16 b .. 16 b + 15; lane l takes
 // row 16 b + l / 4, slot l % 4, and swizzle(row) = (l / 16) & 3 for every jj.
@@ -127,7 +133,7 @@ __device__ __forceinline__ uint32_t kc_lane_offset(int64_t ld, int wave, int lan
 }
 // K-rows 32 x 256 tile: block b is k-rows 2 b, 2 b + 1; lane l takes row
 // 2 b + l / 32, slot l % 32, and xswz(row) = 4 ((2 w + l / 32) & 3) for
-// every jj.
+// every jj (b = w + 8 jj).
 __device__ __forceinline__ uint32_t kr_lane_offset(int64_t ld, int wave, int lane) {
   const int r = 2 * wave + (lane >> 5);
   const int u = (lane & 31) ^ xswz(r);
@@ -140,19 +146,19 @@ template <bool KROWS>
 __device__ __forceinline__ void issue_tile(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
                                            int wave) {
   const char* base = reinterpret_cast<const char*>(g);
-  constexpr int kRowsPerJ = KROWS ? 8 : 64;
+  constexpr int kRowsPerJ = KROWS ? 2 * kWaves : 16 * kWaves;
 #pragma unroll
   for (int jj = 0; jj < kLoadsPerTile; ++jj)
-    load_lds16(base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off, lds + 1024 * (wave + 4 * jj));
+    load_lds16(base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off, lds + 1024 * (wave + kWaves * jj));
 }
 
 // One of the kLoadsPerTile DMA instructions of an operand tile.
 template <bool KROWS>
 __device__ __forceinline__ void issue_tile_part(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
                                                 int wave, int jj) {
-  constexpr int kRowsPerJ = KROWS ? 8 : 64;
+  constexpr int kRowsPerJ = KROWS ? 2 * kWaves : 16 * kWaves;
   load_lds16(reinterpret_cast<const char*>(g) + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off,
-             lds + 1024 * (wave + 4 * jj));
+             lds + 1024 * (wave + kWaves * jj));
 }
 
 // K-rows tiles: per-lane LDS read address (relative to a stage) of the
@@ -188,11 +194,11 @@ __device__ __forceinline__ FragAddr frag_addresses(int lane, int wm, int wn) {
   for (int ks = 0; ks < 2; ++ks) {
     const int unit = (2 * ks + frag_half) ^ swz;
     a.p[ks] = (wm * 128 + frag_row) * 64 + unit * 16;
-    if constexpr (!Q_KROWS) a.q[ks] = kTileBytes + (wn * 128 + frag_row) * 64 + unit * 16;
+    if constexpr (!Q_KROWS) a.q[ks] = kTileBytes + (wn * kWaveCols + frag_row) * 64 + unit * 16;
   }
   if constexpr (Q_KROWS) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) a.q[x] = tr_addr(kTileBytes, wn * 128, x, lane);
+    for (int x = 0; x < kCT; ++x) a.q[x] = tr_addr(kTileBytes, wn * kWaveCols, x, lane);
   } else {
     a.q[2] = a.q[3] = 0;
   }
@@ -201,8 +207,8 @@ __device__ __forceinline__ FragAddr frag_addresses(int lane, int wm, int wn) {
 
 // Fragment registers of one k16 sub-step.
 struct Frags {
-  bf16x8 a[4];  // right tile (output columns): MFMA "A" operand
-  bf16x8 b[4];  // left tile (output rows): MFMA "B" operand
+  bf16x8 a[kCT];  // right tile (output columns): MFMA "A" operand
+  bf16x8 b[4];    // left tile (output rows): MFMA "B" operand
 };
 
 __device__ __forceinline__ bf16x8 tr_frag(uint32_t addr) {
@@ -220,25 +226,28 @@ __device__ __forceinline__ void load_frags(const FragAddr& fadr, uint32_t stage_
   for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
   if constexpr (Q_KROWS) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) f.a[x] = tr_frag(stage_base + fadr.q[x] + ks * 8192);
+    for (int x = 0; x < kCT; ++x) f.a[x] = tr_frag(stage_base + fadr.q[x] + ks * 8192);
   } else {
     const uint32_t qb = stage_base + fadr.q[ks];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) f.a[x] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(qb + x * 2048));
+    for (int x = 0; x < kCT; ++x) f.a[x] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(qb + x * 2048));
   }
 }
 
-// Part g of a sub-step's fragments: left tile y = g and right tile x = g.
+// Part g of a sub-step's fragments: left tiles y = 2 g, 2 g + 1 and right
+// tile x = g.
 template <bool Q_KROWS>
 __device__ __forceinline__ void load_frags_part(const FragAddr& fadr, uint32_t stage_base, int ks, int g,
                                                 Frags& f) {
-  f.b[g] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.p[ks] + g * 2048));
+#pragma unroll
+  for (int y = 2 * g; y < 2 * g + 2; ++y)
+    f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.p[ks] + y * 2048));
   if constexpr (Q_KROWS) f.a[g] = tr_frag(stage_base + fadr.q[g] + ks * 8192);
   else f.a[g] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.q[ks] + g * 2048));
 }
 
 // The 4 MFMAs of right tile x = g.
-__device__ __forceinline__ void mfma_4(const Frags& f, int g, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void mfma_4(const Frags& f, int g, f32x16 (&acc)[kCT][4]) {
 #pragma unroll
   for (int y = 0; y < 4; ++y) acc[g][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[g], f.b[y], acc[g][y], 0, 0, 0);
 }
@@ -252,19 +261,21 @@ __device__ __forceinline__ int64_t blk_off(int r, int c, int nkb) {
   return (static_cast<int64_t>(r >> 8) * nkb + (c >> 5)) * 8192 + (r & 255) * 32 + (c & 31);
 }
 
-// Mirrored store of a symmetric result: the wave's staged 128 x 128 bf16
-// sub-tile (row ii at eb + ii * 256, 16-byte unit u at position u ^ (ii & 15))
-// is written transposed: element (ii, jj) goes to row r0d + jj, column
-// c0d + ii.  Instruction s covers rows ii = R .. R + 7
+// Mirrored store of a symmetric result: a staged 128 x 128 bf16 region (row
+// ii at eb + ii * 256, 16-byte unit u at position u ^ (ii & 15)) is written
+// transposed: element (ii, jj) goes to row r0d + jj, column c0d + ii; each of
+// the region's two waves runs 16 of the 32 instructions, from s_begin.
+// Instruction s covers rows ii = R .. R + 7
 // (R = 8 (s / 2)) and 64 columns: 16-lane group g takes columns
 // C = 64 (s % 2) + 16 g .. + 15, lane i column C + i, which it assembles
 // from two transposed reads of 4 rows each.
 // dst is the matrix base; (r0, c0) the destination of staged element (0, 0)
 // after the transposition; the destination is blocked.
-__device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int r0d, int c0d, int nkb, int lane) {
+__device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int r0d, int c0d, int nkb, int lane,
+                                                 int s_begin) {
   const int g = lane >> 4, i = lane & 15;
 #pragma unroll 4
-  for (int s = 0; s < 32; ++s) {
+  for (int s = s_begin; s < s_begin + 16; ++s) {
     const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
     const int col = C + 4 * (i & 3);
     const int r0 = R + (i >> 2), r1 = r0 + 4;
@@ -292,7 +303,7 @@ struct UpdArgs {
 // SCALED: the launch carries 1 / ||M|| per matrix (the first Newton-Schulz
 // step of the fused path); otherwise the epilogue has no multiply.
 template <int MODE, int UPD, bool SCALED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
                     uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
                     float alpha, float beta, float diag, const float* __restrict__ inv, UpdArgs ua) {
@@ -372,7 +383,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   const uint32_t off_p = kc_lane_offset(ldp, wave, lane);
   const uint32_t off_q = kQKRows ? kr_lane_offset(ldq, wave, lane) : kc_lane_offset(ldq, wave, lane);
@@ -389,9 +400,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   };
   const FragAddr fadr = frag_addresses<kQKRows>(lane, wm, wn);
 
-  f32x16 acc[4][4];
+  f32x16 acc[kCT][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kCT; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
@@ -411,7 +422,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   __syncthreads();
   Frags f0, f1;
   load_frags<kQKRows>(fadr, lds, 0, f0);
-  // One half step: the 16 MFMAs of fragments fc in 4 groups (right tile
+  // One half step: the 8 MFMAs of fragments fc in kCT = 2 groups (right tile
   // x = g), each preceded by one DMA instruction of the refill and followed
   // by part g of the next sub-step's fragment reads into fn.  The DMA asm
   // statements fence the scheduler, so copies and reads stay spread over the
@@ -421,7 +432,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // best of six fixed patterns on MI355X).
   auto half = [&](const Frags& fc, Frags& fn, uint32_t rd_stage, int rd_ks, auto&& dma) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < kCT; ++g) {
       dma(g);
       mfma_4(fc, g, acc);
       load_frags_part<kQKRows>(fadr, rd_stage, rd_ks, g, fn);
@@ -444,46 +455,51 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   }
 
   // ---- epilogue, staged through LDS (free once every stage is consumed).
-  // Wave w owns the 128 x 128 sub-tile at rows i0 + 128 wm, columns
-  // j0 + 128 wn, staged at lds + 32 KB w: row ii at ii * 256 bytes, 16-byte
-  // unit u at position u ^ (ii & 15).  Global traffic is whole 256-byte rows:
-  //   mode 1: the A sub-tile is copied in by DMA and every lane combines it
+  // The tile is staged as four 128 x 128 regions (rows i0 + 128 wm, columns
+  // j0 + 128 (wn / 2)), region k at lds + 32 KB k: row ii at ii * 256 bytes,
+  // 16-byte unit u at position u ^ (ii & 15); the two waves of a region each
+  // write their 64 columns and then take half of its rows of global traffic,
+  // which is whole 256-byte rows:
+  //   mode 1: the A region is copied in by DMA and every lane combines it
   //   with its accumulators, b A + c (A A) (+ a on the diagonal), in place;
   //   modes 0/2: every lane rounds its accumulators into place;
-  //   the sub-tile is stored row by row, 16 bytes per lane;
+  //   the region is stored row by row, 16 bytes per lane;
   //   modes 0/1, off-diagonal tiles: it is also stored mirrored.
   const int frag_row = lane & 31, frag_half = lane >> 5;
-  const int i0w = i0 + wm * 128, j0w = j0 + wn * 128;
+  const int wh = wn & 1;  // which half of the region's columns, and of its passes
+  const int i0w = i0 + wm * 128, j0w = j0 + (wn >> 1) * 128;
   // X is inv_b times the stored X in the first step of the fused path
   const float xs = (inv != nullptr) ? inv[mat] : 1.0f;
 
   wait_vmem<0>();
   __syncthreads();
   uint16_t* O = out + mat * ((MODE == 2) ? nm : nn);
-  const uint32_t eb = lds + wave * 32768;
+  const uint32_t eb = lds + (2 * wm + (wn >> 1)) * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
 
   if constexpr (MODE == 1) {
-    // the A sub-tile, from the blocked layout (64-byte runs, 16 per 4 rows)
+    // the A region, from the blocked layout (64-byte runs, 16 per 4 rows),
+    // half of its rows by each of the region's two waves
     const char* ebase = reinterpret_cast<const char*>(in0 + mat * nn);
 #pragma unroll 4
-    for (int s = 0; s < 32; ++s) {
+    for (int s = 16 * wh; s < 16 * wh + 16; ++s) {
       const int row = 4 * s + (lane >> 4);
       const int u = (lane & 15) ^ (row & 15);
       load_lds16(ebase, static_cast<uint32_t>(blk_off(i0w + row, j0w + 8 * u, nkb) * 2), eb + 1024 * s);
     }
     wait_vmem<0>();
+    __syncthreads();
   }
-  // a I lands on the wave's sub-tile only if it straddles the diagonal
+  // a I lands on the region only if it straddles the diagonal
   const bool on_diag = MODE == 1 && i0w == j0w;
 #pragma unroll
   for (int y = 0; y < 4; ++y) {
     const int ii = y * 32 + frag_row;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < kCT; ++x) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const uint32_t a = st_addr(ii, 4 * x + g) + 8 * frag_half;
+        const uint32_t a = st_addr(ii, 8 * wh + 4 * x + g) + 8 * frag_half;
         float v[4] = {acc[x][y][4 * g + 0], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]};
         if constexpr (MODE == 0 && SCALED) {
           const float s2 = xs * xs;
@@ -496,7 +512,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         if constexpr (MODE == 1) {
           const u32x2 e = *(const lds_u32x2_t*)(uintptr_t)a;
           const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
-          const int jj0 = 32 * x + 8 * g + 4 * frag_half;  // column of v[0] within the sub-tile
+          // column of v[0] within the region
+          const int jj0 = kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float scaled = alpha * ev[q] + beta * v[q];
@@ -508,6 +525,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
     }
   }
+  // the region is complete once both of its waves have written
+  __syncthreads();
   if constexpr (UPD != 0) {
     // Fused update instead of storing X': W <- W - lr * (out_scale * X' + wd * W)
     // with X' rounded to bf16 as between steps; W is n x m, or m x n for a
@@ -560,7 +579,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     // its updates, so the read latency is paid once per batch, not per pass.
     constexpr int kBatch = 16;
     constexpr int kWords = (UPD == 1) ? 1 : 2;  // 16-byte words per 8 elements
-    for (int s0 = 0; s0 < 32; s0 += kBatch) {
+    for (int s0 = 16 * wh; s0 < 16 * wh + 16; s0 += kBatch) {
       u32x4 wbuf[kBatch][kWords];
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
@@ -624,7 +643,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // direct store: 4 rows of 256 bytes per instruction
   {
 #pragma unroll 4
-    for (int s = 0; s < 32; ++s) {
+    for (int s = 16 * wh; s < 16 * wh + 16; ++s) {
       const int row = 4 * s + (lane >> 4), u = lane & 15;
       const u32x4 v = *(const lds_u32x4_t*)(uintptr_t)st_addr(row, u);
       uint16_t* dst = kBlockedOut ? O + blk_off(i0w + row, j0w + 8 * u, nkb)
@@ -633,7 +652,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     }
   }
   if constexpr (MODE != 2) {
-    if (ti != tj) store_transposed(eb, O, j0w, i0w, nkb, lane);
+    if (ti != tj) store_transposed(eb, O, j0w, i0w, nkb, lane, 16 * wh);
   }
 }
 
