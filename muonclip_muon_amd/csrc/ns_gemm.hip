@@ -482,6 +482,51 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const uint32_t eb = lds + (2 * wm + (wn >> 1)) * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
 
+  // Fused update (UPD != 0): this wave's 16 passes of W are loaded before the
+  // accumulators are staged, so their latency overlaps the staging, for bf16
+  // W in the straight case (measured 6 % faster); float32 W (twice the
+  // registers) and transposed W (5 % slower loaded early) are loaded after
+  // the staging.  Pass s:
+  // straight W, lane takes staged row 4 s + lane / 16, unit lane % 16 (W row
+  // i0w + row, 8 columns); transposed W, lane takes staged column
+  // jj = C + lane % 16 and rows R .. R + 7 (two transposed reads), i.e. 8
+  // consecutive elements of W row j0w + jj.
+  constexpr int kEsz = (UPD == 2) ? 4 : 2;
+  constexpr int kWords = (UPD == 2) ? 2 : 1;  // 16-byte words per 8 elements
+  const int ug = lane >> 4, uil = lane & 15;
+  char* const Wb = UPD != 0 ? static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz : nullptr;
+  const int64_t wcols = ua.transposed ? ua.n : ua.m;
+  const bool wvec = wcols % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
+  auto pos = [&](int s, int64_t& wrow, int64_t& wcol, int& valid) {
+    if (!ua.transposed) {
+      const int row = 4 * s + ug;
+      wrow = i0w + row;
+      wcol = j0w + 8 * uil;
+      valid = wrow < ua.n ? min(8, ua.m - static_cast<int>(wcol)) : 0;
+    } else {
+      const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * ug;
+      wrow = j0w + C + uil;
+      wcol = i0w + R;
+      valid = wrow < ua.m ? min(8, ua.n - static_cast<int>(wcol)) : 0;
+    }
+  };
+  u32x4 wbuf[UPD != 0 ? 16 : 1][kWords];
+  auto load_w = [&]() {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      int64_t wrow, wcol;
+      int valid;
+      pos(16 * wh + e, wrow, wcol, valid);
+      if (wvec && valid == 8) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(Wb + (wrow * wcols + wcol) * kEsz);
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) wbuf[e][w] = p[w];
+      }
+    }
+  };
+  const bool w_early = UPD == 1 && !ua.transposed;
+  if (w_early) load_w();
+
   if constexpr (MODE == 1) {
     // the A region, from the blocked layout (64-byte runs, 16 per 4 rows),
     // half of its rows by each of the region's two waves
@@ -539,32 +584,12 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     // one W row per pass: 16-byte accesses, 256-byte row segments per 16
     // lanes (straight) or the mirrored-store pattern (transposed); runs that
     // leave the matrix (padding) or are misaligned go element by element.
-    constexpr int kEsz = (UPD == 1) ? 2 : 4;
-    char* Wb = static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz;
-    const int64_t wcols = ua.transposed ? ua.n : ua.m;
-    const bool vec = wcols % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
+    const bool vec = wvec;
     auto unpack8 = [](u32x4 v, float (&x)[8]) {
       x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
       x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
     };
-    // Pass s: straight W, lane takes staged row 4 s + lane / 16, unit
-    // lane % 16 (W row i0w + row, 8 columns); transposed W, lane takes staged
-    // column jj = C + lane % 16 and rows R .. R + 7 (two transposed reads),
-    // i.e. 8 consecutive elements of W row j0w + jj.
-    const int g = lane >> 4, il = lane & 15;
-    auto pos = [&](int s, int64_t& wrow, int64_t& wcol, int& valid) {
-      if (!ua.transposed) {
-        const int row = 4 * s + g;
-        wrow = i0w + row;
-        wcol = j0w + 8 * il;
-        valid = wrow < ua.n ? min(8, ua.m - static_cast<int>(wcol)) : 0;
-      } else {
-        const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
-        wrow = j0w + C + il;
-        wcol = i0w + R;
-        valid = wrow < ua.m ? min(8, ua.n - static_cast<int>(wcol)) : 0;
-      }
-    };
+    const int g = ug, il = uil;
     auto read_x = [&](int s, float (&x)[8]) {
       if (!ua.transposed) {
         unpack8(*(const lds_u32x4_t*)(uintptr_t)st_addr(4 * s + g, il), x);
@@ -580,23 +605,10 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         unpack8(u32x4{l2.x, l2.y, h2.x, h2.y}, x);
       }
     };
-    // Batches of 16 passes: all W loads of a batch are issued before any of
-    // its updates, so the read latency is paid once per batch, not per pass.
+    // the wave's 16 passes (bf16 W already in wbuf)
+    if (!w_early) load_w();
     constexpr int kBatch = 16;
-    constexpr int kWords = (UPD == 1) ? 1 : 2;  // 16-byte words per 8 elements
     for (int s0 = 16 * wh; s0 < 16 * wh + 16; s0 += kBatch) {
-      u32x4 wbuf[kBatch][kWords];
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        int64_t wrow, wcol;
-        int valid;
-        pos(s0 + e, wrow, wcol, valid);
-        if (vec && valid == 8) {
-          const u32x4* p = reinterpret_cast<const u32x4*>(Wb + (wrow * wcols + wcol) * kEsz);
-#pragma unroll
-          for (int w = 0; w < kWords; ++w) wbuf[e][w] = p[w];
-        }
-      }
 #pragma unroll
       for (int e = 0; e < kBatch; ++e) {
         int64_t wrow, wcol;
