@@ -465,8 +465,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // 16-byte unit u at position u ^ (ii & 15); the two waves of a region each
   // write their 64 columns and then take half of its rows of global traffic,
   // which is whole 256-byte rows:
-  //   mode 1: the A region is copied in by DMA and every lane combines it
-  //   with its accumulators, b A + c (A A) (+ a on the diagonal), in place;
+  //   mode 1: every lane combines its accumulators with the A values at
+  //   their positions, b A + c (A A) (+ a on the diagonal);
   //   modes 0/2: every lane rounds its accumulators into place;
   //   the region is stored row by row, 16 bytes per lane;
   //   modes 0/1, off-diagonal tiles: it is also stored mirrored.
@@ -527,18 +527,20 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const bool w_early = UPD == 1 && !ua.transposed;
   if (w_early) load_w();
 
+  // mode 1: the A values at this lane's accumulator positions (4 consecutive
+  // columns, 8 bytes of the blocked layout, per MFMA register group), loaded
+  // into registers before the staging so their latency overlaps it
+  u32x2 abuf[MODE == 1 ? 4 : 1][MODE == 1 ? kCT : 1][MODE == 1 ? 4 : 1];
   if constexpr (MODE == 1) {
-    // the A region, from the blocked layout (64-byte runs, 16 per 4 rows),
-    // half of its rows by each of the region's two waves
-    const char* ebase = reinterpret_cast<const char*>(in0 + mat * nn);
-#pragma unroll 4
-    for (int s = 16 * wh; s < 16 * wh + 16; ++s) {
-      const int row = 4 * s + (lane >> 4);
-      const int u = (lane & 15) ^ (row & 15);
-      load_lds16(ebase, static_cast<uint32_t>(blk_off(i0w + row, j0w + 8 * u, nkb) * 2), eb + 1024 * s);
-    }
-    wait_vmem<0>();
-    __syncthreads();
+    const uint16_t* Am = in0 + mat * nn;
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int x = 0; x < kCT; ++x)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          abuf[y][x][g] = *reinterpret_cast<const u32x2*>(
+              Am + blk_off(i0w + y * 32 + frag_row, j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, nkb));
   }
   // a I lands on the region only if it straddles the diagonal
   const bool on_diag = MODE == 1 && i0w == j0w;
@@ -560,7 +562,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           for (int q = 0; q < 4; ++q) v[q] *= xs;
         }
         if constexpr (MODE == 1) {
-          const u32x2 e = *(const lds_u32x2_t*)(uintptr_t)a;
+          const u32x2 e = abuf[y][x][g];
           const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
           // column of v[0] within the region
           const int jj0 = kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half;
