@@ -285,7 +285,8 @@ def run(args):
     del L32
 
     # Newton-Schulz alone on one chunk of 64 expert matrices (2048 x 7168):
-    # norm, pre-scale, 5 iterations and the bf16 output, no momentum or update.
+    # pre-scale (with the norm partials), 5 iterations and the bf16 output, no
+    # momentum or update.
     ns_name, _, ns_n, ns_rows, ns_cols = wl.groups[0]
     ns_cnt = min(64, ns_n)
     M_ns = wl.view(ns_name, wl.M, 0, ns_cnt)
@@ -301,7 +302,7 @@ def run(args):
     ns_only_ms = e0.elapsed_time(e1) / 3
     ns_only = {"shape": f"{ns_cnt} x {ns_rows} x {ns_cols}", "ms": round(ns_only_ms, 3),
                "tflops_nominal": round(ns_flops(ns_rows, ns_cols, steps_ns) * ns_cnt / (ns_only_ms * 1e-3) / 1e12, 1),
-               "note": "muon_ns_orthogonalize_batched alone: norm, pre-scale, 5 iterations, bf16 output; "
+               "note": "muon_ns_orthogonalize_batched alone: pre-scale with norm partials, 5 iterations, bf16 output; "
                        "nominal flops 4n^2m + 2n^3 per matrix per iteration"}
     del O_ns
 

@@ -114,7 +114,9 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  * not on the pages and are arguments here.  Pass out_scale =
  * sqrt(max(rows, cols)) * 0.2 for the pages' step.
  *
- * Arithmetic: the norm is accumulated in float32 (combined in double); each
+ * Arithmetic: the norm is accumulated in float32 (combined in double); X_0
+ * is held as bf16(M) and the factor 1 / (||M||_F + eps) is applied in float32
+ * by the first step's GEMMs (X X^T by its square, that step's X by it); each
  * step is evaluated as A = X X^T, B' = a_s I + b_s A + c_s A A, X <- B' X
  * (the same polynomial, with a_s X folded into the last product); X, A and B'
  * are held in bfloat16 between the GEMMs, which run on bf16 MFMA with float32

@@ -76,7 +76,7 @@ mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, c
   *g = mc::ns_geometry(batch, rows, cols);
   if (workspace_bytes < g->total) return MC_EWORKSPACE;
   const int64_t tiles = (g->n_pad / mc::kNsTile) * (g->m_pad / mc::kNsTile);
-  if (tiles * batch > kGridMax || batch > 65535 || g->sumsq_chunks > kGridMax) return MC_ESHAPE;
+  if (tiles * batch > kGridMax || batch > 65535) return MC_ESHAPE;
   if (gemm_events)
     for (int i = 0; i < 6 * steps; ++i)
       if (!gemm_events[i]) return MC_EINVAL;
@@ -148,12 +148,12 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   const bool m_bf16 = m_dtype == MC_BF16, o_bf16 = o_dtype == MC_BF16;
-  hipError_t e = mc::launch_ns_norm(M, m_bf16, m_batch_stride, g, eps, ws, s);
-  if (e != hipSuccess) return MC_EHIP;
-  e = mc::launch_ns_prescale(M, m_bf16, m_batch_stride, g, ws, s);
-  if (e != hipSuccess) return MC_EHIP;
+  // X_0 = bf16(M) unscaled plus 1 / (||M||_F + eps), applied by the first
+  // step's GEMM epilogues, as in the fused call
+  if (mc::launch_ns_prescale_unscaled(M, m_bf16, m_batch_stride, g, eps, ws, s) != hipSuccess) return MC_EHIP;
+  const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
   uint16_t* X = nullptr;
-  if (run_ns_steps(g, ws, steps, coeffs, nullptr, nullptr, s, gemm_events, &X) != hipSuccess) return MC_EHIP;
+  if (run_ns_steps(g, ws, steps, coeffs, inv, nullptr, s, gemm_events, &X) != hipSuccess) return MC_EHIP;
   return from_hip(mc::launch_ns_output(X, g, O, o_bf16, o_batch_stride, out_scale, s));
 }
 

@@ -28,8 +28,7 @@ struct NsGeometry {
   int64_t n, m;          // logical
   int64_t n_pad, m_pad;  // padded to kNsTile
   bool transposed;       // rows > cols: X = M^T
-  int64_t sumsq_chunks;    // partial sums per matrix of the stand-alone norm
-  int64_t prescale_tiles;  // 4096-element blocks per matrix of the fused pre-scale (norm partials)
+  int64_t prescale_tiles;  // 4096-element blocks per matrix of the pre-scale (norm partials)
   // byte offsets inside the workspace: X (two ping-pong copies, n_pad x m_pad),
   // A and B' (n_pad x n_pad), norm partials, 1/norm
   size_t off_x0, off_x1, off_a, off_b, off_partials, off_invnorm, total;
@@ -37,10 +36,11 @@ struct NsGeometry {
 constexpr int64_t kNsTile = 256;
 NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols);
 
-hipError_t launch_ns_norm(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
-                          float eps, char* ws, hipStream_t stream);
-hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride,
-                              const NsGeometry& g, char* ws, hipStream_t stream);
+// X_0 = bf16(M_b) unscaled at off_x0 (M only read, float32 or bf16, batch
+// matrices of rows x cols at m_batch_stride) and 1 / (||M_b||_F + eps) per
+// matrix at off_invnorm (applied by the first step's GEMMs).
+hipError_t launch_ns_prescale_unscaled(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
+                                       float eps, char* ws, hipStream_t stream);
 // Fused: M <- mu M + G in place (float32, batch matrices of rows x cols at
 // batch_stride), X_0 = bf16(M) unscaled at off_x0, and 1 / (||M||_F + eps)
 // per matrix at off_invnorm (to be applied by the first step's GEMMs).

@@ -1,16 +1,14 @@
 // Newton-Schulz input and output stages.
 //
-//   norm      ||M_b||_F per matrix: float32 partial sums of squares per chunk,
-//             then one block per matrix combines them in double in a fixed
-//             order (deterministic), giving inv_b = 1 / (||M_b||_F + eps).
-//   prescale  X_0 = bf16(inv_b * M_b), or of M_b^T when rows > cols, written
-//             into the zero-padded n_pad x m_pad workspace layout the GEMMs
-//             use.
-//   output    O_b = out_scale * X (or X^T), cast to the output dtype.
-//   momentum + pre-scale (the fused step): M_b <- mu M_b + G_b in place, and
-//             in the same pass X_0 = bf16(M_b) unscaled plus per-tile partial
-//             sums of squares of the new M_b; the 1 / (||M_b||_F + eps) is
-//             applied inside the first Newton-Schulz step's GEMM epilogues.
+//   pre-scale  X_0 = bf16(M_b), or of M_b^T when rows > cols, unscaled,
+//              written into the zero-padded n_pad x m_pad workspace layout
+//              the GEMMs use, plus float32 partial sums of squares per 4096-
+//              element block; one block per matrix then combines them in
+//              double in a fixed order (deterministic), giving
+//              inv_b = 1 / (||M_b||_F + eps), which the first Newton-Schulz
+//              step's GEMM epilogues apply.  In the fused step the same pass
+//              first does M_b <- mu M_b + G_b in place.
+//   output     O_b = out_scale * X (or X^T), cast to the output dtype.
 // Both move 8-element runs (16-byte vectors where the row length and the
 // alignment allow); the transposing variants go through a 64 x 64 LDS tile so
 // both the read and the write side are coalesced.
@@ -22,8 +20,7 @@ namespace mc {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int64_t kNormChunk = 32768;  // elements per partial sum
-constexpr int kT = 64;                 // transpose tile
+constexpr int kT = 64;  // transpose tile
 }  // namespace
 
 static inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
@@ -39,7 +36,6 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   g.m = g.transposed ? rows : cols;
   g.n_pad = round_up(g.n, kNsTile);
   g.m_pad = round_up(g.m, kNsTile);
-  g.sumsq_chunks = (rows * cols + kNormChunk - 1) / kNormChunk;
   g.prescale_tiles = (g.n_pad / kT) * (g.m_pad / kT);
   const size_t xb = static_cast<size_t>(batch) * g.n_pad * g.m_pad * 2;
   const size_t ab = static_cast<size_t>(batch) * g.n_pad * g.n_pad * 2;
@@ -48,7 +44,7 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   g.off_x1 = off; off = align256(off + xb);
   g.off_a = off; off = align256(off + ab);
   g.off_b = off; off = align256(off + ab);
-  const int64_t partials = g.sumsq_chunks > g.prescale_tiles ? g.sumsq_chunks : g.prescale_tiles;
+  const int64_t partials = g.prescale_tiles;
   g.off_partials = off; off = align256(off + static_cast<size_t>(batch * partials) * 4);
   g.off_invnorm = off; off = align256(off + static_cast<size_t>(batch) * 4);
   g.total = off;
@@ -56,12 +52,6 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
 }
 
 namespace {
-
-template <bool BF16>
-__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
-  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  else return static_cast<const float*>(p)[i];
-}
 
 __device__ __forceinline__ float block_sum(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -72,25 +62,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   if (threadIdx.x == 0)
     for (int i = 0; i < kThreads / 64; ++i) s += red[i];
   return s;
-}
-
-// grid (chunks, batch)
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void sumsq_kernel(const void* __restrict__ M,
-                                                        int64_t batch_stride, int64_t count,
-                                                        int64_t chunks, float* __restrict__ partials) {
-  __shared__ float red[kThreads / 64];
-  const int64_t b = blockIdx.y;
-  const char* base = static_cast<const char*>(M) + static_cast<size_t>(b * batch_stride) * (BF16 ? 2 : 4);
-  const int64_t begin = blockIdx.x * kNormChunk;
-  const int64_t end = min(count, begin + kNormChunk);
-  float acc = 0.f;
-  for (int64_t i = begin + threadIdx.x; i < end; i += kThreads) {
-    const float x = load_elem<BF16>(base, i);
-    acc = fmaf(x, x, acc);
-  }
-  const float s = block_sum(acc, red);
-  if (threadIdx.x == 0) partials[b * chunks + blockIdx.x] = s;
 }
 
 // grid (batch): inv_b = 1 / (sqrt(sum of partials) + eps), combined in double
@@ -110,86 +81,36 @@ __global__ __launch_bounds__(kThreads) void invnorm_kernel(const float* __restri
   if (threadIdx.x == 0) invnorm[b] = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(eps)));
 }
 
-// Pre-scale.  M_b is R x C (rows x cols); it is scaled by
-// inv_b = 1 / (||M_b||_F + eps), rounded once to bf16 and written zero-padded
-// either as it is into S (R_pad x C_pad; rows <= cols: X_0 = M) or transposed
-// into T (C_pad x R_pad; rows > cols: X_0 = M^T); the other pointer is null.
-// grid (C_pad / 64, R_pad / 64, batch); each block reads one 64 x 64 tile in
-// 8-element runs (vector loads when VEC) and writes it straight from
-// registers or transposed through LDS.
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void prescale_kernel(const void* __restrict__ M, int64_t batch_stride,
-                                                           int64_t R, int64_t C, int64_t R_pad,
-                                                           int64_t C_pad, const float* __restrict__ invnorm,
-                                                           uint16_t* __restrict__ S,
-                                                           uint16_t* __restrict__ T) {
-  __shared__ float tile[kT][kT + 1];
-  const int64_t b = blockIdx.z;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kT, r0 = static_cast<int64_t>(blockIdx.y) * kT;
-  const float inv = invnorm[b];
-  const char* base = static_cast<const char*>(M) + static_cast<size_t>(b * batch_stride) * (BF16 ? 2 : 4);
-  uint16_t* sb = S + static_cast<size_t>(b) * R_pad * C_pad;
-  uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
-  const int q = threadIdx.x & 7;  // 8-element run within a row
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int rr = pass * 32 + (threadIdx.x >> 3);
-    const int64_t r = r0 + rr, c = c0 + 8 * q;
-    float x[8];
-    if constexpr (VEC) {
-      // C % 8 == 0: a run is wholly inside or wholly outside the matrix
-      if (r < R && c < C) {
-        if constexpr (BF16) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(base + (r * C + c) * 2);
-          x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-          x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-        } else {
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(base + (r * C + c) * 4);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(base + (r * C + c + 4) * 4);
-          x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-          x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] *= inv;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (r < R && c + e < C) ? load_elem<BF16>(base, r * C + c + e) * inv : 0.f;
-    }
-    if (S != nullptr) {
-      const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                       pack_bf16x2(x[6], x[7])};
-      *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = o;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
-    }
-  }
-  if (S != nullptr) return;
-  __syncthreads();
-  // T[c0 + cc][r0 + 8 q' .. + 7] = tile[8 q' ..][cc]
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int cc = pass * 32 + (threadIdx.x >> 3);
-    const int rq = 8 * q;
-    const u32x4 o = {pack_bf16x2(tile[rq + 0][cc], tile[rq + 1][cc]), pack_bf16x2(tile[rq + 2][cc], tile[rq + 3][cc]),
-                     pack_bf16x2(tile[rq + 4][cc], tile[rq + 5][cc]), pack_bf16x2(tile[rq + 6][cc], tile[rq + 7][cc])};
-    *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = o;
+// Fused momentum and pre-scale (SRC = 0).  M_b, G_b are R x C float32 (rows
+// x cols); M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the
+// stand-alone momentum), and the new M_b is written unscaled as bf16 into S
+// (R_pad x C_pad) or transposed into T (C_pad x R_pad), zero-padded, as in
+// prescale_kernel.  Each block also writes the float32 sum of squares of its
+// tile's new M values to partials[b * tiles + tile].  SRC = 1 (float32 M) or
+// 2 (bf16 M): the same without momentum (G unused, M only read), the
+// unscaled pre-scale of the stand-alone Newton-Schulz call.
+// grid (C_pad / 64, R_pad / 64, batch).
+template <int SRC>
+__device__ __forceinline__ void load8_src(const void* M, int64_t idx, float (&x)[8]) {
+  if constexpr (SRC == 2) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(M) + idx));
+    x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
+    x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(M) + idx);
+    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
 }
+template <int SRC>
+__device__ __forceinline__ float load1_src(const void* M, int64_t idx) {
+  if constexpr (SRC == 2) return bf16_to_f32(static_cast<const uint16_t*>(M)[idx]);
+  else return static_cast<const float*>(M)[idx];
+}
 
-// Fused momentum and pre-scale.  M_b, G_b are R x C float32 (rows x cols);
-// M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the stand-alone
-// momentum), and the new M_b is written unscaled as bf16 into S (R_pad x
-// C_pad) or transposed into T (C_pad x R_pad), zero-padded, as in
-// prescale_kernel.  Each block also writes the float32 sum of squares of its
-// tile's new M values to partials[b * tiles + tile].
-// grid (C_pad / 64, R_pad / 64, batch).
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __restrict__ M,
+template <bool VEC, int SRC>
+__global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __restrict__ Mv,
                                                                     const float* __restrict__ G,
                                                                     int64_t batch_stride, float mu, int64_t R,
                                                                     int64_t C, int64_t R_pad, int64_t C_pad,
@@ -200,8 +121,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
   __shared__ float red[kThreads / 64];
   const int64_t b = blockIdx.z;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kT, r0 = static_cast<int64_t>(blockIdx.y) * kT;
-  float* mb = M + b * batch_stride;
-  const float* gb = G + b * batch_stride;
+  float* mb = static_cast<float*>(Mv) + (SRC == 2 ? 0 : b * batch_stride);
+  const void* msrc = SRC == 2 ? static_cast<const void*>(static_cast<const uint16_t*>(Mv) + b * batch_stride)
+                              : static_cast<const void*>(mb);
+  const float* gb = SRC == 0 ? G + b * batch_stride : nullptr;
   uint16_t* sb = S + static_cast<size_t>(b) * R_pad * C_pad;
   uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
   const int q = threadIdx.x & 7;
@@ -214,22 +137,26 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
     if constexpr (VEC) {
       // C % 8 == 0: a run is wholly inside or wholly outside the matrix
       if (r < R && c < C) {
-        f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
-        const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
-        f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
-        const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
-        m0.x = momentum_op(m0.x, g0.x, mu);
-        m0.y = momentum_op(m0.y, g0.y, mu);
-        m0.z = momentum_op(m0.z, g0.z, mu);
-        m0.w = momentum_op(m0.w, g0.w, mu);
-        m1.x = momentum_op(m1.x, g1.x, mu);
-        m1.y = momentum_op(m1.y, g1.y, mu);
-        m1.z = momentum_op(m1.z, g1.z, mu);
-        m1.w = momentum_op(m1.w, g1.w, mu);
-        __builtin_nontemporal_store(m0, mp);
-        __builtin_nontemporal_store(m1, mp + 1);
-        x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
-        x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
+        if constexpr (SRC != 0) {
+          load8_src<SRC>(msrc, r * C + c, x);
+        } else {
+          f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
+          const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
+          f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
+          const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
+          m0.x = momentum_op(m0.x, g0.x, mu);
+          m0.y = momentum_op(m0.y, g0.y, mu);
+          m0.z = momentum_op(m0.z, g0.z, mu);
+          m0.w = momentum_op(m0.w, g0.w, mu);
+          m1.x = momentum_op(m1.x, g1.x, mu);
+          m1.y = momentum_op(m1.y, g1.y, mu);
+          m1.z = momentum_op(m1.z, g1.z, mu);
+          m1.w = momentum_op(m1.w, g1.w, mu);
+          __builtin_nontemporal_store(m0, mp);
+          __builtin_nontemporal_store(m1, mp + 1);
+          x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
+          x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -239,9 +166,13 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
       for (int e = 0; e < 8; ++e) {
         x[e] = 0.f;
         if (r < R && c + e < C) {
-          const float m = momentum_op(mb[r * C + c + e], gb[r * C + c + e], mu);
-          mb[r * C + c + e] = m;
-          x[e] = m;
+          if constexpr (SRC != 0) {
+            x[e] = load1_src<SRC>(msrc, r * C + c + e);
+          } else {
+            const float m = momentum_op(mb[r * C + c + e], gb[r * C + c + e], mu);
+            mb[r * C + c + e] = m;
+            x[e] = m;
+          }
         }
       }
     }
@@ -275,15 +206,19 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(float* __re
 // columns (one column panel of X), so every row segment it reads is 1 KB of
 // M and of G and every X_0 segment it writes is 512 contiguous bytes.
 // grid (C_pad / 256, R_pad / 16, batch); 4096 elements per block, like the
-// 64 x 64 tiles, so the partial-sum count per matrix is the same.
+// 64 x 64 tiles, so the partial-sum count per matrix is the same.  SRC as in
+// momentum_prescale_kernel.
+template <int SRC>
 __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
-    float* __restrict__ M, const float* __restrict__ G, int64_t batch_stride, float mu, int64_t R, int64_t C,
+    void* __restrict__ Mv, const float* __restrict__ G, int64_t batch_stride, float mu, int64_t R, int64_t C,
     int64_t R_pad, int64_t C_pad, uint16_t* __restrict__ X0, float* __restrict__ partials) {
   __shared__ float red[kThreads / 64];
   const int64_t b = blockIdx.z;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + 8 * (threadIdx.x & 31);
-  float* mb = M + b * batch_stride;
-  const float* gb = G + b * batch_stride;
+  float* mb = static_cast<float*>(Mv) + (SRC == 2 ? 0 : b * batch_stride);
+  const void* msrc = SRC == 2 ? static_cast<const void*>(static_cast<const uint16_t*>(Mv) + b * batch_stride)
+                              : static_cast<const void*>(mb);
+  const float* gb = SRC == 0 ? G + b * batch_stride : nullptr;
   uint16_t* xb = X0 + static_cast<size_t>(b) * R_pad * C_pad;
   float ss = 0.f;
 #pragma unroll
@@ -291,22 +226,26 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     const int64_t r = static_cast<int64_t>(blockIdx.y) * 16 + pass * 8 + (threadIdx.x >> 5);
     float x[8];
     if (r < R && c < C) {  // C % 8 == 0: a run is wholly inside or outside
-      f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
-      const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
-      f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
-      const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
-      m0.x = momentum_op(m0.x, g0.x, mu);
-      m0.y = momentum_op(m0.y, g0.y, mu);
-      m0.z = momentum_op(m0.z, g0.z, mu);
-      m0.w = momentum_op(m0.w, g0.w, mu);
-      m1.x = momentum_op(m1.x, g1.x, mu);
-      m1.y = momentum_op(m1.y, g1.y, mu);
-      m1.z = momentum_op(m1.z, g1.z, mu);
-      m1.w = momentum_op(m1.w, g1.w, mu);
-      __builtin_nontemporal_store(m0, mp);
-      __builtin_nontemporal_store(m1, mp + 1);
-      x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
-      x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
+      if constexpr (SRC != 0) {
+        load8_src<SRC>(msrc, r * C + c, x);
+      } else {
+        f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
+        const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
+        f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
+        const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
+        m0.x = momentum_op(m0.x, g0.x, mu);
+        m0.y = momentum_op(m0.y, g0.y, mu);
+        m0.z = momentum_op(m0.z, g0.z, mu);
+        m0.w = momentum_op(m0.w, g0.w, mu);
+        m1.x = momentum_op(m1.x, g1.x, mu);
+        m1.y = momentum_op(m1.y, g1.y, mu);
+        m1.z = momentum_op(m1.z, g1.z, mu);
+        m1.w = momentum_op(m1.w, g1.w, mu);
+        __builtin_nontemporal_store(m0, mp);
+        __builtin_nontemporal_store(m1, mp + 1);
+        x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
+        x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -430,53 +369,11 @@ __global__ __launch_bounds__(kThreads) void output_t_kernel(const uint16_t* __re
 
 }  // namespace
 
-hipError_t launch_ns_norm(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
-                          float eps, char* ws, hipStream_t stream) {
-  float* partials = reinterpret_cast<float*>(ws + g.off_partials);
-  float* invnorm = reinterpret_cast<float*>(ws + g.off_invnorm);
-  dim3 grid(static_cast<unsigned>(g.sumsq_chunks), static_cast<unsigned>(g.batch));
-  if (m_bf16)
-    hipLaunchKernelGGL(sumsq_kernel<true>, grid, dim3(kThreads), 0, stream, M, m_batch_stride,
-                       g.rows * g.cols, g.sumsq_chunks, partials);
-  else
-    hipLaunchKernelGGL(sumsq_kernel<false>, grid, dim3(kThreads), 0, stream, M, m_batch_stride,
-                       g.rows * g.cols, g.sumsq_chunks, partials);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(invnorm_kernel, dim3(static_cast<unsigned>(g.batch)), dim3(kThreads), 0, stream,
-                     partials, g.sumsq_chunks, eps, invnorm);
-  return hipGetLastError();
-}
-
-hipError_t launch_ns_prescale(const void* M, bool m_bf16, int64_t m_batch_stride,
-                              const NsGeometry& g, char* ws, hipStream_t stream) {
-  const float* invnorm = reinterpret_cast<const float*>(ws + g.off_invnorm);
-  uint16_t* X0 = reinterpret_cast<uint16_t*>(ws + g.off_x0);
-  // M is R x C = rows x cols; X_0 = M (straight) or M^T (transposed)
-  const int64_t R = g.rows, C = g.cols;
-  const int64_t R_pad = g.transposed ? g.m_pad : g.n_pad, C_pad = g.transposed ? g.n_pad : g.m_pad;
-  uint16_t* S = g.transposed ? nullptr : X0;
-  uint16_t* T = g.transposed ? X0 : nullptr;
-  const size_t esz = m_bf16 ? 2 : 4;
-  const bool vec = C % 8 == 0 && (g.batch == 1 || m_batch_stride % 8 == 0) &&
-                   reinterpret_cast<uintptr_t>(M) % (8 * esz) == 0;
-  dim3 grid(static_cast<unsigned>(C_pad / kT), static_cast<unsigned>(R_pad / kT), static_cast<unsigned>(g.batch));
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, m_batch_stride, R, C, R_pad, C_pad, invnorm,
-                       S, T);
-  };
-  if (m_bf16) {
-    if (vec) go(prescale_kernel<true, true>);
-    else go(prescale_kernel<true, false>);
-  } else {
-    if (vec) go(prescale_kernel<false, true>);
-    else go(prescale_kernel<false, false>);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
-                                    const NsGeometry& g, float eps, char* ws, hipStream_t stream) {
+namespace {
+// SRC 0: momentum (M float32, G); 1 / 2: float32 / bf16 M alone
+template <int SRC>
+hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_stride, float mu, const NsGeometry& g,
+                                    float eps, char* ws, hipStream_t stream) {
   float* partials = reinterpret_cast<float*>(ws + g.off_partials);
   float* invnorm = reinterpret_cast<float*>(ws + g.off_invnorm);
   uint16_t* X0 = reinterpret_cast<uint16_t*>(ws + g.off_x0);
@@ -484,25 +381,40 @@ hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stri
   const int64_t R_pad = g.transposed ? g.m_pad : g.n_pad, C_pad = g.transposed ? g.n_pad : g.m_pad;
   uint16_t* S = g.transposed ? nullptr : X0;
   uint16_t* T = g.transposed ? X0 : nullptr;
+  const size_t align = SRC == 2 ? 16 : 32;  // one 8-element run
   const bool vec = C % 8 == 0 && (g.batch == 1 || batch_stride % 8 == 0) &&
-                   reinterpret_cast<uintptr_t>(M) % 32 == 0 && reinterpret_cast<uintptr_t>(G) % 32 == 0;
+                   reinterpret_cast<uintptr_t>(M) % align == 0 &&
+                   (SRC != 0 || reinterpret_cast<uintptr_t>(G) % 32 == 0);
   dim3 grid(static_cast<unsigned>(C_pad / kT), static_cast<unsigned>(R_pad / kT), static_cast<unsigned>(g.batch));
   if (vec && S != nullptr)
-    hipLaunchKernelGGL(momentum_prescale_rows_kernel,
+    hipLaunchKernelGGL(momentum_prescale_rows_kernel<SRC>,
                        dim3(static_cast<unsigned>(C_pad / 256), static_cast<unsigned>(R_pad / 16),
                             static_cast<unsigned>(g.batch)),
                        dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C, R_pad, C_pad, S, partials);
   else if (vec)
-    hipLaunchKernelGGL(momentum_prescale_kernel<true>, grid, dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C,
-                       R_pad, C_pad, S, T, partials);
+    hipLaunchKernelGGL((momentum_prescale_kernel<true, SRC>), grid, dim3(kThreads), 0, stream, M, G, batch_stride,
+                       mu, R, C, R_pad, C_pad, S, T, partials);
   else
-    hipLaunchKernelGGL(momentum_prescale_kernel<false>, grid, dim3(kThreads), 0, stream, M, G, batch_stride, mu, R,
-                       C, R_pad, C_pad, S, T, partials);
+    hipLaunchKernelGGL((momentum_prescale_kernel<false, SRC>), grid, dim3(kThreads), 0, stream, M, G,
+                       batch_stride, mu, R, C, R_pad, C_pad, S, T, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(invnorm_kernel, dim3(static_cast<unsigned>(g.batch)), dim3(kThreads), 0, stream, partials,
                      g.prescale_tiles, eps, invnorm);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
+                                    const NsGeometry& g, float eps, char* ws, hipStream_t stream) {
+  return launch_prescale_unscaled<0>(M, G, batch_stride, mu, g, eps, ws, stream);
+}
+
+hipError_t launch_ns_prescale_unscaled(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
+                                       float eps, char* ws, hipStream_t stream) {
+  void* Mv = const_cast<void*>(M);  // read only for SRC 1 and 2
+  if (m_bf16) return launch_prescale_unscaled<2>(Mv, nullptr, m_batch_stride, 0.f, g, eps, ws, stream);
+  return launch_prescale_unscaled<1>(Mv, nullptr, m_batch_stride, 0.f, g, eps, ws, stream);
 }
 
 hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
