@@ -81,15 +81,8 @@ __global__ __launch_bounds__(kThreads) void invnorm_kernel(const float* __restri
   if (threadIdx.x == 0) invnorm[b] = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(eps)));
 }
 
-// Fused momentum and pre-scale (SRC = 0).  M_b, G_b are R x C float32 (rows
-// x cols); M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the
-// stand-alone momentum), and the new M_b is written unscaled as bf16 into S
-// (R_pad x C_pad) or transposed into T (C_pad x R_pad), zero-padded, as in
-// prescale_kernel.  Each block also writes the float32 sum of squares of its
-// tile's new M values to partials[b * tiles + tile].  SRC = 1 (float32 M) or
-// 2 (bf16 M): the same without momentum (G unused, M only read), the
-// unscaled pre-scale of the stand-alone Newton-Schulz call.
-// grid (C_pad / 64, R_pad / 64, batch).
+// 8 consecutive elements of M (float32 for SRC 1, bf16 for SRC 2) at idx,
+// and one element
 template <int SRC>
 __device__ __forceinline__ void load8_src(const void* M, int64_t idx, float (&x)[8]) {
   if constexpr (SRC == 2) {
@@ -109,6 +102,18 @@ __device__ __forceinline__ float load1_src(const void* M, int64_t idx) {
   else return static_cast<const float*>(M)[idx];
 }
 
+// Fused momentum and pre-scale (SRC = 0).  M_b, G_b are R x C float32 (rows
+// x cols); M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the
+// stand-alone momentum), and the new M_b is written unscaled as bf16 into S
+// (R_pad x C_pad; rows <= cols: X_0 = M) or transposed into T (C_pad x
+// R_pad; rows > cols: X_0 = M^T), zero-padded; the other pointer is null.
+// Each block reads one 64 x 64 tile in 8-element runs (vector loads when
+// VEC) and writes it straight from registers or transposed through LDS; it
+// also writes the float32 sum of squares of its tile's new M values to
+// partials[b * tiles + tile].  SRC = 1 (float32 M) or 2 (bf16 M): the same
+// without momentum (G unused, M only read), the unscaled pre-scale of the
+// stand-alone Newton-Schulz call.
+// grid (C_pad / 64, R_pad / 64, batch).
 template <bool VEC, int SRC>
 __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __restrict__ Mv,
                                                                     const float* __restrict__ G,
