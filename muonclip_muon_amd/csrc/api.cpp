@@ -152,9 +152,10 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   // step's GEMM epilogues, as in the fused call
   if (mc::launch_ns_prescale_unscaled(M, m_bf16, m_batch_stride, g, eps, ws, s) != hipSuccess) return MC_EHIP;
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
+  // the last step's X' = B' X writes O = out_scale * X' (transposed back)
+  mc::NsUpdate out{O, o_bf16, o_batch_stride, out_scale, 0.f, 0.f, true};
   uint16_t* X = nullptr;
-  if (run_ns_steps(g, ws, steps, coeffs, inv, nullptr, s, gemm_events, &X) != hipSuccess) return MC_EHIP;
-  return from_hip(mc::launch_ns_output(X, g, O, o_bf16, o_batch_stride, out_scale, s));
+  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &out, s, gemm_events, &X));
 }
 
 mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, void* W, int w_dtype,
@@ -182,7 +183,7 @@ mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, 
   char* ws = static_cast<char*>(workspace);
   if (mc::launch_momentum_prescale(M, G, batch_stride, mu, g, eps, ws, s) != hipSuccess) return MC_EHIP;
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
-  mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, out_scale, lr, weight_decay};
+  mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, out_scale, lr, weight_decay, false};
   uint16_t* X = nullptr;
   return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events, &X));
 }

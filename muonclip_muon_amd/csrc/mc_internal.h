@@ -48,12 +48,15 @@ hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stri
                                     const NsGeometry& g, float eps, char* ws, hipStream_t stream);
 // In-place update applied by the last step's X' = B' X instead of storing X':
 // W_b <- W_b - lr * (out_scale * X'_b (transposed back for a tall matrix) +
-// wd * W_b), W_b rows x cols at W + b * w_stride, float32 or bf16.
+// wd * W_b), W_b rows x cols at W + b * w_stride, float32 or bf16.  With
+// output set, W_b <- out_scale * X'_b instead (W is then the output O, only
+// written; lr and wd unused).
 struct NsUpdate {
   void* W;
   bool w_bf16;
   int64_t w_stride;
   float out_scale, lr, wd;
+  bool output;
 };
 // One GEMM of the polynomial step, on the whole batch:
 //   mode 0: A = X X^T                          (in0: X, out: A)
@@ -64,9 +67,6 @@ struct NsUpdate {
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
                           uint16_t* out, float alpha, float beta, float diag, const float* inv,
                           const NsUpdate* upd, hipStream_t stream);
-// O_b = out_scale * X_b (rows <= cols) or X_b^T (rows > cols), rows x cols.
-hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
-                            int64_t o_batch_stride, float out_scale, hipStream_t stream);
 
 // ---------------------------------------------------------------- max logit
 hipError_t launch_maxlogit_init(float* smax, int64_t H, hipStream_t stream);

@@ -300,7 +300,9 @@ struct UpdArgs {
   float out_scale, lr, wd;
 };
 
-// UPD: 0 = store X' (or A, B'); 1 = update bf16 W; 2 = update float32 W.
+// UPD: 0 = store X' (or A, B'); 1 = update bf16 W; 2 = update float32 W;
+// 3 / 4 = write O = out_scale * X' (transposed back for a matrix iterated on
+// as its transpose) to a bf16 / float32 W, which is then the output.
 // SCALED: the launch carries 1 / ||M|| per matrix (the first Newton-Schulz
 // step of the fused path); otherwise the epilogue has no multiply.
 template <int MODE, int UPD, bool SCALED>
@@ -491,8 +493,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // i0w + row, 8 columns); transposed W, lane takes staged column
   // jj = C + lane % 16 and rows R .. R + 7 (two transposed reads), i.e. 8
   // consecutive elements of W row j0w + jj.
-  constexpr int kEsz = (UPD == 2) ? 4 : 2;
-  constexpr int kWords = (UPD == 2) ? 2 : 1;  // 16-byte words per 8 elements
+  constexpr bool kReadW = UPD == 1 || UPD == 2;  // 3 / 4 only write
+  constexpr int kEsz = (UPD == 2 || UPD == 4) ? 4 : 2;
+  constexpr int kWords = (UPD == 2 || UPD == 4) ? 2 : 1;  // 16-byte words per 8 elements
   const int ug = lane >> 4, uil = lane & 15;
   char* const Wb = UPD != 0 ? static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz : nullptr;
   const int64_t wcols = ua.transposed ? ua.n : ua.m;
@@ -510,7 +513,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       valid = wrow < ua.m ? min(8, ua.n - static_cast<int>(wcol)) : 0;
     }
   };
-  u32x4 wbuf[UPD != 0 ? 16 : 1][kWords];
+  u32x4 wbuf[kReadW ? 16 : 1][kWords];
   auto load_w = [&]() {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -581,8 +584,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   __syncthreads();
   if constexpr (UPD != 0) {
     // Fused update instead of storing X': W <- W - lr * (out_scale * X' + wd * W)
-    // with X' rounded to bf16 as between steps; W is n x m, or m x n for a
-    // matrix iterated on as its transpose.  Each lane handles 8 elements of
+    // (UPD 1 / 2), or the output W = out_scale * X' (UPD 3 / 4), with X'
+    // rounded to bf16 as between steps; W is n x m, or m x n for a matrix
+    // iterated on as its transpose.  Each lane handles 8 elements of
     // one W row per pass: 16-byte accesses, 256-byte row segments per 16
     // lanes (straight) or the mirrored-store pattern (transposed); runs that
     // leave the matrix (padding) or are misaligned go element by element.
@@ -608,7 +612,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
     };
     // the wave's 16 passes (bf16 W already in wbuf)
-    if (!w_early) load_w();
+    if (kReadW && !w_early) load_w();
     constexpr int kBatch = 16;
     for (int s0 = 16 * wh; s0 < 16 * wh + 16; s0 += kBatch) {
 #pragma unroll
@@ -626,7 +630,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         const int64_t idx = wrow * wcols + wcol;
         if (vec && valid == 8) {
           u32x4* p = reinterpret_cast<u32x4*>(Wb + idx * kEsz);
-          if constexpr (UPD == 1) {
+          if constexpr (UPD == 3) {
+            p[0] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                         pack_bf16x2(o[6], o[7])};
+          } else if constexpr (UPD == 4) {
+            p[0] = __builtin_bit_cast(u32x4, f32x4{o[0], o[1], o[2], o[3]});
+            p[1] = __builtin_bit_cast(u32x4, f32x4{o[4], o[5], o[6], o[7]});
+          } else if constexpr (UPD == 1) {
             u32x4 w = wbuf[e][0];
             w.x = pack_bf16x2(update_op(bf16_lo(w.x), o[0], ua.lr, ua.wd), update_op(bf16_hi(w.x), o[1], ua.lr, ua.wd));
             w.y = pack_bf16x2(update_op(bf16_lo(w.y), o[2], ua.lr, ua.wd), update_op(bf16_hi(w.y), o[3], ua.lr, ua.wd));
@@ -646,7 +656,11 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           }
         } else {
           for (int q = 0; q < valid; ++q) {
-            if constexpr (UPD == 1) {
+            if constexpr (UPD == 3) {
+              reinterpret_cast<uint16_t*>(Wb)[idx + q] = f32_to_bf16(o[q]);
+            } else if constexpr (UPD == 4) {
+              reinterpret_cast<float*>(Wb)[idx + q] = o[q];
+            } else if constexpr (UPD == 1) {
               uint16_t* pw = reinterpret_cast<uint16_t*>(Wb) + idx + q;
               *pw = f32_to_bf16(update_op(bf16_to_f32(*pw), o[q], ua.lr, ua.wd));
             } else {
@@ -706,6 +720,8 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
   if (mode == 0) sc ? go(ns_gemm_kernel<0, 0, true>) : go(ns_gemm_kernel<0, 0, false>);
   else if (mode == 1) go(ns_gemm_kernel<1, 0, false>);
   else if (upd == nullptr) sc ? go(ns_gemm_kernel<2, 0, true>) : go(ns_gemm_kernel<2, 0, false>);
+  else if (upd->output && upd->w_bf16) sc ? go(ns_gemm_kernel<2, 3, true>) : go(ns_gemm_kernel<2, 3, false>);
+  else if (upd->output) sc ? go(ns_gemm_kernel<2, 4, true>) : go(ns_gemm_kernel<2, 4, false>);
   else if (upd->w_bf16) sc ? go(ns_gemm_kernel<2, 1, true>) : go(ns_gemm_kernel<2, 1, false>);
   else sc ? go(ns_gemm_kernel<2, 2, true>) : go(ns_gemm_kernel<2, 2, false>);
   return hipGetLastError();

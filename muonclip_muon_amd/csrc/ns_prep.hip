@@ -1,4 +1,5 @@
-// Newton-Schulz input and output stages.
+// Newton-Schulz input stage: the workspace geometry, the pre-scale and the
+// norm.
 //
 //   pre-scale  X_0 = bf16(M_b), or of M_b^T when rows > cols, unscaled,
 //              written into the zero-padded n_pad x m_pad workspace layout
@@ -8,10 +9,10 @@
 //              inv_b = 1 / (||M_b||_F + eps), which the first Newton-Schulz
 //              step's GEMM epilogues apply.  In the fused step the same pass
 //              first does M_b <- mu M_b + G_b in place.
-//   output     O_b = out_scale * X (or X^T), cast to the output dtype.
-// Both move 8-element runs (16-byte vectors where the row length and the
-// alignment allow); the transposing variants go through a 64 x 64 LDS tile so
-// both the read and the write side are coalesced.
+// The pre-scale moves 8-element runs (16-byte vectors where the row length
+// and the alignment allow); the transposing variant goes through a 64 x 64
+// LDS tile so both the read and the write side are coalesced.  The output
+// O = out_scale * X (or X^T) is written by the last step's GEMM epilogue.
 
 #include "mc_device.h"
 #include "mc_internal.h"
@@ -265,116 +266,6 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
   if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = block_ss;
 }
 
-template <bool OBF16>
-__device__ __forceinline__ void store_out(void* O, int64_t idx, float v) {
-  if constexpr (OBF16) static_cast<uint16_t*>(O)[idx] = f32_to_bf16(v);
-  else static_cast<float*>(O)[idx] = v;
-}
-
-// Output, element by element: O[r][c] = s * X[r][c] (X in the panel layout).
-// grid (ceil(R * C / 256), batch)
-template <bool OBF16>
-__global__ __launch_bounds__(kThreads) void output_kernel(const uint16_t* __restrict__ src, int64_t R,
-                                                         int64_t C, int64_t n_pad, int64_t src_stride,
-                                                         void* __restrict__ O, int64_t o_stride, float s) {
-  const int64_t b = blockIdx.y;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (e >= R * C) return;
-  const int64_t r = e / C, c = e % C;
-  const float x = bf16_to_f32(src[b * src_stride + x_off(r, c, n_pad)]);
-  char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride) * (OBF16 ? 2 : 4);
-  store_out<OBF16>(ob, e, x * s);
-}
-
-// Output, 8 elements per thread (C % 8 == 0 and 16-byte aligned rows of O).
-// grid (ceil(R * C / 8 / 256), batch)
-template <bool OBF16>
-__global__ __launch_bounds__(kThreads) void output_vec_kernel(const uint16_t* __restrict__ src, int64_t R,
-                                                             int64_t C, int64_t n_pad, int64_t src_stride,
-                                                             void* __restrict__ O, int64_t o_stride,
-                                                             float s) {
-  const int64_t b = blockIdx.y;
-  const int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t per_row = C / 8;
-  if (v >= R * per_row) return;
-  const int64_t r = v / per_row, c = (v % per_row) * 8;
-  const u32x4 x = *reinterpret_cast<const u32x4*>(src + b * src_stride + x_off(r, c, n_pad));
-  const float y[8] = {bf16_lo(x.x) * s, bf16_hi(x.x) * s, bf16_lo(x.y) * s, bf16_hi(x.y) * s,
-                      bf16_lo(x.z) * s, bf16_hi(x.z) * s, bf16_lo(x.w) * s, bf16_hi(x.w) * s};
-  char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride + r * C + c) * (OBF16 ? 2 : 4);
-  if constexpr (OBF16) {
-    const u32x4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                     pack_bf16x2(y[6], y[7])};
-    *reinterpret_cast<u32x4*>(ob) = o;
-  } else {
-    const f32x4 o0 = {y[0], y[1], y[2], y[3]}, o1 = {y[4], y[5], y[6], y[7]};
-    reinterpret_cast<f32x4*>(ob)[0] = o0;
-    reinterpret_cast<f32x4*>(ob)[1] = o1;
-  }
-}
-
-// Transposing output (rows > cols): O[r][c] = s * X[c][r], O is R x C =
-// m x n, X is n_pad x m_pad in the panel layout.  grid (R_pad / 64, C_pad / 64, batch): each block
-// reads 64 rows x 64 columns of X in 16-byte runs and writes the transposed
-// 64 x 64 block of O, in 8-element runs when VEC (C % 8 == 0 and 16-byte
-// aligned rows), else element by element.
-template <bool OBF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void output_t_kernel(const uint16_t* __restrict__ X, int64_t R,
-                                                           int64_t C, int64_t n_pad, int64_t src_stride,
-                                                           void* __restrict__ O, int64_t o_stride,
-                                                           float s) {
-  __shared__ float tile[kT][kT + 1];
-  const int64_t b = blockIdx.z;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kT, c0 = static_cast<int64_t>(blockIdx.y) * kT;
-  const uint16_t* xb = X + b * src_stride;
-  const int q = threadIdx.x & 7;
-  // tile[cc][rr] = X[c0 + cc][r0 + rr]
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int cc = pass * 32 + (threadIdx.x >> 3);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xb + x_off(c0 + cc, r0 + 8 * q, n_pad));
-    tile[cc][8 * q + 0] = bf16_lo(v.x) * s;
-    tile[cc][8 * q + 1] = bf16_hi(v.x) * s;
-    tile[cc][8 * q + 2] = bf16_lo(v.y) * s;
-    tile[cc][8 * q + 3] = bf16_hi(v.y) * s;
-    tile[cc][8 * q + 4] = bf16_lo(v.z) * s;
-    tile[cc][8 * q + 5] = bf16_hi(v.z) * s;
-    tile[cc][8 * q + 6] = bf16_lo(v.w) * s;
-    tile[cc][8 * q + 7] = bf16_hi(v.w) * s;
-  }
-  __syncthreads();
-  char* ob = static_cast<char*>(O) + static_cast<size_t>(b * o_stride) * (OBF16 ? 2 : 4);
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int rr = pass * 32 + (threadIdx.x >> 3);
-    const int64_t r = r0 + rr, c = c0 + 8 * q;
-    if (r >= R) continue;
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = tile[8 * q + e][rr];
-    if constexpr (VEC) {
-      if (c >= C) continue;  // C % 8 == 0: the run is wholly in or out
-      char* dst = ob + (r * C + c) * (OBF16 ? 2 : 4);
-      if constexpr (OBF16) {
-        const u32x4 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                         pack_bf16x2(y[6], y[7])};
-        *reinterpret_cast<u32x4*>(dst) = o;
-      } else {
-        const f32x4 o0 = {y[0], y[1], y[2], y[3]}, o1 = {y[4], y[5], y[6], y[7]};
-        reinterpret_cast<f32x4*>(dst)[0] = o0;
-        reinterpret_cast<f32x4*>(dst)[1] = o1;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (c + e < C) store_out<OBF16>(ob, r * C + c + e, y[e]);
-    }
-  }
-}
-
-}  // namespace
-
-namespace {
 // SRC 0: momentum (M float32, G); 1 / 2: float32 / bf16 M alone
 template <int SRC>
 hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_stride, float mu, const NsGeometry& g,
@@ -422,46 +313,5 @@ hipError_t launch_ns_prescale_unscaled(const void* M, bool m_bf16, int64_t m_bat
   return launch_prescale_unscaled<1>(Mv, nullptr, m_batch_stride, 0.f, g, eps, ws, stream);
 }
 
-hipError_t launch_ns_output(const uint16_t* X, const NsGeometry& g, void* O, bool o_bf16,
-                            int64_t o_batch_stride, float out_scale, hipStream_t stream) {
-  const int64_t R = g.rows, C = g.cols;
-  const int64_t src_stride = g.n_pad * g.m_pad;
-  const bool vec = C % 8 == 0 && (g.batch == 1 || o_batch_stride % 8 == 0) &&
-                   reinterpret_cast<uintptr_t>(O) % 16 == 0;
-  if (g.transposed) {
-    dim3 grid(static_cast<unsigned>(g.m_pad / kT), static_cast<unsigned>(g.n_pad / kT),
-              static_cast<unsigned>(g.batch));
-    auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O, o_batch_stride,
-                         out_scale);
-    };
-    if (o_bf16) {
-      if (vec) go(output_t_kernel<true, true>);
-      else go(output_t_kernel<true, false>);
-    } else {
-      if (vec) go(output_t_kernel<false, true>);
-      else go(output_t_kernel<false, false>);
-    }
-  } else if (vec) {
-    const int64_t vecs = R * C / 8;
-    dim3 grid(static_cast<unsigned>((vecs + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
-    if (o_bf16)
-      hipLaunchKernelGGL(output_vec_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O,
-                         o_batch_stride, out_scale);
-    else
-      hipLaunchKernelGGL(output_vec_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride,
-                         O, o_batch_stride, out_scale);
-  } else {
-    const int64_t count = R * C;
-    dim3 grid(static_cast<unsigned>((count + kThreads - 1) / kThreads), static_cast<unsigned>(g.batch));
-    if (o_bf16)
-      hipLaunchKernelGGL(output_kernel<true>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O,
-                         o_batch_stride, out_scale);
-    else
-      hipLaunchKernelGGL(output_kernel<false>, grid, dim3(kThreads), 0, stream, X, R, C, g.n_pad, src_stride, O,
-                         o_batch_stride, out_scale);
-  }
-  return hipGetLastError();
-}
 
 }  // namespace mc
