@@ -321,6 +321,43 @@ def test_newton_schulz_misaligned(mc):
         assert rel_fro(f64(Ov[b]), ref) <= 2e-2
 
 
+@pytest.mark.parametrize("case", [
+    # (batch, rows, cols, O dtype, steps): with one step the first GEMMs'
+    # normalisation and the output epilogue are the same launch
+    (2, 300, 520, torch.float32, 1),
+    (1, 520, 300, torch.bfloat16, 1),
+    (2, 256, 768, torch.bfloat16, 2),
+])
+def test_newton_schulz_few_steps(mc, case):
+    batch, rows, cols, odt, steps = case
+    say("newton-schulz few steps", case)
+    g = workloads.generator(40 + rows + steps, "cpu")
+    M = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32)
+    coeffs = mc.NS_COEFFS[:steps]
+    scale = mc.muon_out_scale(rows, cols)
+    O = mc.muon_ns_orthogonalize_batched(M.to(DEV), steps=steps, coeffs=coeffs, out_scale=scale, out_dtype=odt)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref = oracle.muon_orthogonalised_update(f64(M[b]), coeffs=coeffs)
+        assert rel_fro(f64(O[b]), ref) <= 2e-2, b
+
+
+def test_newton_schulz_output_over_input(mc):
+    """O may be M's own buffer (same dtype and strides): M is read only by the
+    pre-scale, before the last step writes O."""
+    say("newton-schulz O = M")
+    batch, rows, cols = 2, 384, 640
+    g = workloads.generator(61, "cpu")
+    M = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32)
+    Md = M.to(DEV)
+    scale = mc.muon_out_scale(rows, cols)
+    mc.muon_ns_orthogonalize_batched(Md, Md, out_scale=scale)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        ref = oracle.muon_orthogonalised_update(f64(M[b]))
+        assert rel_fro(f64(Md[b]), ref) <= 2e-2, b
+
+
 FUSED_CASES = [
     # (batch, rows, cols, W dtype, NS steps)
     (2, 256, 512, torch.bfloat16, 5),   # vector paths throughout
