@@ -56,6 +56,8 @@
 // holds row/column l % 32, k = 8 * (l / 32) + [0, 8); result register r of
 // lane l is row 8 * (r / 4) + 4 * (l / 32) + r % 4, column l % 32.
 
+#include <type_traits>
+
 #include "mc_device.h"
 #include "mc_internal.h"
 
@@ -296,7 +298,6 @@ struct UpdArgs {
   void* W;
   int64_t w_stride;  // elements between matrices
   int n, m;          // logical X shape
-  int transposed;
   float out_scale, lr, wd;
 };
 
@@ -304,13 +305,16 @@ struct UpdArgs {
 // 3 / 4 = write O = out_scale * X' (transposed back for a matrix iterated on
 // as its transpose) to a bf16 / float32 W, which is then the output.
 // SCALED: the launch carries 1 / ||M|| per matrix (the first Newton-Schulz
-// step of the fused path); otherwise the epilogue has no multiply.
-template <int MODE, int UPD, bool SCALED>
+// step); otherwise the epilogue has no multiply.  TR (UPD != 0 only): W is
+// the transpose of X' (a matrix iterated on as its transpose); a template
+// parameter so each epilogue is compiled for its own access pattern.
+template <int MODE, int UPD, bool SCALED, bool TR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
                     uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
                     float alpha, float beta, float diag, const float* __restrict__ inv, UpdArgs ua) {
   static_assert(UPD == 0 || MODE == 2, "only X' = B' X can apply the update");
+  static_assert(UPD != 0 || !TR, "TR describes W");
   constexpr bool kQKRows = MODE == 2;      // right operand X as K-rows tiles
   constexpr bool kBlockedOut = MODE != 2;  // A, B' results in the blocked layout
   // X' = B'X runs fastest with 4 stages, the symmetric products with 5
@@ -492,22 +496,25 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // straight W, lane takes staged row 4 s + lane / 16, unit lane % 16 (W row
   // i0w + row, 8 columns); transposed W, lane takes staged column
   // jj = C + lane % 16 and rows R .. R + 7 (two transposed reads), i.e. 8
-  // consecutive elements of W row j0w + jj.
+  // consecutive elements of W row j0w + jj, with C = 16 (s % 8) and
+  // R = 64 (s / 16) + 32 (s / 8 % 2) + 8 (lane / 16): the four 16-lane
+  // groups take the same 16 W rows and 32 consecutive columns, so an
+  // instruction touches 16 rows x 64 bytes of W rather than 64 rows x 16.
   constexpr bool kReadW = UPD == 1 || UPD == 2;  // 3 / 4 only write
   constexpr int kEsz = (UPD == 2 || UPD == 4) ? 4 : 2;
   constexpr int kWords = (UPD == 2 || UPD == 4) ? 2 : 1;  // 16-byte words per 8 elements
   const int ug = lane >> 4, uil = lane & 15;
   char* const Wb = UPD != 0 ? static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz : nullptr;
-  const int64_t wcols = ua.transposed ? ua.n : ua.m;
+  const int64_t wcols = TR ? ua.n : ua.m;
   const bool wvec = wcols % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
   auto pos = [&](int s, int64_t& wrow, int64_t& wcol, int& valid) {
-    if (!ua.transposed) {
+    if constexpr (!TR) {
       const int row = 4 * s + ug;
       wrow = i0w + row;
       wcol = j0w + 8 * uil;
       valid = wrow < ua.n ? min(8, ua.m - static_cast<int>(wcol)) : 0;
     } else {
-      const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * ug;
+      const int R = 64 * (s >> 4) + 32 * ((s >> 3) & 1) + 8 * ug, C = 16 * (s & 7);
       wrow = j0w + C + uil;
       wcol = i0w + R;
       valid = wrow < ua.m ? min(8, ua.n - static_cast<int>(wcol)) : 0;
@@ -527,7 +534,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
     }
   };
-  const bool w_early = UPD == 1 && !ua.transposed;
+  constexpr bool w_early = UPD == 1 && !TR;
   if (w_early) load_w();
 
   // mode 1: the A values at this lane's accumulator positions (4 consecutive
@@ -597,10 +604,10 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     };
     const int g = ug, il = uil;
     auto read_x = [&](int s, float (&x)[8]) {
-      if (!ua.transposed) {
+      if constexpr (!TR) {
         unpack8(*(const lds_u32x4_t*)(uintptr_t)st_addr(4 * s + g, il), x);
       } else {
-        const int R = 8 * (s >> 1), C = 64 * (s & 1) + 16 * g;
+        const int R = 64 * (s >> 4) + 32 * ((s >> 3) & 1) + 8 * g, C = 16 * (s & 7);
         const int col = C + 4 * (il & 3);
         const int r0 = R + (il >> 2), r1 = r0 + 4;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -707,7 +714,6 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
     ua.w_stride = upd->w_stride;
     ua.n = static_cast<int>(g.n);
     ua.m = static_cast<int>(g.m);
-    ua.transposed = g.transposed ? 1 : 0;
     ua.out_scale = upd->out_scale;
     ua.lr = upd->lr;
     ua.wd = upd->wd;
@@ -716,14 +722,20 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad, tiles_n, tiles_per_mat,
                        alpha, beta, diag, inv, ua);
   };
-  const bool sc = inv != nullptr;
-  if (mode == 0) sc ? go(ns_gemm_kernel<0, 0, true>) : go(ns_gemm_kernel<0, 0, false>);
-  else if (mode == 1) go(ns_gemm_kernel<1, 0, false>);
-  else if (upd == nullptr) sc ? go(ns_gemm_kernel<2, 0, true>) : go(ns_gemm_kernel<2, 0, false>);
-  else if (upd->output && upd->w_bf16) sc ? go(ns_gemm_kernel<2, 3, true>) : go(ns_gemm_kernel<2, 3, false>);
-  else if (upd->output) sc ? go(ns_gemm_kernel<2, 4, true>) : go(ns_gemm_kernel<2, 4, false>);
-  else if (upd->w_bf16) sc ? go(ns_gemm_kernel<2, 1, true>) : go(ns_gemm_kernel<2, 1, false>);
-  else sc ? go(ns_gemm_kernel<2, 2, true>) : go(ns_gemm_kernel<2, 2, false>);
+  const bool sc = inv != nullptr, tr = g.transposed;
+  // the last step's epilogue: one instance per scaling and W orientation
+  auto go_upd = [&](auto kind) {
+    constexpr int U = decltype(kind)::value;
+    if (sc) tr ? go(ns_gemm_kernel<2, U, true, true>) : go(ns_gemm_kernel<2, U, true, false>);
+    else tr ? go(ns_gemm_kernel<2, U, false, true>) : go(ns_gemm_kernel<2, U, false, false>);
+  };
+  if (mode == 0) sc ? go(ns_gemm_kernel<0, 0, true, false>) : go(ns_gemm_kernel<0, 0, false, false>);
+  else if (mode == 1) go(ns_gemm_kernel<1, 0, false, false>);
+  else if (upd == nullptr) sc ? go(ns_gemm_kernel<2, 0, true, false>) : go(ns_gemm_kernel<2, 0, false, false>);
+  else if (upd->output && upd->w_bf16) go_upd(std::integral_constant<int, 3>{});
+  else if (upd->output) go_upd(std::integral_constant<int, 4>{});
+  else if (upd->w_bf16) go_upd(std::integral_constant<int, 1>{});
+  else go_upd(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 
