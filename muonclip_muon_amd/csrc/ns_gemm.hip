@@ -523,21 +523,24 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     }
   };
   u32x4 wbuf[kReadW ? 16 : 1][kWords];
+  // W's 16 vector runs of this wave (UPD 1 / 2 only; wbuf has one slot otherwise)
   auto load_w = [&]() {
+    if constexpr (kReadW) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      int64_t wrow, wcol;
-      int valid;
-      pos(16 * wh + e, wrow, wcol, valid);
-      if (wvec && valid == 8) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(Wb + (wrow * wcols + wcol) * kEsz);
+      for (int e = 0; e < 16; ++e) {
+        int64_t wrow, wcol;
+        int valid;
+        pos(16 * wh + e, wrow, wcol, valid);
+        if (wvec && valid == 8) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(Wb + (wrow * wcols + wcol) * kEsz);
 #pragma unroll
-        for (int w = 0; w < kWords; ++w) wbuf[e][w] = p[w];
+          for (int w = 0; w < kWords; ++w) wbuf[e][w] = p[w];
+        }
       }
     }
   };
   constexpr bool w_early = UPD == 1 && !TR;
-  if (w_early) load_w();
+  if constexpr (w_early) load_w();
 
   // mode 1: the A values at this lane's accumulator positions (4 consecutive
   // columns, 8 bytes of the blocked layout, per MFMA register group), loaded
@@ -621,7 +624,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
     };
     // the wave's 16 passes (bf16 W already in wbuf)
-    if (kReadW && !w_early) load_w();
+    if constexpr (kReadW && !w_early) load_w();
     constexpr int kBatch = 16;
     for (int s0 = 16 * wh; s0 < 16 * wh + 16; s0 += kBatch) {
 #pragma unroll
