@@ -300,16 +300,19 @@ def test_newton_schulz(mc, case):
         assert err <= 2e-2, (b, err)
 
 
-def test_newton_schulz_misaligned(mc):
+@pytest.mark.parametrize("rows,cols,odt", [(192, 320, torch.bfloat16), (320, 192, torch.bfloat16),
+                                           (320, 192, torch.float32)])
+def test_newton_schulz_misaligned(mc, rows, cols, odt):
     """M and O that start one element past a 16-byte boundary (row length a
-    multiple of 8): the copies must fall back to element-wise access."""
-    say("newton-schulz misaligned")
-    batch, rows, cols = 2, 192, 320
+    multiple of 8): the pre-scale and the output epilogue (straight and, for
+    a tall matrix, transposed) must fall back to element-wise access."""
+    say("newton-schulz misaligned", rows, cols, odt)
+    batch = 2
     g = workloads.generator(77, "cpu")
     M = workloads.normal((batch, rows, cols), 1e-3, g, "cpu", torch.float32)
     Mbuf = torch.zeros(batch * rows * cols + 1, device=DEV)
     Mbuf[1:] = M.reshape(-1).to(DEV)
-    Obuf = torch.full((batch * rows * cols + 1,), 7.0, device=DEV, dtype=torch.bfloat16)
+    Obuf = torch.full((batch * rows * cols + 1,), 7.0, device=DEV, dtype=odt)
     Mv = Mbuf[1:].view(batch, rows, cols)
     Ov = Obuf[1:].view(batch, rows, cols)
     scale = mc.muon_out_scale(rows, cols)
