@@ -14,9 +14,10 @@ One step = every row of the path, on one stream:
   per-head max logit -> QK-Clip of W_q / W_kc.
 
 Prints one JSON line on stdout (progress goes to stderr).  `value` is the
-step's MFMA work (nominal Newton-Schulz GEMM flops 4n^2m + 2n^3 per matrix
-per iteration, plus 2 B H Sq Sk d for the max logit) divided by the step
-time.  `roofline` covers the dominant kernel, timed per launch with HIP
+step's MFMA work divided by the step time, counting what the method needs:
+per matrix and Newton-Schulz iteration 3n^2m + n^3 (X X^T and A A are
+symmetric, so half of each is redundant; B'X is 2n^2m), plus 2 B H Sq Sk d
+for the max logit.  The dense count 4n^2m + 2n^3 is reported beside it.  `roofline` covers the dominant kernel, timed per launch with HIP
 events on the library's stream.  `cpu_baseline` times the fp64 oracle on a
 bounded sample of the same workload.
 """
@@ -66,8 +67,27 @@ def measured_traffic():
 
 
 def ns_flops(rows, cols, steps):
+    """Dense (nominal) Newton-Schulz flops: 4n^2m + 2n^3 per iteration."""
     n, m = min(rows, cols), max(rows, cols)
     return steps * (4 * n * n * m + 2 * n ** 3)
+
+
+def ns_flops_sym(rows, cols, steps):
+    """The method's Newton-Schulz work with the symmetric products counted
+    once: X X^T n^2m, A A n^3, B'X 2n^2m per iteration."""
+    n, m = min(rows, cols), max(rows, cols)
+    return steps * (3 * n * n * m + n ** 3)
+
+
+def gemm_flops_executed(rows, cols):
+    """MFMA flops each GEMM of one iteration executes for one matrix: X X^T and
+    A A compute the upper-triangle 256 x 256 tiles of the zero-padded matrix,
+    B'X every tile."""
+    n, m = min(rows, cols), max(rows, cols)
+    n_pad, m_pad = -(-n // 256) * 256, -(-m // 256) * 256
+    t = n_pad // 256
+    tri = t * (t + 1) // 2
+    return {0: tri * 2 * 256 * 256 * m_pad, 1: tri * 2 * 256 * 256 * n_pad, 2: 2 * n_pad * n_pad * m_pad}
 
 
 class Workload:
@@ -204,7 +224,9 @@ def run(args):
     # timed region: K steps bracketed by synchronisation
     acc = {"momentum": 0.0, "maxlogit": 0.0, "clip": 0.0, "ns": 0.0, "update": 0.0}
     gemm_ms = {0: [], 1: [], 2: []} if args.unfused else {0: [], 1: [], 2: [], "2u": []}
-    gemm_flops = {k: [] for k in gemm_ms}
+    gemm_flops = {k: [] for k in gemm_ms}       # the method's flops (symmetric products counted once)
+    gemm_flops_nom = {k: [] for k in gemm_ms}   # dense 2 n^2 m / 2 n^3
+    gemm_flops_exe = {k: [] for k in gemm_ms}   # what the MFMAs execute (tiles, padding)
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -219,7 +241,9 @@ def run(args):
             if args.unfused:
                 acc["update"] += upd_ev[k][0].elapsed_time(upd_ev[k][1])
             n_, m_ = min(rows, cols), max(rows, cols)
-            per = {0: 2 * n_ * n_ * m_, 1: 2 * n_ ** 3, 2: 2 * n_ * n_ * m_}
+            per = {0: n_ * n_ * m_, 1: n_ ** 3, 2: 2 * n_ * n_ * m_}
+            per_nom = {0: 2 * n_ * n_ * m_, 1: 2 * n_ ** 3, 2: 2 * n_ * n_ * m_}
+            per_exe = gemm_flops_executed(rows, cols)
             for st in range(steps_ns):
                 for gm in range(3):
                     a, b = gemm_ev[k][2 * (3 * st + gm)], gemm_ev[k][2 * (3 * st + gm) + 1]
@@ -227,6 +251,8 @@ def run(args):
                     key = "2u" if (gm == 2 and st == steps_ns - 1 and not args.unfused) else gm
                     gemm_ms[key].append(a.elapsed_time(b))
                     gemm_flops[key].append(per[gm] * cnt)
+                    gemm_flops_nom[key].append(per_nom[gm] * cnt)
+                    gemm_flops_exe[key].append(per_exe[gm] * cnt)
         log(f"step {i + 1}/{args.steps} done")
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -235,9 +261,11 @@ def run(args):
     K = args.steps
     ms_per_step = total_ms / K
 
-    ns_fl = sum(ns_flops(r, c, steps_ns) * n for _, _, n, r, c in wl.groups)
+    ns_fl = sum(ns_flops_sym(r, c, steps_ns) * n for _, _, n, r, c in wl.groups)
+    ns_fl_nom = sum(ns_flops(r, c, steps_ns) * n for _, _, n, r, c in wl.groups)
     ml_fl = 2.0 * B * H * Sq * Sk * dq
     value = (ns_fl + ml_fl) / (ms_per_step * 1e-3) / 1e12
+    value_nominal = (ns_fl_nom + ml_fl) / (ms_per_step * 1e-3) / 1e12
     E = wl.numel
     n_clip = int((clipped == 1).sum().item())
     d_in = D_MODEL
@@ -301,9 +329,10 @@ def run(args):
     torch.cuda.synchronize()
     ns_only_ms = e0.elapsed_time(e1) / 3
     ns_only = {"shape": f"{ns_cnt} x {ns_rows} x {ns_cols}", "ms": round(ns_only_ms, 3),
+               "tflops": round(ns_flops_sym(ns_rows, ns_cols, steps_ns) * ns_cnt / (ns_only_ms * 1e-3) / 1e12, 1),
                "tflops_nominal": round(ns_flops(ns_rows, ns_cols, steps_ns) * ns_cnt / (ns_only_ms * 1e-3) / 1e12, 1),
                "note": "muon_ns_orthogonalize_batched alone: pre-scale with norm partials, 5 iterations, bf16 output; "
-                       "nominal flops 4n^2m + 2n^3 per matrix per iteration"}
+                       "tflops counts 3n^2m + n^3 per matrix per iteration, tflops_nominal 4n^2m + 2n^3"}
     del O_ns
 
     # Self-measured ceilings on this GPU (measurement aids, outside the step):
@@ -349,6 +378,9 @@ def run(args):
         ("newton_schulz_ms" if args.unfused else "momentum_ns_update_ms"): round(acc["ns"] / K, 3),
         ("newton_schulz_tflops" if args.unfused else "momentum_ns_update_tflops"):
             round(ns_fl / (acc["ns"] / K * 1e-3) / 1e12, 1),
+        "value_nominal_tflops": round(value_nominal, 2),
+        "value_note": "value counts 3n^2m + n^3 per Newton-Schulz iteration (symmetric X X^T and A A once); "
+                      "value_nominal_tflops the dense 4n^2m + 2n^3",
         "maxlogit_ms": round(acc["maxlogit"] / K, 4),
         "maxlogit_tflops": round(ml_fl / (acc["maxlogit"] / K * 1e-3) / 1e12, 1),
     }
@@ -365,6 +397,14 @@ def run(args):
         "clipped_heads": n_clip,
         "gemm_tflops": {str(g): round(sum(gemm_flops[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
                         for g in gemm_ms},
+        "gemm_tflops_executed": {str(g): round(sum(gemm_flops_exe[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
+                                 for g in gemm_ms},
+        "gemm_frac_executed": {str(g): round(sum(gemm_flops_exe[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12
+                                             / MFMA_BF16_PEAK_TFLOPS, 4) for g in gemm_ms},
+        "gemm_tflops_nominal": {str(g): round(sum(gemm_flops_nom[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
+                                for g in gemm_ms},
+        "gemm_note": "per GEMM (0 X X^T, 1 aI+bA+cAA, 2 B'X, 2u the last B'X applying the update): gemm_tflops on "
+                     "the method's flops (n^2m, n^3, 2n^2m), executed on the tiles the MFMAs compute, nominal dense",
         "newton_schulz_only": ns_only,
         "maxlogit_long_context": ml_long,
         "probes": dict(probes, dominant_gemm_frac_of_mfma_probe=round(

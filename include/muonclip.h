@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MC_ABI_VERSION 1
+#define MC_ABI_VERSION 2
 
 /* Entry points are the only symbols the library exports. */
 #if defined(__GNUC__) || defined(__clang__)
@@ -93,6 +93,19 @@ MC_API const char* mc_status_string(int status);
 MC_API mc_status_t muonclip_momentum(float* M, const float* G, int64_t numel, float mu, void* stream);
 
 /*
+ * The Muon output scale sqrt(max(rows, cols)) * 0.2, which matches the RMS of
+ * the update to AdamW's (Algorithm 1 of "Kimi K2 内部机制": O_t =
+ * NewtonSchulz(M_t) * sqrt(max(n, m)) * 0.2; the Zhihu MuonClip formula,
+ * "Match Adam Update RMS"), computed in double and rounded once to float32.
+ * Returns 0 when rows < 1 or cols < 1.
+ */
+MC_API float muon_rms_match_scale(int64_t rows, int64_t cols);
+
+/* Pass as out_scale to the Newton-Schulz calls to have the library apply
+ * muon_rms_match_scale(rows, cols); every negative out_scale does the same. */
+#define MC_OUT_SCALE_RMS_MATCH (-1.0f)
+
+/*
  * Workspace bytes that muon_ns_orthogonalize_batched needs for `batch`
  * matrices of rows x cols.  Returns 0 for invalid sizes.
  */
@@ -112,7 +125,8 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  * the singular values toward 1 ("Kimi K2, explained.", Muon update bullets).
  * The polynomial coefficients, the step count and the Frobenius pre-scale are
  * not on the pages and are arguments here.  Pass out_scale =
- * sqrt(max(rows, cols)) * 0.2 for the pages' step.
+ * MC_OUT_SCALE_RMS_MATCH (any negative value) for the pages' step: the
+ * library then uses muon_rms_match_scale(rows, cols).
  *
  * Arithmetic: the norm is accumulated in float32 (combined in double); X_0
  * is held as bf16(M) and the factor 1 / (||M||_F + eps) is applied in float32
@@ -127,7 +141,8 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  *   O              device, o_dtype, same layout with o_batch_stride; O may be
  *                  the same buffer as M when dtypes and strides match
  *   steps          1..64; coeffs: host float[steps][3] = (a_s, b_s, c_s)
- *   eps            >= 0; out_scale: any finite value
+ *   eps            >= 0; out_scale: finite; negative = the RMS-matching
+ *                  scale sqrt(max(rows, cols)) * 0.2
  *   workspace      device, >= muon_ns_workspace_bytes(batch, rows, cols)
  *                  bytes, 256-byte aligned; contents on entry are ignored
  *   gemm_events    NULL, or host array of 6 * steps hipEvent_t (as void*):
@@ -182,7 +197,9 @@ MC_API mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_
  *   W          device, w_dtype (MC_F32 or MC_BF16), in/out
  *   batch_stride  elements between consecutive matrices of M, G and W
  *                 (>= rows * cols when batch > 1)
- *   mu, lr, weight_decay, out_scale: finite; eps >= 0
+ *   mu, lr, weight_decay, out_scale: finite; eps >= 0; out_scale < 0
+ *                 (MC_OUT_SCALE_RMS_MATCH) = sqrt(max(rows, cols)) * 0.2, the
+ *                 pages' step
  *   workspace  device, >= muon_ns_workspace_bytes(batch, rows, cols) bytes,
  *              256-byte aligned
  *   gemm_events as muon_ns_orthogonalize_batched (the last step's third GEMM

@@ -13,7 +13,6 @@ Agentic Intelligence", section 3.2) on top of them.
 """
 
 import ctypes
-import math
 import os
 
 import torch
@@ -38,6 +37,7 @@ __all__ = [
     "qk_clip_apply_total",
     "attention_fwd_maxlogit",
     "muon_out_scale",
+    "OUT_SCALE_RMS_MATCH",
     "muonclip_step",
 ]
 
@@ -77,6 +77,8 @@ def _load():
     L.mc_status_string.argtypes = [ctypes.c_int]
     L.muonclip_momentum.restype = ctypes.c_int
     L.muonclip_momentum.argtypes = [vp, vp, i64, f32, vp]
+    L.muon_rms_match_scale.restype = ctypes.c_float
+    L.muon_rms_match_scale.argtypes = [i64, i64]
     L.muon_ns_workspace_bytes.restype = ctypes.c_size_t
     L.muon_ns_workspace_bytes.argtypes = [i64, i64, i64]
     L.muon_ns_orthogonalize_batched.restype = ctypes.c_int
@@ -138,6 +140,16 @@ def _stream(t, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype, device, stream):
+    """A new tensor whose memory is ordered on the launch stream: torch's caching
+    allocator then never hands it to another stream while the library's kernels
+    on `stream` may still use it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def muonclip_momentum(M, G, mu=0.95, stream=None):
     """M <- fl32(fl32(mu * M) + G) in place (float32, any shape)."""
     _dev(M, "M"), _dev(G, "G")
@@ -152,9 +164,13 @@ def muon_ns_workspace_bytes(batch, rows, cols):
     return lib.muon_ns_workspace_bytes(batch, rows, cols)
 
 
+# out_scale value that has the library apply its RMS-matching scale
+OUT_SCALE_RMS_MATCH = -1.0
+
+
 def muon_out_scale(rows, cols):
-    """sqrt(max(n, m)) * 0.2, the Adam-RMS matching factor of Algorithm 1."""
-    return math.sqrt(max(rows, cols)) * 0.2
+    """The library's sqrt(max(rows, cols)) * 0.2 (float32), the Adam-RMS matching factor."""
+    return lib.muon_rms_match_scale(rows, cols)
 
 
 def _coeffs(steps, coeffs):
@@ -166,10 +182,10 @@ def _coeffs(steps, coeffs):
     return (ctypes.c_float * len(flat))(*flat)
 
 
-def _workspace(workspace, batch, rows, cols, device):
+def _workspace(workspace, batch, rows, cols, device, stream):
     need = lib.muon_ns_workspace_bytes(batch, rows, cols)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        workspace = _empty(max(need, 1), torch.uint8, device, stream)
     return _dev(workspace, "workspace")
 
 
@@ -200,12 +216,12 @@ def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS
         raise ValueError("M must be [rows, cols] or [batch, rows, cols]")
     batch, rows, cols = M3.shape
     if O is None:
-        O = torch.empty(M.shape, dtype=out_dtype or M.dtype, device=M.device)
+        O = _empty(M.shape, out_dtype or M.dtype, M.device, stream)
     _dev(O, "O")
     if O.shape != M.shape:
         raise ValueError("O must have M's shape")
     c_coeffs = _coeffs(steps, coeffs)
-    workspace = _workspace(workspace, batch, rows, cols, M.device)
+    workspace = _workspace(workspace, batch, rows, cols, M.device, stream)
     ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_ns_orthogonalize_batched(
         M.data_ptr(), _dtype(M, "M"), batch, rows, cols, rows * cols, O.data_ptr(), _dtype(O, "O"),
@@ -232,7 +248,7 @@ def muon_momentum_ns_update_batched(M, G, W, lr, weight_decay=0.1, mu=0.95, step
     M <- mu M + G; W <- W - lr * (out_scale * NS(M) + weight_decay * W).
 
     M, G float32; W float32 or bfloat16, all the same shape.  ``out_scale``
-    defaults to muon_out_scale(rows, cols)."""
+    None lets the library apply its sqrt(max(rows, cols)) * 0.2."""
     _dev(M, "M"), _dev(G, "G"), _dev(W, "W")
     if M.dtype != torch.float32 or G.dtype != torch.float32:
         raise ValueError("M and G must be float32")
@@ -243,9 +259,9 @@ def muon_momentum_ns_update_batched(M, G, W, lr, weight_decay=0.1, mu=0.95, step
         raise ValueError("M must be [rows, cols] or [batch, rows, cols]")
     batch, rows, cols = M3.shape
     if out_scale is None:
-        out_scale = muon_out_scale(rows, cols)
+        out_scale = OUT_SCALE_RMS_MATCH
     c_coeffs = _coeffs(steps, coeffs)
-    workspace = _workspace(workspace, batch, rows, cols, M.device)
+    workspace = _workspace(workspace, batch, rows, cols, M.device, stream)
     ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_momentum_ns_update_batched(
         M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
@@ -274,7 +290,7 @@ def qk_maxlogit(Q, Kc, Kr=None, smax=None, accumulate=False, stream=None):
     if d != d_c + d_r or Kc.dtype != Q.dtype:
         raise ValueError("Q's head dim must be d_c + d_r and Q, Kc must share a dtype")
     if smax is None:
-        smax = torch.empty(H, dtype=torch.float32, device=Q.device)
+        smax = _empty(H, torch.float32, Q.device, stream)
     _dev(smax, "smax")
     status = lib.qk_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
                              _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, smax.data_ptr(), int(bool(accumulate)),
@@ -300,9 +316,9 @@ def attention_fwd_maxlogit(Q, Kc, Kr, V, causal=False, O=None, lse=None, smax=No
             Kr is not None and Kr.shape[:2] != (B, Sk)):
         raise ValueError("inconsistent attention shapes")
     if O is None:
-        O = torch.empty((B, H, Sq, d_v), dtype=Q.dtype, device=Q.device)
+        O = _empty((B, H, Sq, d_v), Q.dtype, Q.device, stream)
     if smax is None:
-        smax = torch.empty(H, dtype=torch.float32, device=Q.device)
+        smax = _empty(H, torch.float32, Q.device, stream)
     status = lib.attention_fwd_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
                                         V.data_ptr(), _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, d_v,
                                         int(bool(causal)), O.data_ptr(), lse.data_ptr() if lse is not None else None,
@@ -338,9 +354,9 @@ def _qk_clip(fn, smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, 
     if Wq.numel() != H * q_rows_per_head * d_in or Wk.numel() != H * k_rows_per_head * d_in:
         raise ValueError("Wq must be [H * q_rows_per_head, d_in] and Wk [H * k_rows_per_head, d_in]")
     if gamma is None:
-        gamma = torch.empty(H, dtype=torch.float32, device=smax.device)
+        gamma = _empty(H, torch.float32, smax.device, stream)
     if clipped is None:
-        clipped = torch.empty(H, dtype=torch.int32, device=smax.device)
+        clipped = _empty(H, torch.int32, smax.device, stream)
     status = getattr(lib, fn)(smax.data_ptr(), H, tau, alpha, Wq.data_ptr(), Wk.data_ptr(),
                               _dtype(Wq, "Wq"), d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
                               gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
@@ -353,7 +369,7 @@ def probe_mfma_bf16(workgroups, iters, zero_operands=False, out=None, device=Non
 
     Returns (out, flop) with flop = workgroups * 4 * iters * 16 * 32768."""
     if out is None:
-        out = torch.empty(workgroups * 256, dtype=torch.float32, device=device or "cuda")
+        out = _empty(workgroups * 256, torch.float32, device or "cuda", stream)
     _dev(out, "out")
     _check("mc_probe_mfma_bf16", lib.mc_probe_mfma_bf16(workgroups, iters, 1 if zero_operands else 0,
                                                         out.data_ptr(), _stream(out, stream)))

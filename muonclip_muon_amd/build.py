@@ -23,13 +23,14 @@ LIB = os.path.join(PKG, "libmuonclip.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "elementwise.hip", "qkclip.hip", "ns_prep.hip", "ns_gemm.hip", "maxlogit.hip",
-           "attention.hip", "probe.hip"]
+           "maxlogit_generic.hip", "attention.hip", "probe.hip"]
 
 COMMON_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    "-Werror",
     "-fvisibility=hidden",
     f"--offload-arch={ARCH}",
     # Packed FP32 instructions (v_pk_add/mul/fma_f32) are kept out of every
@@ -40,12 +41,14 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-source additions.  maxlogit.hip: MFMA results in VGPRs (the query
-# fragments then sit in AGPRs, which MFMA reads directly), so the running max
-# reads the logits without a v_accvgpr_read per value; and no NaN semantics
-# for float operations, so fmaxf becomes a bare v_max3_f32 instead of first
-# quieting each operand (the hardware maximum still skips quiet NaNs, and the
-# file tests for NaN on the bits).
+# Per-source additions.  maxlogit.hip (the bf16 MFMA kernel only): MFMA
+# results in VGPRs (the query fragments then sit in AGPRs, which MFMA reads
+# directly), so the running max reads the logits without a v_accvgpr_read per
+# value; and no NaN semantics for float operations, so fmaxf becomes a bare
+# v_max3_f32 instead of first quieting each operand (the hardware maximum
+# still skips quiet NaNs, and the file tests for NaN on the bits).  The
+# float32 fallback kernel lives in maxlogit_generic.hip, built with the
+# default (IEEE) NaN semantics.
 SOURCE_FLAGS = {
     "maxlogit.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     "attention.hip": ["-fno-honor-nans"],

@@ -49,6 +49,11 @@ mc_status_t muonclip_momentum(float* M, const float* G, int64_t numel, float mu,
   return from_hip(mc::launch_momentum(M, G, numel, mu, static_cast<hipStream_t>(stream)));
 }
 
+float muon_rms_match_scale(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1) return 0.0f;
+  return mc::rms_match_scale(rows, cols);
+}
+
 size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
   if (batch < 0 || rows < 1 || cols < 1) return 0;
   const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
@@ -153,16 +158,21 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   if (mc::launch_ns_prescale_unscaled(M, m_bf16, m_batch_stride, g, eps, ws, s) != hipSuccess) return MC_EHIP;
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
   // the last step's X' = B' X writes O = out_scale * X' (transposed back)
-  mc::NsUpdate out{O, o_bf16, o_batch_stride, out_scale, 0.f, 0.f, true};
+  mc::NsUpdate out{O, o_bf16, o_batch_stride, mc::resolve_out_scale(out_scale, rows, cols), 0.f, 0.f, true};
   uint16_t* X = nullptr;
   return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &out, s, gemm_events, &X));
 }
 
-mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, void* W, int w_dtype,
-                                            int64_t batch, int64_t rows, int64_t cols, int64_t batch_stride,
-                                            int32_t steps, const float* coeffs, float eps, float out_scale,
-                                            float lr, float weight_decay, void* workspace,
-                                            size_t workspace_bytes, void* stream, void* const* gemm_events) {
+}  // extern "C"
+
+namespace {
+
+// The fused Muon call on a given scratch buffer (a caller workspace or the
+// library's static scratch); every check runs before anything is enqueued.
+mc_status_t fused_muon(float* M, const float* G, float mu, void* W, int w_dtype, int64_t batch, int64_t rows,
+                       int64_t cols, int64_t batch_stride, int32_t steps, const float* coeffs, float eps,
+                       float out_scale, float lr, float weight_decay, void* workspace, size_t workspace_bytes,
+                       void* stream, void* const* gemm_events) {
   if (batch < 0 || rows < 1 || cols < 1) return MC_EINVAL;
   if (!valid_dtype(w_dtype)) return MC_EDTYPE;
   {
@@ -183,9 +193,23 @@ mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, 
   char* ws = static_cast<char*>(workspace);
   if (mc::launch_momentum_prescale(M, G, batch_stride, mu, g, eps, ws, s) != hipSuccess) return MC_EHIP;
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
-  mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, out_scale, lr, weight_decay, false};
+  mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, mc::resolve_out_scale(out_scale, rows, cols), lr,
+                   weight_decay, false};
   uint16_t* X = nullptr;
   return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events, &X));
+}
+
+}  // namespace
+
+extern "C" {
+
+mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, void* W, int w_dtype,
+                                            int64_t batch, int64_t rows, int64_t cols, int64_t batch_stride,
+                                            int32_t steps, const float* coeffs, float eps, float out_scale,
+                                            float lr, float weight_decay, void* workspace,
+                                            size_t workspace_bytes, void* stream, void* const* gemm_events) {
+  return fused_muon(M, G, mu, W, w_dtype, batch, rows, cols, batch_stride, steps, coeffs, eps, out_scale, lr,
+                    weight_decay, workspace, workspace_bytes, stream, gemm_events);
 }
 
 mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, int64_t numel,

@@ -11,8 +11,8 @@
 // bf16, (d_c, d_r, d_v) in {(128, 64, 128), (64, 0, 64)}, Sk >= 64.
 // A 256-thread workgroup (4 wave64s) owns 256 query rows of one (b, h); each
 // wave keeps its 64 rows of Q as MFMA fragments in registers.  Keys and
-// values stream through 3 LDS stages of 64 keys (K rows and V rows, filled by
-// LDS DMA two blocks ahead, one barrier per block).  A block is two phases of
+// values stream through 4 LDS stages of 64 keys (K rows and V rows, filled by
+// LDS DMA three blocks ahead, one barrier per block).  A block is two phases of
 // 32 keys; per phase and wave:
 //   S = K Q^T     2 x (d/16) v_mfma_f32_32x32x16_bf16 (keys as the MFMA rows,
 //                 so each lane holds 16 keys of one query row);
@@ -79,12 +79,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-__device__ __forceinline__ void atomic_max_float(float* addr, float x) {
-  if ((__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u) return;
-  if (__float_as_int(x) >= 0) atomicMax(reinterpret_cast<int*>(addr), __float_as_int(x));
-  else atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(x));
 }
 
 // x of this lane and of lane l ^ 32 (the other half-wave), with

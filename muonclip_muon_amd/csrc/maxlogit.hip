@@ -17,7 +17,8 @@
 //   Kc[b,h,j] and the shared rotary part Kr[b,j] (MLA).  Consecutive
 //   workgroups of one (b, h) are kept on one XCD so the key stream is read
 //   from that XCD's L2.
-// float32 path (any other shape, either dtype): a plain LDS-tiled FMA kernel.
+// Any other shape (float32, other head dims, Sk < 64) goes to the float32
+// LDS-tiled kernel of maxlogit_generic.hip, which keeps NaN semantics.
 //
 // Both finish with a workgroup max and one atomic max per workgroup into
 // smax[h] (float max through integer atomics; exact and order-independent).
@@ -31,21 +32,6 @@
 
 namespace mc {
 namespace {
-
-// Float atomic max through integer atomics: for x >= 0 the int order of the
-// bits is the float order; for x < 0 the unsigned order is reversed.
-__device__ __forceinline__ void atomic_max_float(float* addr, float x) {
-  // NaN test on the bits: this file is compiled without NaN semantics for
-  // float comparisons (see the running max below)
-  if ((__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u) return;
-  if (__float_as_int(x) >= 0) atomicMax(reinterpret_cast<int*>(addr), __float_as_int(x));
-  else atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(x));
-}
-
-__global__ void init_kernel(float* smax, int64_t H) {
-  const int64_t h = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (h < H) smax[h] = -INFINITY;
-}
 
 // ------------------------------------------------------------------ bf16 MFMA
 constexpr int kMfmaThreads = 256;
@@ -96,6 +82,7 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           float* __restrict__ smax, float scale) {
   constexpr int D = DC + DR;
   constexpr int kUc = DC / 8, kUr = DR / 8;        // 16-byte units per row and part
+  constexpr int kUrNz = kUr > 0 ? kUr : 1;          // divisor for the Kr loop, which is empty when DR = 0
   constexpr int kSteps = D / 16;                   // MFMA k-steps
   constexpr int kKcBytes = kKeys * DC * 2, kKrBytes = kKeys * DR * 2;
   constexpr int kStageBytes = kKcBytes + kKrBytes;
@@ -157,7 +144,7 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
   for (int l = 0; l < kLoadsR; ++l) {
     const int p = 64 * (wave + 4 * l) + lane;
-    const int r = p / kUr, u = (p % kUr) ^ (r & 7);
+    const int r = p / kUrNz, u = (p % kUrNz) ^ (r & 7);
     off_r[l] = static_cast<uint32_t>((r * DR + 8 * u) * 2);
   }
   const int NJ = (Sk + kKeys - 1) / kKeys;
@@ -277,75 +264,6 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   }
 }
 
-// ------------------------------------------------------------------ generic
-constexpr int kGenThreads = 256;
-constexpr int kGenTile = 64;  // 64 x 64 logits per iteration, 4 x 4 per thread
-constexpr int kGenDk = 32;    // head-dim slice staged in LDS
-
-template <bool BF16>
-__device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
-  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  else return static_cast<const float*>(p)[i];
-}
-
-// grid (ceil(Sq/64), H, B)
-template <bool BF16>
-__global__ __launch_bounds__(kGenThreads) void maxlogit_generic_kernel(
-    const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Kr, int64_t H,
-    int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* __restrict__ smax, float scale) {
-  __shared__ float qs[kGenTile][kGenDk + 1];
-  __shared__ float kt[kGenTile][kGenDk + 1];
-  __shared__ float red[kGenThreads / 64];
-  const int64_t b = blockIdx.z, h = blockIdx.y, i0 = static_cast<int64_t>(blockIdx.x) * kGenTile;
-  const int64_t d = d_c + d_r;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  const int64_t qbase = (b * H + h) * Sq * d;
-  const int64_t kcbase = (b * H + h) * Sk * d_c;
-  const int64_t krbase = b * Sk * d_r;
-  float m = -INFINITY;
-  for (int64_t j0 = 0; j0 < Sk; j0 += kGenTile) {
-    float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < d; k0 += kGenDk) {
-      for (int e = tid; e < kGenTile * kGenDk; e += kGenThreads) {
-        const int r = e / kGenDk, c = e % kGenDk;
-        const int64_t i = i0 + r, j = j0 + r, k = k0 + c;
-        qs[r][c] = (i < Sq && k < d) ? ld_elem<BF16>(Q, qbase + i * d + k) : 0.f;
-        float kv = 0.f;
-        if (j < Sk && k < d) kv = k < d_c ? ld_elem<BF16>(Kc, kcbase + j * d_c + k)
-                                          : ld_elem<BF16>(Kr, krbase + j * d_r + (k - d_c));
-        kt[r][c] = kv;
-      }
-      __syncthreads();
-#pragma unroll 4
-      for (int c = 0; c < kGenDk; ++c) {
-        float qv[4], kv[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) qv[a] = qs[ty + 16 * a][c];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) kv[a] = kt[tx + 16 * a][c];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[a][e] = fmaf(qv[a], kv[e], acc[a][e]);
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i0 + ty + 16 * a < Sq && j0 + tx + 16 * e < Sk) m = fmaxf(m, acc[a][e]);
-  }
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    float w = red[0];
-    for (int i = 1; i < kGenThreads / 64; ++i) w = fmaxf(w, red[i]);
-    if (w != -INFINITY) atomic_max_float(&smax[h], w * scale);
-  }
-}
-
 template <int DC, int DR>
 hipError_t launch_mfma(const void* Q, const void* Kc, const void* Kr, int64_t B, int64_t H, int64_t Sq,
                        int64_t Sk, float* smax, float scale, hipStream_t stream) {
@@ -359,12 +277,6 @@ hipError_t launch_mfma(const void* Q, const void* Kc, const void* Kr, int64_t B,
 }
 
 }  // namespace
-
-hipError_t launch_maxlogit_init(float* smax, int64_t H, hipStream_t stream) {
-  hipLaunchKernelGGL(init_kernel, dim3(static_cast<unsigned>((H + 255) / 256)), dim3(256), 0, stream,
-                     smax, H);
-  return hipGetLastError();
-}
 
 hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool bf16, int64_t B,
                            int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
@@ -386,15 +298,7 @@ hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool b
     if (d_c == 64 && d_r == 64) return launch_mfma<64, 64>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
     if (d_c == 128 && d_r == 64) return launch_mfma<128, 64>(Q, Kc, Kr, B, H, Sq, Sk, smax, scale, stream);
   }
-  dim3 grid(static_cast<unsigned>((Sq + kGenTile - 1) / kGenTile), static_cast<unsigned>(H),
-            static_cast<unsigned>(B));
-  if (bf16)
-    hipLaunchKernelGGL(maxlogit_generic_kernel<true>, grid, dim3(kGenThreads), 0, stream, Q, Kc, Kr, H,
-                       Sq, Sk, d_c, d_r, smax, scale);
-  else
-    hipLaunchKernelGGL(maxlogit_generic_kernel<false>, grid, dim3(kGenThreads), 0, stream, Q, Kc, Kr,
-                       H, Sq, Sk, d_c, d_r, smax, scale);
-  return hipGetLastError();
+  return launch_maxlogit_generic(Q, Kc, Kr, bf16, B, H, Sq, Sk, d_c, d_r, smax, scale, stream);
 }
 
 }  // namespace mc

@@ -58,6 +58,16 @@ __device__ __forceinline__ float update_op(float w, float o, float lr, float wd)
   return w - v;
 }
 
+// Float atomic max through integer atomics (exact and order-independent): for
+// x >= 0 the signed-int order of the bits is the float order; for x < 0 the
+// unsigned order is the reverse of it.  NaN is skipped, tested on the bits so
+// the test holds in files compiled without NaN semantics for float compares.
+__device__ __forceinline__ void atomic_max_float(float* addr, float x) {
+  if ((__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u) return;
+  if (__float_as_int(x) >= 0) atomicMax(reinterpret_cast<int*>(addr), __float_as_int(x));
+  else atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(x));
+}
+
 // Layout of the Newton-Schulz state X (n_pad x m_pad bf16) in the workspace:
 // column panels of 256, each n_pad x 256 row-major, so a 32 x 256 K-rows tile
 // (the right operand of B' X) is one contiguous 16 KB run and a row panel of

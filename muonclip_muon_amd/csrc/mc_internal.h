@@ -19,6 +19,17 @@ hipError_t launch_update(void* W, bool w_bf16, const void* O, bool o_bf16, int64
                          float weight_decay, hipStream_t stream);
 
 // ---------------------------------------------------------------- Newton-Schulz
+// The Muon output scale that matches the update RMS of AdamW:
+// sqrt(max(rows, cols)) * 0.2 (Algorithm 1 of "Kimi K2 内部机制"; the Zhihu
+// MuonClip formula, "Match Adam Update RMS"), rounded once to float32.
+inline float rms_match_scale(int64_t rows, int64_t cols) {
+  const double n = static_cast<double>(rows > cols ? rows : cols);
+  return static_cast<float>(__builtin_sqrt(n) * 0.2);
+}
+// out_scale < 0 selects the RMS-matching scale (MC_OUT_SCALE_RMS_MATCH).
+inline float resolve_out_scale(float out_scale, int64_t rows, int64_t cols) {
+  return out_scale < 0.0f ? rms_match_scale(rows, cols) : out_scale;
+}
 // Padded internal geometry of one batch of matrices.  X is n x m with
 // n = min(rows, cols), m = max(rows, cols); both are padded to multiples of
 // the GEMM tile so no kernel needs a bounds check.  Padding is zero, which the
@@ -74,6 +85,11 @@ hipError_t launch_maxlogit_init(float* smax, int64_t H, hipStream_t stream);
 hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool bf16, int64_t B,
                            int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
                            hipStream_t stream);
+// The float32 LDS-tiled kernel (maxlogit_generic.hip, built with NaN
+// semantics) for shapes the MFMA kernel does not cover; scale = 1/sqrt(d).
+hipError_t launch_maxlogit_generic(const void* Q, const void* Kc, const void* Kr, bool bf16, int64_t B,
+                                   int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,
+                                   float scale, hipStream_t stream);
 
 // ------------------------------------------------------ attention forward
 bool attention_fwd_supported(int64_t d_c, int64_t d_r, int64_t d_v);

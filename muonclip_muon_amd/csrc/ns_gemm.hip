@@ -71,7 +71,6 @@ constexpr int kCT = kWaveCols / 32;                  // 32-column MFMA tiles per
 constexpr int kMaxStages = 5;  // LDS stages in flight (prefetch distance stages - 1), per mode below
 constexpr int kTileBytes = kBK * kBN * 2;  // 16 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kLdsBytes = kMaxStages * kStageBytes;
 constexpr int kLoadsPerTile = kTileBytes / 1024 / kWaves;  // DMA instructions per wave per operand tile
 constexpr int kLoadsPerStage = 2 * kLoadsPerTile;
 

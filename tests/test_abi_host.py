@@ -219,3 +219,23 @@ def test_headers_compile_as_c_and_link(mc, tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+def test_rms_match_scale_in_the_library(mc):
+    # O_t = NewtonSchulz(M_t) * sqrt(max(n, m)) * 0.2 (the internals page's
+    # Algorithm 1; the Zhihu MuonClip formula): the factor comes from the C
+    # library, rounded once to float32; 0.2 is the pages' constant.
+    import json
+
+    import numpy as np
+    golden = json.load(open(os.path.join(ROOT, "tests", "golden", "page_constants.json")))
+    k = float(golden["rms_match_factor"]["value"])
+    for rows, cols in ((2048, 7168), (7168, 2048), (12288, 7168), (64, 7168), (256, 256), (1, 1), (3, 5)):
+        want = np.float32(np.sqrt(float(max(rows, cols))) * k)
+        assert mc.lib.muon_rms_match_scale(rows, cols) == want
+        assert mc.muon_out_scale(rows, cols) == want
+    assert mc.lib.muon_rms_match_scale(0, 7) == 0.0 and mc.lib.muon_rms_match_scale(7, -1) == 0.0
+    assert mc.OUT_SCALE_RMS_MATCH < 0
+    text = open(HEADER).read()
+    assert float(re.search(r"#define MC_OUT_SCALE_RMS_MATCH \((-?[\d.]+)f\)", text).group(1)) < 0
+

@@ -252,6 +252,27 @@ def test_maxlogit_nan_is_skipped(mc):
     assert rel_err(s[:1], ref[:1]).max() <= 1e-4
 
 
+@pytest.mark.parametrize("dtype,d_c,d_r,Sk", [(torch.float32, 64, 0, 128), (torch.float32, 48, 16, 100),
+                                              (torch.bfloat16, 40, 0, 70)])
+def test_maxlogit_nan_is_skipped_generic_kernel(mc, dtype, d_c, d_r, Sk):
+    """The same on the float32 LDS-tiled kernel (float32 inputs and head dims
+    the MFMA kernel does not take), which is built with IEEE NaN semantics."""
+    say("maxlogit NaN, generic kernel", dtype, d_c, d_r, Sk)
+    g = workloads.generator(14 + d_c, "cpu")
+    Q = workloads.normal((2, 3, 90, d_c + d_r), 1.0, g, "cpu", dtype)
+    Kc = workloads.normal((2, 3, Sk, d_c), 1.0, g, "cpu", dtype)
+    Kr = workloads.normal((2, Sk, d_r), 1.0, g, "cpu", dtype) if d_r else None
+    Q[1, 0, 7, 2] = float("nan")      # one NaN row of logits in head 0
+    Kc[0, 2, 11, 0] = float("nan")    # one NaN key in head 2
+    Q[:, 1] = float("nan")            # head 1: every logit NaN
+    s = mc.qk_maxlogit(Q.to(DEV), Kc.to(DEV), Kr.to(DEV) if Kr is not None else None).cpu().numpy()
+    ref = oracle.max_logit(f64(Q), f64(Kc), f64(Kr) if Kr is not None else None)
+    assert ref[1] == -np.inf and s[1] == -np.inf
+    keep = [0, 2]
+    assert np.all(np.isfinite(s[keep]))
+    assert rel_err(s[keep], ref[keep]).max() <= (1e-5 if dtype == torch.float32 else 1e-4)
+
+
 def test_maxlogit_signed_and_closed_form(mc):
     say("maxlogit closed form")
     d, S, c = 64, 96, 3.0
@@ -469,3 +490,38 @@ def test_full_step_tiny_attention(mc, reading):
         dg = f64(W[n]) - f64(t.W[n])
         do = new_w[n] - f64(t.W[n])
         assert rel_fro(dg, do) <= 2e-2, n
+
+
+@pytest.mark.parametrize("reading", ["std", "variance"])
+def test_full_step_tiny_attention_from_oracle_smax(mc, reading):
+    """The tiny fp32 layer end to end with nothing shared between the two
+    sides: the oracle projects Q, K itself (fp64, CPU), takes its own S_max and
+    runs its own step; the GPU path projects on the device, measures S_max with
+    qk_maxlogit and runs muonclip_step.  Clipped sets identical, gamma and
+    S_max within 1e-5 relative, weight deltas within 2e-2."""
+    say("full step tiny from the oracle's S_max", reading)
+    t = workloads.tiny_attention(seed=1, device="cpu", weight_reading=reading)
+    H, hd = t.n_heads, t.head_dim
+    # the oracle's own forward
+    Wn = {n: f64(w) for n, w in t.W.items()}
+    rq = oracle.project_heads(f64(t.X), Wn["q"], H)
+    rk = oracle.project_heads(f64(t.X), Wn["k"], H)
+    ref_s = oracle.max_logit(rq, rk)
+    att = dict(q="q", k="k", q_rows_per_head=hd, q_c_rows=hd, k_rows_per_head=hd)
+    new_w, _, rg, rc = oracle.muonclip_step(Wn, {n: g_.numpy() for n, g_ in t.G.items()}, {}, ref_s, att,
+                                            lr=0.02, w_dtype="f32")
+    # the library's
+    Xd = t.X.to(DEV)
+    W = {n: w.to(DEV) for n, w in t.W.items()}
+    G = {n: g_.to(DEV) for n, g_ in t.G.items()}
+    Qd = (Xd @ W["q"].t().contiguous()).view(2, 128, H, hd).transpose(1, 2).contiguous()
+    Kd = (Xd @ W["k"].t().contiguous()).view(2, 128, H, hd).transpose(1, 2).contiguous()
+    smax = mc.qk_maxlogit(Qd, Kd)
+    gamma, clipped = mc.muonclip_step(W, G, {}, smax, att, lr=0.02)
+    torch.cuda.synchronize()
+    assert rel_err(smax.cpu().numpy(), ref_s).max() <= 1e-5
+    assert clipped.cpu().tolist() == rc.tolist()
+    assert (rc[0] == 1) == (reading == "variance")
+    assert rel_err(gamma.cpu().numpy(), rg).max() <= 1e-5
+    for n in ("q", "k", "v"):
+        assert rel_fro(f64(W[n]) - Wn[n], new_w[n] - Wn[n]) <= 2e-2, n
