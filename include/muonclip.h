@@ -215,6 +215,36 @@ MC_API mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, flo
                                                    void* const* gemm_events);
 
 /*
+ * muon_momentum_ns_update_batched_noalloc -- the same fused Muon call for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace: its scratch is a static device array of the library,
+ * MC_NOALLOC_SCRATCH_BYTES (192 MiB) on each GPU the library runs on, held
+ * from the library's first use on that GPU until the process ends.  The
+ * call itself allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller passes M, G, W and the coefficients as for
+ * muon_momentum_ns_update_batched, with the same results bit for bit.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (no part of it needs to start at zero: each call writes
+ * every byte it reads).  Calls that overlap in time on one GPU (different
+ * streams, or host threads) race on it and give undefined results: order
+ * them on one stream.  The first call on a GPU looks up the array's address
+ * (hipGetSymbolAddress) with that GPU current; later calls reuse it.
+ *
+ * Arguments, sizes and errors as muon_momentum_ns_update_batched, plus
+ * MC_EWORKSPACE when muon_ns_workspace_bytes(batch, rows, cols) exceeds
+ * MC_NOALLOC_SCRATCH_BYTES (for example one 2048 x 7168 matrix fits, a
+ * batch of two does not), and MC_EHIP when the address lookup fails.
+ */
+#define MC_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+MC_API mc_status_t muon_momentum_ns_update_batched_noalloc(float* M, const float* G, float mu, void* W,
+                                                           int w_dtype, int64_t batch, int64_t rows, int64_t cols,
+                                                           int64_t batch_stride, int32_t steps,
+                                                           const float* coeffs, float eps, float out_scale,
+                                                           float lr, float weight_decay, void* stream);
+
+/*
  * Per-head max logit over a batch, the logits never stored:
  *   S_max^h = (1/sqrt(d)) * max_{b, i, j} Q[b,h,i,:] . K[b,h,j,:]
  * with K[b,h,j,:] = [Kc[b,h,j,0:d_c] || Kr[b,j,0:d_r]] (MLA: the rotary key

@@ -32,6 +32,7 @@ __all__ = [
     "muon_ns_orthogonalize_batched",
     "muon_apply_update",
     "muon_momentum_ns_update_batched",
+    "muon_momentum_ns_update_batched_noalloc",
     "qk_maxlogit",
     "qk_clip_apply",
     "qk_clip_apply_total",
@@ -89,6 +90,9 @@ def _load():
     L.muon_momentum_ns_update_batched.argtypes = [vp, vp, f32, vp, ctypes.c_int, i64, i64, i64, i64, i32,
                                                   ctypes.POINTER(f32), f32, f32, f32, f32, vp, ctypes.c_size_t,
                                                   vp, ctypes.POINTER(vp)]
+    L.muon_momentum_ns_update_batched_noalloc.restype = ctypes.c_int
+    L.muon_momentum_ns_update_batched_noalloc.argtypes = [vp, vp, f32, vp, ctypes.c_int, i64, i64, i64, i64, i32,
+                                                          ctypes.POINTER(f32), f32, f32, f32, f32, vp]
     L.muon_apply_update.restype = ctypes.c_int
     L.muon_apply_update.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, f32, f32, vp]
     L.qk_maxlogit.restype = ctypes.c_int
@@ -267,6 +271,29 @@ def muon_momentum_ns_update_batched(M, G, W, lr, weight_decay=0.1, mu=0.95, step
         M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
         c_coeffs, eps, out_scale, lr, weight_decay, workspace.data_ptr(), workspace.numel(), _stream(M, stream), ev)
     _check("muon_momentum_ns_update_batched", status)
+    return W
+
+
+def muon_momentum_ns_update_batched_noalloc(M, G, W, lr, weight_decay=0.1, mu=0.95, steps=NS_STEPS, coeffs=None,
+                                            eps=NS_EPS, out_scale=None, stream=None):
+    """muon_momentum_ns_update_batched with the library's static scratch instead
+    of a workspace: the call allocates nothing (for graph capture and loops that
+    must not allocate).  Calls on one GPU share the scratch, so they must not
+    overlap in time; sizes whose workspace exceeds the scratch raise."""
+    _dev(M, "M"), _dev(G, "G"), _dev(W, "W")
+    if M.dtype != torch.float32 or G.dtype != torch.float32:
+        raise ValueError("M and G must be float32")
+    if M.shape != G.shape or M.shape != W.shape:
+        raise ValueError("M, G and W must have the same shape")
+    M3 = M.unsqueeze(0) if M.dim() == 2 else M
+    if M3.dim() != 3:
+        raise ValueError("M must be [rows, cols] or [batch, rows, cols]")
+    batch, rows, cols = M3.shape
+    status = lib.muon_momentum_ns_update_batched_noalloc(
+        M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
+        _coeffs(steps, coeffs), eps, OUT_SCALE_RMS_MATCH if out_scale is None else out_scale, lr, weight_decay,
+        _stream(M, stream))
+    _check("muon_momentum_ns_update_batched_noalloc", status)
     return W
 
 

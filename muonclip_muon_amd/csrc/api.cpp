@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "mc_internal.h"
 
 namespace {
@@ -199,6 +201,31 @@ mc_status_t fused_muon(float* M, const float* G, float mu, void* W, int w_dtype,
   return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events, &X));
 }
 
+// Scratch of the allocation-free entry point: a file-scope device array, one
+// copy per GPU, resident from the library's first use on that GPU until the
+// process ends.  The name is a host-side stand-in for the device symbol; its
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kStaticScratchBytes = MC_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the device's first
+// call, with that device current), or null on failure.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -210,6 +237,26 @@ mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, float mu, 
                                             size_t workspace_bytes, void* stream, void* const* gemm_events) {
   return fused_muon(M, G, mu, W, w_dtype, batch, rows, cols, batch_stride, steps, coeffs, eps, out_scale, lr,
                     weight_decay, workspace, workspace_bytes, stream, gemm_events);
+}
+
+mc_status_t muon_momentum_ns_update_batched_noalloc(float* M, const float* G, float mu, void* W, int w_dtype,
+                                                    int64_t batch, int64_t rows, int64_t cols,
+                                                    int64_t batch_stride, int32_t steps, const float* coeffs,
+                                                    float eps, float out_scale, float lr, float weight_decay,
+                                                    void* stream) {
+  // shape checks first (a size beyond the static scratch is MC_EWORKSPACE;
+  // nothing is looked up or enqueued for an invalid call)
+  if (batch < 0 || rows < 1 || cols < 1) return MC_EINVAL;
+  {
+    const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
+    if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  }
+  if (batch == 0) return MC_OK;
+  if (mc::ns_geometry(batch, rows, cols).total > kStaticScratchBytes) return MC_EWORKSPACE;
+  void* ws = static_scratch();
+  if (!ws) return MC_EHIP;
+  return fused_muon(M, G, mu, W, w_dtype, batch, rows, cols, batch_stride, steps, coeffs, eps, out_scale, lr,
+                    weight_decay, ws, kStaticScratchBytes, stream, nullptr);
 }
 
 mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, int64_t numel,

@@ -239,3 +239,20 @@ def test_rms_match_scale_in_the_library(mc):
     text = open(HEADER).read()
     assert float(re.search(r"#define MC_OUT_SCALE_RMS_MATCH \((-?[\d.]+)f\)", text).group(1)) < 0
 
+
+def test_noalloc_validation(mc):
+    # the allocation-free entry point rejects bad arguments and sizes beyond
+    # its static scratch before any HIP call (no device is touched here)
+    L = mc.lib
+    coeffs = (ctypes.c_float * 15)(*([3.4445, -4.775, 2.0315] * 5))
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define MC_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", text).group(1)) << 20
+    assert L.muon_ns_workspace_bytes(1, 2048, 7168) <= limit < L.muon_ns_workspace_bytes(4, 2048, 7168)
+    args = (0.95, FAKE, 1, 4, 2048, 7168, 2048 * 7168, 5, coeffs, 1e-7, -1.0, 2e-4, 0.1, None)
+    assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, *args) == EWORKSPACE
+    assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, 0.95, FAKE, 1, 0, 256, 256, 0, 5, coeffs, 1e-7,
+                                                     -1.0, 2e-4, 0.1, None) == 0  # empty batch: nothing enqueued
+    assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, 0.95, FAKE, 1, 1, 0, 256, 0, 5, coeffs, 1e-7,
+                                                     -1.0, 2e-4, 0.1, None) == EINVAL
+    assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, 0.95, FAKE, 1, 1, 20000, 20000, 0, 5, coeffs,
+                                                     1e-7, -1.0, 2e-4, 0.1, None) == ESHAPE
