@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <utility>
 
 #include "mc_internal.h"
 
@@ -90,16 +91,21 @@ mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, c
   return MC_OK;
 }
 
-// The steps' GEMMs, X_0 at off_x0.  X <- (a I + b A + c A^2) X with
-// A = X X^T.  inv0 (or null): the stored X_0 is to be scaled per matrix by
-// inv0 (applied inside the first step).  upd (or null): the last step
-// updates W instead of storing X.  Returns the buffer holding the final X.
+// The steps' GEMMs, X_0 at off_x0 (high part) and off_xl0 (low part):
+// A = Xh Xh^T; B = b A + c A A = diag(d) + N; X <- (a + d) X + N Xh (X
+// carried as a bf16 pair, d in float32).
+// inv0 (or null): the stored X_0 is to be scaled per matrix by inv0 (applied
+// inside the first step).  upd (or null): the last step updates W (or writes
+// the output) instead of storing X.
 hipError_t run_ns_steps(const mc::NsGeometry& g, char* ws, int32_t steps, const float* coeffs, const float* inv0,
-                        const mc::NsUpdate* upd, hipStream_t s, void* const* gemm_events, uint16_t** x_final) {
+                        const mc::NsUpdate* upd, hipStream_t s, void* const* gemm_events) {
   uint16_t* X = reinterpret_cast<uint16_t*>(ws + g.off_x0);
   uint16_t* Xn = reinterpret_cast<uint16_t*>(ws + g.off_x1);
+  uint16_t* XL = reinterpret_cast<uint16_t*>(ws + g.off_xl0);
+  uint16_t* XLn = reinterpret_cast<uint16_t*>(ws + g.off_xl1);
   uint16_t* A = reinterpret_cast<uint16_t*>(ws + g.off_a);
   uint16_t* B = reinterpret_cast<uint16_t*>(ws + g.off_b);
+  float* D = reinterpret_cast<float*>(ws + g.off_d);
   auto record = [&](int idx) -> hipError_t {
     return gemm_events ? hipEventRecord(static_cast<hipEvent_t>(gemm_events[idx]), s) : hipSuccess;
   };
@@ -107,23 +113,21 @@ hipError_t run_ns_steps(const mc::NsGeometry& g, char* ws, int32_t steps, const 
   for (int st = 0; st < steps; ++st) {
     const float a = coeffs[3 * st], b = coeffs[3 * st + 1], c = coeffs[3 * st + 2];
     const float* inv = st == 0 ? inv0 : nullptr;
-    const uint16_t* in0[3] = {X, A, B};
-    const uint16_t* in1[3] = {nullptr, nullptr, X};
-    uint16_t* out[3] = {A, B, Xn};
-    const float alpha[3] = {0.f, b, 0.f}, beta[3] = {0.f, c, 0.f}, diag[3] = {0.f, a, 0.f};
-    const float* invs[3] = {inv, nullptr, inv};
-    const mc::NsUpdate* upds[3] = {nullptr, nullptr, st == steps - 1 ? upd : nullptr};
+    const bool last = st == steps - 1;
     for (int gm = 0; gm < 3; ++gm) {
       if ((e = record(2 * (3 * st + gm))) != hipSuccess) return e;
-      e = mc::launch_ns_gemm(gm, g, in0[gm], in1[gm], out[gm], alpha[gm], beta[gm], diag[gm], invs[gm], upds[gm], s);
+      if (gm == 0)
+        e = mc::launch_ns_gemm(0, g, X, nullptr, nullptr, A, nullptr, nullptr, 0.f, 0.f, 0.f, inv, nullptr, s);
+      else if (gm == 1)
+        e = mc::launch_ns_gemm(1, g, A, nullptr, nullptr, B, nullptr, D, b, c, 0.f, nullptr, nullptr, s);
+      else
+        e = mc::launch_ns_gemm(2, g, B, X, XL, Xn, XLn, D, 0.f, 0.f, a, inv, last ? upd : nullptr, s);
       if (e != hipSuccess) return e;
       if ((e = record(2 * (3 * st + gm) + 1)) != hipSuccess) return e;
     }
-    uint16_t* tmp = X;
-    X = Xn;
-    Xn = tmp;
+    std::swap(X, Xn);
+    std::swap(XL, XLn);
   }
-  *x_final = X;
   return hipSuccess;
 }
 
@@ -161,8 +165,7 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
   // the last step's X' = B' X writes O = out_scale * X' (transposed back)
   mc::NsUpdate out{O, o_bf16, o_batch_stride, mc::resolve_out_scale(out_scale, rows, cols), 0.f, 0.f, true};
-  uint16_t* X = nullptr;
-  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &out, s, gemm_events, &X));
+  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &out, s, gemm_events));
 }
 
 }  // extern "C"
@@ -197,8 +200,7 @@ mc_status_t fused_muon(float* M, const float* G, float mu, void* W, int w_dtype,
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
   mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, mc::resolve_out_scale(out_scale, rows, cols), lr,
                    weight_decay, false};
-  uint16_t* X = nullptr;
-  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events, &X));
+  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events));
 }
 
 // Scratch of the allocation-free entry point: a file-scope device array, one

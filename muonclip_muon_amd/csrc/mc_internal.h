@@ -40,21 +40,24 @@ struct NsGeometry {
   int64_t n_pad, m_pad;  // padded to kNsTile
   bool transposed;       // rows > cols: X = M^T
   int64_t prescale_tiles;  // 4096-element blocks per matrix of the pre-scale (norm partials)
-  // byte offsets inside the workspace: X (two ping-pong copies, n_pad x m_pad),
-  // A and B' (n_pad x n_pad), norm partials, 1/norm
-  size_t off_x0, off_x1, off_a, off_b, off_partials, off_invnorm, total;
+  // byte offsets inside the workspace: X as bf16 high and low parts (two
+  // ping-pong copies of each, n_pad x m_pad), A and B (n_pad x n_pad), B's
+  // diagonal (float32, n_pad), norm partials, 1/norm
+  size_t off_x0, off_x1, off_xl0, off_xl1, off_a, off_b, off_d, off_partials, off_invnorm, total;
 };
 constexpr int64_t kNsTile = 256;
 NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols);
 
-// X_0 = bf16(M_b) unscaled at off_x0 (M only read, float32 or bf16, batch
-// matrices of rows x cols at m_batch_stride) and 1 / (||M_b||_F + eps) per
+// X_0 = M_b unscaled as a bf16 pair, high part bf16(M) at off_x0 and low
+// part bf16(M - high) at off_xl0 (M only read, float32 or bf16, batch
+// matrices of rows x cols at m_batch_stride), and 1 / (||M_b||_F + eps) per
 // matrix at off_invnorm (applied by the first step's GEMMs).
 hipError_t launch_ns_prescale_unscaled(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
                                        float eps, char* ws, hipStream_t stream);
 // Fused: M <- mu M + G in place (float32, batch matrices of rows x cols at
-// batch_stride), X_0 = bf16(M) unscaled at off_x0, and 1 / (||M||_F + eps)
-// per matrix at off_invnorm (to be applied by the first step's GEMMs).
+// batch_stride), X_0 = M unscaled as a bf16 pair at off_x0 / off_xl0, and
+// 1 / (||M||_F + eps) per matrix at off_invnorm (to be applied by the first
+// step's GEMMs).
 hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
                                     const NsGeometry& g, float eps, char* ws, hipStream_t stream);
 // In-place update applied by the last step's X' = B' X instead of storing X':
@@ -69,15 +72,19 @@ struct NsUpdate {
   float out_scale, lr, wd;
   bool output;
 };
-// One GEMM of the polynomial step, on the whole batch:
-//   mode 0: A = X X^T                          (in0: X, out: A)
-//   mode 1: B' = diag I + alpha A + beta A A   (in0: A, out: B')
-//   mode 2: X' = B' X                          (in0: B', in1: X, out: X', or upd)
+// One GEMM of the polynomial step, on the whole batch.  X is carried as a
+// pair of bf16 matrices, X = Xh + Xl (high part and the rounding residual),
+// and B = b A + c A A as its float32 diagonal d and a bf16 matrix N with a
+// zero diagonal; the products read the high part of X only:
+//   mode 0: A = Xh Xh^T                          (in0: Xh, out: A)
+//   mode 1: B = alpha A + beta A A               (in0: A, out: N, dg: d)
+//   mode 2: X' = (a + d) X + N Xh, a = `a`       (in0: N, in1: Xh, xl: Xl, dg: d;
+//           out: X'h, xl_out: X'l, or the update / output through upd)
 // inv (device, per matrix, or null): X is inv_b times the stored X (the first
-// step of the fused path); mode 0 scales A by inv_b^2, mode 2 X' by inv_b.
+// step); mode 0 scales A by inv_b^2, mode 2 X' by inv_b.
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          uint16_t* out, float alpha, float beta, float diag, const float* inv,
-                          const NsUpdate* upd, hipStream_t stream);
+                          const uint16_t* xl, uint16_t* out, uint16_t* xl_out, float* dg, float alpha, float beta,
+                          float a, const float* inv, const NsUpdate* upd, hipStream_t stream);
 
 // ---------------------------------------------------------------- max logit
 hipError_t launch_maxlogit_init(float* smax, int64_t H, hipStream_t stream);

@@ -1,16 +1,34 @@
 // Batched bf16 MFMA GEMMs of one Newton-Schulz step (gfx950).
 //
 // One step of the odd polynomial p(X) = a X + b (X X^T) X + c (X X^T)^2 X is
-// three GEMMs on the zero-padded n_pad x m_pad bf16 state X:
-//   mode 0  A  = X X^T                    K = m_pad   (out n_pad x n_pad)
-//   mode 1  B' = a I + b A + c A A        K = n_pad   (A symmetric: A A = A^T A)
-//   mode 2  X' = B' X                     K = n_pad   (out n_pad x m_pad)
-// All three accumulate in float32 on v_mfma_f32_32x32x16_bf16 and round the
-// epilogue result once to bf16.  Folding a I into B' makes the third product
-// a plain GEMM (no re-read of X after its K loop); B' is then rounded once
-// with its diagonal included.  A and B' are symmetric, so modes 0/1 compute
-// only the tiles on and above the diagonal and write each off-diagonal tile
-// twice.
+// three GEMMs on the zero-padded n_pad x m_pad state X:
+//   mode 0  A  = Xh Xh^T                  K = m_pad   (out n_pad x n_pad)
+//   mode 1  B  = b A + c A A              K = n_pad   (A symmetric: A A = A^T A)
+//   mode 2  X' = (a + d) X + N Xh         K = n_pad   (out n_pad x m_pad)
+// with B split into its diagonal d (float32, one value per row) and the
+// rest N (bf16, zero diagonal).
+// X is carried as two bf16 matrices, X = Xh + Xl (the high part and the
+// rounding residual, about 16 significant bits together).  The products read
+// the high part only, on v_mfma_f32_32x32x16_bf16 with float32 accumulation;
+// the diagonal term (a + d) X is added in float32 in the epilogue of the
+// third product, from both parts of X, and X' is split into its two parts
+// again.  Why:
+// along singular directions with small singular values the iteration acts
+// as x -> a x (a = 3.4445), so an error there grows about a^5 ~ 490-fold over
+// five steps; rounding X (or a B' = a I + B with a folded diagonal) to bf16
+// puts an error of 2^-9 of X's largest components into every direction,
+// which for low-rank or decaying spectra swamps the small components (a bf16
+// emulation against the exact result: relative Frobenius error 1.2 for rank
+// 1, 0.38 for rank 16 plus noise, 0.037 for four decades of singular values
+// at 2048 x 7168).  With the linear term exact to 16 bits those errors drop
+// to 3.1e-3, 2.9e-3 and 4.9e-3; the errors that N Xh keeps fall along B's
+// range, the large singular directions, where they are relatively small.
+// Keeping B's diagonal out of the bf16 rounding matters where a + d nearly
+// cancels (d -> 1 - a as a singular value converges): rounding B whole
+// costs Gaussian matrices 1.1e-2, tiny ones (1 x 40) 2.4e-2; with d exact,
+// 5.1e-3 and 2.0e-3 (the folded bf16 form: 7.0e-3 and 1.0e-2).  A and B are
+// symmetric, so modes 0/1 compute only the tiles on and above the diagonal
+// and write each off-diagonal tile twice.
 //
 // Tiling: a 512-thread workgroup (8 wave64s, 2 x 4, two per SIMD) owns a
 // 256 x 256 output tile; each wave owns 128 x 64 = 4 x 2 MFMA tiles of
@@ -309,11 +327,16 @@ struct UpdArgs {
 // step); otherwise the epilogue has no multiply.  TR (UPD != 0 only): W is
 // the transpose of X' (a matrix iterated on as its transpose); a template
 // parameter so each epilogue is compiled for its own access pattern.
+// Mode 1: B = alpha A + beta A A, its diagonal written to dg (float32,
+// n_pad per matrix) and zero in `out`.  Mode 2 reads X's low part xl (with
+// in1 = Xh) and B's diagonal dg and, unless UPD, writes X''s low part to
+// xl_out; acoef is a.
 template <int MODE, int UPD, bool SCALED, bool TR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
-                    uint16_t* __restrict__ out, int n_pad, int m_pad, int tiles_n, int tiles_per_mat,
-                    float alpha, float beta, float diag, const float* __restrict__ inv, UpdArgs ua) {
+                    const uint16_t* __restrict__ xl, uint16_t* __restrict__ out, uint16_t* __restrict__ xl_out,
+                    float* __restrict__ dg, int n_pad, int m_pad, int tiles_n, int tiles_per_mat, float alpha,
+                    float beta, float acoef, const float* __restrict__ inv, UpdArgs ua) {
   static_assert(UPD == 0 || MODE == 2, "only X' = B' X can apply the update");
   static_assert(UPD != 0 || !TR, "TR describes W");
   constexpr bool kQKRows = MODE == 2;      // right operand X as K-rows tiles
@@ -483,17 +506,57 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // X is inv_b times the stored X in the first step of the fused path
   const float xs = (inv != nullptr) ? inv[mat] : 1.0f;
 
+  // Mode 2: X' = (a + d) X + N Xh, the diagonal term in float32 from both
+  // parts of X at this lane's accumulator positions (4 consecutive columns, 8 bytes
+  // of each part per MFMA register group), half of the tile's rows at a time
+  // to bound the registers held; the accumulators become X' / xs.  Done
+  // before anything else of the epilogue holds registers (the W of the
+  // update, A of mode 1).
+  if constexpr (MODE == 2) {
+    const uint16_t* Xh = in1 + mat * nm;
+    const uint16_t* Xl = xl + mat * nm;
+    float lin[4];  // a + d_i of this lane's 4 rows
+#pragma unroll
+    for (int y = 0; y < 4; ++y) lin[y] = acoef + dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row];
+#pragma unroll
+    for (int yh = 0; yh < 4; yh += 2) {
+      u32x2 hb[2][kCT][4], lb[2][kCT][4];
+#pragma unroll
+      for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+        for (int x = 0; x < kCT; ++x)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t o = x_off(i0w + (yh + yy) * 32 + frag_row,
+                                    j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, n_pad);
+            hb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xh + o);
+            lb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xl + o);
+          }
+#pragma unroll
+      for (int yy = 0; yy < 2; ++yy)
+#pragma unroll
+        for (int x = 0; x < kCT; ++x)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 h = hb[yy][x][g], l = lb[yy][x][g];
+            const float xv[4] = {bf16_lo(h.x) + bf16_lo(l.x), bf16_hi(h.x) + bf16_hi(l.x),
+                                 bf16_lo(h.y) + bf16_lo(l.y), bf16_hi(h.y) + bf16_hi(l.y)};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[x][yh + yy][4 * g + q] += lin[yh + yy] * xv[q];
+          }
+    }
+  }
   wait_vmem<0>();
   __syncthreads();
   uint16_t* O = out + mat * ((MODE == 2) ? nm : nn);
   const uint32_t eb = lds + (2 * wm + (wn >> 1)) * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
 
-  // Fused update (UPD != 0): this wave's 16 passes of W are loaded before the
-  // accumulators are staged, so their latency overlaps the staging, for bf16
-  // W in the straight case (measured 6 % faster); float32 W (twice the
-  // registers) and transposed W (5 % slower loaded early) are loaded after
-  // the staging.  Pass s:
+  // Fused update (UPD != 0): this wave's 16 passes of W are loaded after the
+  // accumulators are staged (loading bf16 W before the staging overlapped
+  // its latency, 6 % faster without the linear-term fold, but W, the fold's
+  // X values and the accumulators no longer fit in the registers together).
+  // Pass s:
   // straight W, lane takes staged row 4 s + lane / 16, unit lane % 16 (W row
   // i0w + row, 8 columns); transposed W, lane takes staged column
   // jj = C + lane % 16 and rows R .. R + 7 (two transposed reads), i.e. 8
@@ -538,8 +601,6 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
     }
   };
-  constexpr bool w_early = UPD == 1 && !TR;
-  if constexpr (w_early) load_w();
 
   // mode 1: the A values at this lane's accumulator positions (4 consecutive
   // columns, 8 bytes of the blocked layout, per MFMA register group), loaded
@@ -556,41 +617,61 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           abuf[y][x][g] = *reinterpret_cast<const u32x2*>(
               Am + blk_off(i0w + y * 32 + frag_row, j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, nkb));
   }
-  // a I lands on the region only if it straddles the diagonal
+  // the region straddles B's diagonal (mode 1)
   const bool on_diag = MODE == 1 && i0w == j0w;
+  // The value of accumulator group (y, x, g) as the epilogue rounds it:
+  // scaled by 1/||M|| in the first step, combined with A in mode 1.
+  auto value = [&](int y, int x, int g, float (&v)[4]) {
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int ii = y * 32 + frag_row;
+    for (int q = 0; q < 4; ++q) v[q] = acc[x][y][4 * g + q];
+    if constexpr (MODE == 0 && SCALED) {
+      const float s2 = xs * xs;
 #pragma unroll
-    for (int x = 0; x < kCT; ++x) {
+      for (int q = 0; q < 4; ++q) v[q] *= s2;
+    } else if constexpr (MODE == 2 && SCALED) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t a = st_addr(ii, 8 * wh + 4 * x + g) + 8 * frag_half;
-        float v[4] = {acc[x][y][4 * g + 0], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]};
-        if constexpr (MODE == 0 && SCALED) {
-          const float s2 = xs * xs;
+      for (int q = 0; q < 4; ++q) v[q] *= xs;
+    }
+    if constexpr (MODE == 1) {
+      const u32x2 e = abuf[y][x][g];
+      const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] *= s2;
-        } else if constexpr (MODE == 2 && SCALED) {
+      for (int q = 0; q < 4; ++q) v[q] = alpha * ev[q] + beta * v[q];
+      // the diagonal leaves the bf16 matrix for dg (float32)
+      if (on_diag) {
+        const int ii = y * 32 + frag_row, jj0 = kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] *= xs;
-        }
-        if constexpr (MODE == 1) {
-          const u32x2 e = abuf[y][x][g];
-          const float ev[4] = {bf16_lo(e.x), bf16_hi(e.x), bf16_lo(e.y), bf16_hi(e.y)};
-          // column of v[0] within the region
-          const int jj0 = kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float scaled = alpha * ev[q] + beta * v[q];
-            v[q] = (on_diag && ii == jj0 + q) ? scaled + diag : scaled;
+        for (int q = 0; q < 4; ++q)
+          if (ii == jj0 + q) {
+            dg[static_cast<int64_t>(mat) * n_pad + i0w + ii] = v[q];
+            v[q] = 0.f;
           }
-        }
-        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *(lds_u32x2_t*)(uintptr_t)a = o;
       }
     }
-  }
+  };
+  // Stage the bf16 high parts (LO false) or the low parts v - bf16(v).
+  auto stage = [&](bool lo) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int ii = y * 32 + frag_row;
+#pragma unroll
+      for (int x = 0; x < kCT; ++x) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t a = st_addr(ii, 8 * wh + 4 * x + g) + 8 * frag_half;
+          float v[4];
+          value(y, x, g, v);
+          if (lo) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] -= bf16_to_f32(f32_to_bf16(v[q]));
+          }
+          const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(lds_u32x2_t*)(uintptr_t)a = o;
+        }
+      }
+    }
+  };
+  stage(false);
   // the region is complete once both of its waves have written
   __syncthreads();
   if constexpr (UPD != 0) {
@@ -622,8 +703,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         unpack8(u32x4{l2.x, l2.y, h2.x, h2.y}, x);
       }
     };
-    // the wave's 16 passes (bf16 W already in wbuf)
-    if constexpr (kReadW && !w_early) load_w();
+    // the wave's 16 passes
+    if constexpr (kReadW) load_w();
     constexpr int kBatch = 16;
     for (int s0 = 16 * wh; s0 < 16 * wh + 16; s0 += kBatch) {
 #pragma unroll
@@ -685,26 +766,34 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     return;
   }
   // direct store: 4 rows of 256 bytes per instruction
-  {
+  auto store_rows = [&](uint16_t* D) {
 #pragma unroll 4
     for (int s = 16 * wh; s < 16 * wh + 16; ++s) {
       const int row = 4 * s + (lane >> 4), u = lane & 15;
       const u32x4 v = *(const lds_u32x4_t*)(uintptr_t)st_addr(row, u);
-      uint16_t* dst = kBlockedOut ? O + blk_off(i0w + row, j0w + 8 * u, nkb)
-                                  : O + x_off(i0w + row, j0w + 8 * u, n_pad);
+      uint16_t* dst = kBlockedOut ? D + blk_off(i0w + row, j0w + 8 * u, nkb)
+                                  : D + x_off(i0w + row, j0w + 8 * u, n_pad);
       *reinterpret_cast<u32x4*>(dst) = v;
     }
-  }
+  };
+  store_rows(O);
   if constexpr (MODE != 2) {
     if (ti != tj) store_transposed(eb, O, j0w, i0w, nkb, lane, 16 * wh);
+  } else {
+    // X''s low part through the same staging, once every wave has read the
+    // high part
+    __syncthreads();
+    stage(true);
+    __syncthreads();
+    store_rows(xl_out + mat * nm);
   }
 }
 
 }  // namespace
 
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          uint16_t* out, float alpha, float beta, float diag, const float* inv,
-                          const NsUpdate* upd, hipStream_t stream) {
+                          const uint16_t* xl, uint16_t* out, uint16_t* xl_out, float* dg, float alpha, float beta,
+                          float a, const float* inv, const NsUpdate* upd, hipStream_t stream) {
   const int n_pad = static_cast<int>(g.n_pad), m_pad = static_cast<int>(g.m_pad);
   const int tiles_m = n_pad / kBM;
   const int tiles_n = (mode == 2) ? m_pad / kBN : n_pad / kBN;
@@ -723,8 +812,8 @@ hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, co
     ua.wd = upd->wd;
   }
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, in0, in1, out, n_pad, m_pad, tiles_n, tiles_per_mat,
-                       alpha, beta, diag, inv, ua);
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, in0, in1, xl, out, xl_out, dg, n_pad, m_pad,
+                       tiles_n, tiles_per_mat, alpha, beta, a, inv, ua);
   };
   const bool sc = inv != nullptr, tr = g.transposed;
   // the last step's epilogue: one instance per scaling and W orientation

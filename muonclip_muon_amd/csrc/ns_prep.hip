@@ -1,9 +1,11 @@
 // Newton-Schulz input stage: the workspace geometry, the pre-scale and the
 // norm.
 //
-//   pre-scale  X_0 = bf16(M_b), or of M_b^T when rows > cols, unscaled,
-//              written into the zero-padded n_pad x m_pad workspace layout
-//              the GEMMs use, plus float32 partial sums of squares per 4096-
+//   pre-scale  X_0 = M_b, or M_b^T when rows > cols, unscaled, as a pair of
+//              bf16 matrices (high part bf16(x), low part bf16(x - high):
+//              about 16 significant bits), written into the zero-padded
+//              n_pad x m_pad workspace layout the GEMMs use, plus float32
+//              partial sums of squares per 4096-
 //              element block; one block per matrix then combines them in
 //              double in a fixed order (deterministic), giving
 //              inv_b = 1 / (||M_b||_F + eps), which the first Newton-Schulz
@@ -43,8 +45,11 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   size_t off = 0;
   g.off_x0 = off; off = align256(off + xb);
   g.off_x1 = off; off = align256(off + xb);
+  g.off_xl0 = off; off = align256(off + xb);
+  g.off_xl1 = off; off = align256(off + xb);
   g.off_a = off; off = align256(off + ab);
   g.off_b = off; off = align256(off + ab);
+  g.off_d = off; off = align256(off + static_cast<size_t>(batch) * g.n_pad * 4);
   const int64_t partials = g.prescale_tiles;
   g.off_partials = off; off = align256(off + static_cast<size_t>(batch * partials) * 4);
   g.off_invnorm = off; off = align256(off + static_cast<size_t>(batch) * 4);
@@ -63,6 +68,15 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   if (threadIdx.x == 0)
     for (int i = 0; i < kThreads / 64; ++i) s += red[i];
   return s;
+}
+
+// 8 values as bf16 high parts and as the low parts bf16(x - high)
+__device__ __forceinline__ void pack_hi_lo8(const float (&x)[8], u32x4& hi, u32x4& lo) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e] - bf16_to_f32(f32_to_bf16(x[e]));
+  hi = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+  lo = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
 }
 
 // grid (batch): inv_b = 1 / (sqrt(sum of partials) + eps), combined in double
@@ -105,9 +119,10 @@ __device__ __forceinline__ float load1_src(const void* M, int64_t idx) {
 
 // Fused momentum and pre-scale (SRC = 0).  M_b, G_b are R x C float32 (rows
 // x cols); M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the
-// stand-alone momentum), and the new M_b is written unscaled as bf16 into S
-// (R_pad x C_pad; rows <= cols: X_0 = M) or transposed into T (C_pad x
-// R_pad; rows > cols: X_0 = M^T), zero-padded; the other pointer is null.
+// stand-alone momentum), and the new M_b is written unscaled as a bf16 pair
+// (high parts into S, low parts into SL; R_pad x C_pad; rows <= cols:
+// X_0 = M) or transposed (T, TL; C_pad x R_pad; rows > cols: X_0 = M^T),
+// zero-padded; the other two pointers are null.
 // Each block reads one 64 x 64 tile in 8-element runs (vector loads when
 // VEC) and writes it straight from registers or transposed through LDS; it
 // also writes the float32 sum of squares of its tile's new M values to
@@ -122,6 +137,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
                                                                     int64_t C, int64_t R_pad, int64_t C_pad,
                                                                     uint16_t* __restrict__ S,
                                                                     uint16_t* __restrict__ T,
+                                                                    uint16_t* __restrict__ SL,
+                                                                    uint16_t* __restrict__ TL,
                                                                     float* __restrict__ partials) {
   __shared__ float tile[kT][kT + 1];
   __shared__ float red[kThreads / 64];
@@ -133,6 +150,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
   const float* gb = SRC == 0 ? G + b * batch_stride : nullptr;
   uint16_t* sb = S + static_cast<size_t>(b) * R_pad * C_pad;
   uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
+  uint16_t* slb = SL + static_cast<size_t>(b) * R_pad * C_pad;
+  uint16_t* tlb = TL + static_cast<size_t>(b) * R_pad * C_pad;
   const int q = threadIdx.x & 7;
   float ss = 0.f;
 #pragma unroll
@@ -185,9 +204,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
     if (S != nullptr) {
-      const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                       pack_bf16x2(x[6], x[7])};
-      *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = o;
+      u32x4 hi, lo;
+      pack_hi_lo8(x, hi, lo);
+      *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = hi;
+      *reinterpret_cast<u32x4*>(slb + x_off(r, c, R_pad)) = lo;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
@@ -201,9 +221,13 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
   for (int pass = 0; pass < 2; ++pass) {
     const int cc = pass * 32 + (threadIdx.x >> 3);
     const int rq = 8 * q;
-    const u32x4 o = {pack_bf16x2(tile[rq + 0][cc], tile[rq + 1][cc]), pack_bf16x2(tile[rq + 2][cc], tile[rq + 3][cc]),
-                     pack_bf16x2(tile[rq + 4][cc], tile[rq + 5][cc]), pack_bf16x2(tile[rq + 6][cc], tile[rq + 7][cc])};
-    *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = o;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[rq + e][cc];
+    u32x4 hi, lo;
+    pack_hi_lo8(v, hi, lo);
+    *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = hi;
+    *reinterpret_cast<u32x4*>(tlb + x_off(c0 + cc, r0 + rq, C_pad)) = lo;
   }
 }
 
@@ -217,7 +241,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
 template <int SRC>
 __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     void* __restrict__ Mv, const float* __restrict__ G, int64_t batch_stride, float mu, int64_t R, int64_t C,
-    int64_t R_pad, int64_t C_pad, uint16_t* __restrict__ X0, float* __restrict__ partials) {
+    int64_t R_pad, int64_t C_pad, uint16_t* __restrict__ X0, uint16_t* __restrict__ X0l,
+    float* __restrict__ partials) {
   __shared__ float red[kThreads / 64];
   const int64_t b = blockIdx.z;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + 8 * (threadIdx.x & 31);
@@ -226,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
                               : static_cast<const void*>(mb);
   const float* gb = SRC == 0 ? G + b * batch_stride : nullptr;
   uint16_t* xb = X0 + static_cast<size_t>(b) * R_pad * C_pad;
+  uint16_t* xlb = X0l + static_cast<size_t>(b) * R_pad * C_pad;
   float ss = 0.f;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -258,9 +284,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-    const u32x4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                     pack_bf16x2(x[6], x[7])};
-    *reinterpret_cast<u32x4*>(xb + x_off(r, c, R_pad)) = o;
+    u32x4 hi, lo;
+    pack_hi_lo8(x, hi, lo);
+    *reinterpret_cast<u32x4*>(xb + x_off(r, c, R_pad)) = hi;
+    *reinterpret_cast<u32x4*>(xlb + x_off(r, c, R_pad)) = lo;
   }
   const float block_ss = block_sum(ss, red);
   if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = block_ss;
@@ -273,10 +300,13 @@ hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_strid
   float* partials = reinterpret_cast<float*>(ws + g.off_partials);
   float* invnorm = reinterpret_cast<float*>(ws + g.off_invnorm);
   uint16_t* X0 = reinterpret_cast<uint16_t*>(ws + g.off_x0);
+  uint16_t* X0l = reinterpret_cast<uint16_t*>(ws + g.off_xl0);
   const int64_t R = g.rows, C = g.cols;
   const int64_t R_pad = g.transposed ? g.m_pad : g.n_pad, C_pad = g.transposed ? g.n_pad : g.m_pad;
   uint16_t* S = g.transposed ? nullptr : X0;
   uint16_t* T = g.transposed ? X0 : nullptr;
+  uint16_t* SL = g.transposed ? nullptr : X0l;
+  uint16_t* TL = g.transposed ? X0l : nullptr;
   const size_t align = SRC == 2 ? 16 : 32;  // one 8-element run
   const bool vec = C % 8 == 0 && (g.batch == 1 || batch_stride % 8 == 0) &&
                    reinterpret_cast<uintptr_t>(M) % align == 0 &&
@@ -286,13 +316,13 @@ hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_strid
     hipLaunchKernelGGL(momentum_prescale_rows_kernel<SRC>,
                        dim3(static_cast<unsigned>(C_pad / 256), static_cast<unsigned>(R_pad / 16),
                             static_cast<unsigned>(g.batch)),
-                       dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C, R_pad, C_pad, S, partials);
+                       dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C, R_pad, C_pad, S, SL, partials);
   else if (vec)
     hipLaunchKernelGGL((momentum_prescale_kernel<true, SRC>), grid, dim3(kThreads), 0, stream, M, G, batch_stride,
-                       mu, R, C, R_pad, C_pad, S, T, partials);
+                       mu, R, C, R_pad, C_pad, S, T, SL, TL, partials);
   else
     hipLaunchKernelGGL((momentum_prescale_kernel<false, SRC>), grid, dim3(kThreads), 0, stream, M, G,
-                       batch_stride, mu, R, C, R_pad, C_pad, S, T, partials);
+                       batch_stride, mu, R, C, R_pad, C_pad, S, T, SL, TL, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(invnorm_kernel, dim3(static_cast<unsigned>(g.batch)), dim3(kThreads), 0, stream, partials,

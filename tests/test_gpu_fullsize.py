@@ -142,20 +142,23 @@ def test_maxlogit_long_context_32k(mc):
         assert rel_err(s[h], ref) <= 1e-4
 
 
-@pytest.mark.parametrize("shape", [(64, 2048, 7168), (8, 7168, 2048)])
+@pytest.mark.parametrize("shape", [(64, 2048, 7168), (64, 7168, 2048), (1, 12288, 7168), (1, 8192, 7168),
+                                   (1, 64, 7168)])
 def test_fused_expert_batch(mc, shape):
-    """The fused momentum + Newton-Schulz + update call at the benchmark's chunk
-    shapes (64 gate/up experts; 8 down-projection experts, iterated on the
-    transpose): sampled momentum elements bit-exact, and W_t - W_{t-1} of two
-    matrices against the oracle (lr 1 so that the update, not the bf16
-    rounding of W, dominates the difference)."""
+    """The fused momentum + Newton-Schulz + update call at every shape the
+    benchmark times, in its launch configuration: chunks of 64 gate/up
+    experts and of 64 down-projection experts (iterated on the transpose),
+    and W_q, W_kc, W_kr one matrix per call.  Sampled momentum elements
+    bit-exact, and W_t - W_{t-1} of the first and last matrix against the
+    oracle (lr 1 so that the update, not the bf16 rounding of W, dominates
+    the difference)."""
     batch, rows, cols = shape
     say("full size fused:", shape)
     gen = workloads.generator(31 + rows, DEV)
     M = workloads.normal(shape, 1e-4, gen, DEV)
     G = workloads.normal(shape, 1e-4, gen, DEV)
     W = workloads.normal(shape, 0.02, gen, DEV, torch.bfloat16)
-    idx_t = torch.from_numpy(_sample(M.numel(), 1 << 20, 3)).to(DEV)
+    idx_t = torch.from_numpy(_sample(M.numel(), min(1 << 20, M.numel()), 3)).to(DEV)
     m0 = M.view(-1)[idx_t].cpu().numpy()
     g0 = G.view(-1)[idx_t].cpu().numpy()
     picks = (0, batch - 1)

@@ -29,6 +29,8 @@ __all__ = [
     "mla_project",
     "mla_logits",
     "randperm_heads",
+    "spectral_momentum",
+    "SPECTRAL_KINDS",
 ]
 
 
@@ -157,3 +159,43 @@ def mla_logits(seed=3, device="cpu", batch=8, seq=4096, d_model=7168, n_heads=64
     Q, Kc, Kr = mla_project(X, Wq, Wkc, Wkr, n_heads)
     del X
     return MlaLogits(Q, Kc, Kr, hot)
+
+
+# ---------------------------------------------------------------------------
+# Momentum matrices with prescribed spectra, for Newton-Schulz parity beyond
+# Gaussian inputs.  A rarely routed expert's gradient is a sum of a few
+# token outer products (low rank); accumulated momentum mixes them with
+# small noise; trained weights' momenta have decaying spectra.
+# ---------------------------------------------------------------------------
+SPECTRAL_KINDS = ("gauss", "decay4", "rank16_noise", "rank1", "rank4")
+
+
+def spectral_momentum(kind, rows, cols, seed=0, std=1e-3, device="cpu"):
+    """A float32 rows x cols matrix with entries of size ~std whose spectrum is:
+    'gauss'         i.i.d. N(0, std);
+    'decay4'        singular values logspace(0, -4, min(rows, cols)) (four
+                    decades) with Haar-random singular vectors (QR of Gaussian
+                    matrices);
+    'rank16_noise'  a rank-16 product of Gaussian factors plus i.i.d. noise of
+                    1e-3 times its entry size;
+    'rank1'         an exact outer product u v^T of Gaussian vectors;
+    'rank4'         an exact rank-4 product of Gaussian factors.
+    Drawn in float64 on the CPU from `seed`, rounded to float32 once."""
+    g = generator(seed, "cpu")
+    n = min(rows, cols)
+    f64 = torch.float64
+    if kind == "gauss":
+        M = torch.randn(rows, cols, generator=g, dtype=f64)
+    elif kind == "decay4":
+        U, _ = torch.linalg.qr(torch.randn(rows, n, generator=g, dtype=f64))
+        V, _ = torch.linalg.qr(torch.randn(cols, n, generator=g, dtype=f64))
+        M = (U * torch.logspace(0, -4, n, dtype=f64)) @ V.T
+    elif kind in ("rank16_noise", "rank1", "rank4"):
+        r = {"rank16_noise": 16, "rank1": 1, "rank4": 4}[kind]
+        M = torch.randn(rows, r, generator=g, dtype=f64) @ torch.randn(r, cols, generator=g, dtype=f64)
+        if kind == "rank16_noise":
+            M = M + 1e-3 * M.std() * torch.randn(rows, cols, generator=g, dtype=f64)
+    else:
+        raise ValueError(f"unknown spectrum kind {kind!r}")
+    M = M * (std / M.std())
+    return M.to(torch.float32).to(device)
