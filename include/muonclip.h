@@ -129,12 +129,17 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  * library then uses muon_rms_match_scale(rows, cols).
  *
  * Arithmetic: the norm is accumulated in float32 (combined in double); X_0
- * is held as bf16(M) and the factor 1 / (||M||_F + eps) is applied in float32
- * by the first step's GEMMs (X X^T by its square, that step's X by it); each
- * step is evaluated as A = X X^T, B' = a_s I + b_s A + c_s A A, X <- B' X
- * (the same polynomial, with a_s X folded into the last product); X, A and B'
- * are held in bfloat16 between the GEMMs, which run on bf16 MFMA with float32
- * accumulation, and each GEMM result is rounded once.
+ * is held unscaled and the factor 1 / (||M||_F + eps) is applied in float32
+ * by the first step's GEMMs (X X^T by its square, that step's X by it).  X
+ * is carried as a pair of bf16 matrices X = Xh + Xl (about 16 significant
+ * bits); each step computes A = Xh Xh^T and B = b_s A + c_s A A on bf16 MFMA
+ * with float32 accumulation (A rounded to bf16; B's diagonal d kept in
+ * float32 and the rest rounded to bf16), then X <- a_s X + d Xh + N Xh (N =
+ * B off its diagonal) in float32, split into its two parts again.  Keeping
+ * a_s X exact to 16 bits stops rounding errors from growing along the small
+ * singular directions (where a step multiplies by about a_s), so low-rank
+ * and decaying spectra keep the Gaussian case's accuracy.  The last step's
+ * X is rounded to bf16 before out_scale is applied.
  *
  *   M              device, m_dtype (MC_F32 or MC_BF16); matrix b starts at
  *                  element b * m_batch_stride and is row-major rows x cols
@@ -185,10 +190,11 @@ MC_API mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_
  * (Algorithm 1 of "Kimi K2 内部机制", MuonClip section; the paper notes'
  * muonclip_step pseudocode, section 3.2.)  The momentum is bit-identical to
  * muonclip_momentum.  O is never stored: the last Newton-Schulz GEMM applies
- * the update as it finishes each tile of X (rounded to bf16 as between steps;
- * O = out_scale * X is formed in float32, not rounded to a storage type).
- * The new M is converted to bf16 once, in the momentum pass, together
- * with float32 partial sums of its squares; the normalisation
+ * the update as it finishes each tile of X (X rounded to bf16 as in the
+ * output of muon_ns_orthogonalize_batched; O = out_scale * X formed in
+ * float32, not rounded to a storage type).  The new M is converted to its
+ * bf16 pair once, in the momentum pass, together with float32 partial sums
+ * of its squares; the normalisation
  * 1 / (||M_b||_F + eps) is applied inside the first Newton-Schulz step (to
  * X X^T squared and to the step's result), which equals normalising X_0 up
  * to rounding.  Steps and coefficients as muon_ns_orthogonalize_batched.

@@ -92,7 +92,7 @@ mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, c
 }
 
 // The steps' GEMMs, X_0 at off_x0 (high part) and off_xl0 (low part):
-// A = Xh Xh^T; B = b A + c A A = diag(d) + N; X <- (a + d) X + N Xh (X
+// A = Xh Xh^T; B = b A + c A A = diag(d) + N; X <- a X + d Xh + N Xh (X
 // carried as a bf16 pair, d in float32).
 // inv0 (or null): the stored X_0 is to be scaled per matrix by inv0 (applied
 // inside the first step).  upd (or null): the last step updates W (or writes

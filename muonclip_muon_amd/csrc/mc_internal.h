@@ -78,7 +78,7 @@ struct NsUpdate {
 // zero diagonal; the products read the high part of X only:
 //   mode 0: A = Xh Xh^T                          (in0: Xh, out: A)
 //   mode 1: B = alpha A + beta A A               (in0: A, out: N, dg: d)
-//   mode 2: X' = (a + d) X + N Xh, a = `a`       (in0: N, in1: Xh, xl: Xl, dg: d;
+//   mode 2: X' = a X + d Xh + N Xh, a = `a`      (in0: N, in1: Xh, xl: Xl, dg: d;
 //           out: X'h, xl_out: X'l, or the update / output through upd)
 // inv (device, per matrix, or null): X is inv_b times the stored X (the first
 // step); mode 0 scales A by inv_b^2, mode 2 X' by inv_b.

@@ -4,31 +4,31 @@
 // three GEMMs on the zero-padded n_pad x m_pad state X:
 //   mode 0  A  = Xh Xh^T                  K = m_pad   (out n_pad x n_pad)
 //   mode 1  B  = b A + c A A              K = n_pad   (A symmetric: A A = A^T A)
-//   mode 2  X' = (a + d) X + N Xh         K = n_pad   (out n_pad x m_pad)
+//   mode 2  X' = a X + d Xh + N Xh        K = n_pad   (out n_pad x m_pad)
 // with B split into its diagonal d (float32, one value per row) and the
-// rest N (bf16, zero diagonal).
-// X is carried as two bf16 matrices, X = Xh + Xl (the high part and the
-// rounding residual, about 16 significant bits together).  The products read
-// the high part only, on v_mfma_f32_32x32x16_bf16 with float32 accumulation;
-// the diagonal term (a + d) X is added in float32 in the epilogue of the
-// third product, from both parts of X, and X' is split into its two parts
-// again.  Why:
-// along singular directions with small singular values the iteration acts
-// as x -> a x (a = 3.4445), so an error there grows about a^5 ~ 490-fold over
-// five steps; rounding X (or a B' = a I + B with a folded diagonal) to bf16
-// puts an error of 2^-9 of X's largest components into every direction,
-// which for low-rank or decaying spectra swamps the small components (a bf16
-// emulation against the exact result: relative Frobenius error 1.2 for rank
-// 1, 0.38 for rank 16 plus noise, 0.037 for four decades of singular values
-// at 2048 x 7168).  With the linear term exact to 16 bits those errors drop
-// to 3.1e-3, 2.9e-3 and 4.9e-3; the errors that N Xh keeps fall along B's
-// range, the large singular directions, where they are relatively small.
-// Keeping B's diagonal out of the bf16 rounding matters where a + d nearly
-// cancels (d -> 1 - a as a singular value converges): rounding B whole
-// costs Gaussian matrices 1.1e-2, tiny ones (1 x 40) 2.4e-2; with d exact,
-// 5.1e-3 and 2.0e-3 (the folded bf16 form: 7.0e-3 and 1.0e-2).  A and B are
-// symmetric, so modes 0/1 compute only the tiles on and above the diagonal
-// and write each off-diagonal tile twice.
+// rest N (bf16, zero diagonal), so X' = a X + B Xh with B's diagonal never
+// rounded.  X is carried as two bf16 matrices, X = Xh + Xl (the high part
+// and the rounding residual, about 16 significant bits together).  The
+// products read the high part only, on v_mfma_f32_32x32x16_bf16 with float32
+// accumulation; the epilogue of the third product adds a (Xh + Xl) + d Xh in
+// float32 and splits X' into its two parts again.
+//
+// Why: along singular directions with small singular values the iteration
+// acts as x -> a x (a = 3.4445), so an error there grows about a^5 ~ 490-fold
+// over five steps.  Rounding X (or B' = a I + B with a folded diagonal) to
+// bf16 puts an error of 2^-9 of X's largest components into every direction,
+// which swamps the small ones of low-rank or decaying spectra.  With a X
+// exact to 16 bits, the error left is B's rounding and the dropped B Xl, both
+// along B's range (the large singular directions), where it is relatively
+// small; d stays exact because a + d nearly cancels as a singular value
+// converges (d -> 1 - a), which would magnify a rounded d.  A bf16 emulation
+// against the exact result at 2048 x 7168, relative Frobenius error of this
+// form (of the folded all-bf16 form): rank 1 2.6e-3 (1.18), rank 16 plus
+// noise 2.4e-3 (0.38), four decades of singular values 4.8e-3 (3.7e-2),
+// Gaussian 8.3e-3 (7.0e-3).  (Adding d Xl as well would help Gaussian
+// matrices but move the dropped remainder off B's range: rank 1 at 4 x 300
+// then reaches 0.3.)  A and B are symmetric, so modes 0/1 compute only the
+// tiles on and above the diagonal and write each off-diagonal tile twice.
 //
 // Tiling: a 512-thread workgroup (8 wave64s, 2 x 4, two per SIMD) owns a
 // 256 x 256 output tile; each wave owns 128 x 64 = 4 x 2 MFMA tiles of
@@ -506,16 +506,19 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // X is inv_b times the stored X in the first step of the fused path
   const float xs = (inv != nullptr) ? inv[mat] : 1.0f;
 
-  // Mode 2: X' = (a + d) X + N Xh, the diagonal term in float32 from both
+  // Mode 2 (see kRowEpi below for all but the update of a transposed W):
+  // X' = a (Xh + Xl) + d Xh + N Xh, the diagonal terms in float32 from both
   // parts of X at this lane's accumulator positions (4 consecutive columns, 8 bytes
   // of each part per MFMA register group), half of the tile's rows at a time
   // to bound the registers held; the accumulators become X' / xs.  Done
   // before anything else of the epilogue holds registers (the W of the
-  // update, A of mode 1).
-  if constexpr (MODE == 2) {
+  // update).  These loads touch 32 rows x 16 bytes per instruction, which
+  // the row-ordered pass avoids.
+  constexpr bool kRowEpi = MODE == 2 && !(UPD != 0 && TR);
+  if constexpr (MODE == 2 && !kRowEpi) {
     const uint16_t* Xh = in1 + mat * nm;
     const uint16_t* Xl = xl + mat * nm;
-    float lin[4];  // a + d_i of this lane's 4 rows
+    float lin[4];  // a + d_i of this lane's 4 rows (the factor of Xh)
 #pragma unroll
     for (int y = 0; y < 4; ++y) lin[y] = acoef + dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row];
 #pragma unroll
@@ -539,15 +542,157 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const u32x2 h = hb[yy][x][g], l = lb[yy][x][g];
-            const float xv[4] = {bf16_lo(h.x) + bf16_lo(l.x), bf16_hi(h.x) + bf16_hi(l.x),
-                                 bf16_lo(h.y) + bf16_lo(l.y), bf16_hi(h.y) + bf16_hi(l.y)};
+            const float hv[4] = {bf16_lo(h.x), bf16_hi(h.x), bf16_lo(h.y), bf16_hi(h.y)};
+            const float lv[4] = {bf16_lo(l.x), bf16_hi(l.x), bf16_lo(l.y), bf16_hi(l.y)};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[x][yh + yy][4 * g + q] += lin[yh + yy] * xv[q];
+            for (int q = 0; q < 4; ++q) acc[x][yh + yy][4 * g + q] += lin[yh + yy] * hv[q] + acoef * lv[q];
           }
     }
   }
   wait_vmem<0>();
   __syncthreads();
+
+  // Mode 2, row-ordered epilogue: the accumulators are staged in float32,
+  // half of the tile (256 rows x 128 columns, 128 KB) at a time, by the four
+  // waves that own those columns; then every lane takes 8 consecutive
+  // columns of a row per pass (16 lanes per row), reads X's two parts there
+  // with 16-byte loads (whole 256-byte row segments per 16 lanes), forms
+  // X' = xs (a (Xh + Xl) + d_i Xh + N Xh) in float32 and writes X''s two
+  // parts, or
+  // applies the update / writes the output, with 16-byte accesses.  Staged
+  // row r holds 16-byte unit u (4 columns) at u ^ (r & 31).
+  if constexpr (kRowEpi) {
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+    const uint16_t* Xh = in1 + mat * nm;
+    const uint16_t* Xlm = xl + mat * nm;
+    const float* dgm = dg + static_cast<int64_t>(mat) * n_pad;
+    auto fst = [&](int r, int u) -> uint32_t { return lds + r * 512 + ((u ^ (r & 31)) << 4); };
+    const int cg = tid & 15, rsub = tid >> 4;
+    constexpr bool kReadW = UPD == 1 || UPD == 2;
+    constexpr int kEsz = (UPD == 2 || UPD == 4) ? 4 : 2;
+    constexpr int kWords = (UPD == 2 || UPD == 4) ? 2 : 1;  // 16-byte words per 8 elements of W
+    char* const Wb = UPD != 0 ? static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz : nullptr;
+    const bool wvec = UPD != 0 && ua.m % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
+    constexpr int kRB = 4;  // passes per batch of loads
+    for (int h = 0; h < 2; ++h) {
+      if ((wn >> 1) == h) {
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+          for (int x = 0; x < kCT; ++x)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int r = wm * 128 + y * 32 + frag_row, u = 16 * wh + 8 * x + 2 * g + frag_half;
+              *(lds_f32x4_t*)(uintptr_t)fst(r, u) =
+                  f32x4{acc[x][y][4 * g + 0], acc[x][y][4 * g + 1], acc[x][y][4 * g + 2], acc[x][y][4 * g + 3]};
+            }
+      }
+      __syncthreads();
+      const int jc = j0 + 128 * h + 8 * cg;  // first column of this lane's run
+#pragma unroll 1
+      for (int p0 = 0; p0 < 8; p0 += kRB) {
+        u32x4 xhv[kRB], xlv[kRB];
+        u32x4 wv[kReadW ? kRB : 1][kWords];
+        float lin[kRB];
+#pragma unroll
+        for (int q = 0; q < kRB; ++q) {
+          const int row = i0 + (p0 + q) * 32 + rsub;
+          const int64_t off = x_off(row, jc, n_pad);
+          xhv[q] = *reinterpret_cast<const u32x4*>(Xh + off);
+          xlv[q] = *reinterpret_cast<const u32x4*>(Xlm + off);
+          lin[q] = acoef + dgm[row];
+          if constexpr (kReadW) {
+            if (wvec && row < ua.n && jc + 8 <= ua.m) {
+              const u32x4* pw = reinterpret_cast<const u32x4*>(Wb + (static_cast<int64_t>(row) * ua.m + jc) * kEsz);
+#pragma unroll
+              for (int w = 0; w < kWords; ++w) wv[q][w] = pw[w];
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kRB; ++q) {
+          const int r = (p0 + q) * 32 + rsub, row = i0 + r;
+          const f32x4 a0 = *(const lds_f32x4_t*)(uintptr_t)fst(r, 2 * cg);
+          const f32x4 a1 = *(const lds_f32x4_t*)(uintptr_t)fst(r, 2 * cg + 1);
+          const u32x4 hq = xhv[q], lq = xlv[q];
+          const float hv[8] = {bf16_lo(hq.x), bf16_hi(hq.x), bf16_lo(hq.y), bf16_hi(hq.y),
+                               bf16_lo(hq.z), bf16_hi(hq.z), bf16_lo(hq.w), bf16_hi(hq.w)};
+          const float lv[8] = {bf16_lo(lq.x), bf16_hi(lq.x), bf16_lo(lq.y), bf16_hi(lq.y),
+                               bf16_lo(lq.z), bf16_hi(lq.z), bf16_lo(lq.w), bf16_hi(lq.w)};
+          const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            v[e] = av[e] + lin[q] * hv[e] + acoef * lv[e];
+            if constexpr (SCALED) v[e] *= xs;
+          }
+          if constexpr (UPD == 0) {
+            float lo[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf16_to_f32(f32_to_bf16(v[e]));
+            const int64_t off = x_off(row, jc, n_pad);
+            *reinterpret_cast<u32x4*>(out + mat * nm + off) =
+                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+            *reinterpret_cast<u32x4*>(xl_out + mat * nm + off) = u32x4{
+                pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7])};
+          } else {
+            // the last step: X' rounded to bf16, then O = out_scale X'
+            if (row >= ua.n || jc >= ua.m) continue;
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = ua.out_scale * bf16_to_f32(f32_to_bf16(v[e]));
+            const int64_t idx = static_cast<int64_t>(row) * ua.m + jc;
+            if (wvec && jc + 8 <= ua.m) {
+              u32x4* pw = reinterpret_cast<u32x4*>(Wb + idx * kEsz);
+              if constexpr (UPD == 3) {
+                pw[0] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])};
+              } else if constexpr (UPD == 4) {
+                pw[0] = __builtin_bit_cast(u32x4, f32x4{o[0], o[1], o[2], o[3]});
+                pw[1] = __builtin_bit_cast(u32x4, f32x4{o[4], o[5], o[6], o[7]});
+              } else if constexpr (UPD == 1) {
+                u32x4 w = wv[q][0];
+                w.x = pack_bf16x2(update_op(bf16_lo(w.x), o[0], ua.lr, ua.wd), update_op(bf16_hi(w.x), o[1], ua.lr, ua.wd));
+                w.y = pack_bf16x2(update_op(bf16_lo(w.y), o[2], ua.lr, ua.wd), update_op(bf16_hi(w.y), o[3], ua.lr, ua.wd));
+                w.z = pack_bf16x2(update_op(bf16_lo(w.z), o[4], ua.lr, ua.wd), update_op(bf16_hi(w.z), o[5], ua.lr, ua.wd));
+                w.w = pack_bf16x2(update_op(bf16_lo(w.w), o[6], ua.lr, ua.wd), update_op(bf16_hi(w.w), o[7], ua.lr, ua.wd));
+                pw[0] = w;
+              } else {
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                  f32x4 t = __builtin_bit_cast(f32x4, wv[q][w]);
+                  t.x = update_op(t.x, o[4 * w + 0], ua.lr, ua.wd);
+                  t.y = update_op(t.y, o[4 * w + 1], ua.lr, ua.wd);
+                  t.z = update_op(t.z, o[4 * w + 2], ua.lr, ua.wd);
+                  t.w = update_op(t.w, o[4 * w + 3], ua.lr, ua.wd);
+                  pw[w] = __builtin_bit_cast(u32x4, t);
+                }
+              }
+            } else {
+              const int valid = min(8, ua.m - jc);
+              for (int e = 0; e < valid; ++e) {
+                if constexpr (UPD == 3) {
+                  reinterpret_cast<uint16_t*>(Wb)[idx + e] = f32_to_bf16(o[e]);
+                } else if constexpr (UPD == 4) {
+                  reinterpret_cast<float*>(Wb)[idx + e] = o[e];
+                } else if constexpr (UPD == 1) {
+                  uint16_t* pw = reinterpret_cast<uint16_t*>(Wb) + idx + e;
+                  *pw = f32_to_bf16(update_op(bf16_to_f32(*pw), o[e], ua.lr, ua.wd));
+                } else {
+                  float* pw = reinterpret_cast<float*>(Wb) + idx + e;
+                  *pw = update_op(*pw, o[e], ua.lr, ua.wd);
+                }
+              }
+            }
+          }
+        }
+      }
+      // the next half reuses the staging
+      __syncthreads();
+    }
+    return;
+  }
+
   uint16_t* O = out + mat * ((MODE == 2) ? nm : nn);
   const uint32_t eb = lds + (2 * wm + (wn >> 1)) * 32768;
   auto st_addr = [&](int ii, int u) -> uint32_t { return eb + ii * 256 + ((u ^ (ii & 15)) << 4); };
@@ -649,8 +794,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
     }
   };
-  // Stage the bf16 high parts (LO false) or the low parts v - bf16(v).
-  auto stage = [&](bool lo) {
+  // Stage the bf16 values (modes 0/1, and mode 2 for a transposed W's update).
+  auto stage = [&]() {
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       const int ii = y * 32 + frag_row;
@@ -661,17 +806,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           const uint32_t a = st_addr(ii, 8 * wh + 4 * x + g) + 8 * frag_half;
           float v[4];
           value(y, x, g, v);
-          if (lo) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] -= bf16_to_f32(f32_to_bf16(v[q]));
-          }
           const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *(lds_u32x2_t*)(uintptr_t)a = o;
         }
       }
     }
   };
-  stage(false);
+  stage();
   // the region is complete once both of its waves have written
   __syncthreads();
   if constexpr (UPD != 0) {
@@ -776,16 +917,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       *reinterpret_cast<u32x4*>(dst) = v;
     }
   };
-  store_rows(O);
   if constexpr (MODE != 2) {
+    store_rows(O);
     if (ti != tj) store_transposed(eb, O, j0w, i0w, nkb, lane, 16 * wh);
-  } else {
-    // X''s low part through the same staging, once every wave has read the
-    // high part
-    __syncthreads();
-    stage(true);
-    __syncthreads();
-    store_rows(xl_out + mat * nm);
   }
 }
 
