@@ -573,7 +573,25 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     constexpr int kWords = (UPD == 2 || UPD == 4) ? 2 : 1;  // 16-byte words per 8 elements of W
     char* const Wb = UPD != 0 ? static_cast<char*>(ua.W) + static_cast<int64_t>(mat) * ua.w_stride * kEsz : nullptr;
     const bool wvec = UPD != 0 && ua.m % 8 == 0 && reinterpret_cast<uintptr_t>(Wb) % 16 == 0;
-    constexpr int kRB = 4;  // passes per batch of loads
+    // X's two parts for the lane's 16 passes (8 per half, s = 8 h + p) in a
+    // ring of kRing (4; 2 for float32 W, whose loads take the registers):
+    // the first kRing are loaded before the staging (their latency overlaps
+    // it), pass s + kRing as pass s is consumed.  a + d_i per pass row.
+    constexpr int kRing = UPD == 2 ? 2 : 4;
+    u32x4 xhv[kRing], xlv[kRing];
+    float lin[8];
+    auto load_x = [&](int sq) {
+      const int64_t off = x_off(i0 + (sq & 7) * 32 + rsub, j0 + 128 * (sq >> 3) + 8 * cg, n_pad);
+      xhv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xh + off);
+      xlv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xlm + off);
+    };
+#pragma unroll
+    for (int sq = 0; sq < kRing; ++sq) load_x(sq);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) lin[p] = acoef + dgm[i0 + p * 32 + rsub];
+    // W of the update, read in batches of kWB passes
+    constexpr int kWB = UPD == 2 ? 2 : (UPD == 1 ? 2 : 4);
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
       if ((wn >> 1) == h) {
 #pragma unroll
@@ -589,19 +607,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       }
       __syncthreads();
       const int jc = j0 + 128 * h + 8 * cg;  // first column of this lane's run
-#pragma unroll 1
-      for (int p0 = 0; p0 < 8; p0 += kRB) {
-        u32x4 xhv[kRB], xlv[kRB];
-        u32x4 wv[kReadW ? kRB : 1][kWords];
-        float lin[kRB];
 #pragma unroll
-        for (int q = 0; q < kRB; ++q) {
-          const int row = i0 + (p0 + q) * 32 + rsub;
-          const int64_t off = x_off(row, jc, n_pad);
-          xhv[q] = *reinterpret_cast<const u32x4*>(Xh + off);
-          xlv[q] = *reinterpret_cast<const u32x4*>(Xlm + off);
-          lin[q] = acoef + dgm[row];
-          if constexpr (kReadW) {
+      for (int p0 = 0; p0 < 8; p0 += kWB) {
+        u32x4 wv[kReadW ? kWB : 1][kWords];
+        if constexpr (kReadW) {
+#pragma unroll
+          for (int q = 0; q < kWB; ++q) {
+            const int row = i0 + (p0 + q) * 32 + rsub;
             if (wvec && row < ua.n && jc + 8 <= ua.m) {
               const u32x4* pw = reinterpret_cast<const u32x4*>(Wb + (static_cast<int64_t>(row) * ua.m + jc) * kEsz);
 #pragma unroll
@@ -610,20 +622,22 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           }
         }
 #pragma unroll
-        for (int q = 0; q < kRB; ++q) {
-          const int r = (p0 + q) * 32 + rsub, row = i0 + r;
+        for (int q = 0; q < kWB; ++q) {
+          const int p = p0 + q, r = p * 32 + rsub, row = i0 + r;
           const f32x4 a0 = *(const lds_f32x4_t*)(uintptr_t)fst(r, 2 * cg);
           const f32x4 a1 = *(const lds_f32x4_t*)(uintptr_t)fst(r, 2 * cg + 1);
-          const u32x4 hq = xhv[q], lq = xlv[q];
+          const int sq = 8 * h + p;
+          const u32x4 hq = xhv[sq % kRing], lq = xlv[sq % kRing];
           const float hv[8] = {bf16_lo(hq.x), bf16_hi(hq.x), bf16_lo(hq.y), bf16_hi(hq.y),
                                bf16_lo(hq.z), bf16_hi(hq.z), bf16_lo(hq.w), bf16_hi(hq.w)};
           const float lv[8] = {bf16_lo(lq.x), bf16_hi(lq.x), bf16_lo(lq.y), bf16_hi(lq.y),
                                bf16_lo(lq.z), bf16_hi(lq.z), bf16_lo(lq.w), bf16_hi(lq.w)};
+          if (sq + kRing < 16) load_x(sq + kRing);
           const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            v[e] = av[e] + lin[q] * hv[e] + acoef * lv[e];
+            v[e] = av[e] + lin[p] * hv[e] + acoef * lv[e];
             if constexpr (SCALED) v[e] *= xs;
           }
           if constexpr (UPD == 0) {
