@@ -336,6 +336,31 @@ MC_API mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float 
                           void* stream);
 
 /*
+ * qk_clip_apply_layers -- QK-Clip of every attention layer in one call: for
+ * each layer l and head h with smax[l * H + h] > tau, the rows of head h of
+ * layer l's W_q and W_k are rescaled exactly as qk_clip_apply rescales them
+ * (the pages clip every head of every attention layer: Algorithm 1 of "Kimi
+ * K2 内部机制" loops over the heads of each attention layer; the Zhihu
+ * MuonClip formula indexes S_max by layer and head).
+ *
+ *   smax         device float32 [L, H] row-major (the forward's per-layer
+ *                per-head max logits)
+ *   Wq, Wk       HOST arrays of L device pointers: layer l's W_q
+ *                [H*qph, d_in] and W_k [H*kph, d_in] (same dtype, shapes and
+ *                row split for every layer)
+ *   gamma_out    device float32 [L, H] or NULL;  clipped_out device int32
+ *                [L, H] or NULL (1 clipped, 0 not, -1 NaN)
+ * Up to 64 layers go in one kernel launch (their pointers travel in the
+ * kernel arguments); more layers take one launch per 64.  Arguments and
+ * errors otherwise as qk_clip_apply, plus MC_EINVAL for L < 0, a NULL
+ * pointer array or a NULL layer pointer, and MC_ESHAPE for L * H > 65535.
+ */
+MC_API mc_status_t qk_clip_apply_layers(const float* smax, int64_t L, int64_t H, float tau, float alpha,
+                                        void* const* Wq, void* const* Wk, int w_dtype, int64_t d_in,
+                                        int64_t q_rows_per_head, int64_t q_c_rows, int64_t k_rows_per_head,
+                                        float* gamma_out, int32_t* clipped_out, void* stream);
+
+/*
  * qk_clip_apply_total -- the total-clip variant: one gamma for all heads.
  *
  * S = max_h smax[h] (NaN entries skipped); if S > tau, gamma = tau / S and

@@ -36,6 +36,7 @@ __all__ = [
     "qk_maxlogit",
     "qk_clip_apply",
     "qk_clip_apply_total",
+    "qk_clip_apply_layers",
     "attention_fwd_maxlogit",
     "muon_out_scale",
     "OUT_SCALE_RMS_MATCH",
@@ -102,6 +103,9 @@ def _load():
     L.attention_fwd_maxlogit.restype = ctypes.c_int
     L.attention_fwd_maxlogit.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i32, vp,
                                          vp, vp, i32, vp]
+    L.qk_clip_apply_layers.restype = ctypes.c_int
+    L.qk_clip_apply_layers.argtypes = [vp, i64, i64, f32, f32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                       i64, i64, i64, i64, vp, vp, vp]
     L.qk_clip_apply_total.restype = ctypes.c_int
     L.qk_clip_apply_total.argtypes = L.qk_clip_apply.argtypes
     L.mc_probe_mfma_bf16.restype = ctypes.c_int
@@ -372,6 +376,39 @@ def qk_clip_apply_total(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head
                     alpha, gamma, clipped, stream)
 
 
+def qk_clip_apply_layers(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau=100.0, alpha=0.5,
+                         gamma=None, clipped=None, stream=None):
+    """QK-Clip of every attention layer in one call: smax float32 [L, H];
+    Wq, Wk sequences of L tensors [H * q_rows_per_head, d_in] and
+    [H * k_rows_per_head, d_in].  Returns (gamma, clipped), both [L, H]."""
+    _dev(smax, "smax")
+    if smax.dim() != 2:
+        raise ValueError("smax must be [L, H]")
+    L, H = smax.shape
+    Wq, Wk = list(Wq), list(Wk)
+    if len(Wq) != L or len(Wk) != L:
+        raise ValueError("Wq and Wk need one tensor per layer")
+    for w in Wq + Wk:
+        _dev(w, "W")
+        if w.dtype != Wq[0].dtype:
+            raise ValueError("every W_q / W_k must share a dtype")
+    d_in = Wq[0].shape[-1]
+    for wq, wk in zip(Wq, Wk):
+        if wq.numel() != H * q_rows_per_head * d_in or wk.numel() != H * k_rows_per_head * d_in:
+            raise ValueError("each layer's Wq must be [H * q_rows_per_head, d_in] and Wk [H * k_rows_per_head, d_in]")
+    if gamma is None:
+        gamma = _empty((L, H), torch.float32, smax.device, stream)
+    if clipped is None:
+        clipped = _empty((L, H), torch.int32, smax.device, stream)
+    qp = (ctypes.c_void_p * L)(*[w.data_ptr() for w in Wq])
+    kp = (ctypes.c_void_p * L)(*[w.data_ptr() for w in Wk])
+    status = lib.qk_clip_apply_layers(smax.data_ptr(), L, H, tau, alpha, qp, kp, _dtype(Wq[0], "Wq"), d_in,
+                                      q_rows_per_head, q_c_rows, k_rows_per_head, gamma.data_ptr(),
+                                      clipped.data_ptr(), _stream(smax, stream))
+    _check("qk_clip_apply_layers", status)
+    return gamma, clipped
+
+
 def _qk_clip(fn, smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, alpha, gamma, clipped, stream):
     _dev(smax, "smax"), _dev(Wq, "Wq"), _dev(Wk, "Wk")
     H = smax.numel()
@@ -415,28 +452,72 @@ def probe_copy(src, dst, stream=None):
 
 
 def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1, momentum=0.95,
-                  tau=100.0, alpha=0.5, steps=NS_STEPS, coeffs=None, eps=NS_EPS, fused=False):
-    """One MuonClip step over dicts of 2-D tensors, in place.
+                  tau=100.0, alpha=0.5, steps=NS_STEPS, coeffs=None, eps=NS_EPS, chunk=64, workspace=None,
+                  fused=True, stream=None):
+    """One MuonClip step, in place (Algorithm 1 of the internals page; the
+    paper notes' muonclip_step): the Muon update of every matrix, then QK-Clip
+    of every attention layer.
 
-    weights: name -> W (float32 or bfloat16); grads: name -> float32 G;
-    momenta: name -> float32 M (created as zeros when missing: M_0 = 0);
-    smax: float32 [H] max logits recorded by the forward; attention: dict with
-    'q', 'k' (weight names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head'.
-    fused: use muon_momentum_ns_update_batched instead of the three calls.
-    Returns (gamma, clipped)."""
+    weights: name -> W, float32 or bfloat16, 2-D [rows, cols] or a stack of
+    equally shaped matrices [count, rows, cols] (e.g. all experts of a
+    layer); grads: name -> float32 G of the same shape; momenta: name ->
+    float32 M (created as zeros when missing: M_0 = 0).  Each entry goes
+    through the fused momentum + Newton-Schulz + update call in chunks of at
+    most `chunk` matrices; every call shares one workspace (the given one, or
+    one allocated here for the largest chunk), so nothing is allocated per
+    matrix.  fused=False runs momentum, Newton-Schulz and update as three
+    calls per chunk instead (same workspace, plus one O buffer).
+
+    smax: the forward's max logits, [H] for one attention layer or [L, H];
+    attention: one layer dict, or a list of L of them, with 'q', 'k' (weight
+    names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head' (the same row
+    split for every layer).  All layers are clipped in one call.
+    Returns (gamma, clipped), shaped like smax."""
+    entries = []
     for name, W in weights.items():
         M = momenta.get(name)
         if M is None:
             M = momenta[name] = torch.zeros(W.shape, dtype=torch.float32, device=W.device)
-        if fused:
-            muon_momentum_ns_update_batched(M, grads[name], W, lr, weight_decay, momentum, steps=steps,
-                                            coeffs=coeffs, eps=eps)
-            continue
-        muonclip_momentum(M, grads[name], momentum)
-        rows, cols = W.shape
-        O = muon_ns_orthogonalize_batched(M, steps=steps, coeffs=coeffs, eps=eps,
-                                          out_scale=muon_out_scale(rows, cols), out_dtype=W.dtype)
-        muon_apply_update(W, O, lr, weight_decay)
-    return qk_clip_apply(smax, weights[attention["q"]], weights[attention["k"]],
-                         attention["q_rows_per_head"], attention["q_c_rows"], attention["k_rows_per_head"],
-                         tau, alpha)
+        G = grads[name]
+        if W.dim() not in (2, 3):
+            raise ValueError(f"{name}: weights must be [rows, cols] or [count, rows, cols]")
+        W3, M3, G3 = (t.unsqueeze(0) if t.dim() == 2 else t for t in (W, M, G))
+        entries.append((name, W3, M3, G3))
+    need = max((muon_ns_workspace_bytes(min(chunk, W3.shape[0]), W3.shape[1], W3.shape[2])
+                for _, W3, _, _ in entries), default=0)
+    if workspace is None:
+        workspace = _empty(max(need, 1), torch.uint8, next(iter(weights.values())).device, stream)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    O_buf = None
+    if not fused:
+        o_elems = max(min(chunk, W3.shape[0]) * W3.shape[1] * W3.shape[2] for _, W3, _, _ in entries)
+        O_buf = _empty(o_elems, torch.float32, workspace.device, stream)
+    for name, W3, M3, G3 in entries:
+        count, rows, cols = W3.shape
+        for s0 in range(0, count, chunk):
+            s1 = min(count, s0 + chunk)
+            M, G, W = M3[s0:s1], G3[s0:s1], W3[s0:s1]
+            if fused:
+                muon_momentum_ns_update_batched(M, G, W, lr, weight_decay, momentum, steps=steps, coeffs=coeffs,
+                                                eps=eps, workspace=workspace, stream=stream)
+                continue
+            muonclip_momentum(M, G, momentum, stream=stream)
+            O = O_buf[:(s1 - s0) * rows * cols].view(s1 - s0, rows, cols)
+            muon_ns_orthogonalize_batched(M, O, steps=steps, coeffs=coeffs, eps=eps,
+                                          out_scale=OUT_SCALE_RMS_MATCH, workspace=workspace, stream=stream)
+            muon_apply_update(W, O, lr, weight_decay, stream=stream)
+    layers = attention if isinstance(attention, (list, tuple)) else [attention]
+    one_layer = smax.dim() == 1
+    smax2 = smax.view(1, -1) if one_layer else smax
+    if smax2.shape[0] != len(layers):
+        raise ValueError("smax needs one row per attention layer")
+    a0 = layers[0]
+    for a in layers:
+        if (a["q_rows_per_head"], a["q_c_rows"], a["k_rows_per_head"]) != (
+                a0["q_rows_per_head"], a0["q_c_rows"], a0["k_rows_per_head"]):
+            raise ValueError("every attention layer must share the row split")
+    gamma, clipped = qk_clip_apply_layers(smax2, [weights[a["q"]] for a in layers], [weights[a["k"]] for a in layers],
+                                          a0["q_rows_per_head"], a0["q_c_rows"], a0["k_rows_per_head"], tau, alpha,
+                                          stream=stream)
+    return (gamma.view(-1), clipped.view(-1)) if one_layer else (gamma, clipped)

@@ -326,15 +326,22 @@ mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr
                                            smax_out, s));
 }
 
-static mc_status_t qk_clip_common(const float* smax, int64_t H, bool total_clip, float tau, float alpha,
-                                  void* Wq, void* Wk, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
-                                  int64_t q_c_rows, int64_t k_rows_per_head, float* gamma_out,
-                                  int32_t* clipped_out, void* stream) {
+static mc_status_t qk_clip_check(int64_t H, float tau, float alpha, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
+                                 int64_t q_c_rows, int64_t k_rows_per_head) {
   if (H < 0 || d_in < 1 || q_rows_per_head < 0 || q_c_rows < 0 || q_c_rows > q_rows_per_head ||
       k_rows_per_head < 0)
     return MC_EINVAL;
   if (!valid_dtype(w_dtype)) return MC_EDTYPE;
   if (!(tau > 0.0f) || !isfinite(tau) || !(alpha >= 0.0f && alpha <= 1.0f)) return MC_EINVAL;
+  return MC_OK;
+}
+
+static mc_status_t qk_clip_common(const float* smax, int64_t H, bool total_clip, float tau, float alpha,
+                                  void* Wq, void* Wk, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
+                                  int64_t q_c_rows, int64_t k_rows_per_head, float* gamma_out,
+                                  int32_t* clipped_out, void* stream) {
+  mc_status_t st = qk_clip_check(H, tau, alpha, w_dtype, d_in, q_rows_per_head, q_c_rows, k_rows_per_head);
+  if (st != MC_OK) return st;
   if (H == 0) return MC_OK;
   if (!smax) return MC_EINVAL;
   if ((q_rows_per_head > 0 && !Wq) || (k_rows_per_head > 0 && !Wk)) return MC_EINVAL;
@@ -344,9 +351,39 @@ static mc_status_t qk_clip_common(const float* smax, int64_t H, bool total_clip,
       (gamma_out && !aligned(gamma_out, 4)) || (clipped_out && !aligned(clipped_out, 4)))
     return MC_EALIGN;
   if ((q_rows_per_head + k_rows_per_head) * d_in / 8 / 1024 + 1 > kGridMax) return MC_ESHAPE;
-  return from_hip(mc::launch_qk_clip(smax, H, total_clip, tau, alpha, Wq, Wk, w_dtype == MC_BF16, d_in,
-                                     q_rows_per_head, q_c_rows, k_rows_per_head, gamma_out,
-                                     clipped_out, static_cast<hipStream_t>(stream)));
+  return from_hip(mc::launch_qk_clip(smax, 1, H, total_clip, tau, alpha, &Wq, &Wk, w_dtype == MC_BF16, d_in,
+                                     q_rows_per_head, q_c_rows, k_rows_per_head, gamma_out, clipped_out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+mc_status_t qk_clip_apply_layers(const float* smax, int64_t L, int64_t H, float tau, float alpha, void* const* Wq,
+                                 void* const* Wk, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
+                                 int64_t q_c_rows, int64_t k_rows_per_head, float* gamma_out, int32_t* clipped_out,
+                                 void* stream) {
+  if (L < 0) return MC_EINVAL;
+  mc_status_t st = qk_clip_check(H, tau, alpha, w_dtype, d_in, q_rows_per_head, q_c_rows, k_rows_per_head);
+  if (st != MC_OK) return st;
+  if (L == 0 || H == 0) return MC_OK;
+  if (!smax || !Wq || !Wk) return MC_EINVAL;
+  const size_t es = dtype_size(w_dtype);
+  for (int64_t l = 0; l < L; ++l) {
+    if ((q_rows_per_head > 0 && !Wq[l]) || (k_rows_per_head > 0 && !Wk[l])) return MC_EINVAL;
+    if ((Wq[l] && !aligned(Wq[l], es)) || (Wk[l] && !aligned(Wk[l], es))) return MC_EALIGN;
+  }
+  if (L * H > 65535) return MC_ESHAPE;
+  if (!aligned(smax, 4) || (gamma_out && !aligned(gamma_out, 4)) || (clipped_out && !aligned(clipped_out, 4)))
+    return MC_EALIGN;
+  if ((q_rows_per_head + k_rows_per_head) * d_in / 8 / 1024 + 1 > kGridMax) return MC_ESHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t l0 = 0; l0 < L; l0 += mc::kClipMaxLayers) {
+    const int64_t nl = L - l0 < mc::kClipMaxLayers ? L - l0 : mc::kClipMaxLayers;
+    const hipError_t e = mc::launch_qk_clip(smax + l0 * H, nl, H, false, tau, alpha, Wq + l0, Wk + l0,
+                                            w_dtype == MC_BF16, d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
+                                            gamma_out ? gamma_out + l0 * H : nullptr,
+                                            clipped_out ? clipped_out + l0 * H : nullptr, s);
+    if (e != hipSuccess) return MC_EHIP;
+  }
+  return MC_OK;
 }
 
 mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,

@@ -105,9 +105,13 @@ hipError_t launch_attention_fwd(const void* Q, const void* Kc, const void* Kr, c
                                 bool causal, void* O, float* lse, float* smax, hipStream_t stream);
 
 // ---------------------------------------------------------------- QK-Clip
-hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float tau, float alpha, void* Wq, void* Wk,
-                          bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
-                          float* gamma_out, int32_t* clipped_out, hipStream_t stream);
+// Layers per launch (their W_q / W_k pointers travel in the kernel arguments).
+constexpr int kClipMaxLayers = 64;
+// smax [L, H]; Wq / Wk host arrays of L (<= kClipMaxLayers) device pointers;
+// gamma_out / clipped_out [L, H] or null.  total_clip requires L == 1.
+hipError_t launch_qk_clip(const float* smax, int64_t L, int64_t H, bool total_clip, float tau, float alpha,
+                          void* const* Wq, void* const* Wk, bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows,
+                          int64_t kph, float* gamma_out, int32_t* clipped_out, hipStream_t stream);
 
 // Measurement aids (probe.hip).
 hipError_t launch_mfma_probe(int64_t workgroups, int64_t iters, bool zero_operands, float* out, hipStream_t stream);

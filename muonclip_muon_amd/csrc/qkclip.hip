@@ -14,14 +14,18 @@
 // NaN leaves everything untouched), applied to every head with the same
 // split when S_max > tau.  Each block reduces the H values itself.
 //
-// A head's rows are two contiguous row blocks (W_q and W_k are row-major with
-// head-major rows), so the kernels stream them with 16-byte accesses.
-// Compact kernel (H up to 1024): every block reads the H values of S_max,
-// lists the clipped heads with their factors in LDS, and the grid, sized for
-// the case where every head is clipped, shares out only the listed heads'
-// elements, so few clipped heads still spread over every CU and no block is
-// launched just to find its head unclipped.  Larger H: a grid of
-// (chunks, H) whose blocks of unclipped heads return after reading one float.
+// Several attention layers (the pages clip every head of every attention
+// layer) go in one launch: S_max is [L, H] row-major, layer l's W_q / W_k
+// come from a table of L pointers in the kernel arguments, and "head" below
+// means one of the L x H (layer, head) pairs.  A head's rows are two
+// contiguous row blocks (W_q and W_k are row-major with head-major rows), so
+// the kernels stream them with 16-byte accesses.  Compact kernel (up to 4096
+// heads): every block reads all L x H values of S_max, lists the clipped
+// heads with their factors in LDS, and the grid, sized for the case where
+// every head is clipped, shares out only the listed heads' elements, so few
+// clipped heads still spread over every CU and no block is launched just to
+// find its head unclipped.  More heads: a grid of (chunks, L x H) whose
+// blocks of unclipped heads return after reading one float.
 //
 // The multiply is a single float op, rounded once to the storage type; FP
 // contraction is off so the result does not depend on the compiler.
@@ -36,6 +40,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVecPerThread = 4;  // 16-byte vectors per thread per block
+
+// W_q / W_k of each layer of one launch
+struct LayerPtrs {
+  void* q[kClipMaxLayers];
+  void* k[kClipMaxLayers];
+};
 
 struct ClipFactors {
   float q_c, q_r, k;
@@ -115,26 +125,25 @@ __device__ float block_max_all(const float* __restrict__ smax, int64_t H) {
 }
 
 // VEC: every row block starts 16-byte aligned and d_in % 8 == 0, so the
-// element ranges below are whole 8-element vectors.  total_clip: one gamma
-// from the largest S_max of all heads.
+// element ranges below are whole 8-element vectors.  total_clip (one layer):
+// one gamma from the largest S_max of all heads.  grid (chunks, L * H).
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restrict__ smax, int64_t H, bool total_clip,
-                                                          float tau, float alpha, void* __restrict__ Wq,
-                                                          void* __restrict__ Wk, int64_t d_in,
+                                                          float tau, float alpha, LayerPtrs lp, int64_t d_in,
                                                           int64_t qph, int64_t q_c_rows, int64_t kph,
                                                           float* __restrict__ gamma_out,
                                                           int32_t* __restrict__ clipped_out) {
-  const int64_t h = blockIdx.y;
-  const ClipFactors f = clip_factors(total_clip ? block_max_all(smax, H) : smax[h], tau, alpha);
+  const int64_t gh = blockIdx.y, layer = gh / H, h = gh - layer * H;
+  const ClipFactors f = clip_factors(total_clip ? block_max_all(smax, H) : smax[gh], tau, alpha);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (gamma_out) gamma_out[h] = f.gamma;
-    if (clipped_out) clipped_out[h] = f.state;
+    if (gamma_out) gamma_out[gh] = f.gamma;
+    if (clipped_out) clipped_out[gh] = f.state;
   }
   if (f.state != 1) return;
 
   const size_t esz = BF16 ? 2 : 4;
-  char* q_base = static_cast<char*>(Wq) + static_cast<size_t>(h * qph * d_in) * esz;
-  char* k_base = static_cast<char*>(Wk) + static_cast<size_t>(h * kph * d_in) * esz;
+  char* q_base = static_cast<char*>(lp.q[layer]) + static_cast<size_t>(h * qph * d_in) * esz;
+  char* k_base = static_cast<char*>(lp.k[layer]) + static_cast<size_t>(h * kph * d_in) * esz;
   const int64_t q_elems = qph * d_in, q_c_elems = q_c_rows * d_in, k_elems = kph * d_in;
   const int64_t total = q_elems + k_elems;
 
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restri
 }
 
 
-constexpr int kCompactMaxHeads = 1024;
+constexpr int kCompactMaxHeads = 4096;
 constexpr int kCompactMaxBlocks = 2048;
 
 // The clipped heads, their factors and the head count, identical in every
@@ -168,26 +177,27 @@ struct ClipList {
   int wave_count[kThreads / 64];
 };
 
+// NH = L * H heads; H heads per layer (total_clip: one layer, L = 1).
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* __restrict__ smax, int H,
+__global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* __restrict__ smax, int NH, int H,
                                                                   bool total_clip, float tau, float alpha,
-                                                                  void* __restrict__ Wq, void* __restrict__ Wk,
-                                                                  int64_t d_in, int64_t qph, int64_t q_c_rows,
-                                                                  int64_t kph, float* __restrict__ gamma_out,
+                                                                  LayerPtrs lp, int64_t d_in, int64_t qph,
+                                                                  int64_t q_c_rows, int64_t kph,
+                                                                  float* __restrict__ gamma_out,
                                                                   int32_t* __restrict__ clipped_out) {
   __shared__ ClipList L;
   const float s_all = total_clip ? block_max_all(smax, H) : 0.0f;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int count = 0;  // the same in every thread
-  for (int base = 0; base < H; base += kThreads) {
+  for (int base = 0; base < NH; base += kThreads) {
     const int h = base + static_cast<int>(threadIdx.x);
     ClipFactors f = {1.f, 1.f, 1.f, 0, 1.f};
-    if (h < H) f = clip_factors(total_clip ? s_all : smax[h], tau, alpha);
-    if (blockIdx.x == 0 && h < H) {
+    if (h < NH) f = clip_factors(total_clip ? s_all : smax[h], tau, alpha);
+    if (blockIdx.x == 0 && h < NH) {
       if (gamma_out) gamma_out[h] = f.gamma;
       if (clipped_out) clipped_out[h] = f.state;
     }
-    const bool c = h < H && f.state == 1;
+    const bool c = h < NH && f.state == 1;
     const uint64_t m = __ballot(c);
     if (lane == 0) L.wave_count[w] = __popcll(m);
     __syncthreads();
@@ -217,9 +227,10 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
   for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total; v += stride) {
     const int idx = static_cast<int>(v / per_head);
     const int64_t off = v - idx * per_head;
-    const int64_t h = L.head[idx];
-    char* q_base = static_cast<char*>(Wq) + static_cast<size_t>(h * qph * d_in) * esz;
-    char* k_base = static_cast<char*>(Wk) + static_cast<size_t>(h * kph * d_in) * esz;
+    const int gh = L.head[idx], layer = gh / H;
+    const int64_t h = gh - layer * H;
+    char* q_base = static_cast<char*>(lp.q[layer]) + static_cast<size_t>(h * qph * d_in) * esz;
+    char* k_base = static_cast<char*>(lp.k[layer]) + static_cast<size_t>(h * kph * d_in) * esz;
     if constexpr (VEC) {
       if (off < q_items) scale_vec8<BF16>(q_base, off, off < q_c_items ? L.q_c[idx] : L.q_r[idx]);
       else scale_vec8<BF16>(k_base, off - q_items, L.k[idx]);
@@ -231,26 +242,31 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
 }
 }  // namespace
 
-hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float tau, float alpha, void* Wq, void* Wk,
-                          bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows, int64_t kph,
-                          float* gamma_out, int32_t* clipped_out, hipStream_t stream) {
+hipError_t launch_qk_clip(const float* smax, int64_t L, int64_t H, bool total_clip, float tau, float alpha,
+                          void* const* Wq, void* const* Wk, bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows,
+                          int64_t kph, float* gamma_out, int32_t* clipped_out, hipStream_t stream) {
   const size_t esz = w_bf16 ? 2 : 4;
-  const bool vec = (d_in % 8 == 0) && (reinterpret_cast<uintptr_t>(Wq) % 16 == 0) &&
-                   (reinterpret_cast<uintptr_t>(Wk) % 16 == 0) &&
-                   ((qph * d_in * static_cast<int64_t>(esz)) % 16 == 0) &&
-                   ((kph * d_in * static_cast<int64_t>(esz)) % 16 == 0);
+  LayerPtrs lp{};
+  bool vec = (d_in % 8 == 0) && ((qph * d_in * static_cast<int64_t>(esz)) % 16 == 0) &&
+             ((kph * d_in * static_cast<int64_t>(esz)) % 16 == 0);
+  for (int64_t l = 0; l < L; ++l) {
+    lp.q[l] = Wq[l];
+    lp.k[l] = Wk[l];
+    vec = vec && reinterpret_cast<uintptr_t>(Wq[l]) % 16 == 0 && reinterpret_cast<uintptr_t>(Wk[l]) % 16 == 0;
+  }
+  const int64_t NH = L * H;
   const int64_t total = (qph + kph) * d_in;
-  if (H <= kCompactMaxHeads) {
+  if (NH <= kCompactMaxHeads) {
     // grid for every head clipped: one work item per thread, at most
     // kCompactMaxBlocks blocks (then each thread loops)
-    const int64_t items = H * (vec ? total / 8 : total);
+    const int64_t items = NH * (vec ? total / 8 : total);
     int64_t blocks = (items + kThreads - 1) / kThreads;
     if (blocks > kCompactMaxBlocks) blocks = kCompactMaxBlocks;
     if (blocks < 1) blocks = 1;
 #define MC_CLIP_COMPACT(B, V)                                                                                     \
   hipLaunchKernelGGL((qk_clip_compact_kernel<B, V>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
-                     smax, static_cast<int>(H), total_clip, tau, alpha, Wq, Wk, d_in, qph, q_c_rows, kph, gamma_out,   \
-                     clipped_out)
+                     smax, static_cast<int>(NH), static_cast<int>(H), total_clip, tau, alpha, lp, d_in, qph, q_c_rows,  \
+                     kph, gamma_out, clipped_out)
     if (w_bf16) {
       if (vec) MC_CLIP_COMPACT(true, true);
       else MC_CLIP_COMPACT(true, false);
@@ -264,10 +280,10 @@ hipError_t launch_qk_clip(const float* smax, int64_t H, bool total_clip, float t
   const int64_t per_block = static_cast<int64_t>(kThreads) * kVecPerThread * 8;
   int64_t chunks = (total + per_block - 1) / per_block;
   if (chunks < 1) chunks = 1;
-  dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(H));
+  dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(NH));
 #define MC_CLIP_LAUNCH(B, V)                                                                   \
   hipLaunchKernelGGL((qk_clip_kernel<B, V>), grid, dim3(kThreads), 0, stream, smax, H, total_clip, tau, alpha, \
-                     Wq, Wk, d_in, qph, q_c_rows, kph, gamma_out, clipped_out)
+                     lp, d_in, qph, q_c_rows, kph, gamma_out, clipped_out)
   if (w_bf16) {
     if (vec) MC_CLIP_LAUNCH(true, true);
     else MC_CLIP_LAUNCH(true, false);

@@ -396,12 +396,17 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=WEI
                   mu=MU, tau=TAU, alpha=ALPHA, coeffs=NS_COEFFS, eps=NS_EPS, w_dtype="bf16"):
     """One MuonClip step (Algorithm 1 of the internals deep dive).
 
-    weights, grads, momenta: dicts name -> 2-D array (momenta float32; missing
-    entries start at zero).  smax: per-head max logits measured in the forward
-    that produced ``grads`` (at W_{t-1}).  attention: dict with keys
-    'q', 'k' (weight names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head'.
-    Muon part: every matrix; then QK-Clip on the updated attention weights.
-    Returns (new_weights, new_momenta, gamma, clipped).
+    weights, grads, momenta: dicts name -> 2-D array, or a stack of 2-D
+    arrays [count, rows, cols] treated as `count` separate matrices (momenta
+    float32; missing entries start at zero).  smax: per-head max logits
+    measured in the forward that produced ``grads`` (at W_{t-1}), [H] for one
+    attention layer or [L, H].  attention: a dict with keys 'q', 'k' (weight
+    names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head', or a list of L
+    such dicts: Algorithm 1 clips every head of every attention layer, each
+    layer with its own row of smax.  Muon part: every matrix; then QK-Clip on
+    the updated attention weights.
+    Returns (new_weights, new_momenta, gamma, clipped), gamma and clipped
+    shaped like smax.
     """
     new_w, new_m = {}, {}
     for name, W in weights.items():
@@ -409,12 +414,23 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=WEI
         if M_prev is None:
             M_prev = np.zeros(np.shape(W), dtype=np.float32)
         M = momentum_update(M_prev, grads[name], mu)
-        O = muon_orthogonalised_update(M.astype(np.float64), coeffs, eps)
-        new_w[name] = apply_update(W, O, lr, weight_decay, w_dtype)
+        if np.ndim(W) == 3:
+            new_w[name] = np.stack([apply_update(W[i], muon_orthogonalised_update(M[i].astype(np.float64), coeffs, eps),
+                                                 lr, weight_decay, w_dtype) for i in range(np.shape(W)[0])])
+        else:
+            O = muon_orthogonalised_update(M.astype(np.float64), coeffs, eps)
+            new_w[name] = apply_update(W, O, lr, weight_decay, w_dtype)
         new_m[name] = M
-    qn, kn = attention["q"], attention["k"]
-    Wq, Wk, gamma, clipped = qk_clip(smax, new_w[qn], new_w[kn], attention["q_rows_per_head"],
-                                     attention["q_c_rows"], attention["k_rows_per_head"],
-                                     tau, alpha, w_dtype)
-    new_w[qn], new_w[kn] = Wq, Wk
-    return new_w, new_m, gamma, clipped
+    layers = attention if isinstance(attention, (list, tuple)) else [attention]
+    smax2 = np.atleast_2d(np.asarray(smax, dtype=np.float64))
+    gammas, clips = [], []
+    for a, s_l in zip(layers, smax2):
+        qn, kn = a["q"], a["k"]
+        Wq, Wk, gamma, clipped = qk_clip(s_l, new_w[qn], new_w[kn], a["q_rows_per_head"], a["q_c_rows"],
+                                         a["k_rows_per_head"], tau, alpha, w_dtype)
+        new_w[qn], new_w[kn] = Wq, Wk
+        gammas.append(gamma)
+        clips.append(clipped)
+    if not isinstance(attention, (list, tuple)):
+        return new_w, new_m, gammas[0], clips[0]
+    return new_w, new_m, np.stack(gammas), np.stack(clips)

@@ -191,6 +191,57 @@ def test_full_step_composition(rng):
     assert list(clipped) == [1, 0]
 
 
+def test_full_step_clips_every_layer_with_its_own_max_logits(rng):
+    # Two attention layers (Algorithm 1 clips every head of every attention
+    # layer).  With eta = 0 the Muon part leaves W bit-unchanged, so the clip
+    # acts on the weights S was measured on: recomputed per layer, every
+    # clipped head's max logit is tau again and the other heads' rows are
+    # untouched.  Layer 0 has head 1 hot, layer 1 head 0: reading the wrong
+    # layer's row of S, or clipping only one layer, fails.
+    H, dh, d_in, tau = 3, 4, 8, 5.0
+    X = rng.standard_normal((2, 6, d_in))
+    W, att, S = {}, [], []
+    for layer, hot in ((0, 1), (1, 0)):
+        Wq = rng.standard_normal((H * dh, d_in)) * 0.3
+        Wk = rng.standard_normal((H * dh, d_in)) * 0.3
+        Wq[hot * dh:(hot + 1) * dh] *= 6.0
+        Wk[hot * dh:(hot + 1) * dh] *= 6.0
+        W[f"q{layer}"], W[f"k{layer}"] = Wq, Wk
+        att.append(dict(q=f"q{layer}", k=f"k{layer}", q_rows_per_head=dh, q_c_rows=dh, k_rows_per_head=dh))
+        S.append(oracle.max_logit(oracle.project_heads(X, Wq, H), oracle.project_heads(X, Wk, H)))
+    S = np.stack(S)
+    assert S[0, 1] > tau and S[1, 0] > tau and S[0, 0] < tau and S[1, 1] < tau
+    G = {n: np.zeros(w.shape, dtype=np.float32) for n, w in W.items()}
+    new_w, _, gamma, clipped = oracle.muonclip_step(W, G, {}, S, att, lr=0.0, tau=tau, w_dtype="f64")
+    assert gamma.shape == clipped.shape == (2, H)
+    np.testing.assert_array_equal(clipped, (S > tau).astype(np.int32))
+    for layer in range(2):
+        Wq2, Wk2 = new_w[f"q{layer}"], new_w[f"k{layer}"]
+        S2 = oracle.max_logit(oracle.project_heads(X, Wq2, H), oracle.project_heads(X, Wk2, H))
+        for h in range(H):
+            rows = slice(h * dh, (h + 1) * dh)
+            if S[layer, h] > tau:
+                assert S2[h] == pytest.approx(tau, rel=1e-12)
+            else:
+                np.testing.assert_array_equal(Wq2[rows], W[f"q{layer}"][rows])
+                np.testing.assert_array_equal(Wk2[rows], W[f"k{layer}"][rows])
+
+
+def test_full_step_stacked_matrices_are_separate_matrices(rng):
+    # A stack [count, rows, cols] is count independent Muon matrices.
+    W = {"e": oracle.round_to_bf16(rng.standard_normal((3, 8, 16)) * 0.1),
+         "q": oracle.round_to_bf16(rng.standard_normal((8, 16)) * 0.1),
+         "k": oracle.round_to_bf16(rng.standard_normal((8, 16)) * 0.1)}
+    G = {n: (rng.standard_normal(w.shape) * 1e-3).astype(np.float32) for n, w in W.items()}
+    att = dict(q="q", k="k", q_rows_per_head=4, q_c_rows=4, k_rows_per_head=4)
+    new_w, _, _, _ = oracle.muonclip_step(W, G, {}, np.array([1.0, 1.0]), att, lr=0.02)
+    for i in range(3):
+        one, _, _, _ = oracle.muonclip_step({"e": W["e"][i], "q": W["q"], "k": W["k"]},
+                                            {"e": G["e"][i], "q": G["q"], "k": G["k"]}, {}, np.array([1.0, 1.0]),
+                                            att, lr=0.02)
+        np.testing.assert_array_equal(new_w["e"][i], one["e"])
+
+
 # ------------------------------------------------------------- total clip ----
 def test_total_clip_brings_the_largest_head_to_tau_and_scales_all_heads(rng):
     # Total clip: one gamma = tau / max_h S^h for every head.  Recomputed on the
