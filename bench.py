@@ -335,6 +335,75 @@ def run(args):
                        "tflops counts 3n^2m + n^3 per matrix per iteration, tflops_nominal 4n^2m + 2n^3"}
     del O_ns
 
+    # The HBM-bound steps on their own (outside the step), each a median over
+    # repetitions:
+    #  * momentum over all parameters in one launch (12 B per element; 205 GB,
+    #    far past the 256 MB last-level cache);
+    #  * the update on one 64-expert chunk (bf16 W and O: 6 B per element);
+    #  * QK-Clip of the 4 hot heads (36.7 MB) and of all 64 heads (587 MB),
+    #    with 1 GiB written between repetitions so the rows come from HBM;
+    #  * QK-Clip of 61 attention layers (Kimi K2's count) with 4 hot heads
+    #    each, one launch.
+    def timed(fn, reps, flush=None):
+        ts = []
+        for _ in range(reps):
+            if flush is not None:
+                flush()
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    hbm = {}
+    ms = timed(lambda: mc.muonclip_momentum(wl.M, wl.G, MU), 3)
+    hbm["momentum"] = {"elements": E, "bytes_per_element": 12, "ms": round(ms, 3),
+                       "gbps": round(12.0 * E / (ms * 1e-3) / 1e9, 1)}
+    ns_name, _, ns_n, ns_rows, ns_cols = wl.groups[0]
+    upd_cnt = min(64, ns_n)
+    W_u = wl.view(ns_name, wl.W, 0, upd_cnt)
+    O_u = torch.empty_like(W_u)
+    O_u.normal_(0.0, 0.2)
+    ms = timed(lambda: mc.muon_apply_update(W_u, O_u, LR, WD), 5)
+    n_u = W_u.numel()
+    hbm["update"] = {"elements": n_u, "bytes_per_element": 6, "ms": round(ms, 3),
+                     "gbps": round(6.0 * n_u / (ms * 1e-3) / 1e9, 1)}
+    del O_u
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(1)  # noqa: E731  (1 GiB written: evicts the 256 MB cache)
+    Wq_v, Wkc_v = wl.view("attn_q")[0], wl.view("attn_kc")[0]
+    for label, s_vals in (("clip_4_hot_heads", smax), ("clip_all_64_heads", torch.full_like(smax, 1000.0))):
+        Wq_c, Wkc_c = Wq_v.clone(), Wkc_v.clone()
+        g_c = torch.empty_like(gamma)
+        c_c = torch.empty_like(clipped)
+        mc.qk_clip_apply(s_vals, Wq_c, Wkc_c, D_NOPE + D_ROPE, D_NOPE, D_NOPE, TAU, ALPHA, gamma=g_c, clipped=c_c)
+        ms = timed(lambda: mc.qk_clip_apply(s_vals, Wq_c, Wkc_c, D_NOPE + D_ROPE, D_NOPE, D_NOPE, TAU, ALPHA,
+                                            gamma=g_c, clipped=c_c), 20, flush)
+        heads = int((c_c == 1).sum().item())
+        nbytes = 2 * heads * ((D_NOPE + D_ROPE) + D_NOPE) * D_MODEL * 2
+        hbm[label] = {"heads": heads, "bytes": nbytes, "ms": round(ms, 4),
+                      "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1), "cache": "flushed (1 GiB written between runs)"}
+        del Wq_c, Wkc_c
+    n_layers = 61
+    Wq_l = [Wq_v.clone() for _ in range(n_layers)]
+    Wk_l = [Wkc_v.clone() for _ in range(n_layers)]
+    s_l = smax.view(1, -1).repeat(n_layers, 1).contiguous()
+    mc.qk_clip_apply_layers(s_l, Wq_l, Wk_l, D_NOPE + D_ROPE, D_NOPE, D_NOPE, TAU, ALPHA)
+    ms = timed(lambda: mc.qk_clip_apply_layers(s_l, Wq_l, Wk_l, D_NOPE + D_ROPE, D_NOPE, D_NOPE, TAU, ALPHA), 10,
+               flush)
+    nbytes = n_layers * rescale_bytes
+    hbm["clip_61_layers_one_launch"] = {"layers": n_layers, "heads_per_layer": n_clip, "bytes": nbytes,
+                                        "ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del Wq_l, Wk_l, flush_buf
+    hbm["note"] = ("medians over repetitions on the step's stream; bytes are algorithmic (read + write); "
+                   "peak 8000 GB/s")
+    for v in hbm.values():
+        if isinstance(v, dict):
+            v["frac_of_peak"] = round(v["gbps"] / HBM_PEAK_GBPS, 3)
+
     # Self-measured ceilings on this GPU (measurement aids, outside the step):
     # the MFMA rate with register operands only (random and zero operands:
     # the clock the chip holds depends on how many bits switch), and a plain
@@ -406,6 +475,7 @@ def run(args):
         "gemm_note": "per GEMM (0 X X^T, 1 aI+bA+cAA, 2 B'X, 2u the last B'X applying the update): gemm_tflops on "
                      "the method's flops (n^2m, n^3, 2n^2m), executed on the tiles the MFMAs compute, nominal dense",
         "newton_schulz_only": ns_only,
+        "hbm_steps": hbm,
         "maxlogit_long_context": ml_long,
         "probes": dict(probes, dominant_gemm_frac_of_mfma_probe=round(
             achieved / probes["mfma_bf16_random_operands_tflops"], 3),

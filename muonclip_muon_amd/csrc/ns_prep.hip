@@ -23,7 +23,11 @@ namespace mc {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kT = 64;  // transpose tile
+// One block covers 8192 elements (one norm partial each): the tiled kernel
+// 64 rows x 128 columns, the row-strip kernel 32 rows x 256 columns.
+constexpr int kBlockElems = 8192;
+constexpr int kTR = 64, kTC = 128;    // tile of the tiled (transposing) kernel
+constexpr int kSR = 32, kSC = 256;    // strip of the row kernel
 }  // namespace
 
 static inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
@@ -39,7 +43,7 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   g.m = g.transposed ? rows : cols;
   g.n_pad = round_up(g.n, kNsTile);
   g.m_pad = round_up(g.m, kNsTile);
-  g.prescale_tiles = (g.n_pad / kT) * (g.m_pad / kT);
+  g.prescale_tiles = g.n_pad * g.m_pad / kBlockElems;
   const size_t xb = static_cast<size_t>(batch) * g.n_pad * g.m_pad * 2;
   const size_t ab = static_cast<size_t>(batch) * g.n_pad * g.n_pad * 2;
   size_t off = 0;
@@ -96,25 +100,59 @@ __global__ __launch_bounds__(kThreads) void invnorm_kernel(const float* __restri
   if (threadIdx.x == 0) invnorm[b] = static_cast<float>(1.0 / (sqrt(red[0]) + static_cast<double>(eps)));
 }
 
-// 8 consecutive elements of M (float32 for SRC 1, bf16 for SRC 2) at idx,
-// and one element
-template <int SRC>
-__device__ __forceinline__ void load8_src(const void* M, int64_t idx, float (&x)[8]) {
-  if constexpr (SRC == 2) {
-    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(M) + idx));
-    x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
-    x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
-  } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(M) + idx);
-    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-}
+// One element of M (float32 for SRC 1, bf16 for SRC 2) at idx
 template <int SRC>
 __device__ __forceinline__ float load1_src(const void* M, int64_t idx) {
   if constexpr (SRC == 2) return bf16_to_f32(static_cast<const uint16_t*>(M)[idx]);
   else return static_cast<const float*>(M)[idx];
+}
+
+// One 8-element run of M (and of G for SRC 0), loaded without a branch: the
+// caller passes a clamped in-bounds index for runs outside the matrix (and
+// zeroes their values), so a thread's loads of several passes are all in
+// flight before the first of them is used.
+template <int SRC>
+struct Run8 {
+  f32x4 m0, m1, g0, g1;
+};
+template <int SRC>
+__device__ __forceinline__ void load_run8(const void* M, const float* G, int64_t idx, Run8<SRC>& v) {
+  if constexpr (SRC == 2) {
+    const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(M) + idx));
+    v.m0 = f32x4{bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y)};
+    v.m1 = f32x4{bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w)};
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(M) + idx);
+    v.m0 = __builtin_nontemporal_load(p);
+    v.m1 = __builtin_nontemporal_load(p + 1);
+    if constexpr (SRC == 0) {
+      const f32x4* q = reinterpret_cast<const f32x4*>(G + idx);
+      v.g0 = __builtin_nontemporal_load(q);
+      v.g1 = __builtin_nontemporal_load(q + 1);
+    }
+  }
+}
+// The new M values of a run (momentum for SRC 0, written back to M at idx
+// when `in`), as 8 floats; zeros outside the matrix.
+template <int SRC>
+__device__ __forceinline__ void apply_run8(Run8<SRC>& v, float* M, int64_t idx, float mu, bool in, float (&x)[8]) {
+  if constexpr (SRC == 0) {
+    v.m0.x = momentum_op(v.m0.x, v.g0.x, mu);
+    v.m0.y = momentum_op(v.m0.y, v.g0.y, mu);
+    v.m0.z = momentum_op(v.m0.z, v.g0.z, mu);
+    v.m0.w = momentum_op(v.m0.w, v.g0.w, mu);
+    v.m1.x = momentum_op(v.m1.x, v.g1.x, mu);
+    v.m1.y = momentum_op(v.m1.y, v.g1.y, mu);
+    v.m1.z = momentum_op(v.m1.z, v.g1.z, mu);
+    v.m1.w = momentum_op(v.m1.w, v.g1.w, mu);
+    if (in) {
+      f32x4* mp = reinterpret_cast<f32x4*>(M + idx);
+      __builtin_nontemporal_store(v.m0, mp);
+      __builtin_nontemporal_store(v.m1, mp + 1);
+    }
+  }
+  x[0] = in ? v.m0.x : 0.f; x[1] = in ? v.m0.y : 0.f; x[2] = in ? v.m0.z : 0.f; x[3] = in ? v.m0.w : 0.f;
+  x[4] = in ? v.m1.x : 0.f; x[5] = in ? v.m1.y : 0.f; x[6] = in ? v.m1.z : 0.f; x[7] = in ? v.m1.w : 0.f;
 }
 
 // Fused momentum and pre-scale (SRC = 0).  M_b, G_b are R x C float32 (rows
@@ -123,13 +161,14 @@ __device__ __forceinline__ float load1_src(const void* M, int64_t idx) {
 // (high parts into S, low parts into SL; R_pad x C_pad; rows <= cols:
 // X_0 = M) or transposed (T, TL; C_pad x R_pad; rows > cols: X_0 = M^T),
 // zero-padded; the other two pointers are null.
-// Each block reads one 64 x 64 tile in 8-element runs (vector loads when
-// VEC) and writes it straight from registers or transposed through LDS; it
-// also writes the float32 sum of squares of its tile's new M values to
-// partials[b * tiles + tile].  SRC = 1 (float32 M) or 2 (bf16 M): the same
-// without momentum (G unused, M only read), the unscaled pre-scale of the
-// stand-alone Newton-Schulz call.
-// grid (C_pad / 64, R_pad / 64, batch).
+// Each block reads one 64 x 128 tile in 8-element runs (vector loads when
+// VEC; 16 lanes cover 512 contiguous bytes of a float32 row) and writes it
+// straight from registers or transposed through LDS (8 lanes per output row,
+// 128 contiguous bytes of each part); it also writes the float32 sum of
+// squares of its tile's new M values to partials[b * tiles + tile].  SRC = 1
+// (float32 M) or 2 (bf16 M): the same without momentum (G unused, M only
+// read), the unscaled pre-scale of the stand-alone Newton-Schulz call.
+// grid (C_pad / 128, R_pad / 64, batch).
 template <bool VEC, int SRC>
 __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __restrict__ Mv,
                                                                     const float* __restrict__ G,
@@ -140,10 +179,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
                                                                     uint16_t* __restrict__ SL,
                                                                     uint16_t* __restrict__ TL,
                                                                     float* __restrict__ partials) {
-  __shared__ float tile[kT][kT + 1];
+  __shared__ float tile[kTR][kTC + 1];
   __shared__ float red[kThreads / 64];
   const int64_t b = blockIdx.z;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kT, r0 = static_cast<int64_t>(blockIdx.y) * kT;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTC, r0 = static_cast<int64_t>(blockIdx.y) * kTR;
   float* mb = static_cast<float*>(Mv) + (SRC == 2 ? 0 : b * batch_stride);
   const void* msrc = SRC == 2 ? static_cast<const void*>(static_cast<const uint16_t*>(Mv) + b * batch_stride)
                               : static_cast<const void*>(mb);
@@ -152,40 +191,29 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
   uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
   uint16_t* slb = SL + static_cast<size_t>(b) * R_pad * C_pad;
   uint16_t* tlb = TL + static_cast<size_t>(b) * R_pad * C_pad;
-  const int q = threadIdx.x & 7;
+  const int q = threadIdx.x & 15;
   float ss = 0.f;
+  // VEC (C % 8 == 0): a run is wholly inside or wholly outside the matrix;
+  // the four passes' loads are issued before any is used
+  Run8<SRC> run[VEC ? 4 : 1];
+  int64_t idx[VEC ? 4 : 1];
+  bool in[VEC ? 4 : 1];
+  if constexpr (VEC) {
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int rr = pass * 32 + (threadIdx.x >> 3);
+    for (int pass = 0; pass < 4; ++pass) {
+      const int64_t r = r0 + pass * 16 + (threadIdx.x >> 4), c = c0 + 8 * q;
+      in[pass] = r < R && c < C;
+      idx[pass] = (r < R ? r : R - 1) * C + (c < C ? c : C - 8);
+      load_run8<SRC>(msrc, gb, idx[pass], run[pass]);
+    }
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int rr = pass * 16 + (threadIdx.x >> 4);
     const int64_t r = r0 + rr, c = c0 + 8 * q;
     float x[8];
     if constexpr (VEC) {
-      // C % 8 == 0: a run is wholly inside or wholly outside the matrix
-      if (r < R && c < C) {
-        if constexpr (SRC != 0) {
-          load8_src<SRC>(msrc, r * C + c, x);
-        } else {
-          f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
-          const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
-          f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
-          const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
-          m0.x = momentum_op(m0.x, g0.x, mu);
-          m0.y = momentum_op(m0.y, g0.y, mu);
-          m0.z = momentum_op(m0.z, g0.z, mu);
-          m0.w = momentum_op(m0.w, g0.w, mu);
-          m1.x = momentum_op(m1.x, g1.x, mu);
-          m1.y = momentum_op(m1.y, g1.y, mu);
-          m1.z = momentum_op(m1.z, g1.z, mu);
-          m1.w = momentum_op(m1.w, g1.w, mu);
-          __builtin_nontemporal_store(m0, mp);
-          __builtin_nontemporal_store(m1, mp + 1);
-          x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
-          x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
+      apply_run8<SRC>(run[pass], mb, idx[pass], mu, in[pass], x);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -218,9 +246,9 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
   if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = tile_ss;
   if (S != nullptr) return;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 4; ++pass) {
     const int cc = pass * 32 + (threadIdx.x >> 3);
-    const int rq = 8 * q;
+    const int rq = 8 * (threadIdx.x & 7);
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[rq + e][cc];
@@ -232,11 +260,11 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
 }
 
 // The same for rows <= cols with 16-byte aligned rows (the common case),
-// with row strips instead of square tiles: a block covers 16 rows x 256
-// columns (one column panel of X), so every row segment it reads is 1 KB of
-// M and of G and every X_0 segment it writes is 512 contiguous bytes.
-// grid (C_pad / 256, R_pad / 16, batch); 4096 elements per block, like the
-// 64 x 64 tiles, so the partial-sum count per matrix is the same.  SRC as in
+// with row strips instead of tiles: a block covers 32 rows x 256 columns
+// (one column panel of X), so every row segment it reads is 1 KB of M and
+// of G and every X_0 segment it writes is 512 contiguous bytes of each part.
+// grid (C_pad / 256, R_pad / 32, batch); 8192 elements per block, like the
+// tiles, so the partial-sum count per matrix is the same.  SRC as in
 // momentum_prescale_kernel.
 template <int SRC>
 __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
@@ -253,35 +281,22 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
   uint16_t* xb = X0 + static_cast<size_t>(b) * R_pad * C_pad;
   uint16_t* xlb = X0l + static_cast<size_t>(b) * R_pad * C_pad;
   float ss = 0.f;
+  // C % 8 == 0: a run is wholly inside or outside the matrix
+  Run8<SRC> run[4];
+  int64_t idx[4];
+  bool in[4];
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int64_t r = static_cast<int64_t>(blockIdx.y) * 16 + pass * 8 + (threadIdx.x >> 5);
+  for (int pass = 0; pass < 4; ++pass) {
+    const int64_t r = static_cast<int64_t>(blockIdx.y) * kSR + pass * 8 + (threadIdx.x >> 5);
+    in[pass] = r < R && c < C;
+    idx[pass] = (r < R ? r : R - 1) * C + (c < C ? c : C - 8);
+    load_run8<SRC>(msrc, gb, idx[pass], run[pass]);
+  }
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int64_t r = static_cast<int64_t>(blockIdx.y) * kSR + pass * 8 + (threadIdx.x >> 5);
     float x[8];
-    if (r < R && c < C) {  // C % 8 == 0: a run is wholly inside or outside
-      if constexpr (SRC != 0) {
-        load8_src<SRC>(msrc, r * C + c, x);
-      } else {
-        f32x4* mp = reinterpret_cast<f32x4*>(mb + r * C + c);
-        const f32x4* gp = reinterpret_cast<const f32x4*>(gb + r * C + c);
-        f32x4 m0 = __builtin_nontemporal_load(mp), m1 = __builtin_nontemporal_load(mp + 1);
-        const f32x4 g0 = __builtin_nontemporal_load(gp), g1 = __builtin_nontemporal_load(gp + 1);
-        m0.x = momentum_op(m0.x, g0.x, mu);
-        m0.y = momentum_op(m0.y, g0.y, mu);
-        m0.z = momentum_op(m0.z, g0.z, mu);
-        m0.w = momentum_op(m0.w, g0.w, mu);
-        m1.x = momentum_op(m1.x, g1.x, mu);
-        m1.y = momentum_op(m1.y, g1.y, mu);
-        m1.z = momentum_op(m1.z, g1.z, mu);
-        m1.w = momentum_op(m1.w, g1.w, mu);
-        __builtin_nontemporal_store(m0, mp);
-        __builtin_nontemporal_store(m1, mp + 1);
-        x[0] = m0.x; x[1] = m0.y; x[2] = m0.z; x[3] = m0.w;
-        x[4] = m1.x; x[5] = m1.y; x[6] = m1.z; x[7] = m1.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
+    apply_run8<SRC>(run[pass], mb, idx[pass], mu, in[pass], x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
     u32x4 hi, lo;
@@ -311,10 +326,10 @@ hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_strid
   const bool vec = C % 8 == 0 && (g.batch == 1 || batch_stride % 8 == 0) &&
                    reinterpret_cast<uintptr_t>(M) % align == 0 &&
                    (SRC != 0 || reinterpret_cast<uintptr_t>(G) % 32 == 0);
-  dim3 grid(static_cast<unsigned>(C_pad / kT), static_cast<unsigned>(R_pad / kT), static_cast<unsigned>(g.batch));
+  dim3 grid(static_cast<unsigned>(C_pad / kTC), static_cast<unsigned>(R_pad / kTR), static_cast<unsigned>(g.batch));
   if (vec && S != nullptr)
     hipLaunchKernelGGL(momentum_prescale_rows_kernel<SRC>,
-                       dim3(static_cast<unsigned>(C_pad / 256), static_cast<unsigned>(R_pad / 16),
+                       dim3(static_cast<unsigned>(C_pad / kSC), static_cast<unsigned>(R_pad / kSR),
                             static_cast<unsigned>(g.batch)),
                        dim3(kThreads), 0, stream, M, G, batch_stride, mu, R, C, R_pad, C_pad, S, SL, partials);
   else if (vec)

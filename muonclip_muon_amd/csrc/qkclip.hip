@@ -19,9 +19,9 @@
 // come from a table of L pointers in the kernel arguments, and "head" below
 // means one of the L x H (layer, head) pairs.  A head's rows are two
 // contiguous row blocks (W_q and W_k are row-major with head-major rows), so
-// the kernels stream them with 16-byte accesses.  Compact kernel (up to 4096
+// the kernels stream them with 16-byte accesses.  Compact kernel (up to 4000
 // heads): every block reads all L x H values of S_max, lists the clipped
-// heads with their factors in LDS, and the grid, sized for the case where
+// heads with their factors in LDS (16 bytes per head), and the grid, sized for the case where
 // every head is clipped, shares out only the listed heads' elements, so few
 // clipped heads still spread over every CU and no block is launched just to
 // find its head unclipped.  More heads: a grid of (chunks, L x H) whose
@@ -166,77 +166,132 @@ __global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restri
 }
 
 
-constexpr int kCompactMaxHeads = 4096;
+constexpr int kCompactMaxHeads = 4000;  // heads per layer; the list then takes at most 64000 bytes of LDS
 constexpr int kCompactMaxBlocks = 2048;
 
-// The clipped heads, their factors and the head count, identical in every
-// block.  Block 0 also writes gamma_out / clipped_out for every head.
-struct ClipList {
-  int head[kCompactMaxHeads];
-  float q_c[kCompactMaxHeads], q_r[kCompactMaxHeads], k[kCompactMaxHeads];
-  int wave_count[kThreads / 64];
-};
-
-// NH = L * H heads; H heads per layer (total_clip: one layer, L = 1).
+// grid (blocks per layer, L).  Block (x, l) lists layer l's clipped heads
+// (identical in every block of the layer) with their factors in dynamic LDS
+// sized for H entries (16 bytes each), then takes share x of that layer's
+// clipped elements; block (0, l) also writes gamma_out / clipped_out of the
+// layer's heads.  total_clip: one layer, gamma from the largest S_max.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* __restrict__ smax, int NH, int H,
+__global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* __restrict__ smax_all, int H,
                                                                   bool total_clip, float tau, float alpha,
                                                                   LayerPtrs lp, int64_t d_in, int64_t qph,
                                                                   int64_t q_c_rows, int64_t kph,
                                                                   float* __restrict__ gamma_out,
                                                                   int32_t* __restrict__ clipped_out) {
-  __shared__ ClipList L;
+  extern __shared__ __attribute__((aligned(16))) char clip_list[];
+  int* l_head = reinterpret_cast<int*>(clip_list);
+  float* l_qc = reinterpret_cast<float*>(clip_list) + H;
+  float* l_qr = l_qc + H;
+  float* l_k = l_qr + H;
+  __shared__ int wave_count[kThreads / 64];
+  const int layer = blockIdx.y;
+  const float* smax = smax_all + static_cast<int64_t>(layer) * H;
   const float s_all = total_clip ? block_max_all(smax, H) : 0.0f;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int count = 0;  // the same in every thread
-  for (int base = 0; base < NH; base += kThreads) {
+  for (int base = 0; base < H; base += kThreads) {
     const int h = base + static_cast<int>(threadIdx.x);
     ClipFactors f = {1.f, 1.f, 1.f, 0, 1.f};
-    if (h < NH) f = clip_factors(total_clip ? s_all : smax[h], tau, alpha);
-    if (blockIdx.x == 0 && h < NH) {
-      if (gamma_out) gamma_out[h] = f.gamma;
-      if (clipped_out) clipped_out[h] = f.state;
+    if (h < H) f = clip_factors(total_clip ? s_all : smax[h], tau, alpha);
+    if (blockIdx.x == 0 && h < H) {
+      if (gamma_out) gamma_out[static_cast<int64_t>(layer) * H + h] = f.gamma;
+      if (clipped_out) clipped_out[static_cast<int64_t>(layer) * H + h] = f.state;
     }
-    const bool c = h < NH && f.state == 1;
+    const bool c = h < H && f.state == 1;
     const uint64_t m = __ballot(c);
-    if (lane == 0) L.wave_count[w] = __popcll(m);
+    if (lane == 0) wave_count[w] = __popcll(m);
     __syncthreads();
     int slot = count + __popcll(m & ((uint64_t{1} << lane) - 1));
     int round = 0;
     for (int i = 0; i < kThreads / 64; ++i) {
-      if (i < w) slot += L.wave_count[i];
-      round += L.wave_count[i];
+      if (i < w) slot += wave_count[i];
+      round += wave_count[i];
     }
     if (c) {
-      L.head[slot] = h;
-      L.q_c[slot] = f.q_c;
-      L.q_r[slot] = f.q_r;
-      L.k[slot] = f.k;
+      l_head[slot] = h;
+      l_qc[slot] = f.q_c;
+      l_qr[slot] = f.q_r;
+      l_k[slot] = f.k;
     }
     count += round;
     __syncthreads();
   }
   if (count == 0) return;
+  char* const q_layer = static_cast<char*>(lp.q[layer]);
+  char* const k_layer = static_cast<char*>(lp.k[layer]);
 
   const size_t esz = BF16 ? 2 : 4;
   const int64_t unit = VEC ? 8 : 1;  // elements per work item
   const int64_t q_items = qph * d_in / unit, q_c_items = q_c_rows * d_in / unit;
   const int64_t per_head = q_items + kph * d_in / unit;
   const int64_t total = count * per_head;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total; v += stride) {
-    const int idx = static_cast<int>(v / per_head);
-    const int64_t off = v - idx * per_head;
-    const int gh = L.head[idx], layer = gh / H;
-    const int64_t h = gh - layer * H;
-    char* q_base = static_cast<char*>(lp.q[layer]) + static_cast<size_t>(h * qph * d_in) * esz;
-    char* k_base = static_cast<char*>(lp.k[layer]) + static_cast<size_t>(h * kph * d_in) * esz;
-    if constexpr (VEC) {
-      if (off < q_items) scale_vec8<BF16>(q_base, off, off < q_c_items ? L.q_c[idx] : L.q_r[idx]);
-      else scale_vec8<BF16>(k_base, off - q_items, L.k[idx]);
-    } else {
-      if (off < q_items) scale_one<BF16>(q_base, off, off < q_c_items ? L.q_c[idx] : L.q_r[idx]);
-      else scale_one<BF16>(k_base, off - q_items, L.k[idx]);
+  // Each block takes one contiguous range of work items, in batches of
+  // kUnroll x kThreads consecutive items (a thread's kUnroll items kThreads
+  // apart); a batch's loads are all issued before any item is scaled and
+  // stored, so kUnroll 16-byte loads per thread are in flight at once.  The
+  // head of an item follows from the batch's first head without a division
+  // per item.
+  constexpr int kUnroll = 4;
+  constexpr int64_t kBatch = static_cast<int64_t>(kUnroll) * kThreads;
+  const int64_t per_block = ((total + gridDim.x - 1) / gridDim.x + kBatch - 1) / kBatch * kBatch;
+  const int64_t v_begin = static_cast<int64_t>(blockIdx.x) * per_block;
+  const int64_t v_end = min(total, v_begin + per_block);
+  for (int64_t base = v_begin; base < v_end; base += kBatch) {
+    const int idx0 = static_cast<int>(base / per_head);
+    char* addr[kUnroll];
+    float fac[kUnroll];
+    constexpr int kWords = VEC && !BF16 ? 2 : 1;  // 16-byte words per item
+    u32x4 val[kUnroll][kWords];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = base + u * kThreads + threadIdx.x;
+      addr[u] = nullptr;
+      if (v >= v_end) continue;
+      int idx = idx0;
+      int64_t off = v - static_cast<int64_t>(idx0) * per_head;
+      while (off >= per_head) {
+        off -= per_head;
+        ++idx;
+      }
+      const int64_t h = l_head[idx];
+      const bool in_q = off < q_items;
+      char* row_base = in_q ? q_layer + static_cast<size_t>(h * qph * d_in) * esz
+                            : k_layer + static_cast<size_t>(h * kph * d_in) * esz;
+      const int64_t o = in_q ? off : off - q_items;
+      fac[u] = in_q ? (off < q_c_items ? l_qc[idx] : l_qr[idx]) : l_k[idx];
+      addr[u] = row_base + static_cast<size_t>(o * unit) * esz;
+      if constexpr (VEC) {
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) val[u][w] = reinterpret_cast<const u32x4*>(addr[u])[w];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (addr[u] == nullptr) continue;
+      if constexpr (VEC) {
+        if constexpr (BF16) {
+          u32x4 a = val[u][0];
+          const float f = fac[u];
+          a.x = pack_bf16x2(scale_op(bf16_lo(a.x), f), scale_op(bf16_hi(a.x), f));
+          a.y = pack_bf16x2(scale_op(bf16_lo(a.y), f), scale_op(bf16_hi(a.y), f));
+          a.z = pack_bf16x2(scale_op(bf16_lo(a.z), f), scale_op(bf16_hi(a.z), f));
+          a.w = pack_bf16x2(scale_op(bf16_lo(a.w), f), scale_op(bf16_hi(a.w), f));
+          *reinterpret_cast<u32x4*>(addr[u]) = a;
+        } else {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            f32x4 a = __builtin_bit_cast(f32x4, val[u][w % kWords]);
+            a.x = scale_op(a.x, fac[u]); a.y = scale_op(a.y, fac[u]);
+            a.z = scale_op(a.z, fac[u]); a.w = scale_op(a.w, fac[u]);
+            reinterpret_cast<u32x4*>(addr[u])[w] = __builtin_bit_cast(u32x4, a);
+          }
+        }
+      } else {
+        scale_one<BF16>(addr[u], 0, fac[u]);
+      }
     }
   }
 }
@@ -256,17 +311,18 @@ hipError_t launch_qk_clip(const float* smax, int64_t L, int64_t H, bool total_cl
   }
   const int64_t NH = L * H;
   const int64_t total = (qph + kph) * d_in;
-  if (NH <= kCompactMaxHeads) {
-    // grid for every head clipped: one work item per thread, at most
-    // kCompactMaxBlocks blocks (then each thread loops)
-    const int64_t items = NH * (vec ? total / 8 : total);
+  if (H <= kCompactMaxHeads) {
+    // blocks per layer for every head clipped: one work item per thread, at
+    // most kCompactMaxBlocks blocks over all layers (then each thread loops)
+    const int64_t items = H * (vec ? total / 8 : total);
     int64_t blocks = (items + kThreads - 1) / kThreads;
-    if (blocks > kCompactMaxBlocks) blocks = kCompactMaxBlocks;
+    const int64_t cap = kCompactMaxBlocks / L > 0 ? kCompactMaxBlocks / L : 1;
+    if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
 #define MC_CLIP_COMPACT(B, V)                                                                                     \
-  hipLaunchKernelGGL((qk_clip_compact_kernel<B, V>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, \
-                     smax, static_cast<int>(NH), static_cast<int>(H), total_clip, tau, alpha, lp, d_in, qph, q_c_rows,  \
-                     kph, gamma_out, clipped_out)
+  hipLaunchKernelGGL((qk_clip_compact_kernel<B, V>), dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(L)), \
+                     dim3(kThreads), static_cast<unsigned>(H * 16), stream, smax, static_cast<int>(H), total_clip,   \
+                     tau, alpha, lp, d_in, qph, q_c_rows, kph, gamma_out, clipped_out)
     if (w_bf16) {
       if (vec) MC_CLIP_COMPACT(true, true);
       else MC_CLIP_COMPACT(true, false);
