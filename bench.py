@@ -527,6 +527,25 @@ def run(args):
     return out, wl
 
 
+def host_info():
+    """Host cores, affinity mask and BLAS library the oracle runs on."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except AttributeError:  # not on Linux
+        info["affinity_cpus"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        pools = threadpool_info()
+        blas = [p for p in pools if p.get("user_api") == "blas"]
+        info["blas"] = ", ".join(f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                                 for p in blas) or None
+        info["threads"] = max((p.get("num_threads", 1) for p in blas), default=os.cpu_count())
+    except Exception:  # noqa: BLE001
+        info["blas"], info["threads"] = None, os.cpu_count()
+    return info
+
+
 def cpu_baseline(wl, torch, n_matrices=6):
     """The fp64 oracle on a bounded sample of the same workload (about 10 s of
     CPU work): n_matrices expert matrices, alternately 2048x7168 and
@@ -535,36 +554,114 @@ def cpu_baseline(wl, torch, n_matrices=6):
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
-    host = []
+    host = host_info()
+    data = []
     for k in range(n_matrices):
         grp = "expert_gate_up" if k % 2 == 0 else "expert_down"
         m, g, w = (wl.view(grp, buf, k // 2, 1)[0] for buf in (wl.M, wl.G, wl.W))
-        host.append((m.cpu().numpy(), g.cpu().numpy(), w.float().cpu().numpy().astype(np.float64)))
+        data.append((m.cpu().numpy(), g.cpu().numpy(), w.float().cpu().numpy().astype(np.float64)))
     heads = [int(wl.hot[0]), (int(wl.hot[0]) + 1) % N_HEADS]
     Qh = [wl.Q[:, h:h + 1].float().cpu().numpy() for h in heads]
     Kch = [wl.Kc[:, h:h + 1].float().cpu().numpy() for h in heads]
     Kr = wl.Kr.float().cpu().numpy()
     t0 = time.perf_counter()
     flops = 0.0
-    for M, G, W in host:
+    for M, G, W in data:
         Mn = oracle.momentum_update(M, G, MU)
         O = oracle.muon_orthogonalised_update(Mn.astype(np.float64))
         oracle.apply_update(W, O, LR, WD, "bf16")
-        flops += ns_flops(*M.shape, oracle.NS_STEPS)
+        flops += ns_flops_sym(*M.shape, oracle.NS_STEPS)
     for q, k in zip(Qh, Kch):
         oracle.max_logit(q, k, Kr)
         flops += 2.0 * q.shape[0] * q.shape[2] * k.shape[2] * q.shape[3]
     dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 2),
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": host["threads"], "kind": "oracle",
+            "seconds": round(dt, 2), "host": host,
             "sample": f"fp64 oracle: momentum + Newton-Schulz x5 + update of {n_matrices} expert matrices "
                       "(2048x7168 and 7168x2048 alternately) and the max logit of 2 heads over 8 x 4096 "
                       "tokens; same flop accounting as value"}
+
+
+def cpu_baseline_configs():
+    """The oracle per workload, each on a bounded seeded sample, median of 3
+    runs, extrapolated linearly to the whole workload (matrices and heads are
+    independent) and labelled so: the tiny fp32 step (whole), Newton-Schulz
+    alone (2 of 64 matrices), the max logit + QK-Clip at 8 x 4096 (2 of 64
+    heads), the full step for one MoE layer (2 expert matrices of each shape
+    and W_kr whole; W_q and W_kc by their flop share), and the 32K-token max
+    logit (1 of 64 heads)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    def med3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1]
+
+    out = {"host": host_info(), "configs": []}
+    # tiny fp32 attention layer: one whole step
+    t = workloads.tiny_attention(seed=1, device="cpu", weight_reading="variance")
+    Wn = {n: w.double().numpy() for n, w in t.W.items()}
+    Gn = {n: g.numpy() for n, g in t.G.items()}
+    att = dict(q="q", k="k", q_rows_per_head=t.head_dim, q_c_rows=t.head_dim, k_rows_per_head=t.head_dim)
+
+    def tiny():
+        q = oracle.project_heads(t.X.double().numpy(), Wn["q"], t.n_heads)
+        k = oracle.project_heads(t.X.double().numpy(), Wn["k"], t.n_heads)
+        oracle.muonclip_step(Wn, Gn, {}, oracle.max_logit(q, k), att, lr=0.02, w_dtype="f32")
+    s = med3(tiny)
+    out["configs"].append({"workload": "tiny fp32 attention layer, one step", "sample": "whole", "seconds": s})
+    # Newton-Schulz alone, 64 x 2048 x 7168: 2 matrices
+    eb = workloads.expert_batch(seed=2, device="cpu", batch=2)
+    Ms = [oracle.momentum_update(eb.M_prev[i].numpy(), eb.G[i].numpy(), MU) for i in range(2)]
+    s = med3(lambda: [oracle.newton_schulz(m.astype(np.float64)) for m in Ms])
+    fl = ns_flops_sym(2048, 7168, oracle.NS_STEPS) * 64
+    out["configs"].append({"workload": "Newton-Schulz alone, 64 x 2048 x 7168", "sample": "2 of 64 matrices",
+                           "seconds_sample": s, "seconds_extrapolated": s * 32,
+                           "tflops": fl / (s * 32) / 1e12})
+    # max logit + clip at 8 x 4096, 64 heads: 2 heads
+    L = workloads.mla_logits(seed=3, device="cpu", batch=8, seq=4096)
+    Kr = L.Kr.double().numpy()
+    qs = [L.Q[:, h:h + 1].double().numpy() for h in (0, 1)]
+    ks = [L.Kc[:, h:h + 1].double().numpy() for h in (0, 1)]
+    s = med3(lambda: [oracle.max_logit(q, k, Kr) for q, k in zip(qs, ks)])
+    fl = 2.0 * 8 * 64 * 4096 * 4096 * (D_NOPE + D_ROPE)
+    out["configs"].append({"workload": "max logit, 8 x 4096 tokens, 64 heads, d 128+64", "sample": "2 of 64 heads",
+                           "seconds_sample": s, "seconds_extrapolated": s * 32, "tflops": fl / (s * 32) / 1e12})
+    del L, qs, ks, Kr
+    # full step for one MoE layer: 2 matrices of each expert shape
+    g = workloads.generator(4, "cpu")
+    secs = 0.0
+    for rows, cols, count in ((2048, 7168, 768), (7168, 2048, 384)):
+        data = [(workloads.normal((rows, cols), 1e-4, g, "cpu").numpy(), workloads.normal((rows, cols), 1e-4, g, "cpu").numpy(),
+                 workloads.normal((rows, cols), 0.02, g, "cpu", torch.bfloat16).double().numpy()) for _ in range(2)]
+
+        def run(data=data):
+            for M, G, W in data:
+                Mn = oracle.momentum_update(M, G, MU)
+                oracle.apply_update(W, oracle.muon_orthogonalised_update(Mn.astype(np.float64)), LR, WD, "bf16")
+        secs += med3(run) * count / 2
+    expert_fl = ns_flops_sym(2048, 7168, oracle.NS_STEPS) * 1152
+    attn_fl = sum(ns_flops_sym(r, D_MODEL, oracle.NS_STEPS) for r in (12288, 8192, 64))
+    secs_total = secs * (expert_fl + attn_fl) / expert_fl
+    out["configs"].append({"workload": "full MuonClip step, one MoE layer (NS x5 of 1155 matrices)",
+                           "sample": "2 matrices of each expert shape; the attention projections by their flop share",
+                           "seconds_extrapolated": secs_total,
+                           "tflops": (expert_fl + attn_fl) / secs_total / 1e12})
+    # long-context max logit: 1 of 64 heads
+    L = workloads.mla_logits(seed=5, device="cpu", batch=1, seq=32768, n_hot=0)
+    q, k, Kr = L.Q[:, :1].double().numpy(), L.Kc[:, :1].double().numpy(), L.Kr.double().numpy()
+    s = med3(lambda: oracle.max_logit(q, k, Kr, block=4096))
+    fl = 2.0 * 32768 * 32768 * 64 * (D_NOPE + D_ROPE)
+    out["configs"].append({"workload": "max logit, 1 x 32768 tokens, 64 heads", "sample": "1 of 64 heads",
+                           "seconds_sample": s, "seconds_extrapolated": s * 64, "tflops": fl / (s * 64) / 1e12})
+    print(json.dumps(out), flush=True)
 
 
 def copy_calibration():
@@ -592,6 +689,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="momentum, Newton-Schulz and update as three calls (O stored in bf16)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-baseline-configs", action="store_true",
+                    help="time the fp64 oracle per workload on bounded samples (CPU only, several minutes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
@@ -599,6 +698,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.cpu_baseline_configs:
+        cpu_baseline_configs()
         return
     import torch
     if not torch.cuda.is_available():
