@@ -131,8 +131,9 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  * Arithmetic: the norm is accumulated in float32 (combined in double); X_0
  * is held unscaled and the factor 1 / (||M||_F + eps) is applied in float32
  * by the first step's GEMMs (X X^T by its square, that step's X by it).  X
- * is carried as a pair of bf16 matrices X = Xh + Xl (about 16 significant
- * bits); each step computes A = Xh Xh^T and B = b_s A + c_s A A on bf16 MFMA
+ * is carried as X = Xh + Xl, a bf16 high part and the rounding residual as
+ * one signed byte per element, a step of 256 in the binary32 bit pattern
+ * from the high part's (about 16 significant bits together); each step computes A = Xh Xh^T and B = b_s A + c_s A A on bf16 MFMA
  * with float32 accumulation (A rounded to bf16; B's diagonal d kept in
  * float32 and the rest rounded to bf16), then X <- a_s X + d Xh + N Xh (N =
  * B off its diagonal) in float32, split into its two parts again.  Keeping
@@ -193,7 +194,7 @@ MC_API mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_
  * the update as it finishes each tile of X (X rounded to bf16 as in the
  * output of muon_ns_orthogonalize_batched; O = out_scale * X formed in
  * float32, not rounded to a storage type).  The new M is converted to its
- * bf16 pair once, in the momentum pass, together with float32 partial sums
+ * (bf16, int8 code) pair once, in the momentum pass, together with float32 partial sums
  * of its squares; the normalisation
  * 1 / (||M_b||_F + eps) is applied inside the first Newton-Schulz step (to
  * X X^T squared and to the step's result), which equals normalising X_0 up

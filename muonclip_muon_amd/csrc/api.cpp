@@ -93,7 +93,7 @@ mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, c
 
 // The steps' GEMMs, X_0 at off_x0 (high part) and off_xl0 (low part):
 // A = Xh Xh^T; B = b A + c A A = diag(d) + N; X <- a X + d Xh + N Xh (X
-// carried as a bf16 pair, d in float32).
+// carried as bf16 high parts and int8 low-part codes, d in float32).
 // inv0 (or null): the stored X_0 is to be scaled per matrix by inv0 (applied
 // inside the first step).  upd (or null): the last step updates W (or writes
 // the output) instead of storing X.
@@ -101,8 +101,8 @@ hipError_t run_ns_steps(const mc::NsGeometry& g, char* ws, int32_t steps, const 
                         const mc::NsUpdate* upd, hipStream_t s, void* const* gemm_events) {
   uint16_t* X = reinterpret_cast<uint16_t*>(ws + g.off_x0);
   uint16_t* Xn = reinterpret_cast<uint16_t*>(ws + g.off_x1);
-  uint16_t* XL = reinterpret_cast<uint16_t*>(ws + g.off_xl0);
-  uint16_t* XLn = reinterpret_cast<uint16_t*>(ws + g.off_xl1);
+  uint8_t* XL = reinterpret_cast<uint8_t*>(ws + g.off_xl0);
+  uint8_t* XLn = reinterpret_cast<uint8_t*>(ws + g.off_xl1);
   uint16_t* A = reinterpret_cast<uint16_t*>(ws + g.off_a);
   uint16_t* B = reinterpret_cast<uint16_t*>(ws + g.off_b);
   float* D = reinterpret_cast<float*>(ws + g.off_d);

@@ -58,6 +58,34 @@ __device__ __forceinline__ float update_op(float w, float o, float lr, float wd)
   return w - v;
 }
 
+// The low part of a value v carried as a (bf16 high part h, int8 code q)
+// pair.  q counts steps of 256 in v's binary32 bit pattern from h's, and the
+// pair decodes to the float whose bits are (h << 16) + 256 q.  h = bf16(v)
+// (round to nearest) has v's sign, and floats of one sign are ordered like
+// their bit patterns, which are evenly spaced within a binade, so
+// |bits(v) - (h << 16)| <= 2^15 (half a bf16 ulp; also when h is the next
+// power of two) and the decoded value is within 128 binary32 ulps of v
+// (2^-16 relative): about 16 significant bits together.  hs = h << 16, the
+// high part's bits as a binary32.  Inf stays inf; NaN decodes to a NaN.
+__device__ __forceinline__ uint32_t hi_bits(uint32_t packed, int k) {  // k-th bf16 of a dword, << 16
+  return k ? (packed & 0xffff0000u) : (packed << 16);
+}
+__device__ __forceinline__ int32_t enc_lo(float v, uint32_t hs) {
+  const int32_t d = static_cast<int32_t>(__float_as_uint(v) - hs + 128u) >> 8;
+  return min(max(d, -128), 127);
+}
+__device__ __forceinline__ float dec_x(int32_t q, uint32_t hs) {
+  return __uint_as_float(hs + (static_cast<uint32_t>(q) << 8));
+}
+// 4 codes in one dword (byte k = element k) and back
+__device__ __forceinline__ uint32_t pack_i8x4(int32_t a, int32_t b, int32_t c, int32_t d) {
+  return (static_cast<uint32_t>(a) & 0xff) | ((static_cast<uint32_t>(b) & 0xff) << 8) |
+         ((static_cast<uint32_t>(c) & 0xff) << 16) | (static_cast<uint32_t>(d) << 24);
+}
+__device__ __forceinline__ int32_t i8_at(uint32_t w, int k) {
+  return static_cast<int32_t>(static_cast<int8_t>((w >> (8 * k)) & 0xff));
+}
+
 // Float atomic max through integer atomics (exact and order-independent): for
 // x >= 0 the signed-int order of the bits is the float order; for x < 0 the
 // unsigned order is the reverse of it.  NaN is skipped, tested on the bits so

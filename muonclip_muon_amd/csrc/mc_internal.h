@@ -40,22 +40,22 @@ struct NsGeometry {
   int64_t n_pad, m_pad;  // padded to kNsTile
   bool transposed;       // rows > cols: X = M^T
   int64_t prescale_tiles;  // 4096-element blocks per matrix of the pre-scale (norm partials)
-  // byte offsets inside the workspace: X as bf16 high and low parts (two
-  // ping-pong copies of each, n_pad x m_pad), A and B (n_pad x n_pad), B's
+  // byte offsets inside the workspace: X as bf16 high parts and int8 low-part
+  // codes (two ping-pong copies of each, n_pad x m_pad), A and B (n_pad x n_pad), B's
   // diagonal (float32, n_pad), norm partials, 1/norm
   size_t off_x0, off_x1, off_xl0, off_xl1, off_a, off_b, off_d, off_partials, off_invnorm, total;
 };
 constexpr int64_t kNsTile = 256;
 NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols);
 
-// X_0 = M_b unscaled as a bf16 pair, high part bf16(M) at off_x0 and low
-// part bf16(M - high) at off_xl0 (M only read, float32 or bf16, batch
+// X_0 = M_b unscaled as a (high, low) pair, high part bf16(M) at off_x0 and
+// the low part's int8 codes at off_xl0 (M only read, float32 or bf16, batch
 // matrices of rows x cols at m_batch_stride), and 1 / (||M_b||_F + eps) per
 // matrix at off_invnorm (applied by the first step's GEMMs).
 hipError_t launch_ns_prescale_unscaled(const void* M, bool m_bf16, int64_t m_batch_stride, const NsGeometry& g,
                                        float eps, char* ws, hipStream_t stream);
 // Fused: M <- mu M + G in place (float32, batch matrices of rows x cols at
-// batch_stride), X_0 = M unscaled as a bf16 pair at off_x0 / off_xl0, and
+// batch_stride), X_0 = M unscaled as a (bf16, int8 code) pair at off_x0 / off_xl0, and
 // 1 / (||M||_F + eps) per matrix at off_invnorm (to be applied by the first
 // step's GEMMs).
 hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
@@ -72,8 +72,8 @@ struct NsUpdate {
   float out_scale, lr, wd;
   bool output;
 };
-// One GEMM of the polynomial step, on the whole batch.  X is carried as a
-// pair of bf16 matrices, X = Xh + Xl (high part and the rounding residual),
+// One GEMM of the polynomial step, on the whole batch.  X is carried as
+// X = Xh + Xl: a bf16 high part and the rounding residual as int8 codes,
 // and B = b A + c A A as its float32 diagonal d and a bf16 matrix N with a
 // zero diagonal; the products read the high part of X only:
 //   mode 0: A = Xh Xh^T                          (in0: Xh, out: A)
@@ -83,7 +83,7 @@ struct NsUpdate {
 // inv (device, per matrix, or null): X is inv_b times the stored X (the first
 // step); mode 0 scales A by inv_b^2, mode 2 X' by inv_b.
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          const uint16_t* xl, uint16_t* out, uint16_t* xl_out, float* dg, float alpha, float beta,
+                          const uint8_t* xl, uint16_t* out, uint8_t* xl_out, float* dg, float alpha, float beta,
                           float a, const float* inv, const NsUpdate* upd, hipStream_t stream);
 
 // ---------------------------------------------------------------- max logit

@@ -7,8 +7,10 @@
 //   mode 2  X' = a X + d Xh + N Xh        K = n_pad   (out n_pad x m_pad)
 // with B split into its diagonal d (float32, one value per row) and the
 // rest N (bf16, zero diagonal), so X' = a X + B Xh with B's diagonal never
-// rounded.  X is carried as two bf16 matrices, X = Xh + Xl (the high part
-// and the rounding residual, about 16 significant bits together).  The
+// rounded.  X is carried as X = Xh + Xl: the bf16 high part and the rounding
+// residual, coded in one signed byte per element as a step of the binary32
+// bit pattern away from the high part's (enc_lo / dec_x in mc_device.h);
+// about 16 significant bits together.  The
 // products read the high part only, on v_mfma_f32_32x32x16_bf16 with float32
 // accumulation; the epilogue of the third product adds a (Xh + Xl) + d Xh in
 // float32 and splits X' into its two parts again.
@@ -334,7 +336,7 @@ struct UpdArgs {
 template <int MODE, int UPD, bool SCALED, bool TR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict__ in1,
-                    const uint16_t* __restrict__ xl, uint16_t* __restrict__ out, uint16_t* __restrict__ xl_out,
+                    const uint8_t* __restrict__ xl, uint16_t* __restrict__ out, uint8_t* __restrict__ xl_out,
                     float* __restrict__ dg, int n_pad, int m_pad, int tiles_n, int tiles_per_mat, float alpha,
                     float beta, float acoef, const float* __restrict__ inv, UpdArgs ua) {
   static_assert(UPD == 0 || MODE == 2, "only X' = B' X can apply the update");
@@ -517,13 +519,14 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   constexpr bool kRowEpi = MODE == 2 && !(UPD != 0 && TR);
   if constexpr (MODE == 2 && !kRowEpi) {
     const uint16_t* Xh = in1 + mat * nm;
-    const uint16_t* Xl = xl + mat * nm;
-    float lin[4];  // a + d_i of this lane's 4 rows (the factor of Xh)
+    const uint8_t* Xl = xl + mat * nm;
+    float dgr[4];  // d_i of this lane's 4 rows (the factor of Xh; a multiplies X)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) lin[y] = acoef + dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row];
+    for (int y = 0; y < 4; ++y) dgr[y] = dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row];
 #pragma unroll
     for (int yh = 0; yh < 4; yh += 2) {
-      u32x2 hb[2][kCT][4], lb[2][kCT][4];
+      u32x2 hb[2][kCT][4];
+      uint32_t lb[2][kCT][4];
 #pragma unroll
       for (int yy = 0; yy < 2; ++yy)
 #pragma unroll
@@ -533,7 +536,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
             const int64_t o = x_off(i0w + (yh + yy) * 32 + frag_row,
                                     j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, n_pad);
             hb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xh + o);
-            lb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xl + o);
+            lb[yy][x][g] = *reinterpret_cast<const uint32_t*>(Xl + o);
           }
 #pragma unroll
       for (int yy = 0; yy < 2; ++yy)
@@ -541,11 +544,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         for (int x = 0; x < kCT; ++x)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const u32x2 h = hb[yy][x][g], l = lb[yy][x][g];
-            const float hv[4] = {bf16_lo(h.x), bf16_hi(h.x), bf16_lo(h.y), bf16_hi(h.y)};
-            const float lv[4] = {bf16_lo(l.x), bf16_hi(l.x), bf16_lo(l.y), bf16_hi(l.y)};
+            const u32x2 h = hb[yy][x][g];
+            const uint32_t l = lb[yy][x][g];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[x][yh + yy][4 * g + q] += lin[yh + yy] * hv[q] + acoef * lv[q];
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t hs = hi_bits(q < 2 ? h.x : h.y, q & 1);
+              acc[x][yh + yy][4 * g + q] += dgr[yh + yy] * __uint_as_float(hs) + acoef * dec_x(i8_at(l, q), hs);
+            }
           }
     }
   }
@@ -564,7 +569,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   if constexpr (kRowEpi) {
     typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
     const uint16_t* Xh = in1 + mat * nm;
-    const uint16_t* Xlm = xl + mat * nm;
+    const uint8_t* Xlm = xl + mat * nm;
     const float* dgm = dg + static_cast<int64_t>(mat) * n_pad;
     auto fst = [&](int r, int u) -> uint32_t { return lds + r * 512 + ((u ^ (r & 31)) << 4); };
     const int cg = tid & 15, rsub = tid >> 4;
@@ -578,17 +583,18 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     // the first kRing are loaded before the staging (their latency overlaps
     // it), pass s + kRing as pass s is consumed.  a + d_i per pass row.
     constexpr int kRing = UPD == 2 ? 2 : 4;
-    u32x4 xhv[kRing], xlv[kRing];
-    float lin[8];
+    u32x4 xhv[kRing];
+    u32x2 xlv[kRing];
+    float dgr[8];
     auto load_x = [&](int sq) {
       const int64_t off = x_off(i0 + (sq & 7) * 32 + rsub, j0 + 128 * (sq >> 3) + 8 * cg, n_pad);
       xhv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xh + off);
-      xlv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xlm + off);
+      xlv[sq % kRing] = *reinterpret_cast<const u32x2*>(Xlm + off);
     };
 #pragma unroll
     for (int sq = 0; sq < kRing; ++sq) load_x(sq);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) lin[p] = acoef + dgm[i0 + p * 32 + rsub];
+    for (int p = 0; p < 8; ++p) dgr[p] = dgm[i0 + p * 32 + rsub];
     // W of the update, read in batches of kWB passes
     constexpr int kWB = UPD == 2 ? 2 : (UPD == 1 ? 2 : 4);
 #pragma unroll
@@ -627,28 +633,35 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           const f32x4 a0 = *(const lds_f32x4_t*)(uintptr_t)fst(r, 2 * cg);
           const f32x4 a1 = *(const lds_f32x4_t*)(uintptr_t)fst(r, 2 * cg + 1);
           const int sq = 8 * h + p;
-          const u32x4 hq = xhv[sq % kRing], lq = xlv[sq % kRing];
-          const float hv[8] = {bf16_lo(hq.x), bf16_hi(hq.x), bf16_lo(hq.y), bf16_hi(hq.y),
-                               bf16_lo(hq.z), bf16_hi(hq.z), bf16_lo(hq.w), bf16_hi(hq.w)};
-          const float lv[8] = {bf16_lo(lq.x), bf16_hi(lq.x), bf16_lo(lq.y), bf16_hi(lq.y),
-                               bf16_lo(lq.z), bf16_hi(lq.z), bf16_lo(lq.w), bf16_hi(lq.w)};
+          const u32x4 hq = xhv[sq % kRing];
+          const u32x2 lq = xlv[sq % kRing];
+          const uint32_t hw[4] = {hq.x, hq.y, hq.z, hq.w};
+          float hv[8], xv[8];  // Xh and X = Xh + Xl
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t hs = hi_bits(hw[e >> 1], e & 1);
+            hv[e] = __uint_as_float(hs);
+            xv[e] = dec_x(i8_at(e < 4 ? lq.x : lq.y, e & 3), hs);
+          }
           if (sq + kRing < 16) load_x(sq + kRing);
           const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
           float v[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            v[e] = av[e] + lin[p] * hv[e] + acoef * lv[e];
+            v[e] = av[e] + dgr[p] * hv[e] + acoef * xv[e];
             if constexpr (SCALED) v[e] *= xs;
           }
           if constexpr (UPD == 0) {
-            float lo[8];
+            const u32x4 ho = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                              pack_bf16x2(v[6], v[7])};
+            const uint32_t ow[4] = {ho.x, ho.y, ho.z, ho.w};
+            int32_t qv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf16_to_f32(f32_to_bf16(v[e]));
+            for (int e = 0; e < 8; ++e) qv[e] = enc_lo(v[e], hi_bits(ow[e >> 1], e & 1));
             const int64_t off = x_off(row, jc, n_pad);
-            *reinterpret_cast<u32x4*>(out + mat * nm + off) =
-                u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-            *reinterpret_cast<u32x4*>(xl_out + mat * nm + off) = u32x4{
-                pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7])};
+            *reinterpret_cast<u32x4*>(out + mat * nm + off) = ho;
+            *reinterpret_cast<u32x2*>(xl_out + mat * nm + off) =
+                u32x2{pack_i8x4(qv[0], qv[1], qv[2], qv[3]), pack_i8x4(qv[4], qv[5], qv[6], qv[7])};
           } else {
             // the last step: X' rounded to bf16, then O = out_scale X'
             if (row >= ua.n || jc >= ua.m) continue;
@@ -940,7 +953,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 }  // namespace
 
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
-                          const uint16_t* xl, uint16_t* out, uint16_t* xl_out, float* dg, float alpha, float beta,
+                          const uint8_t* xl, uint16_t* out, uint8_t* xl_out, float* dg, float alpha, float beta,
                           float a, const float* inv, const NsUpdate* upd, hipStream_t stream) {
   const int n_pad = static_cast<int>(g.n_pad), m_pad = static_cast<int>(g.m_pad);
   const int tiles_m = n_pad / kBM;

@@ -1,9 +1,10 @@
 // Newton-Schulz input stage: the workspace geometry, the pre-scale and the
 // norm.
 //
-//   pre-scale  X_0 = M_b, or M_b^T when rows > cols, unscaled, as a pair of
-//              bf16 matrices (high part bf16(x), low part bf16(x - high):
-//              about 16 significant bits), written into the zero-padded
+//   pre-scale  X_0 = M_b, or M_b^T when rows > cols, unscaled, as a bf16
+//              matrix of high parts and an int8 matrix coding the low parts
+//              (x - high; about 16 significant bits together, mc_device.h),
+//              written into the zero-padded
 //              n_pad x m_pad workspace layout the GEMMs use, plus float32
 //              partial sums of squares per 4096-
 //              element block; one block per matrix then combines them in
@@ -45,12 +46,13 @@ NsGeometry ns_geometry(int64_t batch, int64_t rows, int64_t cols) {
   g.m_pad = round_up(g.m, kNsTile);
   g.prescale_tiles = g.n_pad * g.m_pad / kBlockElems;
   const size_t xb = static_cast<size_t>(batch) * g.n_pad * g.m_pad * 2;
+  const size_t xlb = static_cast<size_t>(batch) * g.n_pad * g.m_pad;  // int8 low-part codes
   const size_t ab = static_cast<size_t>(batch) * g.n_pad * g.n_pad * 2;
   size_t off = 0;
   g.off_x0 = off; off = align256(off + xb);
   g.off_x1 = off; off = align256(off + xb);
-  g.off_xl0 = off; off = align256(off + xb);
-  g.off_xl1 = off; off = align256(off + xb);
+  g.off_xl0 = off; off = align256(off + xlb);
+  g.off_xl1 = off; off = align256(off + xlb);
   g.off_a = off; off = align256(off + ab);
   g.off_b = off; off = align256(off + ab);
   g.off_d = off; off = align256(off + static_cast<size_t>(batch) * g.n_pad * 4);
@@ -74,13 +76,14 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// 8 values as bf16 high parts and as the low parts bf16(x - high)
-__device__ __forceinline__ void pack_hi_lo8(const float (&x)[8], u32x4& hi, u32x4& lo) {
-  float r[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = x[e] - bf16_to_f32(f32_to_bf16(x[e]));
+// 8 values as bf16 high parts and the int8 codes of their low parts
+__device__ __forceinline__ void pack_hi_lo8(const float (&x)[8], u32x4& hi, u32x2& lo) {
   hi = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
-  lo = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
+  const uint32_t w[4] = {hi.x, hi.y, hi.z, hi.w};
+  int32_t q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q[e] = enc_lo(x[e], hi_bits(w[e >> 1], e & 1));
+  lo = u32x2{pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])};
 }
 
 // grid (batch): inv_b = 1 / (sqrt(sum of partials) + eps), combined in double
@@ -157,8 +160,8 @@ __device__ __forceinline__ void apply_run8(Run8<SRC>& v, float* M, int64_t idx, 
 
 // Fused momentum and pre-scale (SRC = 0).  M_b, G_b are R x C float32 (rows
 // x cols); M_b <- fl32(fl32(mu M_b) + G_b) in place (bit-identical to the
-// stand-alone momentum), and the new M_b is written unscaled as a bf16 pair
-// (high parts into S, low parts into SL; R_pad x C_pad; rows <= cols:
+// stand-alone momentum), and the new M_b is written unscaled as a (bf16
+// high part, int8 low-part code) pair (high parts into S, codes into SL; R_pad x C_pad; rows <= cols:
 // X_0 = M) or transposed (T, TL; C_pad x R_pad; rows > cols: X_0 = M^T),
 // zero-padded; the other two pointers are null.
 // Each block reads one 64 x 128 tile in 8-element runs (vector loads when
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
                                                                     int64_t C, int64_t R_pad, int64_t C_pad,
                                                                     uint16_t* __restrict__ S,
                                                                     uint16_t* __restrict__ T,
-                                                                    uint16_t* __restrict__ SL,
-                                                                    uint16_t* __restrict__ TL,
+                                                                    uint8_t* __restrict__ SL,
+                                                                    uint8_t* __restrict__ TL,
                                                                     float* __restrict__ partials) {
   __shared__ float tile[kTR][kTC + 1];
   __shared__ float red[kThreads / 64];
@@ -189,8 +192,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
   const float* gb = SRC == 0 ? G + b * batch_stride : nullptr;
   uint16_t* sb = S + static_cast<size_t>(b) * R_pad * C_pad;
   uint16_t* tb = T + static_cast<size_t>(b) * R_pad * C_pad;
-  uint16_t* slb = SL + static_cast<size_t>(b) * R_pad * C_pad;
-  uint16_t* tlb = TL + static_cast<size_t>(b) * R_pad * C_pad;
+  uint8_t* slb = SL + static_cast<size_t>(b) * R_pad * C_pad;
+  uint8_t* tlb = TL + static_cast<size_t>(b) * R_pad * C_pad;
   const int q = threadIdx.x & 15;
   float ss = 0.f;
   // VEC (C % 8 == 0): a run is wholly inside or wholly outside the matrix;
@@ -232,10 +235,11 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
     if (S != nullptr) {
-      u32x4 hi, lo;
+      u32x4 hi;
+      u32x2 lo;
       pack_hi_lo8(x, hi, lo);
       *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = hi;
-      *reinterpret_cast<u32x4*>(slb + x_off(r, c, R_pad)) = lo;
+      *reinterpret_cast<u32x2*>(slb + x_off(r, c, R_pad)) = lo;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
@@ -252,10 +256,11 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[rq + e][cc];
-    u32x4 hi, lo;
+    u32x4 hi;
+    u32x2 lo;
     pack_hi_lo8(v, hi, lo);
     *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = hi;
-    *reinterpret_cast<u32x4*>(tlb + x_off(c0 + cc, r0 + rq, C_pad)) = lo;
+    *reinterpret_cast<u32x2*>(tlb + x_off(c0 + cc, r0 + rq, C_pad)) = lo;
   }
 }
 
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
 template <int SRC>
 __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     void* __restrict__ Mv, const float* __restrict__ G, int64_t batch_stride, float mu, int64_t R, int64_t C,
-    int64_t R_pad, int64_t C_pad, uint16_t* __restrict__ X0, uint16_t* __restrict__ X0l,
+    int64_t R_pad, int64_t C_pad, uint16_t* __restrict__ X0, uint8_t* __restrict__ X0l,
     float* __restrict__ partials) {
   __shared__ float red[kThreads / 64];
   const int64_t b = blockIdx.z;
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
                               : static_cast<const void*>(mb);
   const float* gb = SRC == 0 ? G + b * batch_stride : nullptr;
   uint16_t* xb = X0 + static_cast<size_t>(b) * R_pad * C_pad;
-  uint16_t* xlb = X0l + static_cast<size_t>(b) * R_pad * C_pad;
+  uint8_t* xlb = X0l + static_cast<size_t>(b) * R_pad * C_pad;
   float ss = 0.f;
   // C % 8 == 0: a run is wholly inside or outside the matrix
   Run8<SRC> run[4];
@@ -299,10 +304,11 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     apply_run8<SRC>(run[pass], mb, idx[pass], mu, in[pass], x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-    u32x4 hi, lo;
+    u32x4 hi;
+    u32x2 lo;
     pack_hi_lo8(x, hi, lo);
     *reinterpret_cast<u32x4*>(xb + x_off(r, c, R_pad)) = hi;
-    *reinterpret_cast<u32x4*>(xlb + x_off(r, c, R_pad)) = lo;
+    *reinterpret_cast<u32x2*>(xlb + x_off(r, c, R_pad)) = lo;
   }
   const float block_ss = block_sum(ss, red);
   if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = block_ss;
@@ -315,13 +321,13 @@ hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_strid
   float* partials = reinterpret_cast<float*>(ws + g.off_partials);
   float* invnorm = reinterpret_cast<float*>(ws + g.off_invnorm);
   uint16_t* X0 = reinterpret_cast<uint16_t*>(ws + g.off_x0);
-  uint16_t* X0l = reinterpret_cast<uint16_t*>(ws + g.off_xl0);
+  uint8_t* X0l = reinterpret_cast<uint8_t*>(ws + g.off_xl0);
   const int64_t R = g.rows, C = g.cols;
   const int64_t R_pad = g.transposed ? g.m_pad : g.n_pad, C_pad = g.transposed ? g.n_pad : g.m_pad;
   uint16_t* S = g.transposed ? nullptr : X0;
   uint16_t* T = g.transposed ? X0 : nullptr;
-  uint16_t* SL = g.transposed ? nullptr : X0l;
-  uint16_t* TL = g.transposed ? X0l : nullptr;
+  uint8_t* SL = g.transposed ? nullptr : X0l;
+  uint8_t* TL = g.transposed ? X0l : nullptr;
   const size_t align = SRC == 2 ? 16 : 32;  // one 8-element run
   const bool vec = C % 8 == 0 && (g.batch == 1 || batch_stride % 8 == 0) &&
                    reinterpret_cast<uintptr_t>(M) % align == 0 &&
