@@ -436,9 +436,10 @@ def run(args):
     dom_avg_ms = sum(gemm_ms[dom]) / dom_launches
     dom_avg_flops = sum(gemm_flops[dom]) / dom_launches
     achieved = dom_avg_flops / (dom_avg_ms * 1e-3) / 1e12
-    kernel_names = {0: "ns_gemm_kernel<0, 0, *> (A = X X^T)", 1: "ns_gemm_kernel<1, 0, false> (B' = aI + bA + cAA)",
-                    2: "ns_gemm_kernel<2, 0, *> (X' = B'X)",
-                    "2u": "ns_gemm_kernel<2, 1, *> (last step: X' = B'X applied as the update of bf16 W)"}
+    kernel_names = {0: "ns_gemm_kernel<0, 0, *> (A = Xh Xh^T)",
+                    1: "ns_gemm_kernel<1, 0, *> (B = bA + cAA: float32 diagonal d, bf16 rest N)",
+                    2: "ns_gemm_kernel<2, 0, *> (X' = aX + d Xh + N Xh)",
+                    "2u": "ns_gemm_kernel<2, 1, *> (last step: X' applied as the update of bf16 W)"}
 
     breakdown = {
         "path": "three calls: momentum, Newton-Schulz, update" if args.unfused else
@@ -472,7 +473,7 @@ def run(args):
                                              / MFMA_BF16_PEAK_TFLOPS, 4) for g in gemm_ms},
         "gemm_tflops_nominal": {str(g): round(sum(gemm_flops_nom[g]) / (sum(gemm_ms[g]) * 1e-3) / 1e12, 1)
                                 for g in gemm_ms},
-        "gemm_note": "per GEMM (0 X X^T, 1 aI+bA+cAA, 2 B'X, 2u the last B'X applying the update): gemm_tflops on "
+        "gemm_note": "per GEMM (0 X X^T, 1 bA+cAA, 2 aX+BX, 2u the last aX+BX applying the update): gemm_tflops on "
                      "the method's flops (n^2m, n^3, 2n^2m), executed on the tiles the MFMAs compute, nominal dense",
         "newton_schulz_only": ns_only,
         "hbm_steps": hbm,
@@ -605,6 +606,10 @@ def cpu_baseline_configs():
         return sorted(ts)[1]
 
     out = {"host": host_info(), "configs": []}
+
+    def done(rec):
+        out["configs"].append(rec)
+        log(f"cpu baseline: {rec['workload']} done")
     # tiny fp32 attention layer: one whole step
     t = workloads.tiny_attention(seed=1, device="cpu", weight_reading="variance")
     Wn = {n: w.double().numpy() for n, w in t.W.items()}
@@ -616,13 +621,13 @@ def cpu_baseline_configs():
         k = oracle.project_heads(t.X.double().numpy(), Wn["k"], t.n_heads)
         oracle.muonclip_step(Wn, Gn, {}, oracle.max_logit(q, k), att, lr=0.02, w_dtype="f32")
     s = med3(tiny)
-    out["configs"].append({"workload": "tiny fp32 attention layer, one step", "sample": "whole", "seconds": s})
+    done({"workload": "tiny fp32 attention layer, one step", "sample": "whole", "seconds": s})
     # Newton-Schulz alone, 64 x 2048 x 7168: 2 matrices
     eb = workloads.expert_batch(seed=2, device="cpu", batch=2)
     Ms = [oracle.momentum_update(eb.M_prev[i].numpy(), eb.G[i].numpy(), MU) for i in range(2)]
     s = med3(lambda: [oracle.newton_schulz(m.astype(np.float64)) for m in Ms])
     fl = ns_flops_sym(2048, 7168, oracle.NS_STEPS) * 64
-    out["configs"].append({"workload": "Newton-Schulz alone, 64 x 2048 x 7168", "sample": "2 of 64 matrices",
+    done({"workload": "Newton-Schulz alone, 64 x 2048 x 7168", "sample": "2 of 64 matrices",
                            "seconds_sample": s, "seconds_extrapolated": s * 32,
                            "tflops": fl / (s * 32) / 1e12})
     # max logit + clip at 8 x 4096, 64 heads: 2 heads
@@ -632,7 +637,7 @@ def cpu_baseline_configs():
     ks = [L.Kc[:, h:h + 1].double().numpy() for h in (0, 1)]
     s = med3(lambda: [oracle.max_logit(q, k, Kr) for q, k in zip(qs, ks)])
     fl = 2.0 * 8 * 64 * 4096 * 4096 * (D_NOPE + D_ROPE)
-    out["configs"].append({"workload": "max logit, 8 x 4096 tokens, 64 heads, d 128+64", "sample": "2 of 64 heads",
+    done({"workload": "max logit, 8 x 4096 tokens, 64 heads, d 128+64", "sample": "2 of 64 heads",
                            "seconds_sample": s, "seconds_extrapolated": s * 32, "tflops": fl / (s * 32) / 1e12})
     del L, qs, ks, Kr
     # full step for one MoE layer: 2 matrices of each expert shape
@@ -650,7 +655,7 @@ def cpu_baseline_configs():
     expert_fl = ns_flops_sym(2048, 7168, oracle.NS_STEPS) * 1152
     attn_fl = sum(ns_flops_sym(r, D_MODEL, oracle.NS_STEPS) for r in (12288, 8192, 64))
     secs_total = secs * (expert_fl + attn_fl) / expert_fl
-    out["configs"].append({"workload": "full MuonClip step, one MoE layer (NS x5 of 1155 matrices)",
+    done({"workload": "full MuonClip step, one MoE layer (NS x5 of 1155 matrices)",
                            "sample": "2 matrices of each expert shape; the attention projections by their flop share",
                            "seconds_extrapolated": secs_total,
                            "tflops": (expert_fl + attn_fl) / secs_total / 1e12})
@@ -659,7 +664,7 @@ def cpu_baseline_configs():
     q, k, Kr = L.Q[:, :1].double().numpy(), L.Kc[:, :1].double().numpy(), L.Kr.double().numpy()
     s = med3(lambda: oracle.max_logit(q, k, Kr, block=4096))
     fl = 2.0 * 32768 * 32768 * 64 * (D_NOPE + D_ROPE)
-    out["configs"].append({"workload": "max logit, 1 x 32768 tokens, 64 heads", "sample": "1 of 64 heads",
+    done({"workload": "max logit, 1 x 32768 tokens, 64 heads", "sample": "1 of 64 heads",
                            "seconds_sample": s, "seconds_extrapolated": s * 64, "tflops": fl / (s * 64) / 1e12})
     print(json.dumps(out), flush=True)
 
