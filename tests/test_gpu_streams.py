@@ -1,0 +1,73 @@
+"""Calls on a stream other than torch's current one, with the scratch memory
+(Newton-Schulz workspace, output buffers) allocated by the binding: the
+results equal, bit for bit, the same calls on the current stream, although
+the current stream allocates and overwrites memory of the same size while
+the side stream's kernels still run.  The binding allocates such scratch in
+the launch stream's pool, so the caching allocator cannot hand it to the
+current stream early.  The first call is also checked against the fp64
+oracle (the Newton-Schulz tolerance, relative Frobenius error 2e-2).
+"""
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import f64, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BATCH, ROWS, COLS = 4, 1024, 4096
+
+
+@pytest.fixture(scope="module")
+def mc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import muonclip_muon_amd
+    return muonclip_muon_amd
+
+
+def _clobber(nbytes):
+    # what another part of a program does on the current stream meanwhile:
+    # allocate blocks of the workspace's size class and fill them
+    return [torch.full((nbytes,), 0x7f, dtype=torch.uint8, device=DEV) for _ in range(3)]
+
+
+def test_ns_on_side_stream(mc):
+    say("NS on a side stream")
+    g = workloads.generator(91, "cpu")
+    M = workloads.normal((BATCH, ROWS, COLS), 1e-3, g, "cpu").to(DEV)
+    ref = mc.muon_ns_orthogonalize_batched(M, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    O = mc.muon_ns_orthogonalize_batched(M, out_dtype=torch.float32, stream=s)
+    junk = _clobber(mc.muon_ns_workspace_bytes(BATCH, ROWS, COLS))
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(O, ref)
+    assert all(int(j[0]) == 0x7f for j in junk)
+    err = rel_fro(f64(O[0]), oracle.newton_schulz(f64(M[0])))
+    assert err <= 2e-2, err
+
+
+def test_fused_on_side_stream(mc):
+    say("fused step on a side stream")
+    g = workloads.generator(92, "cpu")
+    M0 = workloads.normal((BATCH, ROWS, COLS), 1e-3, g, "cpu").to(DEV)
+    G = workloads.normal((BATCH, ROWS, COLS), 1e-3, g, "cpu").to(DEV)
+    W0 = workloads.normal((BATCH, ROWS, COLS), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+    M_ref, W_ref = M0.clone(), W0.clone()
+    mc.muon_momentum_ns_update_batched(M_ref, G, W_ref, 2e-2, 0.1, 0.95)
+    torch.cuda.synchronize()
+    M, W = M0.clone(), W0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    mc.muon_momentum_ns_update_batched(M, G, W, 2e-2, 0.1, 0.95, stream=s)
+    _clobber(mc.muon_ns_workspace_bytes(BATCH, ROWS, COLS))
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(M, M_ref)
+    assert torch.equal(W, W_ref)
