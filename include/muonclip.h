@@ -33,6 +33,13 @@
  *    is then undefined.  No C++ exception crosses the ABI.
  *  - The library holds no mutable global state: calls on different streams
  *    may run concurrently as long as their buffers do not overlap.
+ *  - Debug builds (libmuonclip_debug.so, compiled with MC_DEBUG; host code
+ *    under UndefinedBehaviorSanitizer) check the index ranges of the
+ *    kernels' global accesses and skip any access that fails, synchronise
+ *    the stream at the end of every call and then return MC_ECHECK (with
+ *    the failed checks printed to stderr) if a check failed.  Their results
+ *    otherwise equal the release build's; they are for tests, not speed,
+ *    and do not support overlapping calls.
  *  - Element counts and strides are in elements, not bytes.  Pointers must be
  *    aligned to their element size; wider alignment enables vector paths.
  *  - Dtypes: MC_F32 = IEEE binary32, MC_BF16 = bfloat16 (top half of binary32).
@@ -64,13 +71,17 @@ typedef enum mc_status {
   MC_EDTYPE = 3,     /* dtype code not supported by the call */
   MC_EALIGN = 4,     /* pointer not aligned to its element size */
   MC_EWORKSPACE = 5, /* workspace missing or smaller than the query function's size */
-  MC_EHIP = 6        /* a HIP runtime call or kernel launch failed */
+  MC_EHIP = 6,       /* a HIP runtime call or kernel launch failed */
+  MC_ECHECK = 7      /* debug builds only: a kernel's range check failed (outputs undefined) */
 } mc_status_t;
 
 typedef enum mc_dtype { MC_F32 = 0, MC_BF16 = 1 } mc_dtype_t;
 
 /* MC_ABI_VERSION of the loaded library. */
 MC_API int mc_abi_version(void);
+
+/* 1 for a debug build (MC_DEBUG range checks, see above), else 0. */
+MC_API int mc_debug_build(void);
 
 /* Static, human-readable name of a status code (never NULL). */
 MC_API const char* mc_status_string(int status);

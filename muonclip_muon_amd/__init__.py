@@ -43,7 +43,11 @@ __all__ = [
     "muonclip_step",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuonclip.so")
+# The release library built in-tree; MUONCLIP_LIB may name another build of
+# it, such as the debug library libmuonclip_debug.so (range-checked kernels,
+# host code under UBSan).
+LIB_PATH = os.environ.get("MUONCLIP_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libmuonclip.so")
 
 # Newton-Schulz polynomial used by default: the quintic
 # p(x) = a x + b x^3 + c x^5 with the same (a, b, c) for 5 steps, applied after
@@ -75,6 +79,8 @@ def _load():
     i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
     L.mc_abi_version.restype = ctypes.c_int
     L.mc_abi_version.argtypes = []
+    L.mc_debug_build.restype = ctypes.c_int
+    L.mc_debug_build.argtypes = []
     L.mc_status_string.restype = ctypes.c_char_p
     L.mc_status_string.argtypes = [ctypes.c_int]
     L.muonclip_momentum.restype = ctypes.c_int

@@ -1,12 +1,19 @@
 """Build libmuonclip.so in-tree with hipcc for gfx950.
 
-    python muonclip_muon_amd/build.py        # or __graft_entry__.build()
+    python muonclip_muon_amd/build.py          # release and debug libraries
+    python muonclip_muon_amd/build.py release  # or debug: one of them
 
 (Run as a script, not with -m: importing the package loads the library.)
 
 Each translation unit under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into muonclip_muon_amd/libmuonclip.so.  Always
 recompiles: the build is the check that every kernel compiles.
+
+The debug library, libmuonclip_debug.so (objects in _build_debug/), is the
+same code compiled with MC_DEBUG: range checks at the kernels' global
+accesses, reported by the C ABI after each call (MC_ECHECK), and the host
+code under UndefinedBehaviorSanitizer (any undefined behaviour aborts).  The
+binding loads it instead of the release library when MUONCLIP_LIB names it.
 """
 
 import concurrent.futures
@@ -20,6 +27,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuonclip.so")
+DEBUG_BUILD = os.path.join(PKG, "_build_debug")
+DEBUG_LIB = os.path.join(PKG, "libmuonclip_debug.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "elementwise.hip", "qkclip.hip", "ns_prep.hip", "ns_gemm.hip", "maxlogit.hip",
@@ -62,9 +71,31 @@ def _hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libmuonclip.so)")
 
 
-def _compile(hipcc, src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# Debug builds: MC_DEBUG range checks in the kernels; host code with debug
+# information and UndefinedBehaviorSanitizer, which aborts on the first
+# finding (sanitizers apply to host code only: each flag goes to the host
+# compilation through -Xarch_host).
+DEBUG_FLAGS = ["-DMC_DEBUG", "-Xarch_host", "-g", "-Xarch_host", "-fsanitize=undefined",
+               "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def _sanitizer_runtime_dir():
+    """The directory of clang's shared UBSan runtime (linked by the debug
+    library, found at load time through its rpath)."""
+    import glob
+    base = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm", "lib", "clang")
+    for cand in (base, "/opt/rocm/llvm/lib/clang"):
+        hits = glob.glob(os.path.join(cand, "*", "lib", "*", "libclang_rt.ubsan_standalone*.so"))
+        hits = [h for h in hits if "i386" not in h]
+        if hits:
+            return os.path.dirname(os.path.realpath(hits[0]))
+    raise RuntimeError("clang's shared UBSan runtime was not found (debug build)")
+
+
+def _compile(hipcc, src, debug=False):
+    obj = os.path.join(DEBUG_BUILD if debug else BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc, *COMMON_FLAGS, *(DEBUG_FLAGS if debug else []), *SOURCE_FLAGS.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -75,23 +106,38 @@ def _compile(hipcc, src):
     return obj, out
 
 
-def build(verbose=False):
+def build(verbose=False, debug=False):
+    """Compile and link the release library (debug=False) or the debug one."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(DEBUG_BUILD if debug else BUILD, exist_ok=True)
     jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(hipcc, s), SOURCES))
+        results = list(ex.map(lambda s: _compile(hipcc, s, debug), SOURCES))
     for (obj, out) in results:
         if out and verbose:
             print(out, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    lib = DEBUG_LIB if debug else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
+    if debug:
+        cmd[-2:-2] = ["-Xarch_host", "-fsanitize=undefined", "-shared-libsan",
+                      f"-Wl,-rpath,{_sanitizer_runtime_dir()}"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build_all(verbose=False):
+    return [build(verbose), build(verbose, debug=True)]
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    which = sys.argv[1] if len(sys.argv) > 1 else "all"
+    if which == "release":
+        print(build(verbose=True))
+    elif which == "debug":
+        print(build(verbose=True, debug=True))
+    else:
+        print("\n".join(build_all(verbose=True)))

@@ -6,6 +6,7 @@
 #include "muonclip_probe.h"
 
 #include <math.h>
+#include <stdio.h>
 
 #include <mutex>
 #include <utility>
@@ -19,6 +20,34 @@ inline bool valid_dtype(int d) { return d == MC_F32 || d == MC_BF16; }
 inline size_t dtype_size(int d) { return d == MC_BF16 ? 2 : 4; }
 inline mc_status_t from_hip(hipError_t e) { return e == hipSuccess ? MC_OK : MC_EHIP; }
 
+// The status of an entry point whose launches returned e.  Debug builds
+// (MC_DEBUG) also wait for the stream and read every kernel unit's
+// range-check flags; failed checks are printed and returned as MC_ECHECK.
+mc_status_t done(hipError_t e, void* stream, const char* fn) {
+  if (e != hipSuccess) return MC_EHIP;
+#ifdef MC_DEBUG
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MC_EHIP;
+  struct Unit {
+    const char* name;
+    unsigned int (*take)();
+  };
+  const Unit units[] = {{"ns_gemm", mc::debug_take_ns_gemm}, {"ns_prep", mc::debug_take_ns_prep},
+                        {"qkclip", mc::debug_take_qkclip},   {"maxlogit", mc::debug_take_maxlogit},
+                        {"attention", mc::debug_take_attention}};
+  unsigned int failed = 0;
+  for (const Unit& u : units) {
+    const unsigned int v = u.take();
+    if (v != 0) fprintf(stderr, "libmuonclip (debug): %s: range checks 0x%x failed in %s\n", fn, v, u.name);
+    failed |= v;
+  }
+  if (failed != 0) return MC_ECHECK;
+#else
+  (void)stream;
+  (void)fn;
+#endif
+  return MC_OK;
+}
+
 constexpr int64_t kNsMaxN = 16384;   // min(rows, cols)
 constexpr int64_t kNsMaxM = 65536;   // max(rows, cols)
 constexpr int32_t kNsMaxSteps = 64;
@@ -30,6 +59,14 @@ extern "C" {
 
 int mc_abi_version(void) { return MC_ABI_VERSION; }
 
+int mc_debug_build(void) {
+#ifdef MC_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 const char* mc_status_string(int status) {
   switch (status) {
     case MC_OK: return "ok";
@@ -39,6 +76,7 @@ const char* mc_status_string(int status) {
     case MC_EALIGN: return "misaligned pointer";
     case MC_EWORKSPACE: return "workspace missing or too small";
     case MC_EHIP: return "HIP runtime error";
+    case MC_ECHECK: return "range check failed (debug build)";
     default: return "unknown status";
   }
 }
@@ -49,7 +87,7 @@ mc_status_t muonclip_momentum(float* M, const float* G, int64_t numel, float mu,
   if (!M || !G) return MC_EINVAL;
   if (!isfinite(mu)) return MC_EINVAL;
   if (!aligned(M, 4) || !aligned(G, 4)) return MC_EALIGN;
-  return from_hip(mc::launch_momentum(M, G, numel, mu, static_cast<hipStream_t>(stream)));
+  return done(mc::launch_momentum(M, G, numel, mu, static_cast<hipStream_t>(stream)), stream, __func__);
 }
 
 float muon_rms_match_scale(int64_t rows, int64_t cols) {
@@ -165,7 +203,7 @@ mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t ba
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
   // the last step's X' = B' X writes O = out_scale * X' (transposed back)
   mc::NsUpdate out{O, o_bf16, o_batch_stride, mc::resolve_out_scale(out_scale, rows, cols), 0.f, 0.f, true};
-  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &out, s, gemm_events));
+  return done(run_ns_steps(g, ws, steps, coeffs, inv, &out, s, gemm_events), stream, __func__);
 }
 
 }  // extern "C"
@@ -200,7 +238,7 @@ mc_status_t fused_muon(float* M, const float* G, float mu, void* W, int w_dtype,
   const float* inv = reinterpret_cast<const float*>(ws + g.off_invnorm);
   mc::NsUpdate upd{W, w_dtype == MC_BF16, batch_stride, mc::resolve_out_scale(out_scale, rows, cols), lr,
                    weight_decay, false};
-  return from_hip(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events));
+  return done(run_ns_steps(g, ws, steps, coeffs, inv, &upd, s, gemm_events), stream, "muon_momentum_ns_update_batched");
 }
 
 // Scratch of the allocation-free entry point: a file-scope device array, one
@@ -269,8 +307,9 @@ mc_status_t muon_apply_update(void* W, int w_dtype, const void* O, int o_dtype, 
   if (!W || !O) return MC_EINVAL;
   if (!isfinite(lr) || !isfinite(weight_decay)) return MC_EINVAL;
   if (!aligned(W, dtype_size(w_dtype)) || !aligned(O, dtype_size(o_dtype))) return MC_EALIGN;
-  return from_hip(mc::launch_update(W, w_dtype == MC_BF16, O, o_dtype == MC_BF16, numel, lr,
-                                    weight_decay, static_cast<hipStream_t>(stream)));
+  return done(mc::launch_update(W, w_dtype == MC_BF16, O, o_dtype == MC_BF16, numel, lr, weight_decay,
+                                static_cast<hipStream_t>(stream)),
+              stream, __func__);
 }
 
 mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype, int64_t B, int64_t H,
@@ -296,7 +335,7 @@ mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype
     if (e != hipSuccess) return MC_EHIP;
   }
   if (empty) return MC_OK;
-  return from_hip(mc::launch_maxlogit(Q, Kc, Kr, dtype == MC_BF16, B, H, Sq, Sk, d_c, d_r, smax, s));
+  return done(mc::launch_maxlogit(Q, Kc, Kr, dtype == MC_BF16, B, H, Sq, Sk, d_c, d_r, smax, s), stream, __func__);
 }
 
 mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr, const void* V, int dtype,
@@ -322,8 +361,9 @@ mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr
     if (e != hipSuccess) return MC_EHIP;
   }
   if (empty) return MC_OK;
-  return from_hip(mc::launch_attention_fwd(Q, Kc, Kr, V, B, H, Sq, Sk, d_c, d_r, d_v, causal != 0, O, lse_out,
-                                           smax_out, s));
+  return done(mc::launch_attention_fwd(Q, Kc, Kr, V, B, H, Sq, Sk, d_c, d_r, d_v, causal != 0, O, lse_out,
+                                       smax_out, s),
+              stream, __func__);
 }
 
 static mc_status_t qk_clip_check(int64_t H, float tau, float alpha, int w_dtype, int64_t d_in, int64_t q_rows_per_head,
@@ -351,9 +391,10 @@ static mc_status_t qk_clip_common(const float* smax, int64_t H, bool total_clip,
       (gamma_out && !aligned(gamma_out, 4)) || (clipped_out && !aligned(clipped_out, 4)))
     return MC_EALIGN;
   if ((q_rows_per_head + k_rows_per_head) * d_in / 8 / 1024 + 1 > kGridMax) return MC_ESHAPE;
-  return from_hip(mc::launch_qk_clip(smax, 1, H, total_clip, tau, alpha, &Wq, &Wk, w_dtype == MC_BF16, d_in,
-                                     q_rows_per_head, q_c_rows, k_rows_per_head, gamma_out, clipped_out,
-                                     static_cast<hipStream_t>(stream)));
+  return done(mc::launch_qk_clip(smax, 1, H, total_clip, tau, alpha, &Wq, &Wk, w_dtype == MC_BF16, d_in,
+                                 q_rows_per_head, q_c_rows, k_rows_per_head, gamma_out, clipped_out,
+                                 static_cast<hipStream_t>(stream)),
+              stream, "qk_clip_apply");
 }
 
 mc_status_t qk_clip_apply_layers(const float* smax, int64_t L, int64_t H, float tau, float alpha, void* const* Wq,
@@ -383,7 +424,7 @@ mc_status_t qk_clip_apply_layers(const float* smax, int64_t L, int64_t H, float 
                                             clipped_out ? clipped_out + l0 * H : nullptr, s);
     if (e != hipSuccess) return MC_EHIP;
   }
-  return MC_OK;
+  return done(hipSuccess, stream, __func__);
 }
 
 mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,

@@ -141,9 +141,11 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int i = min(row_base + t * 32 + frag_row, Sq - 1);
+    const bool ok = MC_GUARD(0, i >= 0 && i < Sq);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
-      qf[t][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half));
+      qf[t][s] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half))
+                    : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   // Q in registers before any copy starts (the copies' asm is opaque to the
   // compiler, which would otherwise wait on them before each use of Q), and
@@ -178,6 +180,7 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   auto issue_part = [&](int jb, int l) {
     const int64_t j0 = block_start(jb);
     const uint32_t st = lds + (jb % kStages) * kStageBytes;
+    if (!MC_GUARD(1, j0 >= 0 && j0 + kKeys <= Sk)) return;
     if (l < kLoadsC) {
       load_lds16(Kcbh + j0 * DC * 2 + 4096 * l, lo_c, st + 1024 * (wave + 4 * l));
     } else if (l < kLoadsC + kLoadsR) {
@@ -426,7 +429,7 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const float l_tot = la + lb;
     const float inv = 1.0f / l_tot;
     const int i = row_base + t * 32 + frag_row;
-    if (i < Sq) {
+    if (i < Sq && MC_GUARD(2, i >= 0)) {
       uint16_t* orow = O + (bh64 * Sq + i) * DV;
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt)
@@ -471,6 +474,8 @@ hipError_t launch(const void* Q, const void* Kc, const void* Kr, const void* V, 
 }
 
 }  // namespace
+
+MC_DEBUG_UNIT(attention)
 
 bool attention_fwd_supported(int64_t d_c, int64_t d_r, int64_t d_v) {
   return (d_c == 128 && d_r == 64 && d_v == 128) || (d_c == 64 && d_r == 0 && d_v == 64);

@@ -116,9 +116,11 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int i = min(row_base + t * 32 + frag_row, Sq - 1);
+    const bool ok = MC_GUARD(0, i >= 0 && i < Sq);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s)
-      qf[t][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half));
+      qf[t][s] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half))
+                    : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   // Q is in registers before any key copy starts: otherwise the compiler,
   // which cannot tell the copies from these loads, waits on the copies in
@@ -152,6 +154,7 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   auto issue_part = [&](int jb, int l) {
     const int64_t j0 = min(min(jb, NJ - 1) * kKeys, Sk - kKeys);
     const uint32_t st = lds + (jb % kKeyStages) * kStageBytes;
+    if (!MC_GUARD(1, j0 >= 0 && j0 + kKeys <= Sk)) return;
     if (l < kLoadsC) load_lds16(Kcbh + j0 * DC * 2, off_c[l], st + 1024 * (wave + 4 * l));
     else load_lds16(Krb + j0 * DR * 2, off_r[l - kLoadsC], st + kKcBytes + 1024 * (wave + 4 * (l - kLoadsC)));
   };
@@ -260,7 +263,7 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   if (tid == 0) {
     float w = red[0];
     for (int i = 1; i < kMfmaThreads / 64; ++i) w = fmaxf(w, red[i]);
-    if (w != -INFINITY) atomic_max_float(&smax[h], w * scale);
+    if (w != -INFINITY && MC_GUARD(2, h >= 0 && h < H)) atomic_max_float(&smax[h], w * scale);
   }
 }
 
@@ -277,6 +280,8 @@ hipError_t launch_mfma(const void* Q, const void* Kc, const void* Kr, int64_t B,
 }
 
 }  // namespace
+
+MC_DEBUG_UNIT(maxlogit)
 
 hipError_t launch_maxlogit(const void* Q, const void* Kc, const void* Kr, bool bf16, int64_t B,
                            int64_t H, int64_t Sq, int64_t Sk, int64_t d_c, int64_t d_r, float* smax,

@@ -96,6 +96,34 @@ __device__ __forceinline__ void atomic_max_float(float* addr, float x) {
   else atomicMin(reinterpret_cast<unsigned int*>(addr), __float_as_uint(x));
 }
 
+// Range checks of debug builds (MC_DEBUG).  MC_GUARD(tag, cond) is true in
+// release builds (the check compiles out).  In a debug build a false cond
+// sets bit `tag` of the translation unit's flag word and returns false, and
+// the guarded access is skipped, so a bad index is reported instead of
+// faulting; MC_DEBUG_UNIT(name) defines debug_take_<name>(), which the C ABI
+// calls after each entry point's launches (and after a synchronisation) to
+// read and clear the word.
+#ifdef MC_DEBUG
+static __device__ unsigned int mc_debug_flags;
+__device__ __forceinline__ bool mc_guard(bool ok, unsigned int tag) {
+  if (!ok) atomicOr(&mc_debug_flags, 1u << tag);
+  return ok;
+}
+#define MC_GUARD(tag, cond) ::mc::mc_guard((cond), (tag))
+#define MC_DEBUG_UNIT(name)                                                         \
+  unsigned int debug_take_##name() {                                                \
+    unsigned int v = 0, z = 0;                                                      \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(mc_debug_flags), sizeof v) != hipSuccess) \
+      return 0x80000000u;                                                           \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(mc_debug_flags), &z, sizeof z) != hipSuccess)   \
+      return 0x80000000u;                                                           \
+    return v;                                                                       \
+  }
+#else
+#define MC_GUARD(tag, cond) true
+#define MC_DEBUG_UNIT(name)
+#endif
+
 // Layout of the Newton-Schulz state X (n_pad x m_pad bf16) in the workspace:
 // column panels of 256, each n_pad x 256 row-major, so a 32 x 256 K-rows tile
 // (the right operand of B' X) is one contiguous 16 KB run and a row panel of

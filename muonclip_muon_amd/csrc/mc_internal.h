@@ -10,6 +10,15 @@
 
 namespace mc {
 
+#ifdef MC_DEBUG
+// Range-check flags of each kernel unit (debug builds; read and cleared)
+unsigned int debug_take_ns_gemm();
+unsigned int debug_take_ns_prep();
+unsigned int debug_take_qkclip();
+unsigned int debug_take_maxlogit();
+unsigned int debug_take_attention();
+#endif
+
 // ---------------------------------------------------------------- momentum
 hipError_t launch_momentum(float* M, const float* G, int64_t numel, float mu, hipStream_t stream);
 

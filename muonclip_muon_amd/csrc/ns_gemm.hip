@@ -164,23 +164,26 @@ __device__ __forceinline__ uint32_t kr_lane_offset(int64_t ld, int wave, int lan
 
 // Issue one operand tile: K-contiguous (row 0, column k0 at g; block rows
 // advance by 64 per jj) or K-rows (k-row 0, column 0 at g; 8 rows per jj).
+// `end` is one past the operand's last byte (checked in debug builds only).
 template <bool KROWS>
 __device__ __forceinline__ void issue_tile(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
-                                           int wave) {
+                                           int wave, const char* end) {
   const char* base = reinterpret_cast<const char*>(g);
   constexpr int kRowsPerJ = KROWS ? 2 * kWaves : 16 * kWaves;
 #pragma unroll
-  for (int jj = 0; jj < kLoadsPerTile; ++jj)
-    load_lds16(base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off, lds + 1024 * (wave + kWaves * jj));
+  for (int jj = 0; jj < kLoadsPerTile; ++jj) {
+    const char* src = base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2;
+    if (MC_GUARD(0, src + lane_off + 16 <= end)) load_lds16(src, lane_off, lds + 1024 * (wave + kWaves * jj));
+  }
 }
 
 // One of the kLoadsPerTile DMA instructions of an operand tile.
 template <bool KROWS>
 __device__ __forceinline__ void issue_tile_part(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
-                                                int wave, int jj) {
+                                                int wave, int jj, const char* end) {
   constexpr int kRowsPerJ = KROWS ? 2 * kWaves : 16 * kWaves;
-  load_lds16(reinterpret_cast<const char*>(g) + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2, lane_off,
-             lds + 1024 * (wave + kWaves * jj));
+  const char* src = reinterpret_cast<const char*>(g) + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2;
+  if (MC_GUARD(0, src + lane_off + 16 <= end)) load_lds16(src, lane_off, lds + 1024 * (wave + kWaves * jj));
 }
 
 // K-rows tiles: per-lane LDS read address (relative to a stage) of the
@@ -309,7 +312,8 @@ __device__ __forceinline__ void store_transposed(uint32_t eb, uint16_t* dst, int
         (lds_s16x4_t*)(uintptr_t)(eb + r1 * 256 + (((col >> 3) ^ (r1 & 15)) << 4) + (col & 7) * 2));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
-    *reinterpret_cast<u32x4*>(dst + blk_off(r0d + C + i, c0d + R, nkb)) = v;
+    const int64_t o = blk_off(r0d + C + i, c0d + R, nkb);
+    if (MC_GUARD(3, o + 8 <= static_cast<int64_t>(nkb) * 32 * nkb * 32)) *reinterpret_cast<u32x4*>(dst + o) = v;
   }
 }
 
@@ -405,6 +409,11 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     kstep_q = kBK * 256;
     K = n_pad;
   }
+  // one past each operand (range checks of debug builds): in0 holds X (mode
+  // 0), A or B' (modes 1, 2); in1 holds X (mode 2)
+  const int64_t nmat = gridDim.x / tiles_per_mat;
+  const char* const end_p = reinterpret_cast<const char*>(in0 + nmat * (MODE == 0 ? nm : nn));
+  const char* const end_q = MODE == 2 ? reinterpret_cast<const char*>(in1 + nmat * nm) : end_p;
   // element offset of K-step kt from the operand origin
   auto k_ofs = [&](int kt, int64_t kstep) -> int64_t {
     if constexpr (MODE == 0) {
@@ -427,11 +436,12 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // in-bounds tile is fetched again into a stage nobody reads, which keeps
   // the number of loads in flight (and so the wait counts) fixed.
   auto issue_p = [&](int kt) {
-    issue_tile<false>(Pg + k_ofs(min(kt, KT - 1), kstep_p), ldp, off_p, lds + (kt % kStages) * kStageBytes, wave);
+    issue_tile<false>(Pg + k_ofs(min(kt, KT - 1), kstep_p), ldp, off_p, lds + (kt % kStages) * kStageBytes, wave,
+                      end_p);
   };
   auto issue_q = [&](int kt) {
     issue_tile<kQKRows>(Qg + k_ofs(min(kt, KT - 1), kstep_q), ldq, off_q,
-                        lds + (kt % kStages) * kStageBytes + kTileBytes, wave);
+                        lds + (kt % kStages) * kStageBytes + kTileBytes, wave, end_q);
   };
   const FragAddr fadr = frag_addresses<kQKRows>(lane, wm, wn);
 
@@ -481,13 +491,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     const int kr = min(kt + kStages - 1, KT - 1);
     const uint32_t refill = lds + ((kt + kStages - 1) % kStages) * kStageBytes;
     half(f0, f1, cur, 1, [&](int jj) {
-      issue_tile_part<false>(Pg + k_ofs(kr, kstep_p), ldp, off_p, refill, wave, jj);
+      issue_tile_part<false>(Pg + k_ofs(kr, kstep_p), ldp, off_p, refill, wave, jj, end_p);
     });
     wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerTile>();
     __syncthreads();
     // After the last step this reads a stage of redundant tiles; unused.
     half(f1, f0, nxt, 0, [&](int jj) {
-      issue_tile_part<kQKRows>(Qg + k_ofs(kr, kstep_q), ldq, off_q, refill + kTileBytes, wave, jj);
+      issue_tile_part<kQKRows>(Qg + k_ofs(kr, kstep_q), ldq, off_q, refill + kTileBytes, wave, jj, end_q);
     });
   }
 
@@ -522,7 +532,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     const uint8_t* Xl = xl + mat * nm;
     float dgr[4];  // d_i of this lane's 4 rows (the factor of Xh; a multiplies X)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) dgr[y] = dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row];
+    for (int y = 0; y < 4; ++y)
+      dgr[y] = MC_GUARD(4, i0w + y * 32 + frag_row < n_pad) ? dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row]
+                                                             : 0.f;
 #pragma unroll
     for (int yh = 0; yh < 4; yh += 2) {
       u32x2 hb[2][kCT][4];
@@ -535,8 +547,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
           for (int g = 0; g < 4; ++g) {
             const int64_t o = x_off(i0w + (yh + yy) * 32 + frag_row,
                                     j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, n_pad);
-            hb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xh + o);
-            lb[yy][x][g] = *reinterpret_cast<const uint32_t*>(Xl + o);
+            if (MC_GUARD(5, o + 4 <= nm)) {
+              hb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xh + o);
+              lb[yy][x][g] = *reinterpret_cast<const uint32_t*>(Xl + o);
+            } else {
+              hb[yy][x][g] = u32x2{0u, 0u};
+              lb[yy][x][g] = 0u;
+            }
           }
 #pragma unroll
       for (int yy = 0; yy < 2; ++yy)
@@ -588,13 +605,18 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     float dgr[8];
     auto load_x = [&](int sq) {
       const int64_t off = x_off(i0 + (sq & 7) * 32 + rsub, j0 + 128 * (sq >> 3) + 8 * cg, n_pad);
-      xhv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xh + off);
-      xlv[sq % kRing] = *reinterpret_cast<const u32x2*>(Xlm + off);
+      if (MC_GUARD(5, off + 8 <= nm)) {
+        xhv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xh + off);
+        xlv[sq % kRing] = *reinterpret_cast<const u32x2*>(Xlm + off);
+      } else {
+        xhv[sq % kRing] = u32x4{0u, 0u, 0u, 0u};
+        xlv[sq % kRing] = u32x2{0u, 0u};
+      }
     };
 #pragma unroll
     for (int sq = 0; sq < kRing; ++sq) load_x(sq);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) dgr[p] = dgm[i0 + p * 32 + rsub];
+    for (int p = 0; p < 8; ++p) dgr[p] = MC_GUARD(4, i0 + p * 32 + rsub < n_pad) ? dgm[i0 + p * 32 + rsub] : 0.f;
     // W of the update, read in batches of kWB passes
     constexpr int kWB = UPD == 2 ? 2 : (UPD == 1 ? 2 : 4);
 #pragma unroll
@@ -620,7 +642,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
           for (int q = 0; q < kWB; ++q) {
             const int row = i0 + (p0 + q) * 32 + rsub;
-            if (wvec && row < ua.n && jc + 8 <= ua.m) {
+            if (wvec && row < ua.n && jc + 8 <= ua.m &&
+                MC_GUARD(2, static_cast<int64_t>(row) * ua.m + jc + 8 <= static_cast<int64_t>(ua.n) * ua.m)) {
               const u32x4* pw = reinterpret_cast<const u32x4*>(Wb + (static_cast<int64_t>(row) * ua.m + jc) * kEsz);
 #pragma unroll
               for (int w = 0; w < kWords; ++w) wv[q][w] = pw[w];
@@ -659,9 +682,11 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
             for (int e = 0; e < 8; ++e) qv[e] = enc_lo(v[e], hi_bits(ow[e >> 1], e & 1));
             const int64_t off = x_off(row, jc, n_pad);
-            *reinterpret_cast<u32x4*>(out + mat * nm + off) = ho;
-            *reinterpret_cast<u32x2*>(xl_out + mat * nm + off) =
-                u32x2{pack_i8x4(qv[0], qv[1], qv[2], qv[3]), pack_i8x4(qv[4], qv[5], qv[6], qv[7])};
+            if (MC_GUARD(1, off + 8 <= nm)) {
+              *reinterpret_cast<u32x4*>(out + mat * nm + off) = ho;
+              *reinterpret_cast<u32x2*>(xl_out + mat * nm + off) =
+                  u32x2{pack_i8x4(qv[0], qv[1], qv[2], qv[3]), pack_i8x4(qv[4], qv[5], qv[6], qv[7])};
+            }
           } else {
             // the last step: X' rounded to bf16, then O = out_scale X'
             if (row >= ua.n || jc >= ua.m) continue;
@@ -669,6 +694,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = ua.out_scale * bf16_to_f32(f32_to_bf16(v[e]));
             const int64_t idx = static_cast<int64_t>(row) * ua.m + jc;
+            if (!MC_GUARD(2, idx + min(8, ua.m - jc) <= static_cast<int64_t>(ua.n) * ua.m)) continue;
             if (wvec && jc + 8 <= ua.m) {
               u32x4* pw = reinterpret_cast<u32x4*>(Wb + idx * kEsz);
               if constexpr (UPD == 3) {
@@ -765,7 +791,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
         int64_t wrow, wcol;
         int valid;
         pos(16 * wh + e, wrow, wcol, valid);
-        if (wvec && valid == 8) {
+        if (wvec && valid == 8 && MC_GUARD(2, wrow * wcols + wcol + 8 <= static_cast<int64_t>(ua.n) * ua.m)) {
           const u32x4* p = reinterpret_cast<const u32x4*>(Wb + (wrow * wcols + wcol) * kEsz);
 #pragma unroll
           for (int w = 0; w < kWords; ++w) wbuf[e][w] = p[w];
@@ -786,8 +812,10 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
       for (int x = 0; x < kCT; ++x)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          abuf[y][x][g] = *reinterpret_cast<const u32x2*>(
-              Am + blk_off(i0w + y * 32 + frag_row, j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, nkb));
+        {
+          const int64_t o = blk_off(i0w + y * 32 + frag_row, j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, nkb);
+          abuf[y][x][g] = MC_GUARD(5, o + 4 <= nn) ? *reinterpret_cast<const u32x2*>(Am + o) : u32x2{0u, 0u};
+        }
   }
   // the region straddles B's diagonal (mode 1)
   const bool on_diag = MODE == 1 && i0w == j0w;
@@ -815,7 +843,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (ii == jj0 + q) {
-            dg[static_cast<int64_t>(mat) * n_pad + i0w + ii] = v[q];
+            if (MC_GUARD(4, i0w + ii < n_pad)) dg[static_cast<int64_t>(mat) * n_pad + i0w + ii] = v[q];
             v[q] = 0.f;
           }
       }
@@ -888,6 +916,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
         for (int q = 0; q < 8; ++q) o[q] = ua.out_scale * x[q];
         const int64_t idx = wrow * wcols + wcol;
+        if (!MC_GUARD(2, idx + valid <= static_cast<int64_t>(ua.n) * ua.m)) continue;
         if (vec && valid == 8) {
           u32x4* p = reinterpret_cast<u32x4*>(Wb + idx * kEsz);
           if constexpr (UPD == 3) {
@@ -939,9 +968,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     for (int s = 16 * wh; s < 16 * wh + 16; ++s) {
       const int row = 4 * s + (lane >> 4), u = lane & 15;
       const u32x4 v = *(const lds_u32x4_t*)(uintptr_t)st_addr(row, u);
-      uint16_t* dst = kBlockedOut ? D + blk_off(i0w + row, j0w + 8 * u, nkb)
-                                  : D + x_off(i0w + row, j0w + 8 * u, n_pad);
-      *reinterpret_cast<u32x4*>(dst) = v;
+      const int64_t o = kBlockedOut ? blk_off(i0w + row, j0w + 8 * u, nkb) : x_off(i0w + row, j0w + 8 * u, n_pad);
+      if (MC_GUARD(3, o + 8 <= (kBlockedOut ? nn : nm))) *reinterpret_cast<u32x4*>(D + o) = v;
     }
   };
   if constexpr (MODE != 2) {
@@ -951,6 +979,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 }
 
 }  // namespace
+
+MC_DEBUG_UNIT(ns_gemm)
 
 hipError_t launch_ns_gemm(int mode, const NsGeometry& g, const uint16_t* in0, const uint16_t* in1,
                           const uint8_t* xl, uint16_t* out, uint8_t* xl_out, float* dg, float alpha, float beta,

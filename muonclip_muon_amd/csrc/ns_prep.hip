@@ -207,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
       const int64_t r = r0 + pass * 16 + (threadIdx.x >> 4), c = c0 + 8 * q;
       in[pass] = r < R && c < C;
       idx[pass] = (r < R ? r : R - 1) * C + (c < C ? c : C - 8);
-      load_run8<SRC>(msrc, gb, idx[pass], run[pass]);
+      if (MC_GUARD(0, idx[pass] >= 0 && idx[pass] + 8 <= R * C)) load_run8<SRC>(msrc, gb, idx[pass], run[pass]);
+      else in[pass] = false;
     }
   }
 #pragma unroll
@@ -238,8 +239,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
       u32x4 hi;
       u32x2 lo;
       pack_hi_lo8(x, hi, lo);
-      *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = hi;
-      *reinterpret_cast<u32x2*>(slb + x_off(r, c, R_pad)) = lo;
+      if (MC_GUARD(1, r < R_pad && c + 8 <= C_pad)) {
+        *reinterpret_cast<u32x4*>(sb + x_off(r, c, R_pad)) = hi;
+        *reinterpret_cast<u32x2*>(slb + x_off(r, c, R_pad)) = lo;
+      }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[rr][8 * q + e] = x[e];
@@ -259,8 +262,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
     u32x4 hi;
     u32x2 lo;
     pack_hi_lo8(v, hi, lo);
-    *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = hi;
-    *reinterpret_cast<u32x2*>(tlb + x_off(c0 + cc, r0 + rq, C_pad)) = lo;
+    if (MC_GUARD(1, c0 + cc < C_pad && r0 + rq + 8 <= R_pad)) {
+      *reinterpret_cast<u32x4*>(tb + x_off(c0 + cc, r0 + rq, C_pad)) = hi;
+      *reinterpret_cast<u32x2*>(tlb + x_off(c0 + cc, r0 + rq, C_pad)) = lo;
+    }
   }
 }
 
@@ -295,7 +300,8 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     const int64_t r = static_cast<int64_t>(blockIdx.y) * kSR + pass * 8 + (threadIdx.x >> 5);
     in[pass] = r < R && c < C;
     idx[pass] = (r < R ? r : R - 1) * C + (c < C ? c : C - 8);
-    load_run8<SRC>(msrc, gb, idx[pass], run[pass]);
+    if (MC_GUARD(0, idx[pass] >= 0 && idx[pass] + 8 <= R * C)) load_run8<SRC>(msrc, gb, idx[pass], run[pass]);
+    else in[pass] = false;
   }
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -307,8 +313,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_rows_kernel(
     u32x4 hi;
     u32x2 lo;
     pack_hi_lo8(x, hi, lo);
-    *reinterpret_cast<u32x4*>(xb + x_off(r, c, R_pad)) = hi;
-    *reinterpret_cast<u32x2*>(xlb + x_off(r, c, R_pad)) = lo;
+    if (MC_GUARD(1, r < R_pad && c + 8 <= C_pad)) {
+      *reinterpret_cast<u32x4*>(xb + x_off(r, c, R_pad)) = hi;
+      *reinterpret_cast<u32x2*>(xlb + x_off(r, c, R_pad)) = lo;
+    }
   }
   const float block_ss = block_sum(ss, red);
   if (threadIdx.x == 0) partials[b * gridDim.x * gridDim.y + blockIdx.y * gridDim.x + blockIdx.x] = block_ss;
@@ -333,6 +341,12 @@ hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_strid
                    reinterpret_cast<uintptr_t>(M) % align == 0 &&
                    (SRC != 0 || reinterpret_cast<uintptr_t>(G) % 32 == 0);
   dim3 grid(static_cast<unsigned>(C_pad / kTC), static_cast<unsigned>(R_pad / kTR), static_cast<unsigned>(g.batch));
+#ifdef MC_DEBUG
+  // every grid below writes one partial per block: the workspace holds
+  // prescale_tiles per matrix
+  if ((C_pad / kTC) * (R_pad / kTR) != g.prescale_tiles || (C_pad / kSC) * (R_pad / kSR) != g.prescale_tiles)
+    return hipErrorInvalidValue;
+#endif
   if (vec && S != nullptr)
     hipLaunchKernelGGL(momentum_prescale_rows_kernel<SRC>,
                        dim3(static_cast<unsigned>(C_pad / kSC), static_cast<unsigned>(R_pad / kSR),
@@ -351,6 +365,8 @@ hipError_t launch_prescale_unscaled(void* M, const float* G, int64_t batch_strid
   return hipGetLastError();
 }
 }  // namespace
+
+MC_DEBUG_UNIT(ns_prep)
 
 hipError_t launch_momentum_prescale(float* M, const float* G, int64_t batch_stride, float mu,
                                     const NsGeometry& g, float eps, char* ws, hipStream_t stream) {

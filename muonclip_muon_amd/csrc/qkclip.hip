@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
       if (i < w) slot += wave_count[i];
       round += wave_count[i];
     }
-    if (c) {
+    if (c && MC_GUARD(0, slot < H)) {
       l_head[slot] = h;
       l_qc[slot] = f.q_c;
       l_qr[slot] = f.q_r;
@@ -256,12 +256,14 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
         off -= per_head;
         ++idx;
       }
+      if (!MC_GUARD(1, idx < count)) continue;
       const int64_t h = l_head[idx];
       const bool in_q = off < q_items;
       char* row_base = in_q ? q_layer + static_cast<size_t>(h * qph * d_in) * esz
                             : k_layer + static_cast<size_t>(h * kph * d_in) * esz;
       const int64_t o = in_q ? off : off - q_items;
       fac[u] = in_q ? (off < q_c_items ? l_qc[idx] : l_qr[idx]) : l_k[idx];
+      if (!MC_GUARD(2, h < H && o >= 0 && (o + 1) * unit <= (in_q ? qph : kph) * d_in)) continue;
       addr[u] = row_base + static_cast<size_t>(o * unit) * esz;
       if constexpr (VEC) {
 #pragma unroll
@@ -296,6 +298,8 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
   }
 }
 }  // namespace
+
+MC_DEBUG_UNIT(qkclip)
 
 hipError_t launch_qk_clip(const float* smax, int64_t L, int64_t H, bool total_clip, float tau, float alpha,
                           void* const* Wq, void* const* Wk, bool w_bf16, int64_t d_in, int64_t qph, int64_t q_c_rows,

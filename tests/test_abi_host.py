@@ -46,8 +46,8 @@ def test_library_exports_every_declared_symbol(mc):
 def test_abi_version_and_status_strings(mc):
     text = open(HEADER).read()
     assert mc.abi_version() == int(re.search(r"#define MC_ABI_VERSION (\d+)", text).group(1))
-    for code in range(7):
-        assert mc.lib.mc_status_string(code)
+    for code in range(8):
+        assert mc.lib.mc_status_string(code) != b"unknown status"
     assert mc.lib.mc_status_string(99) == b"unknown status"
 
 
