@@ -118,7 +118,8 @@ MC_API float muon_rms_match_scale(int64_t rows, int64_t cols);
 
 /*
  * Workspace bytes that muon_ns_orthogonalize_batched needs for `batch`
- * matrices of rows x cols.  Returns 0 for invalid sizes.
+ * matrices of rows x cols.  Returns 0 for invalid or unsupported sizes
+ * (those the Newton-Schulz calls reject with MC_EINVAL or MC_ESHAPE).
  */
 MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
 
@@ -165,9 +166,10 @@ MC_API size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
  *   gemm_events    NULL, or host array of 6 * steps hipEvent_t (as void*):
  *                  events[2*(3s+g)] and events[2*(3s+g)+1] are recorded on
  *                  `stream` right before and after GEMM g of step s
- *                  (g = 0: X X^T, 1: a I + b A + c A A, 2: B' X), for timing
+ *                  (g = 0: X X^T, 1: b A + c A A, 2: a X + B X), for timing
  * Sizes: batch >= 0 (0 enqueues nothing); 1 <= rows, cols; min(rows, cols)
- * <= 16384 and max(rows, cols) <= 65536.
+ * <= 16384 and max(rows, cols) <= 65536; batch <= 65535 and batch times the
+ * number of 256 x 256 tiles of X below 2^31 (else MC_ESHAPE).
  * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EWORKSPACE, MC_EHIP.
  */
 MC_API mc_status_t muon_ns_orthogonalize_batched(const void* M, int m_dtype, int64_t batch, int64_t rows,

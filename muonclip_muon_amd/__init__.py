@@ -478,12 +478,20 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
     attention: one layer dict, or a list of L of them, with 'q', 'k' (weight
     names), 'q_rows_per_head', 'q_c_rows', 'k_rows_per_head' (the same row
     split for every layer).  All layers are clipped in one call.
-    Returns (gamma, clipped), shaped like smax."""
+    Returns (gamma, clipped), shaped like smax; attention None or [] skips
+    the clip (smax is then unused) and returns (None, None)."""
     entries = []
     for name, W in weights.items():
         M = momenta.get(name)
         if M is None:
-            M = momenta[name] = torch.zeros(W.shape, dtype=torch.float32, device=W.device)
+            # zero-filled on the launch stream, so the fill is ordered before
+            # the library's first use of it there
+            M = momenta[name] = _empty(W.shape, torch.float32, W.device, stream)
+            if stream is None:
+                M.zero_()
+            else:
+                with torch.cuda.stream(stream):
+                    M.zero_()
         G = grads[name]
         if W.dim() not in (2, 3):
             raise ValueError(f"{name}: weights must be [rows, cols] or [count, rows, cols]")
@@ -514,6 +522,8 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
                                           out_scale=OUT_SCALE_RMS_MATCH, workspace=workspace, stream=stream)
             muon_apply_update(W, O, lr, weight_decay, stream=stream)
     layers = attention if isinstance(attention, (list, tuple)) else [attention]
+    if not layers or layers[0] is None:
+        return None, None  # no attention layer: the Muon part only
     one_layer = smax.dim() == 1
     smax2 = smax.view(1, -1) if one_layer else smax
     if smax2.shape[0] != len(layers):

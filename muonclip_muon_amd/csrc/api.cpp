@@ -53,6 +53,14 @@ constexpr int64_t kNsMaxM = 65536;   // max(rows, cols)
 constexpr int32_t kNsMaxSteps = 64;
 constexpr int64_t kGridMax = 0x7fffffff;
 
+// The batch limits of the Newton-Schulz calls (grid sizes), checked before
+// any size is computed from the batch: at most 65535 matrices (the
+// pre-scale's grid z) and fewer than 2^31 GEMM tiles in one launch.
+inline bool ns_batch_supported(int64_t batch, int64_t n, int64_t m) {
+  const int64_t tiles = ((n + 255) / 256) * ((m + 255) / 256);
+  return batch <= 65535 && tiles * batch <= kGridMax;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,7 +106,7 @@ float muon_rms_match_scale(int64_t rows, int64_t cols) {
 size_t muon_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
   if (batch < 0 || rows < 1 || cols < 1) return 0;
   const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
-  if (n > kNsMaxN || m > kNsMaxM) return 0;
+  if (n > kNsMaxN || m > kNsMaxM || !ns_batch_supported(batch, n, m)) return 0;
   return mc::ns_geometry(batch, rows, cols).total;
 }
 
@@ -112,7 +120,7 @@ mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, c
                      float out_scale, void* workspace, size_t workspace_bytes, void* const* gemm_events,
                      mc::NsGeometry* g) {
   const int64_t n = rows < cols ? rows : cols, m = rows < cols ? cols : rows;
-  if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
+  if (n > kNsMaxN || m > kNsMaxM || !ns_batch_supported(batch, n, m)) return MC_ESHAPE;
   if (!coeffs || !workspace) return MC_EINVAL;
   if (steps < 1 || steps > kNsMaxSteps) return MC_EINVAL;
   if (!(eps >= 0.0f) || !isfinite(eps) || !isfinite(out_scale)) return MC_EINVAL;
@@ -121,8 +129,6 @@ mc_status_t check_ns(int64_t batch, int64_t rows, int64_t cols, int32_t steps, c
   if (!aligned(workspace, 256)) return MC_EALIGN;
   *g = mc::ns_geometry(batch, rows, cols);
   if (workspace_bytes < g->total) return MC_EWORKSPACE;
-  const int64_t tiles = (g->n_pad / mc::kNsTile) * (g->m_pad / mc::kNsTile);
-  if (tiles * batch > kGridMax || batch > 65535) return MC_ESHAPE;
   if (gemm_events)
     for (int i = 0; i < 6 * steps; ++i)
       if (!gemm_events[i]) return MC_EINVAL;
@@ -292,6 +298,7 @@ mc_status_t muon_momentum_ns_update_batched_noalloc(float* M, const float* G, fl
     if (n > kNsMaxN || m > kNsMaxM) return MC_ESHAPE;
   }
   if (batch == 0) return MC_OK;
+  if (!ns_batch_supported(batch, rows < cols ? rows : cols, rows < cols ? cols : rows)) return MC_ESHAPE;
   if (mc::ns_geometry(batch, rows, cols).total > kStaticScratchBytes) return MC_EWORKSPACE;
   void* ws = static_scratch();
   if (!ws) return MC_EHIP;

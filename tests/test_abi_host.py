@@ -79,6 +79,11 @@ def test_ns_validation(mc):
     assert ws_bytes > 0
     assert L.muon_ns_workspace_bytes(4, 0, 512) == 0
     assert L.muon_ns_workspace_bytes(1, 20000, 20000) == 0
+    # batches beyond the grid limits: rejected before any size is computed
+    # (a batch of 2^40 would wrap the byte count)
+    assert L.muon_ns_workspace_bytes(65536, 256, 256) == 0
+    assert L.muon_ns_workspace_bytes(1 << 40, 256, 256) == 0
+    assert L.muon_ns_workspace_bytes(65535, 256, 256) > 0
 
     def call(**kw):
         a = dict(M=FAKE, m_dtype=1, batch=4, rows=256, cols=512, mstride=256 * 512, O=FAKE, o_dtype=1,
@@ -93,6 +98,8 @@ def test_ns_validation(mc):
     assert call(rows=0) == EINVAL
     assert call(m_dtype=7) == EDTYPE
     assert call(rows=20000, cols=20000) == ESHAPE
+    assert call(batch=1 << 40, wsb=(1 << 64) - 1) == ESHAPE
+    assert call(batch=65536, wsb=(1 << 64) - 1) == ESHAPE
     assert call(M=None) == EINVAL
     assert call(steps=0) == EINVAL
     assert call(eps=-1.0) == EINVAL
@@ -256,3 +263,6 @@ def test_noalloc_validation(mc):
                                                      -1.0, 2e-4, 0.1, None) == EINVAL
     assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, 0.95, FAKE, 1, 1, 20000, 20000, 0, 5, coeffs,
                                                      1e-7, -1.0, 2e-4, 0.1, None) == ESHAPE
+    # a batch whose byte count would wrap is a shape error, not a fit
+    assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, 0.95, FAKE, 1, 1 << 40, 256, 256, 65536, 5,
+                                                     coeffs, 1e-7, -1.0, 2e-4, 0.1, None) == ESHAPE

@@ -1,5 +1,5 @@
 """Calls on a stream other than torch's current one, with the scratch memory
-(Newton-Schulz workspace, output buffers) allocated by the binding: the
+(Newton-Schulz workspace, output buffers, new momenta) allocated by the binding: the
 results equal, bit for bit, the same calls on the current stream, although
 the current stream allocates and overwrites memory of the same size while
 the side stream's kernels still run.  The binding allocates such scratch in
@@ -71,3 +71,25 @@ def test_fused_on_side_stream(mc):
     torch.cuda.synchronize()
     assert torch.equal(M, M_ref)
     assert torch.equal(W, W_ref)
+
+
+def test_page_step_on_side_stream(mc):
+    """muonclip_step on a side stream with momenta it creates itself (zero-filled
+    on that stream) and its own workspace, no attention layer: bit-identical to
+    the same step on the current stream."""
+    say("page-level step on a side stream")
+    g = workloads.generator(93, "cpu")
+    W0 = workloads.normal((3, 256, 1024), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+    G = {"experts": workloads.normal((3, 256, 1024), 1e-3, g, "cpu").to(DEV)}
+    W_ref, mom_ref = {"experts": W0.clone()}, {}
+    assert mc.muonclip_step(W_ref, G, mom_ref, None, None, lr=2e-2) == (None, None)
+    torch.cuda.synchronize()
+    W, mom = {"experts": W0.clone()}, {}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    mc.muonclip_step(W, G, mom, None, None, lr=2e-2, stream=s)
+    _clobber(mc.muon_ns_workspace_bytes(3, 256, 1024))
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(mom["experts"], mom_ref["experts"])
+    assert torch.equal(W["experts"], W_ref["experts"])
