@@ -340,9 +340,10 @@ MC_API mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const v
  *   Wq, Wk       device, w_dtype, row-major [H*qph, d_in] and [H*kph, d_in]
  *   gamma_out    device float32[H] or NULL: gamma (1 for untouched heads)
  *   clipped_out  device int32[H] or NULL: 1 clipped, 0 not, -1 smax was NaN
- * Sizes: H >= 0; d_in >= 1; 0 <= q_c_rows <= qph; kph >= 0.
+ * Sizes: H >= 0; d_in >= 1; 0 <= q_c_rows <= qph; kph >= 0; H <= 65535,
+ * qph, kph <= 65536 and d_in <= 2^24 (else MC_ESHAPE).
  * Errors: MC_EINVAL (also tau not finite and > 0, alpha outside [0, 1]),
- * MC_EDTYPE, MC_EALIGN, MC_EHIP.
+ * MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EHIP.
  */
 MC_API mc_status_t qk_clip_apply(const float* smax, int64_t H, float tau, float alpha, void* Wq, void* Wk,
                           int w_dtype, int64_t d_in, int64_t q_rows_per_head, int64_t q_c_rows,

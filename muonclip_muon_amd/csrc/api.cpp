@@ -8,6 +8,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <utility>
 
@@ -52,6 +53,19 @@ constexpr int64_t kNsMaxN = 16384;   // min(rows, cols)
 constexpr int64_t kNsMaxM = 65536;   // max(rows, cols)
 constexpr int32_t kNsMaxSteps = 64;
 constexpr int64_t kGridMax = 0x7fffffff;
+
+// A product of non-negative sizes no larger than 2^46 (far beyond any
+// buffer a GPU holds), computed without overflow: sizes whose element counts
+// or offsets could leave int64 are rejected before any is formed.
+inline bool count_ok(std::initializer_list<int64_t> dims) {
+  __int128 p = 1;
+  for (int64_t d : dims) {
+    if (d < 0) return false;
+    p *= d;
+    if (p > (static_cast<__int128>(1) << 46)) return false;
+  }
+  return true;
+}
 
 // The batch limits of the Newton-Schulz calls (grid sizes), checked before
 // any size is computed from the batch: at most 65535 matrices (the
@@ -328,6 +342,8 @@ mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, int dtype
   if (H == 0) return MC_OK;
   if (!smax) return MC_EINVAL;
   if (H > 65535 || B > 65535 || (Sq + 63) / 64 > kGridMax) return MC_ESHAPE;
+  if (!count_ok({B, H, Sq, d_c + d_r}) || !count_ok({B, H, Sk, d_c}) || !count_ok({B, Sk, d_r}))
+    return MC_ESHAPE;
   const bool empty = B == 0 || Sq == 0 || Sk == 0;
   if (!empty) {
     if (!Q || !Kc) return MC_EINVAL;
@@ -355,6 +371,9 @@ mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr
   if (!mc::attention_fwd_supported(d_c, d_r, d_v)) return MC_ESHAPE;
   if (!Q || !Kc || !V || !O || !smax_out || (d_r > 0 && !Kr)) return MC_EINVAL;
   if (H > 65535 || Sq > INT32_MAX || Sk > INT32_MAX) return MC_ESHAPE;
+  if (!count_ok({B, H, Sq, d_c + d_r}) || !count_ok({B, H, Sk, d_c + d_v}) || !count_ok({B, Sk, d_r}) ||
+      !count_ok({B, H, Sq, d_v}))
+    return MC_ESHAPE;
   const bool empty = B == 0 || H == 0 || Sq == 0;
   if (!empty && Sk < 64) return MC_ESHAPE;
   if (causal && Sq > Sk) return MC_ESHAPE;
@@ -380,6 +399,9 @@ static mc_status_t qk_clip_check(int64_t H, float tau, float alpha, int w_dtype,
     return MC_EINVAL;
   if (!valid_dtype(w_dtype)) return MC_EDTYPE;
   if (!(tau > 0.0f) || !isfinite(tau) || !(alpha >= 0.0f && alpha <= 1.0f)) return MC_EINVAL;
+  // bounds under which every element count and offset below and in the
+  // kernels fits in int64 (H (qph + kph) d_in < 2^58)
+  if (q_rows_per_head > 65536 || k_rows_per_head > 65536 || d_in > (int64_t{1} << 24)) return MC_ESHAPE;
   return MC_OK;
 }
 

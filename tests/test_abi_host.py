@@ -159,6 +159,8 @@ def test_maxlogit_validation(mc):
     assert L.qk_maxlogit(FAKE, FAKE, None, 1, 1, 2, 8, 8, 600, 0, FAKE, 0, None) == ESHAPE
     assert L.qk_maxlogit(FAKE, FAKE, None, 1, 1, 2, 8, 8, 64, 0, None, 0, None) == EINVAL
     assert L.qk_maxlogit(ctypes.c_void_p(0x100001), FAKE, None, 1, 1, 2, 8, 8, 64, 0, FAKE, 0, None) == EALIGN
+    # element counts beyond any buffer (their products would leave int64)
+    assert L.qk_maxlogit(FAKE, FAKE, None, 1, 60000, 60000, 1 << 30, 8, 64, 0, FAKE, 0, None) == ESHAPE
 
 
 @pytest.mark.parametrize("fn", ["qk_clip_apply", "qk_clip_apply_total"])
@@ -173,6 +175,11 @@ def test_clip_validation(mc, fn):
     assert f(None, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 4, None, None, None) == EINVAL
     assert f(FAKE, 4, 100.0, 0.5, ctypes.c_void_p(0x100001), FAKE, 1, 16, 6, 4, 4, None, None,
              None) == EALIGN
+    # sizes whose products would leave int64 are shape errors (checked before
+    # any is formed)
+    assert f(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 1, 1 << 40, 6, 4, 4, None, None, None) == ESHAPE
+    assert f(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 1 << 40, 4, 4, None, None, None) == ESHAPE
+    assert f(FAKE, 4, 100.0, 0.5, FAKE, FAKE, 1, 16, 6, 4, 1 << 40, None, None, None) == ESHAPE
 
 
 def test_probe_validation(mc):
