@@ -107,31 +107,6 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const char* Kcbh = reinterpret_cast<const char*>(Kc + (static_cast<int64_t>(b) * H + h) * Sk * DC);
   const char* Krb = reinterpret_cast<const char*>(Kr ? Kr + static_cast<int64_t>(b) * Sk * DR : Kc);
 
-  // ---- this wave's 128 query rows as MFMA "A" fragments (row = lane % 32).
-  // Tails need no masking: a query row past Sq repeats row Sq - 1, and the
-  // last key block is the last 64 keys (it may overlap the previous one), so
-  // every logit computed is one of the real ones and the maximum is exact.
-  const int row_base = ib * kRowsPerBlock + wave * kRowsPerWave;
-  bf16x8 qf[4][kSteps];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int i = min(row_base + t * 32 + frag_row, Sq - 1);
-    const bool ok = MC_GUARD(0, i >= 0 && i < Sq);
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      qf[t][s] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half))
-                    : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  }
-  // Q is in registers before any key copy starts: otherwise the compiler,
-  // which cannot tell the copies from these loads, waits on the copies in
-  // flight before the first use of each Q register inside the loop.  The
-  // empty asm statements consume every Q register (forcing the loads to
-  // complete) and, being volatile, stay ahead of the copies' asm.
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) asm volatile("" : : "v"(qf[t][s]));
-
   // ---- key loads.  DMA instruction l of this wave fills 1 KB at region
   // offset 1024 (wave + 4 l); its lane slot p = 64 (wave + 4 l) + lane holds
   // row r = p / units, unit (p % units) ^ (r & 7).  Lane offsets are relative
@@ -162,6 +137,35 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) issue_part(jb, l);
   };
+  // the first kKeyStages - 1 key blocks, issued before Q's loads
+  for (int s = 0; s < kKeyStages - 1; ++s) issue(s);
+
+  // ---- this wave's 128 query rows as MFMA "A" fragments (row = lane % 32).
+  // Tails need no masking: a query row past Sq repeats row Sq - 1, and the
+  // last key block is the last 64 keys (it may overlap the previous one), so
+  // every logit computed is one of the real ones and the maximum is exact.
+  const int row_base = ib * kRowsPerBlock + wave * kRowsPerWave;
+  bf16x8 qf[4][kSteps];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = min(row_base + t * 32 + frag_row, Sq - 1);
+    const bool ok = MC_GUARD(0, i >= 0 && i < Sq);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      qf[t][s] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(Qbh + static_cast<int64_t>(i) * D + 16 * s + 8 * frag_half))
+                    : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  // Q is in registers before the loop: otherwise the compiler, which cannot
+  // tell the key copies from these loads, waits on the copies in flight
+  // before the first use of each Q register inside the loop.  The empty asm
+  // statements consume every Q register (forcing the loads to complete,
+  // together with the first key copies issued before them, so the two
+  // latencies overlap) and, being volatile, stay ahead of the later copies.
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) asm volatile("" : : "v"(qf[t][s]));
+
 
   // ---- main loop.  A key block is two phases of 32 keys (u = 0, 1); a
   // phase is kSteps k-steps of 4 MFMAs (one per 32-row query tile t) into
@@ -203,8 +207,8 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t][1] = run;
 
-  for (int s = 0; s < kKeyStages - 1; ++s) issue(s);
-  // block 0's loads are older than the 2 newer stages in flight
+  // block 0's loads are older than the 2 newer stages in flight (the wait
+  // for Q above has already covered them)
   wait_vmem<(kKeyStages - 2) * kLoads>();
   __syncthreads();
   bf16x8 kf[4];
