@@ -518,57 +518,75 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // X is inv_b times the stored X in the first step of the fused path
   const float xs = (inv != nullptr) ? inv[mat] : 1.0f;
 
-  // Mode 2 (see kRowEpi below for all but the update of a transposed W):
-  // X' = a (Xh + Xl) + d Xh + N Xh, the diagonal terms in float32 from both
-  // parts of X at this lane's accumulator positions (4 consecutive columns, 8 bytes
-  // of each part per MFMA register group), half of the tile's rows at a time
-  // to bound the registers held; the accumulators become X' / xs.  Done
-  // before anything else of the epilogue holds registers (the W of the
-  // update).  These loads touch 32 rows x 16 bytes per instruction, which
-  // the row-ordered pass avoids.
+  // Mode 2, update of a transposed W (the other launches take the
+  // row-ordered epilogue, kRowEpi below): X' = a (Xh + Xl) + d Xh + N Xh is
+  // formed in the accumulators before they are staged in bf16 for the
+  // transposed update, the diagonal terms in float32 from both parts of X at
+  // this lane's accumulator positions (4 consecutive columns per MFMA
+  // register group).  X is brought into LDS first, half of the tile's rows
+  // at a time (tile rows 128 wm + 32 (yh + yy) + r: 128 rows, 64 KB of high
+  // parts and 32 KB of codes), by DMA in whole 512-byte (256-byte) rows,
+  // 16-byte unit u of LDS row lr at u ^ (lr & 31) (codes: u ^ (lr & 15)),
+  // the swizzle applied on the global side; each lane then reads its values
+  // from LDS.  Loading them from global memory at the accumulator positions
+  // instead touched 32 rows x 16 bytes per instruction (4.31 ms per
+  // 64-matrix launch against 3.64 for the straight update).
   constexpr bool kRowEpi = MODE == 2 && !(UPD != 0 && TR);
   if constexpr (MODE == 2 && !kRowEpi) {
-    const uint16_t* Xh = in1 + mat * nm;
-    const uint8_t* Xl = xl + mat * nm;
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
+    typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+    constexpr uint32_t kCodes = 65536;  // LDS offset of the codes
     float dgr[4];  // d_i of this lane's 4 rows (the factor of Xh; a multiplies X)
 #pragma unroll
     for (int y = 0; y < 4; ++y)
       dgr[y] = MC_GUARD(4, i0w + y * 32 + frag_row < n_pad) ? dg[static_cast<int64_t>(mat) * n_pad + i0w + y * 32 + frag_row]
                                                              : 0.f;
+    // every copy of the K loop has landed and every wave is past its reads
+    wait_vmem<0>();
+    __syncthreads();
+    const char* const xh_tile = reinterpret_cast<const char*>(in1 + mat * nm + x_off(i0, j0, n_pad));
+    const char* const xl_tile = reinterpret_cast<const char*>(xl + mat * nm + x_off(i0, j0, n_pad));
+    [[maybe_unused]] const char* const xh_end = reinterpret_cast<const char*>(in1 + (mat + 1) * nm);
+    [[maybe_unused]] const char* const xl_end = reinterpret_cast<const char*>(xl + (mat + 1) * nm);
 #pragma unroll
     for (int yh = 0; yh < 4; yh += 2) {
-      u32x2 hb[2][kCT][4];
-      uint32_t lb[2][kCT][4];
+      // LDS row lr = 64 wm' + 32 yy + r holds tile row 128 wm' + 32 (yh + yy) + r
+      auto tile_row = [&](int lr) { return 128 * (lr >> 6) + 32 * yh + (lr & 63); };
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {  // high parts: 64 instructions of 1 KB, 8 per wave
+        const int sl = (8 * wave + k) * 64 + lane, lr = sl >> 5, pu = sl & 31;
+        const uint32_t off = static_cast<uint32_t>(tile_row(lr) * 512 + 16 * (pu ^ (lr & 31)));
+        if (MC_GUARD(6, xh_tile + off + 16 <= xh_end)) load_lds16(xh_tile, off, lds + (8 * wave + k) * 1024);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {  // codes: 32 instructions, 4 per wave
+        const int sl = (4 * wave + k) * 64 + lane, lr = sl >> 4, pu = sl & 15;
+        const uint32_t off = static_cast<uint32_t>(tile_row(lr) * 256 + 16 * (pu ^ (lr & 15)));
+        if (MC_GUARD(6, xl_tile + off + 16 <= xl_end))
+          load_lds16(xl_tile, off, lds + kCodes + (4 * wave + k) * 1024);
+      }
+      wait_vmem<0>();
+      __syncthreads();
 #pragma unroll
       for (int yy = 0; yy < 2; ++yy)
 #pragma unroll
         for (int x = 0; x < kCT; ++x)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int64_t o = x_off(i0w + (yh + yy) * 32 + frag_row,
-                                    j0w + kWaveCols * wh + 32 * x + 8 * g + 4 * frag_half, n_pad);
-            if (MC_GUARD(5, o + 4 <= nm)) {
-              hb[yy][x][g] = *reinterpret_cast<const u32x2*>(Xh + o);
-              lb[yy][x][g] = *reinterpret_cast<const uint32_t*>(Xl + o);
-            } else {
-              hb[yy][x][g] = u32x2{0u, 0u};
-              lb[yy][x][g] = 0u;
-            }
-          }
-#pragma unroll
-      for (int yy = 0; yy < 2; ++yy)
-#pragma unroll
-        for (int x = 0; x < kCT; ++x)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x2 h = hb[yy][x][g];
-            const uint32_t l = lb[yy][x][g];
+            const int lr = 64 * wm + 32 * yy + frag_row;
+            const int c = kWaveCols * wn + 32 * x + 8 * g + 4 * frag_half;  // tile column
+            const u32x2 h =
+                *(const lds_u32x2_t*)(uintptr_t)(lds + lr * 512 + 16 * ((c >> 3) ^ (lr & 31)) + (c & 7) * 2);
+            const uint32_t l =
+                *(const lds_u32_t*)(uintptr_t)(lds + kCodes + lr * 256 + 16 * ((c >> 4) ^ (lr & 15)) + (c & 15));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint32_t hs = hi_bits(q < 2 ? h.x : h.y, q & 1);
               acc[x][yh + yy][4 * g + q] += dgr[yh + yy] * __uint_as_float(hs) + acoef * dec_x(i8_at(l, q), hs);
             }
           }
+      // the next half's copies (or the staging) reuse the LDS
+      __syncthreads();
     }
   }
   wait_vmem<0>();
