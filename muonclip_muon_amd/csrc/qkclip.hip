@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void qk_clip_kernel(const float* __restri
 
 
 constexpr int kCompactMaxHeads = 4000;  // heads per layer; the list then takes at most 64000 bytes of LDS
-constexpr int kCompactMaxBlocks = 2048;
+constexpr int kCompactMaxBlocks = 4096;
 
 // grid (blocks per layer, L).  Block (x, l) lists layer l's clipped heads
 // (identical in every block of the layer) with their factors in dynamic LDS
@@ -228,18 +228,20 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
   const int64_t q_items = qph * d_in / unit, q_c_items = q_c_rows * d_in / unit;
   const int64_t per_head = q_items + kph * d_in / unit;
   const int64_t total = count * per_head;
-  // Each block takes one contiguous range of work items, in batches of
-  // kUnroll x kThreads consecutive items (a thread's kUnroll items kThreads
-  // apart); a batch's loads are all issued before any item is scaled and
-  // stored, so kUnroll 16-byte loads per thread are in flight at once.  The
-  // head of an item follows from the batch's first head without a division
-  // per item.
+  // Work items go out in batches of kUnroll x kThreads consecutive items (a
+  // thread's kUnroll items kThreads apart), block x taking batches x,
+  // x + gridDim.x, ..., so the blocks of a layer sweep adjacent memory
+  // together (one contiguous range per block ran 12 % slower on all 64
+  // heads: scattered DRAM rows); a batch's loads are all issued before any
+  // item is scaled and stored, so kUnroll 16-byte loads per thread are in
+  // flight at once, and the accesses are non-temporal (each element is
+  // touched once).  The head of an item follows from the batch's first head
+  // without a division per item.
   constexpr int kUnroll = 4;
   constexpr int64_t kBatch = static_cast<int64_t>(kUnroll) * kThreads;
-  const int64_t per_block = ((total + gridDim.x - 1) / gridDim.x + kBatch - 1) / kBatch * kBatch;
-  const int64_t v_begin = static_cast<int64_t>(blockIdx.x) * per_block;
-  const int64_t v_end = min(total, v_begin + per_block);
-  for (int64_t base = v_begin; base < v_end; base += kBatch) {
+  const int64_t v_end = total;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kBatch; base < v_end;
+       base += static_cast<int64_t>(gridDim.x) * kBatch) {
     const int idx0 = static_cast<int>(base / per_head);
     char* addr[kUnroll];
     float fac[kUnroll];
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
       addr[u] = row_base + static_cast<size_t>(o * unit) * esz;
       if constexpr (VEC) {
 #pragma unroll
-        for (int w = 0; w < kWords; ++w) val[u][w] = reinterpret_cast<const u32x4*>(addr[u])[w];
+        for (int w = 0; w < kWords; ++w) val[u][w] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(addr[u]) + w);
       }
     }
 #pragma unroll
@@ -281,14 +283,14 @@ __global__ __launch_bounds__(kThreads) void qk_clip_compact_kernel(const float* 
           a.y = pack_bf16x2(scale_op(bf16_lo(a.y), f), scale_op(bf16_hi(a.y), f));
           a.z = pack_bf16x2(scale_op(bf16_lo(a.z), f), scale_op(bf16_hi(a.z), f));
           a.w = pack_bf16x2(scale_op(bf16_lo(a.w), f), scale_op(bf16_hi(a.w), f));
-          *reinterpret_cast<u32x4*>(addr[u]) = a;
+          __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(addr[u]));
         } else {
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             f32x4 a = __builtin_bit_cast(f32x4, val[u][w % kWords]);
             a.x = scale_op(a.x, fac[u]); a.y = scale_op(a.y, fac[u]);
             a.z = scale_op(a.z, fac[u]); a.w = scale_op(a.w, fac[u]);
-            reinterpret_cast<u32x4*>(addr[u])[w] = __builtin_bit_cast(u32x4, a);
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, a), reinterpret_cast<u32x4*>(addr[u]) + w);
           }
         }
       } else {
