@@ -31,8 +31,10 @@
  *  - Argument errors are reported before anything is enqueued, and then no
  *    output is touched.  A failed launch returns MC_EHIP; the stream's work
  *    is then undefined.  No C++ exception crosses the ABI.
- *  - The library holds no mutable global state: calls on different streams
- *    may run concurrently as long as their buffers do not overlap.
+ *  - Apart from the allocation-free entry point's static scratch (see
+ *    there) and a debug build's check flags, the library holds no mutable
+ *    global state: calls on different streams may run concurrently as long
+ *    as their buffers do not overlap.
  *  - Debug builds (libmuonclip_debug.so, compiled with MC_DEBUG; host code
  *    under UndefinedBehaviorSanitizer) check the index ranges of the
  *    kernels' global accesses and skip any access that fails, synchronise
