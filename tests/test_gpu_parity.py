@@ -447,6 +447,33 @@ def test_newton_schulz_zero_matrix(mc):
     assert torch.count_nonzero(O).item() == 0
 
 
+def test_newton_schulz_non_finite_momentum(mc):
+    """A NaN or an infinity in one matrix of a batch: that matrix's result is
+    NaN everywhere, as the oracle's is (the norm is NaN or infinite, and the
+    iteration spreads the non-finite entry to every element by its second
+    product), and the batch's other matrices are untouched by it.  Checks
+    that the carried low part never turns a non-finite value into a finite
+    one, in the Newton-Schulz call and in the fused step."""
+    say("newton-schulz non-finite momentum")
+    g = workloads.generator(61, "cpu")
+    M = workloads.normal((3, 256, 512), 1e-3, g, "cpu")
+    M[1, 17, 300] = float("nan")
+    M[2, 200, 5] = float("inf")
+    O = mc.muon_ns_orthogonalize_batched(M.to(DEV), out_scale=1.0, out_dtype=torch.float32).cpu()
+    with np.errstate(invalid="ignore"):  # inf / inf in the oracle's normalisation
+        refs = [oracle.newton_schulz(f64(M[b])) for b in range(3)]
+    assert np.isnan(refs[1]).all() and np.isnan(refs[2]).all()
+    assert torch.isnan(O[1]).all() and torch.isnan(O[2]).all()
+    assert torch.isfinite(O[0]).all() and rel_fro(f64(O[0]), refs[0]) <= 2e-2
+    # the fused step: momentum element-wise, W of the non-finite matrices NaN
+    W0 = workloads.normal((3, 256, 512), 0.02, g, "cpu", torch.bfloat16)
+    Md, W = torch.zeros(3, 256, 512, device=DEV), W0.to(DEV)
+    mc.muon_momentum_ns_update_batched(Md, M.to(DEV), W, 2e-2, 0.1, 0.95)
+    Md, W = Md.cpu(), W.cpu().float()
+    assert torch.isnan(Md[1, 17, 300]) and torch.isfinite(Md[1]).sum() == 256 * 512 - 1
+    assert torch.isnan(W[1]).all() and torch.isnan(W[2]).all() and torch.isfinite(W[0]).all()
+
+
 def test_newton_schulz_gemm_events(mc):
     say("newton-schulz events")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(6 * 5)]
