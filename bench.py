@@ -176,10 +176,16 @@ def run(args):
     for name, off, n, rows, cols in wl.groups:
         for s in range(0, n, chunk):
             ns_calls.append((name, s, min(chunk, n - s), rows, cols))
-    gemm_ev = [[ev() for _ in range(6 * steps_ns)] for _ in ns_calls]
-    call_ev = {k: (ev(), ev()) for k in ("momentum", "maxlogit", "clip")}
-    upd_ev = [(ev(), ev()) for _ in ns_calls]
-    ns_ev = [(ev(), ev()) for _ in ns_calls]
+    def new_events():
+        """One step's events: per Newton-Schulz call its GEMMs' pairs, the call's
+        pair (and the update's, unfused), and the max logit's and clip's pairs.
+        Each timed step gets its own set, so no step waits for the host to
+        read the previous one's."""
+        return ([[ev() for _ in range(6 * steps_ns)] for _ in ns_calls],
+                {k: (ev(), ev()) for k in ("momentum", "maxlogit", "clip")},
+                [(ev(), ev()) for _ in ns_calls], [(ev(), ev()) for _ in ns_calls])
+
+    gemm_ev, call_ev, upd_ev, ns_ev = new_events()
 
     def step(timed):
         # S_max^h comes from the forward pass that precedes the optimizer step
@@ -228,12 +234,23 @@ def run(args):
     gemm_flops_nom = {k: [] for k in gemm_ms}   # dense 2 n^2 m / 2 n^3
     gemm_flops_exe = {k: [] for k in gemm_ms}   # what the MFMAs execute (tiles, padding)
     t_start, t_end = ev(), ev()
+    step_events = [new_events() for _ in range(args.steps)]
+    for g_ev, c_ev, u_ev, n_ev in step_events:  # torch creates an event at its first record
+        for e in [e for pairs in g_ev for e in pairs] + [e for pair in c_ev.values() for e in pair] + \
+                 [e for pair in u_ev + n_ev for e in pair]:
+            e.record(stream)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
+        gemm_ev, call_ev, upd_ev, ns_ev = step_events[i]
         step(True)
-        torch.cuda.synchronize()  # read this step's events before re-recording them
+        log(f"step {i + 1}/{args.steps} enqueued")
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for i in range(args.steps):
+        gemm_ev, call_ev, upd_ev, ns_ev = step_events[i]
         for k in ("momentum", "maxlogit", "clip") if args.unfused else ("maxlogit", "clip"):
             acc[k] += call_ev[k][0].elapsed_time(call_ev[k][1])
         for k, (name, s, cnt, rows, cols) in enumerate(ns_calls):
@@ -253,10 +270,7 @@ def run(args):
                     gemm_flops[key].append(per[gm] * cnt)
                     gemm_flops_nom[key].append(per_nom[gm] * cnt)
                     gemm_flops_exe[key].append(per_exe[gm] * cnt)
-        log(f"step {i + 1}/{args.steps} done")
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    log(f"{args.steps} timed steps done")
     total_ms = t_start.elapsed_time(t_end)
     K = args.steps
     ms_per_step = total_ms / K

@@ -209,8 +209,11 @@ def _events(gemm_events, steps, device, stream):
     if len(gemm_events) != 6 * steps:
         raise ValueError("gemm_events needs 6 * steps events")
     st = stream or torch.cuda.current_stream(device)
-    for e in gemm_events:  # torch creates events lazily; make sure each exists
-        e.record(st)
+    for e in gemm_events:
+        # torch creates an event at its first record; record only those not
+        # created yet (each record is a marker on the stream)
+        if not e.cuda_event:
+            e.record(st)
     return (ctypes.c_void_p * len(gemm_events))(*[e.cuda_event for e in gemm_events])
 
 
