@@ -141,6 +141,16 @@ def _dev(t, name):
     return t
 
 
+def _out(t, name, dtype, numel, device):
+    """A caller-supplied output: on the inputs' device, contiguous, of the
+    dtype and element count the call writes (the kernels write exactly that
+    many elements, so a smaller tensor would be overrun)."""
+    _dev(t, name)
+    if t.dtype != dtype or t.numel() != numel or t.device != torch.device(device):
+        raise ValueError(f"{name} must be a {dtype} tensor of {numel} elements on {device}")
+    return t
+
+
 def _dtype(t, name):
     try:
         return _DTYPES[t.dtype]
@@ -235,8 +245,8 @@ def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS
     if O is None:
         O = _empty(M.shape, out_dtype or M.dtype, M.device, stream)
     _dev(O, "O")
-    if O.shape != M.shape:
-        raise ValueError("O must have M's shape")
+    if O.shape != M.shape or O.device != M.device:
+        raise ValueError("O must have M's shape and device")
     c_coeffs = _coeffs(steps, coeffs)
     workspace = _workspace(workspace, batch, rows, cols, M.device, stream)
     ev = _events(gemm_events, steps, M.device, stream)
@@ -331,7 +341,7 @@ def qk_maxlogit(Q, Kc, Kr=None, smax=None, accumulate=False, stream=None):
         raise ValueError("Q's head dim must be d_c + d_r and Q, Kc must share a dtype")
     if smax is None:
         smax = _empty(H, torch.float32, Q.device, stream)
-    _dev(smax, "smax")
+    _out(smax, "smax", torch.float32, H, Q.device)
     status = lib.qk_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
                              _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, smax.data_ptr(), int(bool(accumulate)),
                              _stream(Q, stream))
@@ -359,6 +369,10 @@ def attention_fwd_maxlogit(Q, Kc, Kr, V, causal=False, O=None, lse=None, smax=No
         O = _empty((B, H, Sq, d_v), Q.dtype, Q.device, stream)
     if smax is None:
         smax = _empty(H, torch.float32, Q.device, stream)
+    _out(O, "O", Q.dtype, B * H * Sq * d_v, Q.device)
+    _out(smax, "smax", torch.float32, H, Q.device)
+    if lse is not None:
+        _out(lse, "lse", torch.float32, B * H * Sq, Q.device)
     status = lib.attention_fwd_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
                                         V.data_ptr(), _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, d_v,
                                         int(bool(causal)), O.data_ptr(), lse.data_ptr() if lse is not None else None,
@@ -409,6 +423,8 @@ def qk_clip_apply_layers(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_hea
         gamma = _empty((L, H), torch.float32, smax.device, stream)
     if clipped is None:
         clipped = _empty((L, H), torch.int32, smax.device, stream)
+    _out(gamma, "gamma", torch.float32, L * H, smax.device)
+    _out(clipped, "clipped", torch.int32, L * H, smax.device)
     qp = (ctypes.c_void_p * L)(*[w.data_ptr() for w in Wq])
     kp = (ctypes.c_void_p * L)(*[w.data_ptr() for w in Wk])
     status = lib.qk_clip_apply_layers(smax.data_ptr(), L, H, tau, alpha, qp, kp, _dtype(Wq[0], "Wq"), d_in,
@@ -430,6 +446,8 @@ def _qk_clip(fn, smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, 
         gamma = _empty(H, torch.float32, smax.device, stream)
     if clipped is None:
         clipped = _empty(H, torch.int32, smax.device, stream)
+    _out(gamma, "gamma", torch.float32, H, smax.device)
+    _out(clipped, "clipped", torch.int32, H, smax.device)
     status = getattr(lib, fn)(smax.data_ptr(), H, tau, alpha, Wq.data_ptr(), Wk.data_ptr(),
                               _dtype(Wq, "Wq"), d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
                               gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
@@ -444,6 +462,8 @@ def probe_mfma_bf16(workgroups, iters, zero_operands=False, out=None, device=Non
     if out is None:
         out = _empty(workgroups * 256, torch.float32, device or "cuda", stream)
     _dev(out, "out")
+    if out.dtype != torch.float32 or out.numel() < workgroups * 256:
+        raise ValueError(f"out must be a float32 tensor of at least {workgroups * 256} elements")
     _check("mc_probe_mfma_bf16", lib.mc_probe_mfma_bf16(workgroups, iters, 1 if zero_operands else 0,
                                                         out.data_ptr(), _stream(out, stream)))
     return out, workgroups * 4 * iters * 16 * 32768

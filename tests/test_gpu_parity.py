@@ -552,3 +552,35 @@ def test_full_step_tiny_attention_from_oracle_smax(mc, reading):
     assert rel_err(gamma.cpu().numpy(), rg).max() <= 1e-5
     for n in ("q", "k", "v"):
         assert rel_fro(f64(W[n]) - Wn[n], new_w[n] - Wn[n]) <= 2e-2, n
+
+
+def test_binding_rejects_bad_outputs(mc):
+    """Caller-supplied outputs of the wrong size, dtype or device raise before
+    anything is launched (the kernels write exactly the call's element count,
+    so a smaller tensor would be overrun); inputs stay untouched."""
+    say("binding output validation")
+    g = workloads.generator(62, "cpu")
+    Q = workloads.normal((1, 4, 64, 192), 1.0, g, "cpu", torch.bfloat16).to(DEV)
+    Kc = workloads.normal((1, 4, 64, 128), 1.0, g, "cpu", torch.bfloat16).to(DEV)
+    Kr = workloads.normal((1, 64, 64), 1.0, g, "cpu", torch.bfloat16).to(DEV)
+    V = workloads.normal((1, 4, 64, 128), 1.0, g, "cpu", torch.bfloat16).to(DEV)
+    with pytest.raises(ValueError):
+        mc.qk_maxlogit(Q, Kc, Kr, smax=torch.empty(3, device=DEV))
+    with pytest.raises(ValueError):
+        mc.qk_maxlogit(Q, Kc, Kr, smax=torch.empty(4, dtype=torch.float64, device=DEV))
+    with pytest.raises(ValueError):
+        mc.attention_fwd_maxlogit(Q, Kc, Kr, V, O=torch.empty(1, 4, 64, 64, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        mc.attention_fwd_maxlogit(Q, Kc, Kr, V, lse=torch.empty(1, 4, 32, device=DEV))
+    Wq = workloads.normal((4 * 6, 32), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+    Wk = workloads.normal((4 * 4, 32), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+    before = (Wq.clone(), Wk.clone())
+    smax = torch.full((4,), 1000.0, device=DEV)
+    with pytest.raises(ValueError):
+        mc.qk_clip_apply(smax, Wq, Wk, 6, 4, 4, gamma=torch.empty(2, device=DEV))
+    with pytest.raises(ValueError):
+        mc.qk_clip_apply(smax, Wq, Wk, 6, 4, 4, clipped=torch.empty(4, device=DEV))  # float32, not int32
+    with pytest.raises(ValueError):
+        mc.qk_clip_apply_layers(smax.view(1, 4), [Wq], [Wk], 6, 4, 4, gamma=torch.empty(1, 3, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(Wq, before[0]) and torch.equal(Wk, before[1])
