@@ -359,6 +359,11 @@ def attention_fwd_maxlogit(Q, Kc, Kr, V, causal=False, O=None, lse=None, smax=No
         _dev(t, n)
     if Kr is not None:
         _dev(Kr, "Kr")
+    if Q.dim() != 4 or Kc.dim() != 4 or V.dim() != 4 or (Kr is not None and Kr.dim() != 3):
+        raise ValueError("Q, Kc, V must be 4-D [B, H, S, d] and Kr 3-D [B, Sk, d_r]")
+    # the kernel reads every operand in Q's element type
+    if any(t is not None and t.dtype != Q.dtype for t in (Kc, Kr, V)):
+        raise ValueError("Q, Kc, Kr and V must share a dtype")
     B, H, Sq, d = Q.shape
     Sk, d_c, d_v = Kc.shape[2], Kc.shape[3], V.shape[3]
     d_r = Kr.shape[2] if Kr is not None else 0
@@ -528,7 +533,7 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
         raise ValueError(f"workspace needs {need} bytes")
     O_buf = None
     if not fused:
-        o_elems = max(min(chunk, W3.shape[0]) * W3.shape[1] * W3.shape[2] for _, W3, _, _ in entries)
+        o_elems = max((min(chunk, W3.shape[0]) * W3.shape[1] * W3.shape[2] for _, W3, _, _ in entries), default=1)
         O_buf = _empty(o_elems, torch.float32, workspace.device, stream)
     for name, W3, M3, G3 in entries:
         count, rows, cols = W3.shape

@@ -554,8 +554,9 @@ def test_full_step_tiny_attention_from_oracle_smax(mc, reading):
         assert rel_fro(f64(W[n]) - Wn[n], new_w[n] - Wn[n]) <= 2e-2, n
 
 
-def test_binding_rejects_bad_outputs(mc):
-    """Caller-supplied outputs of the wrong size, dtype or device raise before
+def test_binding_rejects_bad_tensors(mc):
+    """Caller-supplied outputs of the wrong size, dtype or device, and inputs
+    whose dtype differs from the one the call reads them in, raise before
     anything is launched (the kernels write exactly the call's element count,
     so a smaller tensor would be overrun); inputs stay untouched."""
     say("binding output validation")
@@ -572,6 +573,10 @@ def test_binding_rejects_bad_outputs(mc):
         mc.attention_fwd_maxlogit(Q, Kc, Kr, V, O=torch.empty(1, 4, 64, 64, dtype=torch.bfloat16, device=DEV))
     with pytest.raises(ValueError):
         mc.attention_fwd_maxlogit(Q, Kc, Kr, V, lse=torch.empty(1, 4, 32, device=DEV))
+    with pytest.raises(ValueError):  # a one-byte key read as bf16 would run past its end
+        mc.attention_fwd_maxlogit(Q, Kc.to(torch.float8_e4m3fn), Kr, V)
+    with pytest.raises(ValueError):
+        mc.attention_fwd_maxlogit(Q, Kc, Kr, V.float())
     Wq = workloads.normal((4 * 6, 32), 0.02, g, "cpu", torch.bfloat16).to(DEV)
     Wk = workloads.normal((4 * 4, 32), 0.02, g, "cpu", torch.bfloat16).to(DEV)
     before = (Wq.clone(), Wk.clone())
