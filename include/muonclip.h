@@ -314,7 +314,9 @@ MC_API mc_status_t qk_maxlogit(const void* Q, const void* Kc, const void* Kr, in
  * product) and rounded once to bf16.
  * Supported: dtype MC_BF16 (else MC_EDTYPE); (d_c, d_r, d_v) = (128, 64, 128)
  * (Kimi K2's MLA head) or (64, 0, 64) (else MC_ESHAPE); Sk >= 64 unless the
- * call is empty; Q, Kc, Kr, V 16-byte aligned, O 8-byte aligned (MC_EALIGN).
+ * call is empty (B, H or Sq zero: then only smax_out is written, -inf unless
+ * accumulating, and the other pointers may be NULL); Q, Kc, Kr, V 16-byte
+ * aligned, O 8-byte aligned (MC_EALIGN).
  * Errors: MC_EINVAL, MC_ESHAPE, MC_EDTYPE, MC_EALIGN, MC_EHIP.
  */
 MC_API mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr, const void* V,

@@ -416,6 +416,11 @@ def qk_clip_apply_layers(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_hea
     Wq, Wk = list(Wq), list(Wk)
     if len(Wq) != L or len(Wk) != L:
         raise ValueError("Wq and Wk need one tensor per layer")
+    if L == 0:  # no layer: nothing to clip
+        gamma = _empty((0, H), torch.float32, smax.device, stream) if gamma is None else gamma
+        clipped = _empty((0, H), torch.int32, smax.device, stream) if clipped is None else clipped
+        return _out(gamma, "gamma", torch.float32, 0, smax.device), _out(clipped, "clipped", torch.int32, 0,
+                                                                          smax.device)
     for w in Wq + Wk:
         _dev(w, "W")
         if w.dtype != Wq[0].dtype:
@@ -527,12 +532,14 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
         entries.append((name, W3, M3, G3))
     need = max((muon_ns_workspace_bytes(min(chunk, W3.shape[0]), W3.shape[1], W3.shape[2])
                 for _, W3, _, _ in entries), default=0)
-    if workspace is None:
+    if not entries:
+        pass  # no Muon matrix: no workspace
+    elif workspace is None:
         workspace = _empty(max(need, 1), torch.uint8, next(iter(weights.values())).device, stream)
     elif workspace.numel() < need:
         raise ValueError(f"workspace needs {need} bytes")
     O_buf = None
-    if not fused:
+    if not fused and entries:
         o_elems = max((min(chunk, W3.shape[0]) * W3.shape[1] * W3.shape[2] for _, W3, _, _ in entries), default=1)
         O_buf = _empty(o_elems, torch.float32, workspace.device, stream)
     for name, W3, M3, G3 in entries:

@@ -369,18 +369,22 @@ mc_status_t attention_fwd_maxlogit(const void* Q, const void* Kc, const void* Kr
   if (!valid_dtype(dtype)) return MC_EDTYPE;
   if (dtype != MC_BF16) return MC_EDTYPE;
   if (!mc::attention_fwd_supported(d_c, d_r, d_v)) return MC_ESHAPE;
-  if (!Q || !Kc || !V || !O || !smax_out || (d_r > 0 && !Kr)) return MC_EINVAL;
   if (H > 65535 || Sq > INT32_MAX || Sk > INT32_MAX) return MC_ESHAPE;
   if (!count_ok({B, H, Sq, d_c + d_r}) || !count_ok({B, H, Sk, d_c + d_v}) || !count_ok({B, Sk, d_r}) ||
       !count_ok({B, H, Sq, d_v}))
     return MC_ESHAPE;
+  // an empty call (no batch, head or query row) reads and writes no tensor
+  // but S_max, so only smax_out has to point somewhere (and only for H > 0)
   const bool empty = B == 0 || H == 0 || Sq == 0;
+  if (H > 0 && !smax_out) return MC_EINVAL;
+  if (!empty && (!Q || !Kc || !V || !O || (d_r > 0 && !Kr))) return MC_EINVAL;
   if (!empty && Sk < 64) return MC_ESHAPE;
   if (causal && Sq > Sk) return MC_ESHAPE;
   if (B * H * ((Sq + 255) / 256) > kGridMax) return MC_ESHAPE;
   if (!aligned(Q, 16) || !aligned(Kc, 16) || (Kr && !aligned(Kr, 16)) || !aligned(V, 16) || !aligned(O, 8) ||
       !aligned(smax_out, 4) || (lse_out && !aligned(lse_out, 4)))
     return MC_EALIGN;
+  if (H == 0) return MC_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!accumulate) {
     hipError_t e = mc::launch_maxlogit_init(smax_out, H, s);

@@ -163,6 +163,36 @@ def test_maxlogit_validation(mc):
     assert L.qk_maxlogit(FAKE, FAKE, None, 1, 60000, 60000, 1 << 30, 8, 64, 0, FAKE, 0, None) == ESHAPE
 
 
+def test_attention_validation(mc):
+    L = mc.lib
+    # (Q, Kc, Kr, V, dtype, B, H, Sq, Sk, d_c, d_r, d_v, causal, O, lse, smax, accumulate, stream)
+    ok = (FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 256, 256, 128, 64, 128, 0, FAKE, None, FAKE, 0, None)
+
+    def call(**kw):
+        names = ["Q", "Kc", "Kr", "V", "dtype", "B", "H", "Sq", "Sk", "d_c", "d_r", "d_v", "causal", "O",
+                 "lse", "smax", "acc", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return L.attention_fwd_maxlogit(*[args[n] for n in names])
+
+    # no head: nothing is read or written, every pointer may be null
+    assert call(Q=None, Kc=None, Kr=None, V=None, O=None, smax=None, H=0) == 0
+    assert call(dtype=0) == EDTYPE                      # bf16 only
+    assert call(d_c=96) == ESHAPE                       # head dims (128, 64, 128) or (64, 0, 64)
+    assert call(Q=None) == EINVAL
+    assert call(V=None) == EINVAL
+    assert call(O=None) == EINVAL
+    assert call(Kr=None) == EINVAL                      # d_r > 0 needs the rotary keys
+    assert call(smax=None) == EINVAL
+    assert call(smax=None, Sq=0) == EINVAL              # an empty call still writes S_max
+    assert call(Sk=63) == ESHAPE                        # at least one key block
+    assert call(causal=1, Sq=300, Sk=256) == ESHAPE     # causal needs Sq <= Sk
+    assert call(B=-1) == EINVAL
+    assert call(Q=ctypes.c_void_p(0x100008)) == EALIGN  # 16-byte operands
+    assert call(O=ctypes.c_void_p(0x100004)) == EALIGN
+    assert call(B=1 << 20, H=60000, Sq=1 << 30) == ESHAPE  # element counts beyond any buffer
+
+
 @pytest.mark.parametrize("fn", ["qk_clip_apply", "qk_clip_apply_total"])
 def test_clip_validation(mc, fn):
     f = getattr(mc.lib, fn)
