@@ -199,3 +199,17 @@ def spectral_momentum(kind, rows, cols, seed=0, std=1e-3, device="cpu"):
         raise ValueError(f"unknown spectrum kind {kind!r}")
     M = M * (std / M.std())
     return M.to(torch.float32).to(device)
+
+
+def orthonormal_factors(rows, cols, sigma, seed=0):
+    """Exact SVD factors of a rank-r matrix M = U diag(sigma) V^T: U (rows x r)
+    and V (cols x r) with orthonormal columns (QR of Gaussian matrices drawn
+    from `seed`, float64 on the CPU) and the given singular values.  The
+    matrix itself is formed wherever it is needed (e.g. on the device for the
+    largest shapes), so its SVD is known without computing one."""
+    g = generator(seed, "cpu")
+    sigma = torch.as_tensor(sigma, dtype=torch.float64)
+    r = sigma.numel()
+    U, _ = torch.linalg.qr(torch.randn(rows, r, generator=g, dtype=torch.float64))
+    V, _ = torch.linalg.qr(torch.randn(cols, r, generator=g, dtype=torch.float64))
+    return U, sigma, V
