@@ -8,10 +8,12 @@ Workload (synthetic, seeded, resident in HBM before timing):
     (4 random heads x6 so they exceed tau);
   * Q / K of 8 x 4096 tokens through those projections (64 heads, 128 + 64
     head dim), computed before timing: the max logit is measured on them.
-One step = every row of the path, on one stream:
-  momentum (all matrices, one launch) -> per shape group and chunk of 64
-  matrices: Newton-Schulz x 5 with the Muon scale, decoupled-decay update ->
-  per-head max logit -> QK-Clip of W_q / W_kc.
+One step = every row of the path, on one stream, in a training step's order:
+  per-head max logit on the forward's Q / K -> per shape group and chunk of
+  64 matrices, one fused call: momentum, Newton-Schulz x 5 with the Muon
+  scale, decoupled-decay update (--unfused: momentum over all matrices in one
+  launch, then Newton-Schulz and the update as separate calls) -> QK-Clip of
+  W_q / W_kc with that S_max.
 
 Prints one JSON line on stdout (progress goes to stderr).  `value` is the
 step's MFMA work divided by the step time, counting what the method needs:
