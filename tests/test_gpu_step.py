@@ -149,3 +149,45 @@ def test_step_chunks_share_one_workspace(mc):
         assert rel_fro(f64(Wc["e"][i]) - f64(W0[i]), f64(Wa["e"][i]) - f64(W0[i])) <= 2e-2
     with pytest.raises(ValueError):
         mc.muonclip_step(Wa, {"e": G.to(DEV), "q": Wq, "k": Wq}, {}, smax, att, lr=1.0, chunk=4, workspace=ws)
+
+
+def test_resume_from_saved_state_is_bit_exact(mc):
+    """The optimizer state is W and the momentum M (M_0 = 0; the method keeps
+    nothing else).  Two steps run straight through, and the same second step
+    run again on fresh tensors restored from a host copy of (W, M) taken after
+    the first, give bit-identical W, M, gamma and clip flags: the step is
+    deterministic (the max reductions are exact and order-free), so resuming
+    from a checkpoint of (W, M) reproduces the run."""
+    say("resume from (W, M)")
+    H, hd, d = 4, 64, 256
+    g = workloads.generator(402, "cpu")
+    W = {"q": workloads.normal((H * hd, d), 0.02, g, "cpu", torch.bfloat16),
+         "k": workloads.normal((H * hd, d), 0.02, g, "cpu", torch.bfloat16),
+         "experts": workloads.normal((3, 256, 384), 0.02, g, "cpu", torch.bfloat16),
+         "down": workloads.normal((2, 384, 256), 0.02, g, "cpu", torch.bfloat16)}
+    grads = [{n: workloads.normal(w.shape, 1e-3, g, "cpu") for n, w in W.items()} for _ in range(2)]
+    smaxes = [torch.tensor([150.0, 20.0, 300.0, 99.0]), torch.tensor([101.0, 180.0, 5.0, 250.0])]
+    att = dict(q="q", k="k", q_rows_per_head=hd, q_c_rows=hd, k_rows_per_head=hd)
+
+    def step(Wd, Md, t):
+        Gd = {n: x.to(DEV) for n, x in grads[t].items()}
+        return mc.muonclip_step(Wd, Gd, Md, smaxes[t].to(DEV), att, lr=2e-3, weight_decay=0.1, chunk=2)
+
+    Wd = {n: w.to(DEV) for n, w in W.items()}
+    Md = {}
+    step(Wd, Md, 0)
+    torch.cuda.synchronize()
+    ckpt_w = {n: w.cpu().clone() for n, w in Wd.items()}
+    ckpt_m = {n: m.cpu().clone() for n, m in Md.items()}
+    gamma1, clipped1 = step(Wd, Md, 1)
+    torch.cuda.synchronize()
+
+    Wr = {n: w.to(DEV) for n, w in ckpt_w.items()}
+    Mr = {n: m.to(DEV) for n, m in ckpt_m.items()}
+    gamma2, clipped2 = step(Wr, Mr, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(gamma1, gamma2) and torch.equal(clipped1, clipped2)
+    assert clipped1.cpu().tolist() == [1, 1, 0, 1]
+    for n in W:
+        assert torch.equal(Wd[n].view(torch.int16), Wr[n].view(torch.int16)), n
+        assert torch.equal(Md[n].view(torch.int32), Mr[n].view(torch.int32)), n
