@@ -621,11 +621,15 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     u32x4 xhv[kRing];
     u32x2 xlv[kRing];
     float dgr[8];
+    // Non-temporal loads: each X element is read here once, and at the
+    // default cache policy these 196 KB per tile evict from the XCD's L2 the
+    // operand panels that the other tiles' K loops share (measured: the
+    // launch 1.2-1.4 % faster, results bit-identical).
     auto load_x = [&](int sq) {
       const int64_t off = x_off(i0 + (sq & 7) * 32 + rsub, j0 + 128 * (sq >> 3) + 8 * cg, n_pad);
       if (MC_GUARD(5, off + 8 <= nm)) {
-        xhv[sq % kRing] = *reinterpret_cast<const u32x4*>(Xh + off);
-        xlv[sq % kRing] = *reinterpret_cast<const u32x2*>(Xlm + off);
+        xhv[sq % kRing] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Xh + off));
+        xlv[sq % kRing] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(Xlm + off));
       } else {
         xhv[sq % kRing] = u32x4{0u, 0u, 0u, 0u};
         xlv[sq % kRing] = u32x2{0u, 0u};
