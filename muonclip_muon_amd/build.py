@@ -1,6 +1,6 @@
 """Build libmuonclip.so in-tree with hipcc for gfx950.
 
-    python muonclip_muon_amd/build.py          # release and debug libraries
+    python muonclip_muon_amd/build.py          # release and debug libraries, C client
     python muonclip_muon_amd/build.py release  # or debug: one of them
 
 (Run as a script, not with -m: importing the package loads the library.)
@@ -129,8 +129,27 @@ def build(verbose=False, debug=False):
     return lib
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "step_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_client", "step_client")
+
+
+def build_c_client():
+    """The plain C client of the C ABI (tests/c_client/step_client.c; host
+    code only, gcc), linked against the release library in this package."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), "-D__HIP_PLATFORM_AMD__", C_CLIENT_SRC, "-L", PKG, "-lmuonclip",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../muonclip_muon_amd",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", C_CLIENT]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C client build failed:\n{r.stdout}{r.stderr}")
+    return C_CLIENT
+
+
 def build_all(verbose=False):
-    return [build(verbose), build(verbose, debug=True)]
+    libs = [build(verbose), build(verbose, debug=True)]
+    return libs + [build_c_client()]
 
 
 if __name__ == "__main__":
