@@ -34,8 +34,10 @@ def _sample(n, k, seed):
 
 def test_expert_batch_momentum_ns_update(mc):
     """64 expert matrices 2048 x 7168: momentum over the batch (sampled elements
-    bit-exact), Newton-Schulz x5 with the Muon scale in one 64-matrix call
-    (two whole matrices against the oracle), and the update (sampled)."""
+    bit-exact), Newton-Schulz x5 with the Muon scale in one 64-matrix call on
+    the new momentum (two whole matrices against the oracle's own momentum
+    and Newton-Schulz of the same inputs), and the update with a seeded O
+    (sampled)."""
     say("full size: 64 x 2048 x 7168 momentum + NS + update")
     batch, rows, cols = 64, 2048, 7168
     eb = workloads.expert_batch(seed=2, device=DEV, batch=batch, rows=rows, cols=cols, std=1e-3)
@@ -44,6 +46,9 @@ def test_expert_batch_momentum_ns_update(mc):
     idx_t = torch.from_numpy(idx).to(DEV)
     m0 = M.view(-1)[idx_t].cpu().numpy()
     g0 = G.view(-1)[idx_t].cpu().numpy()
+    picks = (0, 37)
+    m_in = {b: M[b].cpu().numpy() for b in picks}
+    g_in = {b: G[b].cpu().numpy() for b in picks}
     mc.muonclip_momentum(M, G, 0.95)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(M.view(-1)[idx_t].cpu().numpy(), oracle.momentum_update(m0, g0, 0.95))
@@ -52,13 +57,16 @@ def test_expert_batch_momentum_ns_update(mc):
     scale = mc.muon_out_scale(rows, cols)
     O = mc.muon_ns_orthogonalize_batched(M, out_scale=scale, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    for b in (0, 37):
-        say("  oracle NS of matrix", b)
-        ref = oracle.muon_orthogonalised_update(f64(M[b]))
+    for b in picks:
+        say("  oracle momentum and NS of matrix", b)
+        ref = oracle.muon_orthogonalised_update(oracle.momentum_update(m_in[b], g_in[b], 0.95).astype(np.float64))
         err = rel_fro(f64(O[b]), ref)
         assert err <= 2e-2, (b, err)
+    del O
 
-    W = workloads.normal((batch, rows, cols), 0.02, workloads.generator(9, DEV), DEV, torch.bfloat16)
+    gen = workloads.generator(9, DEV)
+    W = workloads.normal((batch, rows, cols), 0.02, gen, DEV, torch.bfloat16)
+    O = workloads.normal((batch, rows, cols), 0.2, gen, DEV, torch.bfloat16)
     w0 = W.view(-1)[idx_t].clone()
     o0 = O.view(-1)[idx_t].clone()
     mc.muon_apply_update(W, O, 2e-4, 0.1)
@@ -119,7 +127,9 @@ def test_maxlogit_and_clip_8x4096(mc):
     for h in range(64):
         qs, ks = slice(192 * h, 192 * h + 192), slice(128 * h, 128 * h + 128)
         if h in gpu_set:
-            rq, rk, _, _ = oracle.qk_clip(np.array([float(s[h])]), f64(Wq0[qs]), f64(Wkc0[ks]), 192, 128, 128)
+            # the oracle's clip from its own S_max (within 1e-4 of the library's,
+            # far inside one bf16 ulp of the scaled rows)
+            rq, rk, _, _ = oracle.qk_clip(np.array([ref[h]]), f64(Wq0[qs]), f64(Wkc0[ks]), 192, 128, 128)
             assert bf16_ulp_diff(bf16_bits(Wq[qs]), oracle.bf16_bits(rq)).max() <= 1
             assert bf16_ulp_diff(bf16_bits(Wkc[ks]), oracle.bf16_bits(rk)).max() <= 1
         else:

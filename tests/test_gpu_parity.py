@@ -495,7 +495,9 @@ def test_full_step_tiny_attention(mc, reading):
     Xd = t.X.to(DEV)
     W = {n: w.to(DEV) for n, w in t.W.items()}
     G = {n: g_.to(DEV) for n, g_ in t.G.items()}
-    # forward at W_{t-1}: Q, K per head (harness projection), S_max from the library
+    # forward at W_{t-1}: Q, K per head (harness projection on the device, an
+    # input of both sides); S_max from the library for the library's step and
+    # the oracle's own S_max of the same Q, K for the oracle's
     Qd = (Xd @ W["q"].t().contiguous()).view(2, 128, H, hd).transpose(1, 2).contiguous()
     Kd = (Xd @ W["k"].t().contiguous()).view(2, 128, H, hd).transpose(1, 2).contiguous()
     smax = mc.qk_maxlogit(Qd, Kd)
@@ -506,7 +508,7 @@ def test_full_step_tiny_attention(mc, reading):
     torch.cuda.synchronize()
     new_w, _, rg, rc = oracle.muonclip_step({n: f64(w) for n, w in t.W.items()},
                                             {n: g_.numpy() for n, g_ in t.G.items()}, {},
-                                            f64(smax), att, lr=0.02, w_dtype="f32")
+                                            ref_s, att, lr=0.02, w_dtype="f32")
     assert clipped.cpu().tolist() == rc.tolist()
     if reading == "variance":
         assert rc[0] == 1  # head 0 is clipped in this reading
