@@ -571,12 +571,16 @@ def cpu_baseline(wl, torch, n_matrices=6):
     import numpy as np
 
     import oracle
+    import workloads
     host = host_info()
+    # seeded inputs of the workload's shapes and distributions, drawn on the
+    # host (not the buffers the library has already stepped)
+    gen = workloads.generator(77, "cpu")
     data = []
     for k in range(n_matrices):
-        grp = "expert_gate_up" if k % 2 == 0 else "expert_down"
-        m, g, w = (wl.view(grp, buf, k // 2, 1)[0] for buf in (wl.M, wl.G, wl.W))
-        data.append((m.cpu().numpy(), g.cpu().numpy(), w.float().cpu().numpy().astype(np.float64)))
+        shape = (D_EXPERT, D_MODEL) if k % 2 == 0 else (D_MODEL, D_EXPERT)
+        data.append((workloads.normal(shape, 1e-4, gen, "cpu").numpy(), workloads.normal(shape, 1e-4, gen, "cpu").numpy(),
+                     workloads.normal(shape, 0.02, gen, "cpu", torch.bfloat16).double().numpy()))
     heads = [int(wl.hot[0]), (int(wl.hot[0]) + 1) % N_HEADS]
     Qh = [wl.Q[:, h:h + 1].float().cpu().numpy() for h in heads]
     Kch = [wl.Kc[:, h:h + 1].float().cpu().numpy() for h in heads]
