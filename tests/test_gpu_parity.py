@@ -366,6 +366,23 @@ def test_newton_schulz_few_steps(mc, case):
         assert rel_fro(f64(O[b]), ref) <= 2e-2, b
 
 
+@pytest.mark.parametrize("rows,cols", [(384, 640), (700, 260)])
+def test_newton_schulz_cubic_ten_steps(mc, rows, cols):
+    """Another polynomial through the same kernels: the textbook cubic
+    p(x) = 1.5 x - 0.5 x^3 (c = 0, so B = b A) for 10 steps, against the
+    oracle with the same coefficients."""
+    say("newton-schulz cubic x10", rows, cols)
+    g = workloads.generator(70 + rows, "cpu")
+    M = workloads.normal((2, rows, cols), 1e-3, g, "cpu")
+    coeffs = ((1.5, -0.5, 0.0),) * 10
+    O = mc.muon_ns_orthogonalize_batched(M.to(DEV), steps=10, coeffs=coeffs, out_scale=1.0,
+                                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(2):
+        ref = oracle.newton_schulz(f64(M[b]), coeffs=coeffs)
+        assert rel_fro(f64(O[b]), ref) <= 2e-2, b
+
+
 def test_newton_schulz_output_over_input(mc):
     """O may be M's own buffer (same dtype and strides): M is read only by the
     pre-scale, before the last step writes O."""
