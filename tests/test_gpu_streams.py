@@ -93,3 +93,54 @@ def test_page_step_on_side_stream(mc):
     torch.cuda.synchronize()
     assert torch.equal(mom["experts"], mom_ref["experts"])
     assert torch.equal(W["experts"], W_ref["experts"])
+
+
+def test_concurrent_host_threads(mc):
+    """Two host threads drive the library at once, each on its own stream with
+    its own inputs, workspace and outputs (the C calls run without the GIL,
+    so argument checking and launching overlap): every result is bit-identical
+    to the same call made alone, since the library keeps no mutable state
+    between calls (the allocation-free entry point's shared scratch aside)."""
+    import threading
+    say("two host threads")
+    g = workloads.generator(93, "cpu")
+    jobs = []
+    for t in range(2):
+        M = workloads.normal((2, 512, 1536), 1e-3, g, "cpu").to(DEV)
+        G = workloads.normal((2, 512, 1536), 1e-3, g, "cpu").to(DEV)
+        W = workloads.normal((2, 512, 1536), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+        ws = torch.empty(mc.muon_ns_workspace_bytes(2, 512, 1536), dtype=torch.uint8, device=DEV)
+        jobs.append(dict(M=M, G=G, W=W, ws=ws, stream=torch.cuda.Stream()))
+    # alone, one after the other: three fused steps each
+    ref = []
+    for j in jobs:
+        M, W = j["M"].clone(), j["W"].clone()
+        for _ in range(3):
+            mc.muon_momentum_ns_update_batched(M, j["G"], W, 2e-3, workspace=j["ws"])
+        torch.cuda.synchronize()
+        ref.append((M, W))
+    # at once, from two threads
+    outs = [None, None]
+    errors = []
+
+    def run(k):
+        try:
+            j = jobs[k]
+            M, W = j["M"].clone(), j["W"].clone()
+            torch.cuda.synchronize()
+            for _ in range(3):
+                mc.muon_momentum_ns_update_batched(M, j["G"], W, 2e-3, workspace=j["ws"], stream=j["stream"])
+            j["stream"].synchronize()
+            outs[k] = (M, W)
+        except Exception as e:  # noqa: BLE001  (reported below)
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    for (M, W), (Mr, Wr) in zip(outs, ref):
+        assert torch.equal(M.view(torch.int32), Mr.view(torch.int32))
+        assert torch.equal(W.view(torch.int16), Wr.view(torch.int16))
