@@ -206,7 +206,13 @@ def _coeffs(steps, coeffs):
     return (ctypes.c_float * len(flat))(*flat)
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _workspace(workspace, batch, rows, cols, device, stream):
+    """The call's workspace: the caller's (any dtype; its size in bytes is what
+    counts), or a new uint8 tensor of the size the library asks for."""
     need = lib.muon_ns_workspace_bytes(batch, rows, cols)
     if workspace is None:
         workspace = _empty(max(need, 1), torch.uint8, device, stream)
@@ -252,7 +258,7 @@ def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS
     ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_ns_orthogonalize_batched(
         M.data_ptr(), _dtype(M, "M"), batch, rows, cols, rows * cols, O.data_ptr(), _dtype(O, "O"),
-        rows * cols, steps, c_coeffs, eps, out_scale, workspace.data_ptr(), workspace.numel(),
+        rows * cols, steps, c_coeffs, eps, out_scale, workspace.data_ptr(), _nbytes(workspace),
         _stream(M, stream), ev)
     _check("muon_ns_orthogonalize_batched", status)
     return O
@@ -292,7 +298,7 @@ def muon_momentum_ns_update_batched(M, G, W, lr, weight_decay=0.1, mu=0.95, step
     ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_momentum_ns_update_batched(
         M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
-        c_coeffs, eps, out_scale, lr, weight_decay, workspace.data_ptr(), workspace.numel(), _stream(M, stream), ev)
+        c_coeffs, eps, out_scale, lr, weight_decay, workspace.data_ptr(), _nbytes(workspace), _stream(M, stream), ev)
     _check("muon_momentum_ns_update_batched", status)
     return W
 
@@ -536,7 +542,7 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
         pass  # no Muon matrix: no workspace
     elif workspace is None:
         workspace = _empty(max(need, 1), torch.uint8, next(iter(weights.values())).device, stream)
-    elif workspace.numel() < need:
+    elif _nbytes(workspace) < need:
         raise ValueError(f"workspace needs {need} bytes")
     O_buf = None
     if not fused and entries:
