@@ -350,6 +350,10 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // X' = B'X runs fastest with 4 stages, the symmetric products with 5
   constexpr int kStages = MODE == 2 ? 4 : kMaxStages;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+  // The epilogue reuses the stages' LDS: four 32 KB regions of the bf16
+  // tile, half of it in float32 (the row-ordered epilogue), or X's parts for
+  // the transposed update (96 KB).  Fewer stages would silently drop writes.
+  static_assert(kStages * kStageBytes >= 4 * 32768, "the epilogue stages 128 KB in the stages' LDS");
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_t*)smem));
 
