@@ -124,12 +124,16 @@ __device__ __forceinline__ bool mc_guard(bool ok, unsigned int tag) {
 #define MC_DEBUG_UNIT(name)
 #endif
 
-// Layout of the Newton-Schulz state X (n_pad x m_pad bf16) in the workspace:
-// column panels of 256, each n_pad x 256 row-major, so a 32 x 256 K-rows tile
-// (the right operand of B' X) is one contiguous 16 KB run and a row panel of
-// X X^T reads 64-byte runs at a 512-byte pitch.  Element offset of (r, c):
+// Layout of the Newton-Schulz state X (n_pad x m_pad bf16; its low-part
+// codes likewise, one byte per element) in the workspace: column panels of
+// 32, each n_pad x 32 row-major (64-byte rows).  A K-step tile of X X^T (256
+// rows x 32 columns) is then one contiguous 16 KB run, and a K-rows tile of
+// B' X (32 rows x 256 columns) eight contiguous 2 KB runs, so every LDS DMA
+// instruction reads 1 KB in one piece.  (Panels of 256 columns, whose rows
+// are 512 bytes, made X X^T read 64-byte pieces at a 512-byte pitch: 6-8 %
+// slower.)  Element offset of (r, c):
 __host__ __device__ __forceinline__ int64_t x_off(int64_t r, int64_t c, int64_t n_pad) {
-  return (c >> 8) * n_pad * 256 + r * 256 + (c & 255);
+  return (c >> 5) * n_pad * 32 + r * 32 + (c & 31);
 }
 
 // Blocks of one launch are distributed round-robin over the 8 XCDs of an

@@ -51,16 +51,17 @@
 // Operand tiles.  The left tile is always K-contiguous in LDS: row r (an
 // output index) holds 32 consecutive k as 4 units of 16 bytes, unit u at
 // u ^ swizzle(r), read with ds_read_b128.  It comes from
-//  * X itself for X X^T (row panels of X, 16 rows x 64 bytes per DMA
-//    instruction), or
+//  * X itself for X X^T (X is stored in panels of 32 columns, so the tile of
+//    a K-step is one contiguous 16 KB run of a panel), or
 //  * A or B' for the other two products, which this file stores in a blocked
 //    layout (256 x 32 blocks, row-major inside): a K-contiguous 256 x 32 tile
 //    of A or B' is one contiguous 16 KB block.  A and B' are symmetric, so
 //    their row panels are the column panels the products need.
 // The right tile is the same kind of tile for X X^T and A A; for B' X it is a
 // "K-rows" tile of X (row-major with K as its row index): 32 k-rows x 256
-// output indices, 2 rows x 512 bytes per DMA instruction, unit u of row r at
-// u ^ 4 (r & 3), and fragments come from ds_read_b64_tr_b16, which hands
+// output indices, the same 32 rows of eight panels (16 rows x 64 bytes, one
+// contiguous 1 KB run, per DMA instruction), and fragments come from
+// ds_read_b64_tr_b16, which hands
 // each lane 4 consecutive k of one column (measured on gfx950: within each
 // 16-lane group, lane i receives element i % 4 of the 4 x 16-bit values
 // addressed by lanes i / 4 + 4 e, e = 0..3); two of them make one 8-k MFMA
@@ -107,10 +108,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // bank groups per 256 bytes.
 __device__ __forceinline__ int swizzle(int r) { return (r >> 2) & 3; }
 
-// K-rows tile: unit u of k-row r sits at u ^ xswz(r).  A transposed read
-// touches rows r..r+3 (and r+8..r+11) in one 64-byte column segment; the XOR
-// moves the four rows to four different 64-byte bank slots.
-__device__ __forceinline__ int xswz(int r) { return 4 * (r & 3); }
 
 // One global_load_lds_dwordx4: 16 bytes from g_uniform + lane_off to LDS
 // address m0 + 16 * lane.  Written as inline asm so the compiler's waitcnt
@@ -141,62 +138,64 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Per-lane byte offsets of the tile loads.  The swizzle of a lane's row does
-// not depend on which 1 KB block it fills, so each lane has one offset per
-// tile and every load is "uniform base + lane offset" (SGPR-base addressing).
-// Wave w fills the 1 KB blocks b = w + 8 jj.
+// Per-lane byte offsets of the tile loads.  A tile is 16 pieces of 1 KB;
+// wave w fills pieces c = w + 8 jj (LDS offset 1024 c, lane l at + 16 l).
+// The swizzle of a lane's row does not depend on jj, so each lane has one
+// offset per tile and every load is "uniform base + jj * stride + lane
+// offset" (SGPR-base addressing).
 //
-// K-contiguous 256 x 32 tile: block b is rows 16 b .. 16 b + 15; lane l takes
-// row 16 b + l / 4, slot l % 4, and swizzle(row) = (l / 16) & 3 for every jj.
+// K-contiguous 256 x 32 tile (row pitch ld elements): piece c is rows
+// 16 c .. 16 c + 15; lane l takes row 16 c + l / 4, slot l % 4, and
+// swizzle(row) = (l / 16) & 3 for every jj; the stride is 128 rows.
 __device__ __forceinline__ uint32_t kc_lane_offset(int64_t ld, int wave, int lane) {
   const int r = 16 * wave + (lane >> 2);
   const int u = (lane & 3) ^ ((lane >> 4) & 3);
   return static_cast<uint32_t>((r * ld + 8 * u) * 2);
 }
-// K-rows 32 x 256 tile: block b is k-rows 2 b, 2 b + 1; lane l takes row
-// 2 b + l / 32, slot l % 32, and xswz(row) = 4 ((2 w + l / 32) & 3) for
-// every jj (b = w + 8 jj).
-__device__ __forceinline__ uint32_t kr_lane_offset(int64_t ld, int wave, int lane) {
-  const int r = 2 * wave + (lane >> 5);
-  const int u = (lane & 31) ^ xswz(r);
-  return static_cast<uint32_t>((r * ld + 8 * u) * 2);
+// K-rows 32 x 256 tile of X (panels of 32 columns, x_off): piece c is rows
+// 16 (c & 1) .. + 15 of the tile's panel c / 2, one contiguous 1 KB run;
+// wave w's pieces are panels w / 2 + 4 jj (the stride is 4 panels), lane l
+// takes row 16 (w & 1) + l / 4, 16-byte unit l % 4.  In LDS, panel b then
+// sits at 2 KB b with 64-byte rows (no swizzle: the four rows a transposed
+// read touches fill four different 64-byte bank slots by themselves).
+__device__ __forceinline__ uint32_t kr_lane_offset(int64_t n_pad, int wave, int lane) {
+  const int r = 16 * (wave & 1) + (lane >> 2);
+  return static_cast<uint32_t>(((wave >> 1) * n_pad * 32 + r * 32 + 8 * (lane & 3)) * 2);
 }
 
-// Issue one operand tile: K-contiguous (row 0, column k0 at g; block rows
-// advance by 64 per jj) or K-rows (k-row 0, column 0 at g; 8 rows per jj).
-// `end` is one past the operand's last byte (checked in debug builds only).
-template <bool KROWS>
-__device__ __forceinline__ void issue_tile(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
+// Issue one operand tile (its pieces at g + jj * stride bytes + the lane
+// offsets); `end` is one past the operand's last byte (checked in debug
+// builds only).
+__device__ __forceinline__ void issue_tile(const uint16_t* g, int64_t stride, uint32_t lane_off, uint32_t lds,
                                            int wave, const char* end) {
   const char* base = reinterpret_cast<const char*>(g);
-  constexpr int kRowsPerJ = KROWS ? 2 * kWaves : 16 * kWaves;
 #pragma unroll
   for (int jj = 0; jj < kLoadsPerTile; ++jj) {
-    const char* src = base + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2;
+    const char* src = base + jj * stride;
     if (MC_GUARD(0, src + lane_off + 16 <= end)) load_lds16(src, lane_off, lds + 1024 * (wave + kWaves * jj));
   }
 }
 
 // One of the kLoadsPerTile DMA instructions of an operand tile.
-template <bool KROWS>
-__device__ __forceinline__ void issue_tile_part(const uint16_t* g, int64_t ld, uint32_t lane_off, uint32_t lds,
+__device__ __forceinline__ void issue_tile_part(const uint16_t* g, int64_t stride, uint32_t lane_off, uint32_t lds,
                                                 int wave, int jj, const char* end) {
-  constexpr int kRowsPerJ = KROWS ? 2 * kWaves : 16 * kWaves;
-  const char* src = reinterpret_cast<const char*>(g) + static_cast<int64_t>(kRowsPerJ * jj) * ld * 2;
+  const char* src = reinterpret_cast<const char*>(g) + jj * stride;
   if (MC_GUARD(0, src + lane_off + 16 <= end)) load_lds16(src, lane_off, lds + 1024 * (wave + kWaves * jj));
 }
 
 // K-rows tiles: per-lane LDS read address (relative to a stage) of the
 // fragment of 32-column MFMA tile x of an operand tile at tile_off, for
-// k-rows 0..7; the k sub-step (+8 KB), the upper four k (+2 KB) and the stage
-// are uniform offsets.  Lane l (16-lane group g = l / 16, i = l % 16)
-// addresses k-row 8 (g / 2) + i / 4 and columns
-// col_base + 32 x + 16 (g & 1) + 4 (i & 3) .. + 3.
+// k-rows 0..3; the upper four k (+256 bytes), the k sub-step (+1 KB) and
+// the stage are uniform offsets.  Lane l (16-lane group g = l / 16,
+// i = l % 16) addresses k-row 8 (g / 2) + i / 4 and columns
+// col_base + 32 x + 16 (g & 1) + 4 (i & 3) .. + 3 (panel
+// (col_base + 32 x) / 32; col_base is a multiple of 32).
+constexpr int kTrHi = 4 * 64, kTrSubstep = 16 * 64;
 __device__ __forceinline__ uint32_t tr_addr(int tile_off, int col_base, int x, int lane) {
   const int g = lane >> 4, i = lane & 15;
   const int r = 8 * (g >> 1) + (i >> 2);
-  const int col = col_base + 32 * x + 16 * (g & 1) + 4 * (i & 3);
-  return tile_off + r * 512 + (((col >> 3) ^ xswz(r)) << 4) + (col & 7) * 2;
+  const int panel = (col_base + 32 * x) >> 5;
+  return tile_off + panel * 2048 + r * 64 + (16 * (g & 1) + 4 * (i & 3)) * 2;
 }
 
 // Per-lane LDS read addresses relative to a stage; everything else that
@@ -238,7 +237,7 @@ struct Frags {
 
 __device__ __forceinline__ bf16x8 tr_frag(uint32_t addr) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(addr));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(addr + 2048));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(addr + kTrHi));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
   return as_bf16x8(v);
@@ -251,7 +250,7 @@ __device__ __forceinline__ void load_frags(const FragAddr& fadr, uint32_t stage_
   for (int y = 0; y < 4; ++y) f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(pb + y * 2048));
   if constexpr (Q_KROWS) {
 #pragma unroll
-    for (int x = 0; x < kCT; ++x) f.a[x] = tr_frag(stage_base + fadr.q[x] + ks * 8192);
+    for (int x = 0; x < kCT; ++x) f.a[x] = tr_frag(stage_base + fadr.q[x] + ks * kTrSubstep);
   } else {
     const uint32_t qb = stage_base + fadr.q[ks];
 #pragma unroll
@@ -267,7 +266,7 @@ __device__ __forceinline__ void load_frags_part(const FragAddr& fadr, uint32_t s
 #pragma unroll
   for (int y = 2 * g; y < 2 * g + 2; ++y)
     f.b[y] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.p[ks] + y * 2048));
-  if constexpr (Q_KROWS) f.a[g] = tr_frag(stage_base + fadr.q[g] + ks * 8192);
+  if constexpr (Q_KROWS) f.a[g] = tr_frag(stage_base + fadr.q[g] + ks * kTrSubstep);
   else f.a[g] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)(stage_base + fadr.q[ks] + g * 2048));
 }
 
@@ -380,37 +379,43 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 
   const int64_t nn = static_cast<int64_t>(n_pad) * n_pad, nm = static_cast<int64_t>(n_pad) * m_pad;
   const int nkb = n_pad / kBK;  // k-blocks per row of the blocked layout
-  // Operand tiles at k = 0, their row pitch and the step between K-steps
-  // (X in the column-panel layout, see x_off; A and B' blocked).
-  //   mode 0: rows i0.. and j0.. of X, K-contiguous: 64-byte runs at the
-  //           panel's 512-byte pitch; a new panel every 8 K-steps
+  // Operand tiles at k = 0, their row pitch (K-contiguous tiles), the byte
+  // stride between a wave's two DMA pieces and the element step between
+  // K-steps (X in panels of 32 columns, see x_off; A and B' blocked).
+  //   mode 0: rows i0.. and j0.. of X, K-contiguous: K-step kt is panel kt,
+  //           one contiguous 16 KB run
   //   mode 1: blocks of A at rows i0.. and j0.. (pitch 32, step one block)
   //   mode 2: blocks of B' at rows i0.. (symmetric: rows are columns), and
-  //           k-rows of X in panel j0 / 256: one contiguous 16 KB run per step
-  const int64_t panel = static_cast<int64_t>(n_pad) * 256;
+  //           k-rows 32 kt.. of X's panels j0 / 32 .. j0 / 32 + 7: eight
+  //           contiguous 2 KB runs
+  const int64_t panel = static_cast<int64_t>(n_pad) * 32;
   const uint16_t* Pg;
   const uint16_t* Qg;
-  int64_t ldp, ldq, kstep_p, kstep_q;
+  int64_t ldp, ldq, kstep_p, kstep_q, jstride_p, jstride_q;
   int K;
   if constexpr (MODE == 0) {
-    Pg = in0 + mat * nm + static_cast<int64_t>(i0) * 256;
-    Qg = in0 + mat * nm + static_cast<int64_t>(j0) * 256;
-    ldp = ldq = 256;
-    kstep_p = kstep_q = 0;  // see k_ofs
+    Pg = in0 + mat * nm + static_cast<int64_t>(i0) * 32;
+    Qg = in0 + mat * nm + static_cast<int64_t>(j0) * 32;
+    ldp = ldq = 32;
+    kstep_p = kstep_q = panel;
+    jstride_p = jstride_q = 128 * 32 * 2;
     K = m_pad;
   } else if constexpr (MODE == 1) {
     Pg = in0 + mat * nn + blk_off(i0, 0, nkb);
     Qg = in0 + mat * nn + blk_off(j0, 0, nkb);
     ldp = ldq = kBK;
     kstep_p = kstep_q = kBM * kBK;
+    jstride_p = jstride_q = 128 * kBK * 2;
     K = n_pad;
   } else {
     Pg = in0 + mat * nn + blk_off(i0, 0, nkb);
-    Qg = in1 + mat * nm + tj * panel;
+    Qg = in1 + mat * nm + x_off(0, j0, n_pad);
     ldp = kBK;
     kstep_p = kBM * kBK;
-    ldq = 256;
-    kstep_q = kBK * 256;
+    jstride_p = 128 * kBK * 2;
+    ldq = n_pad;  // kr_lane_offset takes the panel height
+    kstep_q = kBK * 32;
+    jstride_q = 4 * panel * 2;
     K = n_pad;
   }
   // one past each operand (range checks of debug builds): in0 holds X (mode
@@ -419,14 +424,7 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   const char* const end_p = reinterpret_cast<const char*>(in0 + nmat * (MODE == 0 ? nm : nn));
   const char* const end_q = MODE == 2 ? reinterpret_cast<const char*>(in1 + nmat * nm) : end_p;
   // element offset of K-step kt from the operand origin
-  auto k_ofs = [&](int kt, int64_t kstep) -> int64_t {
-    if constexpr (MODE == 0) {
-      const int k0 = kt * kBK;
-      return (k0 >> 8) * panel + (k0 & 255);
-    } else {
-      return kt * kstep;
-    }
-  };
+  auto k_ofs = [&](int kt, int64_t kstep) -> int64_t { return kt * kstep; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -440,11 +438,11 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // in-bounds tile is fetched again into a stage nobody reads, which keeps
   // the number of loads in flight (and so the wait counts) fixed.
   auto issue_p = [&](int kt) {
-    issue_tile<false>(Pg + k_ofs(min(kt, KT - 1), kstep_p), ldp, off_p, lds + (kt % kStages) * kStageBytes, wave,
+    issue_tile(Pg + k_ofs(min(kt, KT - 1), kstep_p), jstride_p, off_p, lds + (kt % kStages) * kStageBytes, wave,
                       end_p);
   };
   auto issue_q = [&](int kt) {
-    issue_tile<kQKRows>(Qg + k_ofs(min(kt, KT - 1), kstep_q), ldq, off_q,
+    issue_tile(Qg + k_ofs(min(kt, KT - 1), kstep_q), jstride_q, off_q,
                         lds + (kt % kStages) * kStageBytes + kTileBytes, wave, end_q);
   };
   const FragAddr fadr = frag_addresses<kQKRows>(lane, wm, wn);
@@ -495,13 +493,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     const int kr = min(kt + kStages - 1, KT - 1);
     const uint32_t refill = lds + ((kt + kStages - 1) % kStages) * kStageBytes;
     half(f0, f1, cur, 1, [&](int jj) {
-      issue_tile_part<false>(Pg + k_ofs(kr, kstep_p), ldp, off_p, refill, wave, jj, end_p);
+      issue_tile_part(Pg + k_ofs(kr, kstep_p), jstride_p, off_p, refill, wave, jj, end_p);
     });
     wait_vmem<(kStages - 2) * kLoadsPerStage - kLoadsPerTile>();
     __syncthreads();
     // After the last step this reads a stage of redundant tiles; unused.
     half(f1, f0, nxt, 0, [&](int jj) {
-      issue_tile_part<kQKRows>(Qg + k_ofs(kr, kstep_q), ldq, off_q, refill + kTileBytes, wave, jj, end_q);
+      issue_tile_part(Qg + k_ofs(kr, kstep_q), jstride_q, off_q, refill + kTileBytes, wave, jj, end_q);
     });
   }
 
@@ -529,9 +527,10 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // this lane's accumulator positions (4 consecutive columns per MFMA
   // register group).  X is brought into LDS first, half of the tile's rows
   // at a time (tile rows 128 wm + 32 (yh + yy) + r: 128 rows, 64 KB of high
-  // parts and 32 KB of codes), by DMA in whole 512-byte (256-byte) rows,
+  // parts and 32 KB of codes), by DMA into 512-byte (256-byte) LDS rows,
   // 16-byte unit u of LDS row lr at u ^ (lr & 31) (codes: u ^ (lr & 15)),
-  // the swizzle applied on the global side; each lane then reads its values
+  // the swizzle applied on the global side (in X's panels of 32 columns a
+  // row of the tile is eight 64-byte runs); each lane then reads its values
   // from LDS.  Loading them from global memory at the accumulator positions
   // instead touched 32 rows x 16 bytes per instruction (4.31 ms per
   // 64-matrix launch against 3.64 for the straight update).
@@ -552,6 +551,8 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
     const char* const xl_tile = reinterpret_cast<const char*>(xl + mat * nm + x_off(i0, j0, n_pad));
     [[maybe_unused]] const char* const xh_end = reinterpret_cast<const char*>(in1 + (mat + 1) * nm);
     [[maybe_unused]] const char* const xl_end = reinterpret_cast<const char*>(xl + (mat + 1) * nm);
+    // element offset of tile element (R, C) from the tile's origin (x_off)
+    auto toff = [&](int R, int C) -> int64_t { return (C >> 5) * static_cast<int64_t>(n_pad) * 32 + R * 32 + (C & 31); };
 #pragma unroll
     for (int yh = 0; yh < 4; yh += 2) {
       // LDS row lr = 64 wm' + 32 yy + r holds tile row 128 wm' + 32 (yh + yy) + r
@@ -559,13 +560,13 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
 #pragma unroll
       for (int k = 0; k < 8; ++k) {  // high parts: 64 instructions of 1 KB, 8 per wave
         const int sl = (8 * wave + k) * 64 + lane, lr = sl >> 5, pu = sl & 31;
-        const uint32_t off = static_cast<uint32_t>(tile_row(lr) * 512 + 16 * (pu ^ (lr & 31)));
+        const uint32_t off = static_cast<uint32_t>(2 * toff(tile_row(lr), 8 * (pu ^ (lr & 31))));
         if (MC_GUARD(6, xh_tile + off + 16 <= xh_end)) load_lds16(xh_tile, off, lds + (8 * wave + k) * 1024);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {  // codes: 32 instructions, 4 per wave
         const int sl = (4 * wave + k) * 64 + lane, lr = sl >> 4, pu = sl & 15;
-        const uint32_t off = static_cast<uint32_t>(tile_row(lr) * 256 + 16 * (pu ^ (lr & 15)));
+        const uint32_t off = static_cast<uint32_t>(toff(tile_row(lr), 16 * (pu ^ (lr & 15))));
         if (MC_GUARD(6, xl_tile + off + 16 <= xl_end))
           load_lds16(xl_tile, off, lds + kCodes + (4 * wave + k) * 1024);
       }
@@ -599,8 +600,9 @@ void ns_gemm_kernel(const uint16_t* __restrict__ in0, const uint16_t* __restrict
   // Mode 2, row-ordered epilogue: the accumulators are staged in float32,
   // half of the tile (256 rows x 128 columns, 128 KB) at a time, by the four
   // waves that own those columns; then every lane takes 8 consecutive
-  // columns of a row per pass (16 lanes per row), reads X's two parts there
-  // with 16-byte loads (whole 256-byte row segments per 16 lanes), forms
+  // columns of a row per pass (16 lanes per row, 4 consecutive rows per
+  // wave), reads X's two parts there with 16-byte loads (a wave's 64 lanes
+  // cover 256 contiguous bytes of each of 4 panels of 32 columns), forms
   // X' = xs (a (Xh + Xl) + d_i Xh + N Xh) in float32 and writes X''s two
   // parts, or
   // applies the update / writes the output, with 16-byte accesses.  Staged

@@ -273,9 +273,10 @@ __global__ __launch_bounds__(kThreads) void momentum_prescale_kernel(void* __res
 }
 
 // The same for rows <= cols with 16-byte aligned rows (the common case),
-// with row strips instead of tiles: a block covers 32 rows x 256 columns
-// (one column panel of X), so every row segment it reads is 1 KB of M and
-// of G and every X_0 segment it writes is 512 contiguous bytes of each part.
+// with row strips instead of tiles: a block covers 32 rows x 256 columns,
+// so every row segment it reads is 1 KB of M and of G, and it writes the 32
+// rows of eight 32-column panels of X_0 (x_off): 2 KB of high parts and 1 KB
+// of codes contiguous in each panel.
 // grid (C_pad / 256, R_pad / 32, batch); 8192 elements per block, like the
 // tiles, so the partial-sum count per matrix is the same.  SRC as in
 // momentum_prescale_kernel.
