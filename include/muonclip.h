@@ -251,8 +251,11 @@ MC_API mc_status_t muon_momentum_ns_update_batched(float* M, const float* G, flo
  * call's contents (no part of it needs to start at zero: each call writes
  * every byte it reads).  Calls that overlap in time on one GPU (different
  * streams, or host threads) race on it and give undefined results: order
- * them on one stream.  The first call on a GPU looks up the array's address
- * (hipGetSymbolAddress) with that GPU current; later calls reuse it.
+ * them on one stream.  The GPU of a call is the device of its stream (the
+ * calling thread's current device for the null stream); M, G and W must be
+ * on it.  The first call on a GPU looks up the array's address
+ * (hipGetSymbolAddress) with that GPU made current, then restores the
+ * thread's current device; later calls reuse the address.
  *
  * Arguments, sizes and errors as muon_momentum_ns_update_batched, plus
  * MC_EWORKSPACE when muon_ns_workspace_bytes(batch, rows, cols) exceeds

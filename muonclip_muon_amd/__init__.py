@@ -141,6 +141,19 @@ def _dev(t, name):
     return t
 
 
+def _one_device(stream, *tensors):
+    """Every tensor of a call (None entries skipped), and the stream when one
+    is given, on one device: the kernels run on the stream's device and take
+    the tensors' addresses as they are."""
+    tensors = [t for t in tensors if t is not None]
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"every tensor of the call must be on {dev}, not {t.device}")
+    if stream is not None and stream.device != dev:
+        raise ValueError(f"the stream is on {stream.device}, the tensors on {dev}")
+
+
 def _out(t, name, dtype, numel, device):
     """A caller-supplied output: on the inputs' device, contiguous, of the
     dtype and element count the call writes (the kernels write exactly that
@@ -177,6 +190,7 @@ def _empty(shape, dtype, device, stream):
 def muonclip_momentum(M, G, mu=0.95, stream=None):
     """M <- fl32(fl32(mu * M) + G) in place (float32, any shape)."""
     _dev(M, "M"), _dev(G, "G")
+    _one_device(stream, M, G)
     if M.dtype != torch.float32 or G.dtype != torch.float32 or M.numel() != G.numel():
         raise ValueError("M and G must be float32 tensors with the same number of elements")
     _check("muonclip_momentum", lib.muonclip_momentum(M.data_ptr(), G.data_ptr(), M.numel(), mu,
@@ -255,6 +269,7 @@ def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS
         raise ValueError("O must have M's shape and device")
     c_coeffs = _coeffs(steps, coeffs)
     workspace = _workspace(workspace, batch, rows, cols, M.device, stream)
+    _one_device(stream, M, O, workspace)
     ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_ns_orthogonalize_batched(
         M.data_ptr(), _dtype(M, "M"), batch, rows, cols, rows * cols, O.data_ptr(), _dtype(O, "O"),
@@ -267,6 +282,7 @@ def muon_ns_orthogonalize_batched(M, O=None, steps=NS_STEPS, coeffs=None, eps=NS
 def muon_apply_update(W, O, lr, weight_decay=0.1, stream=None):
     """W <- W - lr * (O + weight_decay * W) in place."""
     _dev(W, "W"), _dev(O, "O")
+    _one_device(stream, W, O)
     if W.numel() != O.numel():
         raise ValueError("W and O must have the same number of elements")
     _check("muon_apply_update", lib.muon_apply_update(W.data_ptr(), _dtype(W, "W"), O.data_ptr(),
@@ -295,6 +311,7 @@ def muon_momentum_ns_update_batched(M, G, W, lr, weight_decay=0.1, mu=0.95, step
         out_scale = OUT_SCALE_RMS_MATCH
     c_coeffs = _coeffs(steps, coeffs)
     workspace = _workspace(workspace, batch, rows, cols, M.device, stream)
+    _one_device(stream, M, G, W, workspace)
     ev = _events(gemm_events, steps, M.device, stream)
     status = lib.muon_momentum_ns_update_batched(
         M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
@@ -318,6 +335,7 @@ def muon_momentum_ns_update_batched_noalloc(M, G, W, lr, weight_decay=0.1, mu=0.
     if M3.dim() != 3:
         raise ValueError("M must be [rows, cols] or [batch, rows, cols]")
     batch, rows, cols = M3.shape
+    _one_device(stream, M, G, W)
     status = lib.muon_momentum_ns_update_batched_noalloc(
         M.data_ptr(), G.data_ptr(), mu, W.data_ptr(), _dtype(W, "W"), batch, rows, cols, rows * cols, steps,
         _coeffs(steps, coeffs), eps, OUT_SCALE_RMS_MATCH if out_scale is None else out_scale, lr, weight_decay,
@@ -348,6 +366,7 @@ def qk_maxlogit(Q, Kc, Kr=None, smax=None, accumulate=False, stream=None):
     if smax is None:
         smax = _empty(H, torch.float32, Q.device, stream)
     _out(smax, "smax", torch.float32, H, Q.device)
+    _one_device(stream, Q, Kc, Kr, smax)
     status = lib.qk_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
                              _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, smax.data_ptr(), int(bool(accumulate)),
                              _stream(Q, stream))
@@ -384,6 +403,7 @@ def attention_fwd_maxlogit(Q, Kc, Kr, V, causal=False, O=None, lse=None, smax=No
     _out(smax, "smax", torch.float32, H, Q.device)
     if lse is not None:
         _out(lse, "lse", torch.float32, B * H * Sq, Q.device)
+    _one_device(stream, Q, Kc, Kr, V, O, lse, smax)
     status = lib.attention_fwd_maxlogit(Q.data_ptr(), Kc.data_ptr(), Kr.data_ptr() if Kr is not None else None,
                                         V.data_ptr(), _dtype(Q, "Q"), B, H, Sq, Sk, d_c, d_r, d_v,
                                         int(bool(causal)), O.data_ptr(), lse.data_ptr() if lse is not None else None,
@@ -441,6 +461,7 @@ def qk_clip_apply_layers(smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_hea
         clipped = _empty((L, H), torch.int32, smax.device, stream)
     _out(gamma, "gamma", torch.float32, L * H, smax.device)
     _out(clipped, "clipped", torch.int32, L * H, smax.device)
+    _one_device(stream, smax, *Wq, *Wk)
     qp = (ctypes.c_void_p * L)(*[w.data_ptr() for w in Wq])
     kp = (ctypes.c_void_p * L)(*[w.data_ptr() for w in Wk])
     status = lib.qk_clip_apply_layers(smax.data_ptr(), L, H, tau, alpha, qp, kp, _dtype(Wq[0], "Wq"), d_in,
@@ -464,6 +485,7 @@ def _qk_clip(fn, smax, Wq, Wk, q_rows_per_head, q_c_rows, k_rows_per_head, tau, 
         clipped = _empty(H, torch.int32, smax.device, stream)
     _out(gamma, "gamma", torch.float32, H, smax.device)
     _out(clipped, "clipped", torch.int32, H, smax.device)
+    _one_device(stream, smax, Wq, Wk)
     status = getattr(lib, fn)(smax.data_ptr(), H, tau, alpha, Wq.data_ptr(), Wk.data_ptr(),
                               _dtype(Wq, "Wq"), d_in, q_rows_per_head, q_c_rows, k_rows_per_head,
                               gamma.data_ptr(), clipped.data_ptr(), _stream(smax, stream))
@@ -478,6 +500,7 @@ def probe_mfma_bf16(workgroups, iters, zero_operands=False, out=None, device=Non
     if out is None:
         out = _empty(workgroups * 256, torch.float32, device or "cuda", stream)
     _dev(out, "out")
+    _one_device(stream, out)
     if out.dtype != torch.float32 or out.numel() < workgroups * 256:
         raise ValueError(f"out must be a float32 tensor of at least {workgroups * 256} elements")
     _check("mc_probe_mfma_bf16", lib.mc_probe_mfma_bf16(workgroups, iters, 1 if zero_operands else 0,
@@ -489,6 +512,7 @@ def probe_copy(src, dst, stream=None):
     """Enqueue the copy probe dst <- src over src's bytes (measurement aid)."""
     _dev(src, "src")
     _dev(dst, "dst")
+    _one_device(stream, src, dst)
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst is smaller than src")

@@ -272,15 +272,27 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-// The current device's address of `scratch` (looked up on the device's first
-// call, with that device current), or null on failure.
-void* static_scratch() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+// The address of `scratch` on the device the kernels of a call on `stream`
+// run on (the stream's device; the current device for the null stream),
+// looked up on that device's first call with that device made current, or
+// null on failure.
+void* static_scratch(hipStream_t stream) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+    dev = static_cast<int>(d);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || !p) return nullptr;
     g_scratch_ptr[dev] = p;
   }
   return g_scratch_ptr[dev];
@@ -314,7 +326,7 @@ mc_status_t muon_momentum_ns_update_batched_noalloc(float* M, const float* G, fl
   if (batch == 0) return MC_OK;
   if (!ns_batch_supported(batch, rows < cols ? rows : cols, rows < cols ? cols : rows)) return MC_ESHAPE;
   if (mc::ns_geometry(batch, rows, cols).total > kStaticScratchBytes) return MC_EWORKSPACE;
-  void* ws = static_scratch();
+  void* ws = static_scratch(static_cast<hipStream_t>(stream));
   if (!ws) return MC_EHIP;
   return fused_muon(M, G, mu, W, w_dtype, batch, rows, cols, batch_stride, steps, coeffs, eps, out_scale, lr,
                     weight_decay, ws, kStaticScratchBytes, stream, nullptr);

@@ -303,3 +303,24 @@ def test_noalloc_validation(mc):
     # a batch whose byte count would wrap is a shape error, not a fit
     assert L.muon_momentum_ns_update_batched_noalloc(FAKE, FAKE, 0.95, FAKE, 1, 1 << 40, 256, 256, 65536, 5,
                                                      coeffs, 1e-7, -1.0, 2e-4, 0.1, None) == ESHAPE
+
+
+def test_binding_keeps_a_call_on_one_device(mc):
+    """The binding rejects a call whose tensors (or whose stream) sit on
+    different devices before anything reaches the library: the kernels run on
+    the stream's device and would take the other device's addresses as they
+    are.  Only each object's device matters to the check."""
+    import torch
+
+    class On:
+        def __init__(self, device):
+            self.device = torch.device(device)
+
+    mc._one_device(None, On("cuda:0"), None, On("cuda:0"))
+    mc._one_device(On("cuda:1"), On("cuda:1"), On("cuda:1"))
+    with pytest.raises(ValueError):
+        mc._one_device(None, On("cuda:0"), On("cuda:1"))
+    with pytest.raises(ValueError):
+        mc._one_device(None, On("cuda:0"), None, On("cuda:0"), On("cuda:2"))
+    with pytest.raises(ValueError):
+        mc._one_device(On("cuda:1"), On("cuda:0"), On("cuda:0"))
