@@ -13,6 +13,7 @@ Agentic Intelligence", section 3.2) on top of them.
 """
 
 import ctypes
+import math
 import os
 
 import torch
@@ -543,31 +544,79 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
     split for every layer).  All layers are clipped in one call.
     Returns (gamma, clipped), shaped like smax; attention None or [] skips
     the clip (smax is then unused) and returns (None, None)."""
+    # Every argument is checked before anything is launched, so an invalid
+    # call leaves every weight and momentum as it was (no partial step).
     entries = []
     for name, W in weights.items():
-        M = momenta.get(name)
-        if M is None:
-            # zero-filled on the launch stream, so the fill is ordered before
-            # the library's first use of it there
+        _dev(W, f"weights[{name!r}]")
+        if W.dim() not in (2, 3):
+            raise ValueError(f"{name}: weights must be [rows, cols] or [count, rows, cols]")
+        _dtype(W, f"weights[{name!r}]")
+        if name not in grads:
+            raise ValueError(f"{name}: no gradient")
+        G, M = grads[name], momenta.get(name)
+        for t, what in ((G, "gradient"), (M, "momentum")):
+            if t is None:
+                continue
+            _dev(t, f"{what} of {name!r}")
+            if t.dtype != torch.float32 or t.shape != W.shape:
+                raise ValueError(f"{name}: the {what} must be float32 of the weight's shape {tuple(W.shape)}")
+        _one_device(stream, W, G, M)
+        entries.append((name, W, G))
+    layers = attention if isinstance(attention, (list, tuple)) else [attention]
+    layers = [] if not layers or layers[0] is None else list(layers)
+    if layers:
+        _dev(smax, "smax")
+        if smax.dim() not in (1, 2) or (smax.dim() == 1 and len(layers) != 1) or (
+                smax.dim() == 2 and smax.shape[0] != len(layers)):
+            raise ValueError("smax needs one row per attention layer")
+        a0 = layers[0]
+        for a in layers:
+            if (a["q_rows_per_head"], a["q_c_rows"], a["k_rows_per_head"]) != (
+                    a0["q_rows_per_head"], a0["q_c_rows"], a0["k_rows_per_head"]):
+                raise ValueError("every attention layer must share the row split")
+            for key in ("q", "k"):
+                if a[key] not in weights:
+                    raise ValueError(f"attention weight {a[key]!r} is not among the weights")
+        H = smax.shape[-1]
+        d_in = weights[a0["q"]].shape[-1]
+        for a in layers:
+            wq, wk = weights[a["q"]], weights[a["k"]]
+            if wq.dtype != weights[a0["q"]].dtype or wk.dtype != wq.dtype:
+                raise ValueError("every W_q / W_k must share a dtype")
+            if wq.numel() != H * a0["q_rows_per_head"] * d_in or wk.numel() != H * a0["k_rows_per_head"] * d_in:
+                raise ValueError(f"attention weights {a['q']!r}, {a['k']!r} do not hold {H} heads of the row split")
+        if not (math.isfinite(tau) and tau > 0 and 0.0 <= alpha <= 1.0):
+            raise ValueError("tau must be finite and positive, alpha in [0, 1]")
+    if not (math.isfinite(lr) and math.isfinite(weight_decay) and math.isfinite(momentum)):
+        raise ValueError("lr, weight_decay and momentum must be finite")
+    if not (1 <= steps <= 64 and math.isfinite(eps) and eps >= 0.0):
+        raise ValueError("steps must be in [1, 64] and eps finite and non-negative")
+    if not all(math.isfinite(x) for x in _coeffs(steps, coeffs)):
+        raise ValueError("the Newton-Schulz coefficients must be finite")
+    shapes = [(W.shape[-2], W.shape[-1], min(chunk, W.shape[0]) if W.dim() == 3 else 1) for _, W, _ in entries]
+    if chunk < 1 or any(b > 0 and muon_ns_workspace_bytes(b, r, c) == 0 for r, c, b in shapes):
+        raise ValueError("a matrix shape or chunk the Newton-Schulz calls do not take")
+    need = max((muon_ns_workspace_bytes(b, r, c) for r, c, b in shapes), default=0)
+    if entries and workspace is not None:
+        _dev(workspace, "workspace")
+        _one_device(stream, entries[0][1], workspace)
+        if _nbytes(workspace) < need:
+            raise ValueError(f"workspace needs {need} bytes")
+    # momenta created as zeros (M_0 = 0), zero-filled on the launch stream so
+    # the fill is ordered before the library's first use of them there
+    for name, W, G in entries:
+        if momenta.get(name) is None:
             M = momenta[name] = _empty(W.shape, torch.float32, W.device, stream)
             if stream is None:
                 M.zero_()
             else:
                 with torch.cuda.stream(stream):
                     M.zero_()
-        G = grads[name]
-        if W.dim() not in (2, 3):
-            raise ValueError(f"{name}: weights must be [rows, cols] or [count, rows, cols]")
-        W3, M3, G3 = (t.unsqueeze(0) if t.dim() == 2 else t for t in (W, M, G))
-        entries.append((name, W3, M3, G3))
-    need = max((muon_ns_workspace_bytes(min(chunk, W3.shape[0]), W3.shape[1], W3.shape[2])
-                for _, W3, _, _ in entries), default=0)
-    if not entries:
-        pass  # no Muon matrix: no workspace
-    elif workspace is None:
+    entries = [(name, *(t.unsqueeze(0) if t.dim() == 2 else t for t in (W, momenta[name], G)))
+               for name, W, G in entries]
+    if entries and workspace is None:
         workspace = _empty(max(need, 1), torch.uint8, next(iter(weights.values())).device, stream)
-    elif _nbytes(workspace) < need:
-        raise ValueError(f"workspace needs {need} bytes")
     O_buf = None
     if not fused and entries:
         o_elems = max((min(chunk, W3.shape[0]) * W3.shape[1] * W3.shape[2] for _, W3, _, _ in entries), default=1)
@@ -586,18 +635,11 @@ def muonclip_step(weights, grads, momenta, smax, attention, lr, weight_decay=0.1
             muon_ns_orthogonalize_batched(M, O, steps=steps, coeffs=coeffs, eps=eps,
                                           out_scale=OUT_SCALE_RMS_MATCH, workspace=workspace, stream=stream)
             muon_apply_update(W, O, lr, weight_decay, stream=stream)
-    layers = attention if isinstance(attention, (list, tuple)) else [attention]
-    if not layers or layers[0] is None:
+    if not layers:
         return None, None  # no attention layer: the Muon part only
     one_layer = smax.dim() == 1
     smax2 = smax.view(1, -1) if one_layer else smax
-    if smax2.shape[0] != len(layers):
-        raise ValueError("smax needs one row per attention layer")
     a0 = layers[0]
-    for a in layers:
-        if (a["q_rows_per_head"], a["q_c_rows"], a["k_rows_per_head"]) != (
-                a0["q_rows_per_head"], a0["q_c_rows"], a0["k_rows_per_head"]):
-            raise ValueError("every attention layer must share the row split")
     gamma, clipped = qk_clip_apply_layers(smax2, [weights[a["q"]] for a in layers], [weights[a["k"]] for a in layers],
                                           a0["q_rows_per_head"], a0["q_c_rows"], a0["k_rows_per_head"], tau, alpha,
                                           stream=stream)

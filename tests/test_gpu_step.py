@@ -147,8 +147,56 @@ def test_step_chunks_share_one_workspace(mc):
     assert torch.equal(Wa["e"].view(torch.int16), Wb.view(torch.int16))
     for i in range(5):
         assert rel_fro(f64(Wc["e"][i]) - f64(W0[i]), f64(Wa["e"][i]) - f64(W0[i])) <= 2e-2
-    with pytest.raises(ValueError):
-        mc.muonclip_step(Wa, {"e": G.to(DEV), "q": Wq, "k": Wq}, {}, smax, att, lr=1.0, chunk=4, workspace=ws)
+    with pytest.raises(ValueError):  # a workspace for chunks of 2, not 4
+        mc.muonclip_step(Wa, {"e": G.to(DEV), "q": torch.zeros(8, 16, device=DEV), "k": torch.zeros(8, 16, device=DEV)},
+                         {}, smax, att, lr=1.0, chunk=4, workspace=ws)
+
+
+def test_invalid_step_changes_nothing(mc):
+    """muonclip_step checks every argument before its first launch, so a call
+    that raises leaves every weight and momentum as it was and creates no
+    momentum (no partial step): attention weights that are missing or do not
+    hold the heads of the row split, an S_max of the wrong shape, a missing
+    or mis-shaped gradient, tau, alpha, lr, steps or coefficients out of
+    range, a workspace too small."""
+    say("invalid step")
+    g = workloads.generator(402, "cpu")
+    W0 = workloads.normal((3, 256, 512), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+    G = workloads.normal((3, 256, 512), 1e-3, g, "cpu").to(DEV)
+    M0 = workloads.normal((3, 256, 512), 1e-3, g, "cpu").to(DEV)
+    Wq0 = workloads.normal((8, 16), 0.02, g, "cpu", torch.bfloat16).to(DEV)
+    zeros = torch.zeros(8, 16, device=DEV)
+    att = dict(q="q", k="k", q_rows_per_head=8, q_c_rows=8, k_rows_per_head=8)
+    smax = torch.full((1,), 1000.0, device=DEV)
+    grads = {"e": G, "q": zeros, "k": zeros}
+    small_ws = torch.empty(mc.muon_ns_workspace_bytes(1, 256, 512), dtype=torch.uint8, device=DEV)
+    cases = {
+        "unknown weight": dict(attention=dict(att, k="v")),
+        "row split": dict(attention=dict(att, k_rows_per_head=4)),
+        "smax heads": dict(smax=torch.full((2,), 1000.0, device=DEV)),
+        "smax layers": dict(smax=torch.full((2, 1), 1000.0, device=DEV)),
+        "no gradient": dict(grads={"e": G, "q": zeros}),
+        "gradient shape": dict(grads={"e": G[:2], "q": zeros, "k": zeros}),
+        "gradient dtype": dict(grads={"e": G.bfloat16(), "q": zeros, "k": zeros}),
+        "tau": dict(tau=0.0),
+        "alpha": dict(alpha=1.5),
+        "lr": dict(lr=float("nan")),
+        "steps": dict(steps=0),
+        "coefficients": dict(coeffs=((3.4445, float("inf"), 2.0315),) * 5),
+        "workspace": dict(workspace=small_ws),
+    }
+    for name, over in cases.items():
+        W = {"e": W0.clone(), "q": Wq0.clone(), "k": Wq0.clone()}
+        M = {"e": M0.clone()}
+        kw = dict(weights=W, grads=grads, momenta=M, smax=smax, attention=att, lr=2e-4)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            mc.muonclip_step(**kw)
+        torch.cuda.synchronize()
+        assert torch.equal(W["e"].view(torch.int16), W0.view(torch.int16)), name
+        assert torch.equal(W["q"].view(torch.int16), Wq0.view(torch.int16)), name
+        assert torch.equal(W["k"].view(torch.int16), Wq0.view(torch.int16)), name
+        assert torch.equal(M["e"], M0) and set(M) == {"e"}, name
 
 
 def test_resume_from_saved_state_is_bit_exact(mc):
