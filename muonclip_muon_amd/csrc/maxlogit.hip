@@ -62,6 +62,20 @@ __device__ __forceinline__ void load_lds16(const char* g_uniform, uint32_t lane_
 }
 #pragma clang diagnostic pop
 
+// Position of 16-byte unit u in key row r of a row of U units.  A fragment
+// read (ds_read_b128) serves 16 lanes per cycle, which read one unit of 16
+// consecutive rows, so those 16 reads must fall in 16 different 16-byte bank
+// groups of the 256-byte bank row: 256-byte rows (U = 16) take u ^ (r & 15);
+// rows of 128 or 384 bytes (U = 8, 24), where consecutive rows alternate
+// between the two halves of a bank row, take u ^ ((r / 2) & 7), which stays
+// inside u's aligned group of 8 units.
+template <int U>
+__device__ __forceinline__ int kswz(int u, int r) {
+  static_assert(U == 1 || U == 16 || U % 16 == 8, "rows of 256 bytes or an odd multiple of 128 bytes");
+  if constexpr (U == 1) return u;  // no such part (the loops over it are empty)
+  else return U == 16 ? (u ^ (r & 15)) : (u ^ ((r >> 1) & 7));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
@@ -70,9 +84,11 @@ __device__ __forceinline__ void wait_vmem() {
 
 // Key stage: the 64 key rows' own parts (Kc, DC elements each) in one region
 // and their shared rotary parts (Kr, DR each) in another, each row-major; a
-// 16-byte unit u of row r sits at position u ^ (r & 7) of its row (a
-// permutation inside each aligned group of 8 units), so a fragment read of 32
-// consecutive rows at one unit spreads over 8 bank groups.  Every DMA
+// 16-byte unit u of row r sits at position kswz(u, r) of its row (above), so
+// the 16 lanes of a fragment read that one cycle serves hit 16 different
+// bank groups (SQ_LDS_BANK_CONFLICT 0; with u ^ (r & 7) rows r and r + 8
+// shared one and the counter read 4 cycles per LDS instruction, yet the
+// kernel was only 0.4 % slower: its LDS reads are not what bounds it).  Every DMA
 // instruction then reads whole rows of one source: 1 KB = 1024 / (2 DC) rows
 // of Kc, or 1024 / (2 DR) rows of Kr.
 template <int DC, int DR>
@@ -109,19 +125,19 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   // ---- key loads.  DMA instruction l of this wave fills 1 KB at region
   // offset 1024 (wave + 4 l); its lane slot p = 64 (wave + 4 l) + lane holds
-  // row r = p / units, unit (p % units) ^ (r & 7).  Lane offsets are relative
+  // row r = p / units, unit kswz(p % units, r).  Lane offsets are relative
   // to key row j0 of the block, which moves with the uniform base.
   uint32_t off_c[kLoadsC > 0 ? kLoadsC : 1], off_r[kLoadsR > 0 ? kLoadsR : 1];
 #pragma unroll
   for (int l = 0; l < kLoadsC; ++l) {
     const int p = 64 * (wave + 4 * l) + lane;
-    const int r = p / kUc, u = (p % kUc) ^ (r & 7);
+    const int r = p / kUc, u = kswz<kUc>(p % kUc, r);
     off_c[l] = static_cast<uint32_t>((r * DC + 8 * u) * 2);
   }
 #pragma unroll
   for (int l = 0; l < kLoadsR; ++l) {
     const int p = 64 * (wave + 4 * l) + lane;
-    const int r = p / kUrNz, u = (p % kUrNz) ^ (r & 7);
+    const int r = p / kUrNz, u = kswz<kUrNz>(p % kUrNz, r);
     off_r[l] = static_cast<uint32_t>((r * DR + 8 * u) * 2);
   }
   const int NJ = (Sk + kKeys - 1) / kKeys;
@@ -195,8 +211,8 @@ void maxlogit_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int row = u * 32 + frag_row;
     // 2 s < DC / 8 decides the part at compile time (both parts hold an even
     // number of units)
-    const uint32_t a = (2 * s < kUc) ? stage + row * (2 * DC) + 16 * (unit ^ (row & 7))
-                                     : stage + kKcBytes + row * (2 * DR) + 16 * ((unit - kUc) ^ (row & 7));
+    const uint32_t a = (2 * s < kUc) ? stage + row * (2 * DC) + 16 * kswz<kUc>(unit, row)
+                                     : stage + kKcBytes + row * (2 * DR) + 16 * kswz<kUrNz>(unit - kUc, row);
     return as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
   };
 

@@ -204,6 +204,8 @@ MAXLOGIT_CASES = [
     (torch.bfloat16, 1, 2, 513, 65, 64, 0),
     (torch.bfloat16, 1, 2, 1024, 1024, 128, 0),
     (torch.bfloat16, 1, 1, 1, 1, 128, 64),
+    (torch.bfloat16, 1, 2, 300, 333, 192, 0),  # 384-byte key rows
+    (torch.bfloat16, 2, 2, 200, 129, 64, 64),  # 128-byte rows in both key parts
     (torch.bfloat16, 2, 2, 77, 90, 64, 16),   # d = 80: generic kernel
     (torch.float32, 2, 4, 128, 128, 64, 0),   # the tiny fp32 attention layer's shape
     (torch.float32, 1, 3, 100, 37, 96, 32),
