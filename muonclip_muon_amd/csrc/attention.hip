@@ -92,9 +92,17 @@ __device__ __forceinline__ void halves(float x, float& a, float& b) {
 }
 
 // LDS layout of a stage: K rows (the Kc part, then the Kr part, each its own
-// row-major region; 16-byte unit u of row r at position u ^ (r & 7)), then V
-// rows (row-major, unit u of row r at u ^ vswz(r)).  vswz spreads the 4 rows a
-// transposed read touches (rows r .. r + 3, r % 4 == 0) over different banks.
+// row-major region; 16-byte unit u of row r at position kswz(u, r, units)),
+// then V rows (row-major, unit u of row r at u ^ vswz(r)).  A key fragment
+// read (ds_read_b128) serves 16 lanes per cycle, one unit of 16 consecutive
+// rows, so kswz puts those in 16 different 16-byte bank groups of a 256-byte
+// bank row: u ^ (r & 15) for 256-byte rows, u ^ ((r / 2) & 7) for 128-byte
+// rows (consecutive rows alternate between the halves of a bank row).  vswz
+// spreads the 4 rows a transposed read touches (rows r .. r + 3, r % 4 == 0)
+// over different banks.
+__device__ __forceinline__ int kswz(int u, int r, int units) {
+  return units == 16 ? (u ^ (r & 15)) : units == 8 ? (u ^ ((r >> 1) & 7)) : u;
+}
 template <int DV>
 __device__ __forceinline__ int vswz(int r) {
   return DV == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
@@ -164,7 +172,7 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   auto lane_off = [&](int units, int row_elems, int kind) -> uint32_t {
     const int p = 64 * wave + lane;
     const int r = p / units;
-    const int u = (p % units) ^ (kind == 2 ? vswz<DV>(r) : (r & 7));
+    const int u = kind == 2 ? (p % units) ^ vswz<DV>(r) : kswz(p % units, r, units);
     return static_cast<uint32_t>((r * row_elems + 8 * u) * 2);
   };
   const uint32_t lo_c = lane_off(kUc, DC, 0), lo_r = lane_off(kUr > 0 ? kUr : 1, DR, 1), lo_v = lane_off(kUv, DV, 2);
@@ -211,16 +219,17 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   // Per-lane LDS read offsets with everything that is a compile-time constant
   // left out: K fragments (row lane % 32, unit 2 s + half) repeat their
-  // swizzle every 4 k-steps (the XOR touches the low 3 bits of the unit), so
-  // 4 offsets per K part cover every step (+128 bytes per 4 steps, + 32 rows
+  // swizzle every 4 k-steps: in a 256-byte row k-steps 4..7 are units 8..15,
+  // which kswz puts at the offset of units 0..7 with bit 7 flipped, so 4
+  // offsets per K part cover every step (XOR 128 for steps 4..7, + 32 rows
   // per phase); V transposed reads depend on the column tile only (the
   // phase, k16 step and upper rows are whole multiples of 4 rows).
   uint32_t kc_off[4], kr_off[4], v_off[kDt];
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
     const int unit = 2 * s4 + frag_half;
-    kc_off[s4] = frag_row * (2 * DC) + 16 * (unit ^ (frag_row & 7));
-    kr_off[s4] = kKcBytes + frag_row * (2 * DR) + 16 * (unit ^ (frag_row & 7));
+    kc_off[s4] = frag_row * (2 * DC) + 16 * kswz(unit, frag_row, kUc);
+    kr_off[s4] = kKcBytes + frag_row * (2 * DR) + 16 * kswz(unit, frag_row, kUr);
   }
   {
     const int g = lane >> 4, il = lane & 15;
@@ -244,8 +253,8 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int s = 0; s < kSteps; ++s) {
       // 2 s < DC / 8 decides the part at compile time
       const int sp = (2 * s < kUc) ? s : s - kUc / 2;  // k-step within the part
-      const uint32_t a = (2 * s < kUc) ? st + kc_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DC)
-                                       : st + kr_off[sp & 3] + 128 * (sp >> 2) + u * 32 * (2 * DR);
+      const uint32_t a = (2 * s < kUc) ? st + (kc_off[sp & 3] ^ (128 * (sp >> 2))) + u * 32 * (2 * DC)
+                                       : st + (kr_off[sp & 3] ^ (128 * (sp >> 2))) + u * 32 * (2 * DR);
       const bf16x8 kf = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)a);
 #pragma unroll
       for (int t = 0; t < 2; ++t) S[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t][s], S[t], 0, 0, 0);
@@ -351,8 +360,8 @@ void attention_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int n_items = (mask ? 4 : 0) + 4 + 16;
     auto kaddr = [&](int s) -> uint32_t {
       const int sp = (2 * s < kUc) ? s : s - kUc / 2;  // k-step within the part
-      return (2 * s < kUc) ? st + kc_off[sp & 3] + 128 * (sp >> 2) + u_next * 32 * (2 * DC)
-                           : st + kr_off[sp & 3] + 128 * (sp >> 2) + u_next * 32 * (2 * DR);
+      return (2 * s < kUc) ? st + (kc_off[sp & 3] ^ (128 * (sp >> 2))) + u_next * 32 * (2 * DC)
+                           : st + (kr_off[sp & 3] ^ (128 * (sp >> 2))) + u_next * 32 * (2 * DR);
     };
     bf16x8 kf[3];
     kf[0] = as_bf16x8(*(const lds_u32x4_t*)(uintptr_t)kaddr(0));
