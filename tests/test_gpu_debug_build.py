@@ -6,8 +6,8 @@ return MC_ECHECK (the binding raises), undefined behaviour in host code
 aborts the child, and the results must still match the oracle as in the
 release build.  The small and ragged cases of the parity, step, attention
 and stream tests, the empty and degenerate calls, the largest Newton-Schulz
-shapes, and the fused call at the full step's shapes (expert batches, W_q,
-W_kc, W_kr)."""
+shapes, the fused call at the full step's shapes (expert batches, W_q,
+W_kc, W_kr), strided batches and the seeded random shapes."""
 
 import os
 import subprocess
@@ -30,7 +30,7 @@ def test_gpu_suite_under_the_debug_build():
     args = [sys.executable, "-u", "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "gpu",
             "tests/test_gpu_parity.py", "tests/test_gpu_step.py", "tests/test_gpu_attention.py",
             "tests/test_gpu_streams.py", "tests/test_gpu_edges.py", "tests/test_gpu_maxsize.py",
-            "tests/test_gpu_fullsize.py",
+            "tests/test_gpu_fullsize.py", "tests/test_gpu_strided.py", "tests/test_gpu_shape_sweep.py",
             "-k", "not fullsize_8x4096 and (not test_gpu_fullsize or fused_expert_batch)"]
     r = subprocess.run(args, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     tail = r.stdout[-4000:] + r.stderr[-4000:]
